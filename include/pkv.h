@@ -1,0 +1,280 @@
+/*
+ * pkv.h — paged KV-cache attention for AMD MI355X (gfx950): the C ABI.
+ *
+ * What the library computes. New queries attend to keys and values that a
+ * sequence has cached, stored in fixed-size blocks of a shared pool and found
+ * through the sequence's block table, with an online (running max / running
+ * sum) softmax. Sources, by page title and section:
+ *   [P1] "04. 注意力与 KV 缓存" (niuwancheng.cn, inference series 04)
+ *   [P2] "07｜KV Cache、FlashAttention与PagedAttention的内部过程"
+ *        (ai-engineering-handbook.eonloom.com, chapter 07), Q025–Q028
+ *   [P3] "06 KV Cache、Prefix Cache、PagedAttention 与 vLLM", sections 6.1–6.7
+ *   [P4] "03. KV Cache：用显存换计算" (niuwancheng.cn, llm-inference 03)
+ *
+ * Conventions for every call:
+ *   - Every call returns a pkv_status (0 = ok, negative = error); the reason
+ *     of the last failure on the calling thread is in pkv_last_error().
+ *     No C++ exception crosses this boundary.
+ *   - Device pointers are caller-owned (allocated by the caller, e.g. by
+ *     PyTorch). The library never allocates or frees device memory.
+ *   - Kernels are launched asynchronously on the caller's stream (a
+ *     hipStream_t passed as void*; NULL is the default stream). The caller
+ *     owns synchronisation. A launch failure returns PKV_EHIP.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing. Table ids and lengths that live in
+ *     device memory are not read on the host unless the environment sets
+ *     PKV_CHECK=1, in which case they are copied back (synchronously) and
+ *     range-checked first. Without that check, kernels still never touch
+ *     memory outside the pool: an out-of-range block id contributes nothing
+ *     and an out-of-range slot is skipped.
+ *   - Pool layout: K and V each [num_blocks, num_kv_heads, block_size,
+ *     head_dim], row-major, in the cache dtype. The flat slot of a token is
+ *     physical_block * block_size + offset ([P2] Q028 block-size-4 table).
+ *   - GQA grouping: query head h reads KV head h / (Hq / Hkv) (contiguous
+ *     groups; [P3] 6.3 says query heads share KV heads without fixing the
+ *     order). MHA has Hq == Hkv, MQA has Hkv == 1.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_API __attribute__((visibility("default")))
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,      /* bad shape, size, pointer or id                      */
+  PKV_ENOBLOCKS = -2,   /* allocator: not enough free blocks (state unchanged) */
+  PKV_EDTYPE = -3,      /* unsupported dtype combination                       */
+  PKV_EREF = -4,        /* allocator: reference count misuse                   */
+  PKV_EWORKSPACE = -5,  /* workspace missing or too small                      */
+  PKV_EHIP = -6         /* a HIP runtime call or kernel launch failed          */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2      /* OCP e4m3fn bytes with one fp32 scale per KV head    */
+} pkv_dtype;
+
+typedef void* pkv_stream;   /* a hipStream_t */
+
+/* One layer's paged cache. Borrowed: the library keeps no pointer past a call.
+ * Supported: block_size 16; head_dim 64 or 128; dtype F32, BF16 or FP8_E4M3.
+ * k_scale/v_scale: device fp32 [num_kv_heads], the dequantisation scale of
+ * each KV head (stored byte decoded, times scale, is the value attended to);
+ * required for FP8_E4M3, ignored otherwise. */
+typedef struct pkv_cache {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;            /* pkv_dtype of the stored values */
+  void* k_cache;            /* device */
+  void* v_cache;            /* device */
+  const float* k_scale;     /* device [num_kv_heads] or NULL */
+  const float* v_scale;     /* device [num_kv_heads] or NULL */
+} pkv_cache;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+PKV_API int32_t pkv_version(void);
+
+/* Reason for the last non-OK status returned on this thread ("" if none).
+ * The string stays valid until the next pkv_* call on the same thread. */
+PKV_API const char* pkv_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Slot mapping — [P2] Q028, table "which physical slot logical position 5
+ * maps to": a logical position p lives in logical block p / bs at offset
+ * p % bs; the block table names the physical block; [P3] 6.5 gives the same
+ * flow (position → logical block and offset → kernel reads through the table).
+ * slot = block_table[p / bs] * bs + p % bs.
+ * ------------------------------------------------------------------------- */
+
+/* Host helper. block_table: host int32 [table_len]; writes n slots for the
+ * positions first_pos … first_pos+n-1 into host out_slots[n].
+ * PKV_EINVAL if a position falls beyond table_len blocks or on a negative
+ * table entry, or if block_size <= 0 / n < 0 / first_pos < 0. */
+PKV_API int pkv_slot_mapping(const int32_t* block_table, int32_t table_len, int32_t block_size,
+                             int32_t first_pos, int32_t n, int32_t* out_slots);
+
+/* Device variant for a batch. Sequence s appends new tokens
+ * cu_new[s] … cu_new[s+1]-1 at logical positions first_pos[s], first_pos[s]+1, …
+ *   block_tables: device int32 [num_seqs, max_blocks] (−1 = unused entry)
+ *   cu_new:       device int32 [num_seqs + 1], nondecreasing, cu_new[0] = 0
+ *   first_pos:    device int32 [num_seqs]
+ *   out_slots:    device int32 [n_tokens] (n_tokens = cu_new[num_seqs])
+ * A token whose logical block is beyond max_blocks or whose table entry is
+ * negative gets slot −1 (skipped by pkv_kv_append). */
+PKV_API int pkv_slot_mapping_device(const int32_t* block_tables, int32_t max_blocks,
+                                    int32_t block_size, int32_t num_seqs, const int32_t* cu_new,
+                                    const int32_t* first_pos, int32_t n_tokens,
+                                    int32_t* out_slots, pkv_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * KV append — [P2] Q025 core answer and "generate a new token" paragraph:
+ * in every layer the new token's k and v are appended to that layer's cache
+ * before its query attends; [P3] 6.1 (compute q/k/v → rotate → append k/v →
+ * attend); [P4] lifecycle stage "fill" (prefill writes the prompt's K/V, each
+ * decode step appends one token's).
+ *
+ * k_new, v_new: device [n_tokens, num_kv_heads, head_dim] in in_dtype.
+ * slot_mapping: device int32 [n_tokens]; slot −1 (or any slot outside the
+ *   pool) skips the token.
+ * Stored value: F32→F32 and BF16→BF16 copy bit for bit; BF16 or F32 input
+ *   into an FP8_E4M3 cache stores e4m3(fp32(x) · inv_scale[h]) with round to
+ *   nearest even and saturation at ±448 (NaN stays NaN).
+ * k_inv_scale, v_inv_scale: device fp32 [num_kv_heads], FP8 caches only
+ *   (normally fp32(1 / scale) so that dequantisation inverts quantisation).
+ * Two tokens with the same slot in one call race (the pages never write one
+ * slot twice in a step). */
+PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void* v_new,
+                          int32_t in_dtype, int32_t n_tokens, const int32_t* slot_mapping,
+                          const float* k_inv_scale, const float* v_inv_scale,
+                          pkv_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged decode attention with split-KV — [P2] Q027 (online softmax: running
+ * max m, sum l = Σ exp(s−m), weighted sum u = Σ exp(s−m)·v, output u/l, and
+ * the merge that rescales old statistics by exp(m_old − m_new)); [P2] Q028
+ * and [P3] 6.5 (the kernel reads K/V through the block table); [P1] formula
+ * section and [P4] formula section (softmax(QKᵀ/√d + causal mask)·V).
+ *
+ * Each sequence b has one new query per head at logical position
+ * seq_lens[b] − 1 and attends to all seq_lens[b] cached tokens (its own
+ * just-appended K/V included). seq_lens[b] == 0 writes zeros.
+ *   q:            device [batch, num_q_heads, head_dim] in q_dtype
+ *                 (F32 for an F32 cache; BF16 for BF16 and FP8 caches)
+ *   block_tables: device int32 [batch, max_blocks]
+ *   seq_lens:     device int32 [batch]; values above max_seq_len are clamped
+ *   max_seq_len:  host bound on seq_lens (sizes the grid and the workspace)
+ *   scale:        score scale (1/sqrt(head_dim) for standard attention)
+ *   partition_tokens: tokens per split-KV partition, a multiple of
+ *                 block_size in [16, 1024]; 0 picks one from the shape
+ *   out:          device fp32 [batch, num_q_heads, head_dim]
+ *   workspace:    device, at least pkv_attn_decode_workspace_bytes(...)
+ *                 bytes for the same arguments; may be NULL when that size
+ *                 is 0 (a single partition covers max_seq_len). Partial
+ *                 results fill it from the front; merge counters (one int32
+ *                 per sequence and query head) occupy its last bytes. It must
+ *                 be zero-filled before first use; every completed call
+ *                 leaves the counters at zero, so a buffer sized for the
+ *                 largest batch·num_q_heads and the largest max_seq_len it
+ *                 serves can be reused without clearing. Calls that share a
+ *                 workspace must not overlap (one workspace per stream).
+ * num_q_heads must be a multiple of num_kv_heads with Hq/Hkv <= 64. */
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t max_seq_len,
+                                               int32_t partition_tokens);
+
+PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype,
+                            int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                            float scale, int32_t partition_tokens, float* out,
+                            void* workspace, size_t workspace_bytes, pkv_stream stream);
+
+/* The partition size pkv_attn_decode uses when partition_tokens is 0. */
+PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads,
+                                               int32_t max_seq_len);
+
+/* ---------------------------------------------------------------------------
+ * Causal chunked prefill over a cached prefix — [P3] 6.6 (long prefills are
+ * split into chunks so decodes are not starved); [P2] Q027 core answer and
+ * FlashAttention section (tiles of query rows, scale and mask fused, scores
+ * and probabilities kept on chip, the same exact result); [P2] Q025 table
+ * row 2 (a position sees itself and everything before it).
+ *
+ * Sequence s has C_s = q_start[s+1] − q_start[s] new queries whose K/V are
+ * already appended; with T_s = seq_lens[s] cached tokens in total, query i
+ * sits at position T_s − C_s + i and attends to keys 0 … T_s − C_s + i.
+ *   q:        device [q_start[num_seqs], num_q_heads, head_dim], BF16
+ *   q_start:  device int32 [num_seqs + 1], nondecreasing, q_start[0] = 0
+ *   seq_lens: device int32 [num_seqs], T_s >= C_s
+ *   max_q_len: host bound on C_s (sizes the grid)
+ *   out:      device fp32, same shape as q
+ * Cache dtype BF16; head_dim 64 or 128; Hq/Hkv in {1, 2, 4, 8, 16, 32}.
+ * No workspace is needed (pass NULL, 0). */
+PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
+                                   int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
+                                   const int32_t* block_tables, int32_t max_blocks,
+                                   const int32_t* seq_lens, int32_t max_q_len, float scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   pkv_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Copy-on-write block copy — [P2] Q028 (sharing a partly filled last block
+ * and then writing to it needs a copy, or one sequence's append corrupts the
+ * other's; table row 6); [P3] 6.5 (copy-on-write with reference counts).
+ * Copies whole blocks (K and V, every head): src[i] → dst[i].
+ *   src, dst: device int32 [n]; ids outside the pool are skipped.
+ * Destinations must be distinct and must not also be sources. */
+PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const int32_t* dst,
+                            int32_t n, pkv_stream stream);
+
+/* Test aid: read one sequence back through its table into the semantic
+ * layout [num_kv_heads, seq_len, head_dim] of the stored dtype ([P2] Q025:
+ * K and V each [B, H_kv, T, Dh]; Q028: paging changes placement, not order).
+ *   block_table: device int32 [ceil(seq_len / block_size)]
+ *   k_out, v_out: device, num_kv_heads*seq_len*head_dim stored elements. */
+PKV_API int pkv_debug_gather(const pkv_cache* cache, const int32_t* block_table,
+                             int32_t seq_len, void* k_out, void* v_out, pkv_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator — [P2] Q028 core answer and follow-ups (allocate
+ * blocks on demand, return them to the pool when released, share identical
+ * prefixes with reference counts, copy-on-write for a shared partial tail);
+ * [P3] 6.5 (the request flow); [P1] engine section (a finished request must
+ * not free pages another request still uses). Never touches device memory.
+ *
+ * Single-threaded: calls on one allocator must not overlap. Every call is
+ * all-or-nothing: on error the allocator state is unchanged. Free blocks form
+ * a LIFO stack; the first allocations return free_order[0], free_order[1], …
+ * (or 0, 1, 2, … when free_order is NULL). Only full blocks should be shared;
+ * a shared partial tail is copied on the next append.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_alloc pkv_alloc;
+
+/* free_order: host int32 [num_blocks], a permutation of 0..num_blocks−1, or NULL. */
+PKV_API int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                             pkv_alloc** out);
+PKV_API void pkv_alloc_destroy(pkv_alloc* a);
+
+/* Take n blocks (refcount 1 each) into host out_ids[n]; PKV_ENOBLOCKS if
+ * fewer than n are free. */
+PKV_API int pkv_alloc_allocate(pkv_alloc* a, int32_t n, int32_t* out_ids);
+
+/* Add one reference to each listed live block (sharing a prefix).
+ * PKV_EINVAL for an id outside the pool, PKV_EREF for a free block. */
+PKV_API int pkv_alloc_incref(pkv_alloc* a, const int32_t* ids, int32_t n);
+
+/* Drop one reference per listing; a block returns to the pool at zero.
+ * PKV_EREF if a block would drop below zero (duplicates count). */
+PKV_API int pkv_alloc_decref(pkv_alloc* a, const int32_t* ids, int32_t n);
+
+/* Reference count of a block (>= 0), or PKV_EINVAL. */
+PKV_API int pkv_alloc_refcount(const pkv_alloc* a, int32_t id);
+PKV_API int32_t pkv_alloc_num_free(const pkv_alloc* a);
+
+/* Make the host block_table [max_blocks] of a sequence holding seq_len tokens
+ * cover positions seq_len … seq_len+n_new−1: new blocks are allocated when a
+ * position crosses into an unallocated block ([P2] Q028: positions 10 and 11
+ * fill block 19, position 12 needs a new block), and a shared partially
+ * filled tail is replaced by a private copy first. The copy is reported in
+ * cow_src[0]/cow_dst[0] (host, capacity >= 1) with *n_cow = 1 (else 0); the
+ * caller must run pkv_copy_blocks for it before appending.
+ * PKV_EINVAL if the table would exceed max_blocks or holds an invalid id
+ * within its first ceil(seq_len/bs) entries; PKV_ENOBLOCKS if the pool is short. */
+PKV_API int pkv_alloc_reserve_append(pkv_alloc* a, int32_t* block_table, int32_t max_blocks,
+                                     int32_t seq_len, int32_t n_new, int32_t* cow_src,
+                                     int32_t* cow_dst, int32_t* n_cow);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

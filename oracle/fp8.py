@@ -94,3 +94,25 @@ def dequantize(codes, scale):
     """Value the attention sees for stored bytes: decode(code) · scale, in float64."""
     table = decode_table()
     return table[np.asarray(codes, dtype=np.int64)] * np.float64(np.float32(scale))
+
+
+def _bf16_values():
+    """float32 value of every 16-bit bf16 pattern (pattern << 16 reinterpreted)."""
+    bits = (np.arange(65536, dtype=np.uint32) << 16).astype(np.uint32)
+    return bits.view(np.float32)
+
+
+_TABLES = {}
+
+
+def quantize_bf16_bits(bits, inv_scale):
+    """quantize() for bf16 inputs given as raw uint16 patterns. Same definition,
+    evaluated once for each of the 65536 patterns and then looked up, so large
+    caches quantise in reasonable time."""
+    key = float(np.float32(inv_scale))
+    table = _TABLES.get(key)
+    if table is None:
+        with np.errstate(over="ignore", invalid="ignore"):
+            table = quantize(_bf16_values(), np.float32(inv_scale))
+        _TABLES[key] = table
+    return table[np.asarray(bits, dtype=np.uint16).astype(np.int64)]

@@ -1,0 +1,283 @@
+"""Python binding for libpkv.so, the gfx950 paged KV-cache attention library.
+
+Argument marshalling only: every function here forwards torch tensors'
+device pointers and the current HIP stream to the C entry point of the same
+name (declared in include/pkv.h) and raises PKVError on a non-zero status.
+All computation happens in the library's HIP kernels; there is no fallback —
+if libpkv.so is missing or fails to load, importing the binding's functions
+raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PKVError", "Cache", "BlockAllocator", "load",
+    "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append",
+    "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
+    "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_debug_gather",
+    "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_EDTYPE, PKV_EREF, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4, -5, -6
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+STATUS_NAMES = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ENOBLOCKS", -3: "PKV_EDTYPE",
+                -4: "PKV_EREF", -5: "PKV_EWORKSPACE", -6: "PKV_EHIP"}
+
+
+class PKVError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _CacheStruct(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "pkv_version": (_I32, []),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_slot_mapping": (ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP]),
+    "pkv_slot_mapping_device": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
+    "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "pkv_attn_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32]),
+    "pkv_attn_decode": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32, _VP,
+                                       _I32, ctypes.c_float, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
+    "pkv_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _VP,
+                                              _I32, _VP, _I32, ctypes.c_float, _VP, _VP, ctypes.c_size_t, _VP]),
+    "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP]),
+    "pkv_debug_gather": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, _VP, _VP]),
+    "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _VP, ctypes.POINTER(_VP)]),
+    "pkv_alloc_destroy": (None, [_VP]),
+    "pkv_alloc_allocate": (ctypes.c_int, [_VP, _I32, _VP]),
+    "pkv_alloc_incref": (ctypes.c_int, [_VP, _VP, _I32]),
+    "pkv_alloc_decref": (ctypes.c_int, [_VP, _VP, _I32]),
+    "pkv_alloc_refcount": (ctypes.c_int, [_VP, _I32]),
+    "pkv_alloc_num_free": (_I32, [_VP]),
+    "pkv_alloc_reserve_append": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libpkv.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python __graft_entry__.py` "
+                               "(or paged_kv_cache_430_amd/_build.py) first")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != PKV_OK:
+        raise PKVError(status, load().pkv_last_error().decode())
+    return status
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise PKVError(PKV_EDTYPE, f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise PKVError(PKV_EINVAL, "tensors passed to the library must be contiguous")
+        return t.data_ptr()
+    return t
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _i32_host(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Cache:
+    """One layer's paged cache: K and V pools [num_blocks, Hkv, 16, Dh] in
+    f32, bf16 or e4m3 bytes (uint8), plus per-KV-head fp32 scales for e4m3."""
+
+    def __init__(self, k_cache, v_cache, k_scale=None, v_scale=None):
+        if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+            raise PKVError(PKV_EINVAL, "k_cache and v_cache must both be [num_blocks, Hkv, block_size, Dh]")
+        self.k, self.v, self.k_scale, self.v_scale = k_cache, v_cache, k_scale, v_scale
+        nb, hkv, bs, dh = k_cache.shape
+        self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = nb, hkv, bs, dh
+        self.dtype = _dtype_code(k_cache)
+        self._s = _CacheStruct(nb, bs, hkv, dh, self.dtype, _ptr(k_cache), _ptr(v_cache),
+                               _ptr(k_scale), _ptr(v_scale))
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def pkv_version():
+    return load().pkv_version()
+
+
+def pkv_slot_mapping(block_table, block_size, first_pos, n):
+    """Host slots for n positions from first_pos (numpy int32)."""
+    bt = _i32_host(block_table)
+    out = np.empty(n, dtype=np.int32)
+    _check(load().pkv_slot_mapping(bt.ctypes.data, len(bt), block_size, first_pos, n, out.ctypes.data))
+    return out
+
+
+def pkv_slot_mapping_device(block_tables, cu_new, first_pos, n_tokens, block_size=16, out=None, stream=None):
+    dev = block_tables.device
+    if out is None:
+        out = torch.empty(n_tokens, dtype=torch.int32, device=dev)
+    _check(load().pkv_slot_mapping_device(_ptr(block_tables), block_tables.shape[1], block_size,
+                                          len(first_pos), _ptr(cu_new), _ptr(first_pos), n_tokens,
+                                          _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def pkv_kv_append(cache, k_new, v_new, slot_mapping, k_inv_scale=None, v_inv_scale=None, stream=None):
+    _check(load().pkv_kv_append(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), k_new.shape[0],
+                                _ptr(slot_mapping), _ptr(k_inv_scale), _ptr(v_inv_scale),
+                                _stream(stream, cache.device)))
+
+
+def pkv_attn_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len, partition_tokens=0):
+    return load().pkv_attn_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len, partition_tokens)
+
+
+def pkv_attn_decode_auto_partition(batch, num_q_heads, max_seq_len):
+    return load().pkv_attn_decode_auto_partition(batch, num_q_heads, max_seq_len)
+
+
+def decode_workspace(batch, num_q_heads, head_dim, max_seq_len, partition_tokens, device):
+    """A zero-filled workspace of the size pkv_attn_decode needs (or None)."""
+    n = pkv_attn_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len, partition_tokens)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pkv_attn_decode(cache, q, block_tables, seq_lens, max_seq_len, scale, partition_tokens=0,
+                    out=None, workspace=None, stream=None):
+    b, hq, dh = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty(b, hq, dh, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = decode_workspace(b, hq, dh, max_seq_len, partition_tokens, dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pkv_attn_decode(cache.ref(), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
+                                  partition_tokens, _ptr(out), _ptr(workspace), wbytes, _stream(stream, dev)))
+    return out
+
+
+def pkv_attn_prefill_chunk(cache, q, q_start, block_tables, seq_lens, max_q_len, scale, out=None, stream=None):
+    n, hq, dh = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty(n, hq, dh, dtype=torch.float32, device=dev)
+    _check(load().pkv_attn_prefill_chunk(cache.ref(), _ptr(q), _dtype_code(q), len(seq_lens), hq, _ptr(q_start),
+                                         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), max_q_len,
+                                         float(scale), _ptr(out), None, 0, _stream(stream, dev)))
+    return out
+
+
+def pkv_copy_blocks(cache, src, dst, stream=None):
+    _check(load().pkv_copy_blocks(cache.ref(), _ptr(src), _ptr(dst), src.numel(), _stream(stream, cache.device)))
+
+
+def pkv_debug_gather(cache, block_table, seq_len, stream=None):
+    shape = (cache.num_kv_heads, seq_len, cache.head_dim)
+    k_out = torch.empty(shape, dtype=cache.k.dtype, device=cache.device)
+    v_out = torch.empty(shape, dtype=cache.k.dtype, device=cache.device)
+    _check(load().pkv_debug_gather(cache.ref(), _ptr(block_table), seq_len, _ptr(k_out), _ptr(v_out),
+                                   _stream(stream, cache.device)))
+    return k_out, v_out
+
+
+class BlockAllocator:
+    """Host ref-counted block allocator (pkv_alloc_*)."""
+
+    def __init__(self, num_blocks, block_size=16, free_order=None):
+        lib = load()
+        self._h = ctypes.c_void_p()
+        fo = None if free_order is None else _i32_host(free_order)
+        self._keep = fo
+        _check(lib.pkv_alloc_create(num_blocks, block_size, None if fo is None else fo.ctypes.data,
+                                    ctypes.byref(self._h)))
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_alloc_destroy(h)
+            self._h = None
+
+    def allocate(self, n):
+        out = np.empty(n, dtype=np.int32)
+        _check(load().pkv_alloc_allocate(self._h, n, out.ctypes.data))
+        return out
+
+    def incref(self, ids):
+        ids = _i32_host(ids)
+        _check(load().pkv_alloc_incref(self._h, ids.ctypes.data, len(ids)))
+
+    def decref(self, ids):
+        ids = _i32_host(ids)
+        _check(load().pkv_alloc_decref(self._h, ids.ctypes.data, len(ids)))
+
+    def refcount(self, bid):
+        return _check_nonneg(load().pkv_alloc_refcount(self._h, bid))
+
+    def num_free(self):
+        return load().pkv_alloc_num_free(self._h)
+
+    def reserve_append(self, table, seq_len, n_new):
+        """Grow a host int32 table in place; returns the (src, dst) copies needed."""
+        if not (isinstance(table, np.ndarray) and table.dtype == np.int32 and table.flags.c_contiguous):
+            raise PKVError(PKV_EINVAL, "table must be a contiguous numpy int32 array")
+        src = np.zeros(1, dtype=np.int32)
+        dst = np.zeros(1, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(load().pkv_alloc_reserve_append(self._h, table.ctypes.data, len(table), seq_len, n_new,
+                                               src.ctypes.data, dst.ctypes.data, ctypes.addressof(n)))
+        return [(int(src[0]), int(dst[0]))] if n.value else []
+
+
+def _check_nonneg(v):
+    if v < 0:
+        raise PKVError(v, load().pkv_last_error().decode())
+    return v

@@ -1,0 +1,86 @@
+// Device helpers shared by the gfx950 kernels: bf16/fp8 unpacking, DPP and
+// wave reductions, and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;   // tokens per KV block (the only size the kernels take)
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kNumXcd = 8;       // MI355X: 8 accelerator dies, each with its own L2
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 pair packed in a dword: element 0 in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// a.x*b.x + a.y*b.y + c on two packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two OCP e4m3 bytes of a dword (low pair when hi == false) → packed bf16
+// pair; exact, since every e4m3 value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Two OCP e4m3 bytes → two fp32 (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// Lane exchange inside groups of four lanes (DPP quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+
+// Sum over the four lanes of a quad; every lane of the quad receives it.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp_f32<kQuadXor1>(x);
+  x += dpp_f32<kQuadXor2>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Hardware hands consecutive workgroup ids to the XCDs round-robin. This
+// returns a logical work index such that a contiguous range of logical
+// indices runs on one XCD (and shares its L2): id → (id % 8) * (n / 8) + id / 8,
+// applied when the grid divides evenly, identity otherwise.
+__device__ __forceinline__ uint32_t xcd_logical_index(uint32_t id, uint32_t n) {
+  if (n % kNumXcd != 0) return id;
+  return (id % kNumXcd) * (n / kNumXcd) + id / kNumXcd;
+}
+
+__device__ __forceinline__ uint32_t flat_block_id() {
+  return blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+}
+
+__device__ __forceinline__ uint32_t flat_grid_size() { return gridDim.x * gridDim.y * gridDim.z; }
+
+}  // namespace pkv

@@ -1,0 +1,203 @@
+// Slot mapping, KV append (copy or e4m3 quantise), copy-on-write block copy
+// and the test-only gather, for gfx950.
+//
+// Paging arithmetic follows "07｜KV Cache、FlashAttention与PagedAttention的内部过程",
+// Q028 (block-size-4 table): position p → logical block p / bs, offset p % bs,
+// physical block from the table; slot = physical * bs + offset. The append
+// order (write the new token's K/V, then attend) follows Q025's "generate a
+// new token" paragraph and "06 KV Cache…" section 6.1.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// slot mapping: one workgroup per sequence, threads stride over its new tokens
+// ---------------------------------------------------------------------------
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ block_tables, int max_blocks,
+                                    const int32_t* __restrict__ cu_new,
+                                    const int32_t* __restrict__ first_pos, int n_tokens,
+                                    int32_t* __restrict__ out) {
+  const int s = blockIdx.x;
+  const int lo = cu_new[s];
+  const int hi = min(cu_new[s + 1], n_tokens);
+  const int p0 = first_pos[s];
+  const int32_t* bt = block_tables + (size_t)s * max_blocks;
+  for (int i = lo + (int)threadIdx.x; i < hi; i += blockDim.x) {
+    const int pos = p0 + (i - lo);
+    const int lb = pos / kBlockSize;
+    int slot = -1;
+    if (pos >= 0 && lb < max_blocks) {
+      const int phys = bt[lb];
+      if (phys >= 0) slot = phys * kBlockSize + pos % kBlockSize;
+    }
+    out[i] = slot;
+  }
+}
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int num_seqs,
+                               const int32_t* cu_new, const int32_t* first_pos, int n_tokens,
+                               int32_t* out_slots, hipStream_t s) {
+  if (num_seqs == 0 || n_tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(128), 0, s, block_tables,
+                     max_blocks, cu_new, first_pos, n_tokens, out_slots);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// e4m3fn encode, round to nearest even, saturating at ±448, NaN kept.
+// Integer formulation on the fp32 bit pattern (the round-half-even carry
+// trick on the 3 kept mantissa bits); subnormal outputs use the exact
+// scaling by 2^9 followed by an ties-to-even integer rounding.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t encode_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;            // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;           // >= 448 (and inf): saturate
+  if (a < 0x3c800000u) {                               // below 2^-6: spacing 2^-9
+    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)q;                         // 0..8; 8 is the first normal
+  }
+  // keep 3 mantissa bits with ties to even
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) & 0xfff00000u;
+  const int e = (int)(r >> 23) - 127;                  // -6 … 8 (9 only past 448)
+  const uint32_t m = (r >> 20) & 7u;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | m;
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+// One workgroup per token; threads stride over 16-byte input chunks of K then V.
+template <int IN, int OUT>
+__global__ void kv_append_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+                                 const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
+                                 uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
+                                 const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
+  const int tok = blockIdx.x;
+  const int slot = slots[tok];
+  if (slot < 0 || slot >= num_blocks * kBlockSize) return;
+  const int blk = slot / kBlockSize, off = slot % kBlockSize;
+  constexpr int IN_B = IN == kF32 ? 4 : 2;
+  constexpr int EPC = 16 / IN_B;                       // input elements per 16-byte chunk
+  const int chunks_per_head = dh / EPC;
+  const int chunks = hkv * chunks_per_head;
+  for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
+    const bool is_v = c >= chunks;
+    const int cc = is_v ? c - chunks : c;
+    const int h = cc / chunks_per_head;
+    const int e0 = (cc % chunks_per_head) * EPC;
+    const uint8_t* src = (is_v ? v_new : k_new) + ((size_t)tok * hkv * dh + (size_t)h * dh + e0) * IN_B;
+    const size_t dst_elem = (((size_t)blk * hkv + h) * kBlockSize + off) * dh + e0;
+    uint8_t* dst_base = is_v ? vc : kc;
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    if constexpr (OUT != kFP8) {
+      *reinterpret_cast<uint4*>(dst_base + dst_elem * IN_B) = x;
+    } else {
+      const float inv = (is_v ? v_inv : k_inv)[h];
+      float f[EPC];
+      if constexpr (IN == kBF16) {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+      } else {
+        f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+        f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+      }
+      uint32_t packed[EPC / 4];
+#pragma unroll
+      for (int i = 0; i < EPC / 4; ++i) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b |= encode_e4m3(f[4 * i + j] * inv) << (8 * j);
+        packed[i] = b;
+      }
+      uint8_t* dst = dst_base + dst_elem;
+      if constexpr (EPC == 8) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = packed[0];
+      }
+    }
+  }
+}
+
+hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
+                            int n_tokens, const int32_t* slots, const float* k_inv,
+                            const float* v_inv, hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  const dim3 grid(n_tokens), block(128);
+  auto kn = static_cast<const uint8_t*>(k_new);
+  auto vn = static_cast<const uint8_t*>(v_new);
+  auto kc = static_cast<uint8_t*>(c.k);
+  auto vc = static_cast<uint8_t*>(c.v);
+#define PKV_APPEND(IN, OUT)                                                                      \
+  hipLaunchKernelGGL((kv_append_kernel<IN, OUT>), grid, block, 0, s, kn, vn, slots, kc, vc,      \
+                     c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv)
+  if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
+  else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
+  else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
+  else PKV_APPEND(kF32, kFP8);
+#undef PKV_APPEND
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// copy-on-write: whole blocks, all heads, K and V; one workgroup per pair
+// ---------------------------------------------------------------------------
+__global__ void copy_blocks_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                   int num_blocks, size_t block_bytes) {
+  const int i = blockIdx.x;
+  const int s = src[i], d = dst[i];
+  if ((unsigned)s >= (unsigned)num_blocks || (unsigned)d >= (unsigned)num_blocks) return;
+  const size_t n16 = block_bytes / 16;
+  for (size_t c = threadIdx.x; c < 2 * n16; c += blockDim.x) {
+    uint8_t* base = c < n16 ? kc : vc;
+    const size_t cc = c < n16 ? c : c - n16;
+    const uint4 x = reinterpret_cast<const uint4*>(base + (size_t)s * block_bytes)[cc];
+    reinterpret_cast<uint4*>(base + (size_t)d * block_bytes)[cc] = x;
+  }
+}
+
+hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int32_t* dst, int n,
+                              hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k),
+                     static_cast<uint8_t*>(c.v), src, dst, c.num_blocks, block_bytes);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// test aid: paged → [Hkv, T, Dh] through the same slot arithmetic
+// ---------------------------------------------------------------------------
+__global__ void debug_gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                    const int32_t* __restrict__ table, int seq_len, int num_blocks,
+                                    int hkv, int row_bytes, uint8_t* __restrict__ k_out,
+                                    uint8_t* __restrict__ v_out) {
+  const int p = blockIdx.x;
+  const int h = blockIdx.y;
+  const int phys = table[p / kBlockSize];
+  if ((unsigned)phys >= (unsigned)num_blocks) return;
+  const size_t src = (((size_t)phys * hkv + h) * kBlockSize + p % kBlockSize) * row_bytes;
+  const size_t dst = ((size_t)h * seq_len + p) * row_bytes;
+  for (int b = threadIdx.x * 4; b < row_bytes; b += blockDim.x * 4) {
+    *reinterpret_cast<uint32_t*>(k_out + dst + b) = *reinterpret_cast<const uint32_t*>(kc + src + b);
+    *reinterpret_cast<uint32_t*>(v_out + dst + b) = *reinterpret_cast<const uint32_t*>(vc + src + b);
+  }
+}
+
+hipError_t launch_debug_gather(const CacheView& c, const int32_t* table, int seq_len, void* k_out,
+                               void* v_out, hipStream_t s) {
+  if (seq_len == 0) return hipSuccess;
+  const int row_bytes = c.head_dim * dtype_bytes(c.dtype);
+  hipLaunchKernelGGL(debug_gather_kernel, dim3(seq_len, c.num_kv_heads), dim3(64), 0, s,
+                     static_cast<const uint8_t*>(c.k), static_cast<const uint8_t*>(c.v), table,
+                     seq_len, c.num_blocks, c.num_kv_heads, row_bytes,
+                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
+  return hipGetLastError();
+}
+
+}  // namespace pkv

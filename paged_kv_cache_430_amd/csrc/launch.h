@@ -1,0 +1,67 @@
+// Internal launcher interface between the C ABI (pkv_api.cpp) and the kernel
+// translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
+
+struct CacheView {
+  int num_blocks, num_kv_heads, head_dim, dtype;
+  void* k;
+  void* v;
+  const float* k_scale;
+  const float* v_scale;
+};
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int num_seqs,
+                               const int32_t* cu_new, const int32_t* first_pos, int n_tokens,
+                               int32_t* out_slots, hipStream_t s);
+
+hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
+                            int n_tokens, const int32_t* slots, const float* k_inv,
+                            const float* v_inv, hipStream_t s);
+
+hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int32_t* dst, int n,
+                              hipStream_t s);
+
+hipError_t launch_debug_gather(const CacheView& c, const int32_t* table, int seq_len, void* k_out,
+                               void* v_out, hipStream_t s);
+
+struct DecodeParams {
+  CacheView cache;
+  const void* q;
+  int batch, num_q_heads, max_blocks, max_seq_len, part_tokens, num_parts;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float scale;
+  float* out;
+  float* ws_ml;        // [batch, Hq, num_parts, 2] (m, l) in log2 units
+  float* ws_u;         // [batch, Hq, num_parts, head_dim]
+  int32_t* ws_count;   // [batch, Hq / heads-per-workgroup]
+};
+
+// Heads of one KV group handled by one decode workgroup.
+int decode_heads_per_wg(int group);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+
+struct PrefillParams {
+  CacheView cache;
+  const void* q;
+  int num_seqs, num_q_heads, max_blocks, max_q_len;
+  const int32_t* q_start;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float scale;
+  float* out;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+}  // namespace pkv

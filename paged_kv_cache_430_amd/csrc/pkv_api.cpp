@@ -1,0 +1,335 @@
+// The C ABI: argument validation, launch geometry, error reporting.
+// Every entry point validates on the host first and launches nothing on error.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <cmath>
+
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "errors.h"
+#include "launch.h"
+
+namespace pkv {
+
+std::string& last_error() {
+  thread_local std::string msg;
+  return msg;
+}
+
+namespace {
+
+constexpr int32_t kMaxPartition = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool check_mode() {
+  const char* e = getenv("PKV_CHECK");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int validate_cache(const pkv_cache* c, const char* fn, CacheView* view) {
+  const std::string f(fn);
+  if (!c) return fail(PKV_EINVAL, f + ": cache is NULL");
+  if (c->block_size != 16) return fail(PKV_EINVAL, f + ": block_size must be 16");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(PKV_EINVAL, f + ": head_dim must be 64 or 128");
+  if (c->num_kv_heads <= 0) return fail(PKV_EINVAL, f + ": num_kv_heads must be positive");
+  if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX / 16)
+    return fail(PKV_EINVAL, f + ": num_blocks out of range");
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)
+    return fail(PKV_EDTYPE, f + ": unknown cache dtype");
+  if (!c->k_cache || !c->v_cache) return fail(PKV_EINVAL, f + ": k_cache / v_cache is NULL");
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache))
+    return fail(PKV_EINVAL, f + ": k_cache / v_cache must be 16-byte aligned");
+  if (c->dtype == PKV_FP8_E4M3 && (!c->k_scale || !c->v_scale))
+    return fail(PKV_EINVAL, f + ": an fp8 cache needs k_scale and v_scale");
+  view->num_blocks = c->num_blocks;
+  view->num_kv_heads = c->num_kv_heads;
+  view->head_dim = c->head_dim;
+  view->dtype = c->dtype;
+  view->k = c->k_cache;
+  view->v = c->v_cache;
+  view->k_scale = c->k_scale;
+  view->v_scale = c->v_scale;
+  return PKV_OK;
+}
+
+template <typename T>
+int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return PKV_OK;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost);
+  return hip_status(e, "PKV_CHECK copy");
+}
+
+// PKV_CHECK: every table entry a sequence will read names a pool block.
+int check_tables(const std::vector<int32_t>& bt, int max_blocks, int seq, int tokens,
+                 int num_blocks, const char* fn) {
+  const int nb = (tokens + 15) / 16;
+  if (nb > max_blocks) return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: sequence longer than its table");
+  for (int i = 0; i < nb; ++i) {
+    const int32_t id = bt[(size_t)seq * max_blocks + i];
+    if (id < 0 || id >= num_blocks)
+      return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: sequence " + std::to_string(seq) +
+                                  " block " + std::to_string(i) + " has id " + std::to_string(id));
+  }
+  return PKV_OK;
+}
+
+int32_t auto_partition(int32_t batch, int32_t hq, int32_t max_seq_len) {
+  if (max_seq_len <= 512) return max_seq_len <= 16 ? 16 : (max_seq_len + 15) / 16 * 16;
+  int32_t pt = 512;
+  const int64_t units = (int64_t)batch * (hq >= 4 ? hq / 4 : 1);
+  while (pt > 128 && units * ((max_seq_len + pt - 1) / pt) < 1024) pt /= 2;
+  return pt;
+}
+
+int32_t effective_partition(int32_t batch, int32_t hq, int32_t max_seq_len, int32_t pt) {
+  return pt == 0 ? auto_partition(batch, hq, max_seq_len) : pt;
+}
+
+size_t decode_ws_bytes(int32_t batch, int32_t hq, int32_t dh, int32_t max_seq_len, int32_t pt) {
+  if (batch <= 0 || hq <= 0 || max_seq_len <= 0 || pt <= 0) return 0;
+  const int64_t parts = (max_seq_len + pt - 1) / pt;
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)batch * hq;
+  return (rows * parts * (dh + 2) + rows) * sizeof(float);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+PKV_API int32_t pkv_version(void) { return 100; }
+
+PKV_API const char* pkv_last_error(void) { return last_error().c_str(); }
+
+PKV_API int pkv_slot_mapping(const int32_t* block_table, int32_t table_len, int32_t block_size,
+                             int32_t first_pos, int32_t n, int32_t* out_slots) {
+  clear_error();
+  if (block_size <= 0 || n < 0 || first_pos < 0 || table_len < 0 || (n > 0 && (!block_table || !out_slots)))
+    return fail(PKV_EINVAL, "pkv_slot_mapping: bad argument");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t pos = (int64_t)first_pos + i;
+    const int64_t lb = pos / block_size;
+    if (lb >= table_len) return fail(PKV_EINVAL, "pkv_slot_mapping: position beyond the block table");
+    const int32_t phys = block_table[lb];
+    if (phys < 0) return fail(PKV_EINVAL, "pkv_slot_mapping: position falls on an unallocated table entry");
+    const int64_t slot = (int64_t)phys * block_size + pos % block_size;
+    if (slot > INT32_MAX) return fail(PKV_EINVAL, "pkv_slot_mapping: slot overflows int32");
+    out_slots[i] = (int32_t)slot;
+  }
+  return PKV_OK;
+}
+
+PKV_API int pkv_slot_mapping_device(const int32_t* block_tables, int32_t max_blocks,
+                                    int32_t block_size, int32_t num_seqs, const int32_t* cu_new,
+                                    const int32_t* first_pos, int32_t n_tokens, int32_t* out_slots,
+                                    pkv_stream stream) {
+  clear_error();
+  if (block_size != 16) return fail(PKV_EINVAL, "pkv_slot_mapping_device: block_size must be 16");
+  if (num_seqs < 0 || n_tokens < 0 || max_blocks < 0) return fail(PKV_EINVAL, "pkv_slot_mapping_device: negative size");
+  if (num_seqs > 0 && n_tokens > 0 && (!block_tables || !cu_new || !first_pos || !out_slots))
+    return fail(PKV_EINVAL, "pkv_slot_mapping_device: NULL pointer");
+  return hip_status(launch_slot_mapping(block_tables, max_blocks, num_seqs, cu_new, first_pos,
+                                        n_tokens, out_slots, static_cast<hipStream_t>(stream)),
+                    "pkv_slot_mapping_device");
+}
+
+PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void* v_new,
+                          int32_t in_dtype, int32_t n_tokens, const int32_t* slot_mapping,
+                          const float* k_inv_scale, const float* v_inv_scale, pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_kv_append", &c)) return st;
+  if (n_tokens < 0) return fail(PKV_EINVAL, "pkv_kv_append: n_tokens < 0");
+  if (n_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PKV_EINVAL, "pkv_kv_append: NULL pointer");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(PKV_EINVAL, "pkv_kv_append: k_new / v_new must be 16-byte aligned");
+  const bool ok_dtype = (c.dtype == PKV_F32 && in_dtype == PKV_F32) ||
+                        (c.dtype == PKV_BF16 && in_dtype == PKV_BF16) ||
+                        (c.dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32));
+  if (!ok_dtype) return fail(PKV_EDTYPE, "pkv_kv_append: input dtype does not match the cache");
+  if (c.dtype == PKV_FP8_E4M3 && (!k_inv_scale || !v_inv_scale))
+    return fail(PKV_EINVAL, "pkv_kv_append: fp8 cache needs k_inv_scale and v_inv_scale");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    std::vector<int32_t> slots;
+    if (int st = copy_to_host(slots, slot_mapping, (size_t)n_tokens, s)) return st;
+    for (int32_t v : slots)
+      if (v < -1 || (int64_t)v >= (int64_t)c.num_blocks * 16)
+        return fail(PKV_EINVAL, "pkv_kv_append: PKV_CHECK: slot " + std::to_string(v) + " outside the pool");
+  }
+  return hip_status(launch_kv_append(c, k_new, v_new, in_dtype, n_tokens, slot_mapping, k_inv_scale,
+                                     v_inv_scale, s),
+                    "pkv_kv_append");
+}
+
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                               int32_t max_seq_len, int32_t partition_tokens) {
+  const int32_t pt = effective_partition(batch, num_q_heads, max_seq_len, partition_tokens);
+  return decode_ws_bytes(batch, num_q_heads, head_dim, max_seq_len, pt);
+}
+
+PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads, int32_t max_seq_len) {
+  return auto_partition(batch, num_q_heads, max_seq_len);
+}
+
+PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
+                            int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                            int32_t partition_tokens, float* out, void* workspace,
+                            size_t workspace_bytes, pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_attn_decode", &c)) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_seq_len < 0)
+    return fail(PKV_EINVAL, "pkv_attn_decode: bad size");
+  if (num_q_heads % c.num_kv_heads != 0) return fail(PKV_EINVAL, "pkv_attn_decode: num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / c.num_kv_heads > 64) return fail(PKV_EINVAL, "pkv_attn_decode: more than 64 query heads per KV head");
+  if ((int64_t)max_seq_len > (int64_t)max_blocks * 16)
+    return fail(PKV_EINVAL, "pkv_attn_decode: max_seq_len exceeds max_blocks * block_size");
+  if (partition_tokens != 0 && (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16))
+    return fail(PKV_EINVAL, "pkv_attn_decode: partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
+  const bool ok_q = (c.dtype == PKV_F32 && q_dtype == PKV_F32) ||
+                    (c.dtype != PKV_F32 && q_dtype == PKV_BF16);
+  if (!ok_q) return fail(PKV_EDTYPE, "pkv_attn_decode: q dtype must be F32 for an F32 cache, BF16 otherwise");
+  if (batch == 0) return PKV_OK;
+  if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, "pkv_attn_decode: NULL pointer");
+  if (!aligned16(q)) return fail(PKV_EINVAL, "pkv_attn_decode: q must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_decode: scale is not finite");
+  const int32_t pt = effective_partition(batch, num_q_heads, max_seq_len, partition_tokens);
+  const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
+  const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "pkv_attn_decode: workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    std::vector<int32_t> lens, bt;
+    if (int st = copy_to_host(lens, seq_lens, (size_t)batch, s)) return st;
+    if (int st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks, s)) return st;
+    for (int b = 0; b < batch; ++b) {
+      if (lens[b] < 0 || lens[b] > max_seq_len)
+        return fail(PKV_EINVAL, "pkv_attn_decode: PKV_CHECK: seq_lens[" + std::to_string(b) + "] = " +
+                                    std::to_string(lens[b]) + " outside [0, max_seq_len]");
+      if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, "pkv_attn_decode")) return st;
+    }
+  }
+  DecodeParams p;
+  p.cache = c;
+  p.q = q;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.max_blocks = max_blocks;
+  p.max_seq_len = max_seq_len;
+  p.part_tokens = pt;
+  p.num_parts = parts;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.scale = scale;
+  p.out = out;
+  float* ws = static_cast<float*>(workspace);
+  const size_t rows = (size_t)batch * num_q_heads;
+  p.ws_ml = need ? ws : nullptr;
+  p.ws_u = need ? ws + rows * parts * 2 : nullptr;
+  // counters live in the last `rows` ints of the buffer, so calls of different
+  // shapes sharing one buffer never write partials over each other's counters
+  p.ws_count = need ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (workspace_bytes & ~size_t(3))) -
+                          rows
+                    : nullptr;
+  return hip_status(launch_decode(p, s), "pkv_attn_decode");
+}
+
+PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
+                                   int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
+                                   const int32_t* block_tables, int32_t max_blocks,
+                                   const int32_t* seq_lens, int32_t max_q_len, float scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   pkv_stream stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_attn_prefill_chunk", &c)) return st;
+  if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16)
+    return fail(PKV_EDTYPE, "pkv_attn_prefill_chunk: cache and q must be BF16");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
+    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: bad size");
+  if (num_q_heads % c.num_kv_heads != 0)
+    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: num_q_heads must be a multiple of num_kv_heads");
+  const int group = num_q_heads / c.num_kv_heads;
+  if (!(group == 1 || group == 2 || (group % 4 == 0 && group <= 64)))
+    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: Hq/Hkv must be 1, 2 or a multiple of 4 up to 64");
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!q || !q_start || !block_tables || !seq_lens || !out)
+    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: NULL pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: q and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: scale is not finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    std::vector<int32_t> qs, lens, bt;
+    if (int st = copy_to_host(qs, q_start, (size_t)num_seqs + 1, s)) return st;
+    if (int st = copy_to_host(lens, seq_lens, (size_t)num_seqs, s)) return st;
+    if (int st = copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, s)) return st;
+    if (qs[0] != 0) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: PKV_CHECK: q_start[0] != 0");
+    for (int i = 0; i < num_seqs; ++i) {
+      const int cq = qs[i + 1] - qs[i];
+      if (cq < 0 || cq > max_q_len || lens[i] < cq || (int64_t)lens[i] > (int64_t)max_blocks * 16)
+        return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: PKV_CHECK: bad q_start / seq_lens for sequence " + std::to_string(i));
+      if (int st = check_tables(bt, max_blocks, i, lens[i], c.num_blocks, "pkv_attn_prefill_chunk")) return st;
+    }
+  }
+  PrefillParams p;
+  p.cache = c;
+  p.q = q;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.max_blocks = max_blocks;
+  p.max_q_len = max_q_len;
+  p.q_start = q_start;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.scale = scale;
+  p.out = out;
+  return hip_status(launch_prefill(p, s), "pkv_attn_prefill_chunk");
+}
+
+PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const int32_t* dst, int32_t n,
+                            pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_copy_blocks", &c)) return st;
+  if (n < 0) return fail(PKV_EINVAL, "pkv_copy_blocks: n < 0");
+  if (n == 0) return PKV_OK;
+  if (!src || !dst) return fail(PKV_EINVAL, "pkv_copy_blocks: NULL pointer");
+  return hip_status(launch_copy_blocks(c, src, dst, n, static_cast<hipStream_t>(stream)), "pkv_copy_blocks");
+}
+
+PKV_API int pkv_debug_gather(const pkv_cache* cache, const int32_t* block_table, int32_t seq_len,
+                             void* k_out, void* v_out, pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_debug_gather", &c)) return st;
+  if (seq_len < 0) return fail(PKV_EINVAL, "pkv_debug_gather: seq_len < 0");
+  if (seq_len == 0) return PKV_OK;
+  if (!block_table || !k_out || !v_out) return fail(PKV_EINVAL, "pkv_debug_gather: NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 3u)
+    return fail(PKV_EINVAL, "pkv_debug_gather: outputs must be 4-byte aligned");
+  return hip_status(launch_debug_gather(c, block_table, seq_len, k_out, v_out, static_cast<hipStream_t>(stream)),
+                    "pkv_debug_gather");
+}
+
+}  // extern "C"

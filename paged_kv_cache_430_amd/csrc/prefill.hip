@@ -1,0 +1,271 @@
+// Causal chunked prefill over a paged, cached prefix, on gfx950 MFMA.
+//
+// Method: "07｜KV Cache、FlashAttention与PagedAttention的内部过程", Q027 core
+// answer and the FlashAttention section — attention is computed tile by tile
+// with the scores and probabilities kept on chip, scale and mask fused, and
+// the online softmax (running max m, sum l, weighted sum u, old statistics
+// rescaled by exp(m_old − m_new)) gives the same result as the full softmax.
+// "06 KV Cache…" 6.6 — prefill split into chunks; a chunk's queries see the
+// cached prefix and the chunk's earlier tokens. Q025 table row 2 — the causal
+// mask includes the diagonal.
+//
+// Workgroup = (sequence, KV head g, a chunk of GW ≤ 4 query heads of g, a tile
+// of 64/GW queries); wave w takes head w % GW and 16 queries. Per 64-key tile:
+//   * K (row-major, padded) and V (transposed into groups of four keys per
+//     column) are gathered through the block table into LDS by all 256 threads;
+//     keys past the sequence end are stored as zeros;
+//   * Sᵀ = K·Qᵀ on MFMA 16x16x32 bf16 (keys are the M dimension, so each lane's
+//     scores all belong to one query: lane % 16);
+//   * scale, inclusive causal mask (select to −inf), online softmax in the log2
+//     domain; the row sum stays lane-local until the end;
+//   * Oᵀ += Vᵀ·Pᵀ on MFMA, keys ordered as the score layout left them, so no
+//     shuffle of P is needed; P enters as a bf16 high part plus a bf16 low
+//     part (two MFMAs), which keeps the probabilities to ~16 bits.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKeys = 64;            // keys per tile
+
+struct Args {
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const uint16_t* q;
+  const int32_t* q_start;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;
+  int num_blocks, hkv, hq, max_blocks, num_qtiles, num_chunks;
+  float scale_log2;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int DH, int GW>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
+  constexpr int QT = 64 / GW;              // queries per workgroup
+  constexpr int KROW = DH + 8;             // padded K row in LDS (elements)
+  constexpr int NDC = DH / 32;             // 32-wide k-steps for Q·Kᵀ
+  constexpr int NDT = DH / 16;             // 16-row output tiles of Oᵀ
+  constexpr int CPR = DH / 8;              // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeys * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[(kKeys / 4) * DH * 4];
+
+  const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
+  const int qtile = L % a.num_qtiles;
+  const int chunk = (L / a.num_qtiles) % a.num_chunks;
+  const int g = (L / a.num_qtiles / a.num_chunks) % a.hkv;
+  const int s = L / a.num_qtiles / a.num_chunks / a.hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q_lo = a.q_start[s];
+  const int C = a.q_start[s + 1] - q_lo;                 // queries of this sequence
+  const int T = min(a.seq_lens[s], a.max_blocks * kBlockSize);
+  if (qtile * QT >= C || T <= 0) return;
+  const int base_pos = T - C;                             // position of query 0
+  const int group = a.hq / a.hkv;
+  const int head = g * group + chunk * GW + (w % GW);
+  const int qi0 = qtile * QT + (w / GW) * 16;             // this wave's first query
+  const int col = lane & 15, kg = lane >> 4;
+  const int my_q = qi0 + col;                             // query whose scores this lane holds
+  const bool q_valid = my_q < C;
+  const int my_pos = q_valid ? base_pos + my_q : T - 1;
+  // last key any query of this workgroup sees
+  const int wg_last_q = min(C, qtile * QT + QT) - 1;
+  const int kend = min(T, base_pos + wg_last_q + 1);
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
+
+  // Qᵀ operand: lane holds Q[my_q][dc*32 + kg*8 .. +7]
+  bf16x8_t qreg[NDC];
+  {
+    const int qrow = q_lo + (q_valid ? my_q : 0);
+    const uint16_t* qp = a.q + ((size_t)qrow * a.hq + head) * DH + kg * 8;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      qreg[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + dc * 32));
+  }
+
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const size_t head_stride = (size_t)kBlockSize * DH;    // elements of one (block, head)
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int key0 = kt * kKeys;
+    // ---- gather K tile: 64 rows × CPR chunks ----
+    for (int c = tid; c < kKeys * CPR; c += kThreads) {
+      const int key = c / CPR, ch = c % CPR;
+      const int kabs = key0 + key;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (kabs < kend) {
+        const int phys = bt[kabs / kBlockSize];
+        if ((unsigned)phys < (unsigned)a.num_blocks)
+          x = *reinterpret_cast<const uint4*>(a.kc + ((size_t)phys * a.hkv + g) * head_stride +
+                                              (size_t)(kabs % kBlockSize) * DH + ch * 8);
+      }
+      *reinterpret_cast<uint4*>(&k_lds[key * KROW + ch * 8]) = x;
+    }
+    // ---- gather V tile: thread = (four keys, 8 columns), stored [key/4][col][key%4] ----
+    for (int c = tid; c < (kKeys / 4) * CPR; c += kThreads) {
+      const int kq = c / CPR, ch = c % CPR;
+      uint32_t rw[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kabs = key0 + kq * 4 + r;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (kabs < kend) {
+          const int phys = bt[kabs / kBlockSize];
+          if ((unsigned)phys < (unsigned)a.num_blocks)
+            x = *reinterpret_cast<const uint4*>(a.vc + ((size_t)phys * a.hkv + g) * head_stride +
+                                                (size_t)(kabs % kBlockSize) * DH + ch * 8);
+        }
+        rw[r][0] = x.x; rw[r][1] = x.y; rw[r][2] = x.z; rw[r][3] = x.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {       // dword e holds columns 2e (low) and 2e+1 (high)
+        const uint32_t lo01 = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(rw[3][e], rw[2][e], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(rw[3][e], rw[2][e], 0x07060302u);
+        const int d = ch * 8 + 2 * e;
+        *reinterpret_cast<uint2*>(&v_lds[(kq * DH + d) * 4]) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(&v_lds[(kq * DH + d + 1) * 4]) = make_uint2(hi01, hi23);
+      }
+    }
+    __syncthreads();
+
+    // ---- Sᵀ = K·Qᵀ: four 16-key tiles ----
+    f32x4_t st[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t kk = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[(t4 * 16 + col) * KROW + dc * 32 + kg * 8]));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qreg[dc], acc, 0, 0, 0);
+      }
+      st[t4] = acc;
+    }
+    // ---- scale, mask, online softmax (lane's scores all belong to my_q) ----
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kabs = key0 + t4 * 16 + kg * 4 + i;
+        const float v = kabs <= my_pos ? st[t4][i] * a.scale_log2 : -INFINITY;
+        st[t4][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);                 // finite: key 0 is visible to all
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(st[t4][i] - m_new);
+        st[t4][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+
+    // ---- Oᵀ += Vᵀ·Pᵀ over two 32-key steps ----
+    // P is split into bf16 high and low parts (p = hi + lo to ~16 bits) and
+    // both go through the MFMA: V is exact in bf16, so the product keeps
+    // fp32-level accuracy instead of bf16's 2^-9 relative rounding of p.
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { pv[i] = st[2 * kc2][i]; pv[4 + i] = st[2 * kc2 + 1][i]; }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h0 = (__bf16)pv[2 * i], h1 = (__bf16)pv[2 * i + 1];
+        hw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
+        lw[i] = pack_bf16x2(pv[2 * i] - (float)h0, pv[2 * i + 1] - (float)h1);
+      }
+      const bf16x8_t p_hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8_t p_lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      const int quad_a = (2 * kc2) * 4 + kg;              // keys (2kc2)*16 + kg*4 .. +3
+      const int quad_b = (2 * kc2 + 1) * 4 + kg;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = dt * 16 + col;
+        const uint2 va = *reinterpret_cast<const uint2*>(&v_lds[(quad_a * DH + d) * 4]);
+        const uint2 vb = *reinterpret_cast<const uint2*>(&v_lds[(quad_b * DH + d) * 4]);
+        const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, o[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- finish: l over the four lanes of a query, o = u / l ----
+  float lt = l_run;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (!q_valid) return;
+  const float inv = 1.0f / lt;
+  float* op = a.out + ((size_t)(q_lo + my_q) * a.hq + head) * DH + kg * 4;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const f32x4_t r = o[dt] * inv;
+    *reinterpret_cast<float4*>(op + dt * 16) = make_float4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+template <int DH>
+hipError_t launch_gw(const PrefillParams& p, Args a, int gw, hipStream_t s) {
+  const size_t n = (size_t)p.num_seqs * a.hkv * a.num_chunks * a.num_qtiles;
+  const dim3 grid((unsigned)n), block(kThreads);
+  switch (gw) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<DH, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<DH, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((prefill_kernel<DH, 4>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+  if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
+  const int group = p.num_q_heads / p.cache.num_kv_heads;
+  const int gw = group >= 4 ? 4 : group;     // group is 1, 2 or a multiple of 4
+  Args a;
+  a.kc = static_cast<const uint16_t*>(p.cache.k);
+  a.vc = static_cast<const uint16_t*>(p.cache.v);
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.q_start = p.q_start;
+  a.block_tables = p.block_tables;
+  a.seq_lens = p.seq_lens;
+  a.out = p.out;
+  a.num_blocks = p.cache.num_blocks;
+  a.hkv = p.cache.num_kv_heads;
+  a.hq = p.num_q_heads;
+  a.max_blocks = p.max_blocks;
+  a.num_chunks = group / gw;
+  a.num_qtiles = (p.max_q_len + (64 / gw) - 1) / (64 / gw);
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  return p.cache.head_dim == 64 ? launch_gw<64>(p, a, gw, s) : launch_gw<128>(p, a, gw, s);
+}
+
+}  // namespace pkv

@@ -1,0 +1,78 @@
+"""Shared plumbing for the GPU parity tests: build a paged cache through the
+library (slot mapping + append, the product path) and the oracle's view of the
+same sequences (contiguous float64, fp8 decoded by the oracle's codec)."""
+
+import numpy as np
+import torch
+
+import paged_kv_cache_430_amd as pkv
+from oracle import fp8 as ofp8
+
+NAN_FP8 = 0x7F
+
+
+def device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible GPU")
+    return torch.device("cuda:0")
+
+
+def new_pools(num_blocks, hkv, dh, cache_dtype, dev):
+    shape = (num_blocks, hkv, 16, dh)
+    if cache_dtype == "fp8":
+        k = torch.full(shape, NAN_FP8, dtype=torch.uint8, device=dev)
+    else:
+        dt = torch.float32 if cache_dtype == "f32" else torch.bfloat16
+        k = torch.full(shape, float("nan"), dtype=dt, device=dev)
+    return k, k.clone()
+
+
+def build_cache(w, dev, copies=None):
+    """Pools for a DecodeInputs workload, every sequence appended through the
+    library at positions 0..T-1 (once per table copy)."""
+    kp, vp = new_pools(w.num_blocks, w.hkv, w.head_dim, w.cache_dtype, dev)
+    ks = vs = kinv = vinv = None
+    if w.cache_dtype == "fp8":
+        ks = torch.from_numpy(w.k_scale).to(dev)
+        vs = torch.from_numpy(w.v_scale).to(dev)
+        kinv = torch.from_numpy(w.k_inv_scale).to(dev)
+        vinv = torch.from_numpy(w.v_inv_scale).to(dev)
+    cache = pkv.Cache(kp, vp, ks, vs)
+    for c in range(w.copies if copies is None else copies):
+        slots = np.concatenate([pkv.pkv_slot_mapping(w.block_tables[c, b], 16, 0, int(w.seq_lens[b]))
+                                for b in range(w.batch)] or [np.zeros(0, np.int32)])
+        if len(slots):
+            pkv.pkv_kv_append(cache, w.k, w.v, torch.from_numpy(slots).to(dev), kinv, vinv)
+    return cache
+
+
+def oracle_seq(w, b):
+    """(K, V) of sequence b as the attention sees them: [Hkv, T, Dh] float64."""
+    if w.cache_dtype == "fp8":
+        kq, vq = oracle_fp8_bytes(w, b)
+        k = np.stack([ofp8.dequantize(kq[:, h, :], w.k_scale[h]) for h in range(w.hkv)], axis=1)
+        v = np.stack([ofp8.dequantize(vq[:, h, :], w.v_scale[h]) for h in range(w.hkv)], axis=1)
+    else:
+        k = w.seq_k(b).float().cpu().numpy()
+        v = w.seq_v(b).float().cpu().numpy()
+    return np.transpose(k, (1, 0, 2)).astype(np.float64), np.transpose(v, (1, 0, 2)).astype(np.float64)
+
+
+def bf16_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_fp8_bytes(w, b):
+    """Stored e4m3 bytes of sequence b per the oracle's codec: [T, Hkv, Dh] uint8."""
+    kb, vb = bf16_bits(w.seq_k(b)), bf16_bits(w.seq_v(b))
+    kq = np.stack([ofp8.quantize_bf16_bits(kb[:, h, :], w.k_inv_scale[h]) for h in range(w.hkv)], axis=1)
+    vq = np.stack([ofp8.quantize_bf16_bits(vb[:, h, :], w.v_inv_scale[h]) for h in range(w.hkv)], axis=1)
+    return kq, vq
+
+
+def tables(w, dev, copy=0):
+    return torch.from_numpy(np.ascontiguousarray(w.block_tables[copy])).to(dev)
+
+
+def lens(w, dev):
+    return torch.from_numpy(w.seq_lens.astype(np.int32)).to(dev)

@@ -1,0 +1,195 @@
+"""GPU parity: paged decode (split-KV) against the float64 oracle.
+
+Tolerances: max-abs 1e-5 for fp32 caches, 2e-3 for bf16 and fp8 caches.
+Pools are NaN-filled before the append, so a masked slot that leaks into a
+sum turns the output into NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_430_amd as pkv
+import workloads
+from oracle import attention
+
+from gpu_helpers import build_cache, device, lens, oracle_seq, tables
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-3}
+
+
+def run_decode(w, cache, dev, partition_tokens=0, copy=0, max_seq_len=None):
+    msl = int(w.seq_lens.max()) if max_seq_len is None else max_seq_len
+    out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev, copy), lens(w, dev), msl, w.scale,
+                              partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+def oracle_decode(w, seqs=None):
+    seqs = range(w.batch) if seqs is None else seqs
+    q = w.q.float().cpu().double().numpy()
+    out = {}
+    for b in seqs:
+        k, v = oracle_seq(w, b)
+        out[b] = attention.decode(q[b:b + 1], [k], [v], w.scale)[0]
+    return out
+
+
+def assert_close(got, ref, tol, what):
+    for b, r in ref.items():
+        assert np.isfinite(got[b]).all(), f"{what}: non-finite output for sequence {b}"
+        err = float(np.abs(got[b] - r).max())
+        assert err <= tol, f"{what}: sequence {b} max-abs error {err:.3e} > {tol}"
+
+
+def test_cfg1_fp32_before_and_after_append():
+    dev = device()
+    w = workloads.cfg1(device=dev)
+    w35 = workloads.DecodeInputs(**{f: getattr(w, f) for f in w.__dataclass_fields__})
+    w35.seq_lens = np.array([35], dtype=np.int32)
+    w35.cu_seqlens = np.array([0, 35], dtype=np.int64)
+    w35.k, w35.v = w.k[:35], w.v[:35]
+    cache = build_cache(w35, dev)
+    got35 = run_decode(w35, cache, dev)
+    assert_close({0: got35[0]}, oracle_decode(w35), 1e-5, "cfg1 T=35")
+    # append the 36th token through the slot mapping, then attend over 36
+    s = pkv.pkv_slot_mapping(w.block_tables[0, 0], 16, 35, 1)
+    pkv.pkv_kv_append(cache, w.k[35:].contiguous(), w.v[35:].contiguous(), torch.from_numpy(s).to(dev))
+    got36 = run_decode(w, cache, dev)
+    assert_close({0: got36[0]}, oracle_decode(w), 1e-5, "cfg1 T=36")
+    # split into 16-token partitions: the in-kernel merge must agree too
+    got_split = run_decode(w, cache, dev, partition_tokens=16)
+    assert_close({0: got_split[0]}, oracle_decode(w), 1e-5, "cfg1 T=36 split 16")
+
+
+@pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [
+    ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 32, 1, 128), ("bf16", 6, 3, 64),
+    ("f32", 4, 1, 64), ("f32", 8, 2, 128), ("fp8", 32, 8, 128), ("fp8", 16, 2, 64), ("bf16", 12, 2, 128),
+])
+@pytest.mark.parametrize("pt", [0, 16, 64, 512])
+def test_ragged_lengths_and_partitions(cache_dtype, hq, hkv, dh, pt):
+    dev = device()
+    lens_ = [1, 2, 15, 16, 17, 63, 511, 513, 1000]
+    w = workloads.decode_inputs("ragged", 1234 + hq + dh, lens_, hq, hkv, dh, cache_dtype, dev)
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev, partition_tokens=pt)
+    assert_close(got, oracle_decode(w), TOL[cache_dtype], f"{cache_dtype} {hq}/{hkv} dh{dh} pt{pt}")
+
+
+def test_empty_sequence_and_clamped_length():
+    dev = device()
+    w = workloads.decode_inputs("empty", 7, [0, 40, 0, 5], 8, 2, 128, "bf16", dev)
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev, partition_tokens=16)
+    assert np.array_equal(got[0], np.zeros_like(got[0])) and np.array_equal(got[2], np.zeros_like(got[2]))
+    assert_close({1: got[1], 3: got[3]}, oracle_decode(w, [1, 3]), 2e-3, "mixed empty")
+    # a batch of zero sequences launches nothing
+    out = pkv.pkv_attn_decode(cache, w.q[:0], tables(w, dev)[:0], lens(w, dev)[:0], 48, w.scale)
+    assert out.shape == (0, 8, 128)
+
+
+def test_cfg2_uniform_full_size():
+    dev = device()
+    w = workloads.cfg2("uniform", device=dev)
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev)
+    assert_close(got, oracle_decode(w), 2e-3, "cfg2 uniform")
+
+
+def test_cfg2_all4096_full_size_each_copy():
+    """The metric configuration, every table copy the benchmark rotates through."""
+    dev = device()
+    w = workloads.cfg2("all4096", device=dev, copies=2)
+    cache = build_cache(w, dev)
+    ref = oracle_decode(w)
+    scale_ref = max(float(np.abs(r).max()) for r in ref.values())
+    for c in range(w.copies):
+        got = run_decode(w, cache, dev, copy=c)
+        assert_close(got, ref, 2e-3, f"cfg2 all4096 copy {c}")
+        rel = max(float(np.abs(got[b] - ref[b]).max()) for b in ref) / scale_ref
+        assert rel < 2e-2
+
+
+@pytest.mark.parametrize("kind", ["mha", "gqa", "mqa", "gqa-fp8"])
+def test_cfg5_head_layouts_full_size(kind):
+    dev = device()
+    w = workloads.cfg5(kind, device=dev)
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev)
+    assert_close(got, oracle_decode(w), 2e-3, f"cfg5 {kind}")
+
+
+def test_cfg3_long_context_b1_layers_and_b4():
+    dev = device()
+    layers = workloads.cfg3(batch=1, device=dev, layers=3)
+    for li, w in enumerate(layers):
+        cache = build_cache(w, dev)
+        got = run_decode(w, cache, dev, partition_tokens=512)
+        assert_close(got, oracle_decode(w), 2e-3, f"cfg3 B=1 layer {li}")
+        del cache
+    w4 = workloads.cfg3(batch=4, device=dev, layers=1)[0]
+    cache = build_cache(w4, dev)
+    got = run_decode(w4, cache, dev, partition_tokens=512)
+    assert_close(got, oracle_decode(w4), 2e-3, "cfg3 B=4")
+
+
+@pytest.mark.parametrize("t,pt", [(37, 16), (4096, 0), (4096, 512), (32768, 512), (1, 0)])
+def test_position_probe(t, pt):
+    """q = 0 makes every weight exactly 1. V is one-hot, V[t, 1 + t % 127] = 1,
+    so out[d] = #{t : 1 + t % 127 = d} / T in exact fp32 arithmetic: a dropped
+    or doubled token moves one column by 1/T. Column 0 carries the ramp t/T,
+    whose mean is (T-1)/(2T)."""
+    dev = device()
+    w = workloads.decode_inputs("probe", 3, [t], 8, 2, 128, "f32", dev)
+    w.q.zero_()
+    w.v.zero_()
+    tok = torch.arange(t, device=dev)
+    w.v[tok, :, 0] = (tok.float() / t)[:, None]
+    w.v[tok, :, 1 + tok % 127] = 1.0
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev, partition_tokens=pt)
+    counts = np.bincount(1 + np.arange(t) % 127, minlength=128)[1:] / t
+    assert np.array_equal(got[0, :, 1:], np.broadcast_to(counts.astype(np.float32).astype(np.float64), (8, 127)))
+    assert np.abs(got[0, :, 0] - (t - 1) / (2 * t)).max() <= 1e-5
+
+
+def test_peaked_probe_bf16():
+    dev = device()
+    w = workloads.decode_inputs("peak", 4, [3000], 8, 2, 128, "bf16", dev)
+    hit = 1777
+    w.q[0] = (w.k[hit].repeat_interleave(4, dim=0).float() * 40.0).to(torch.bfloat16)
+    cache = build_cache(w, dev)
+    got = run_decode(w, cache, dev)
+    want = w.v[hit].repeat_interleave(4, dim=0).float().cpu().numpy()
+    assert np.abs(got[0] - want).max() <= 2e-3
+    assert_close({0: got[0]}, oracle_decode(w), 2e-3, "peaked")
+
+
+def test_relabelled_blocks_give_bit_identical_output():
+    dev = device()
+    w = workloads.decode_inputs("relabel", 8, [700, 33, 4096], 32, 8, 128, "bf16", dev, copies=2)
+    cache = build_cache(w, dev)
+    a = run_decode(w, cache, dev, copy=0)
+    b = run_decode(w, cache, dev, copy=1)
+    assert not np.array_equal(w.block_tables[0], w.block_tables[1])
+    assert np.array_equal(a, b)
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """The merge counters re-arm themselves: one zeroed workspace serves many
+    calls with different shapes."""
+    dev = device()
+    ws = torch.zeros(pkv.pkv_attn_decode_workspace_bytes(8, 32, 128, 4096, 16), dtype=torch.uint8, device=dev)
+    for seed, lens_ in [(1, [4096, 100, 17]), (2, [50] * 8), (3, [4096])]:
+        w = workloads.decode_inputs("reuse", seed, lens_, 32, 8, 128, "bf16", dev)
+        cache = build_cache(w, dev)
+        msl = w.max_blocks * 16
+        for _ in range(3):
+            out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev), lens(w, dev), msl, w.scale,
+                                      partition_tokens=16, workspace=ws)
+            torch.cuda.synchronize()
+            assert_close(out.cpu().double().numpy(), oracle_decode(w), 2e-3, f"reuse {seed}")
+    counters = ws.view(torch.int32)[-8 * 32:]
+    assert int(counters.abs().sum()) == 0

@@ -86,3 +86,13 @@ def test_dequantize_is_code_times_scale():
     codes = codes[~np.isnan(fp8.decode_table())]
     d = fp8.dequantize(codes, np.float32(0.25))
     assert np.array_equal(d, fp8.decode_table()[codes] * 0.25)
+
+
+def test_bf16_table_quantize_equals_elementwise():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 65536, size=4000).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    for inv in (np.float32(1.0) / np.float32(0.011), np.float32(3.0)):
+        with np.errstate(over="ignore", invalid="ignore"):
+            want = fp8.quantize(vals, inv)
+        assert np.array_equal(fp8.quantize_bf16_bits(bits, inv), want)
