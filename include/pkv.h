@@ -159,14 +159,15 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
  *   out:          device fp32 [batch, num_q_heads, head_dim]
  *   workspace:    device, at least pkv_attn_decode_workspace_bytes(...)
  *                 bytes for the same arguments; may be NULL when that size
- *                 is 0 (a single partition covers max_seq_len). Partial
- *                 results fill it from the front; merge counters (one int32
- *                 per sequence and query head) occupy its last bytes. It must
- *                 be zero-filled before first use; every completed call
- *                 leaves the counters at zero, so a buffer sized for the
- *                 largest batch·num_q_heads and the largest max_seq_len it
- *                 serves can be reused without clearing. Calls that share a
- *                 workspace must not overlap (one workspace per stream).
+ *                 is 0 (a single partition covers max_seq_len). It holds the
+ *                 partitions' fp32 (m, l) pairs [batch, Hq, P, 2] followed by
+ *                 their weighted sums u [batch, Hq, P, head_dim], P =
+ *                 ceil(max_seq_len / partition). Its contents need no
+ *                 initialisation; calls that share a workspace must not
+ *                 overlap (one workspace per stream).
+ * When more than one partition is needed the call launches two kernels on
+ * the stream: the split kernel, then a small reduce kernel that merges the
+ * partitions.
  * num_q_heads must be a multiple of num_kv_heads with Hq/Hkv <= 64. */
 PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                int32_t head_dim, int32_t max_seq_len,

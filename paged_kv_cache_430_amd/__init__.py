@@ -184,9 +184,10 @@ def pkv_attn_decode_auto_partition(batch, num_q_heads, max_seq_len):
 
 
 def decode_workspace(batch, num_q_heads, head_dim, max_seq_len, partition_tokens, device):
-    """A zero-filled workspace of the size pkv_attn_decode needs (or None)."""
+    """A workspace of the size pkv_attn_decode needs (or None); its contents
+    need no initialisation."""
     n = pkv_attn_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len, partition_tokens)
-    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def pkv_attn_decode(cache, q, block_tables, seq_lens, max_seq_len, scale, partition_tokens=0,

@@ -39,13 +39,15 @@ __device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
 
-// Lane exchange inside groups of four lanes (DPP quad_perm).
+// Lane exchange inside a row of 16 lanes (DPP).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowMirror = 0x140;      // lane i of a 16-lane row reads lane 15 - i
+constexpr int kRowHalfMirror = 0x141;  // lane i of an 8-lane half-row reads lane 7 - i
 
 // Sum over the four lanes of a quad; every lane of the quad receives it.
 __device__ __forceinline__ float quad_sum(float x) {
@@ -64,6 +66,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
   return x;
+}
+
+// Raw buffer loads: a resource names a base address and a byte limit; a load
+// at or past the limit returns zeros and makes no memory access.
+constexpr int kBufferRsrcWord3 = 0x00020000;   // gfx9 raw-buffer format word
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+  return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

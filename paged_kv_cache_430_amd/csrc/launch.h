@@ -44,7 +44,6 @@ struct DecodeParams {
   float* out;
   float* ws_ml;        // [batch, Hq, num_parts, 2] (m, l) in log2 units
   float* ws_u;         // [batch, Hq, num_parts, head_dim]
-  int32_t* ws_count;   // [batch, Hq / heads-per-workgroup]
 };
 
 // Heads of one KV group handled by one decode workgroup.

@@ -103,7 +103,7 @@ size_t decode_ws_bytes(int32_t batch, int32_t hq, int32_t dh, int32_t max_seq_le
   const int64_t parts = (max_seq_len + pt - 1) / pt;
   if (parts <= 1) return 0;
   const size_t rows = (size_t)batch * hq;
-  return (rows * parts * (dh + 2) + rows) * sizeof(float);
+  return rows * parts * (dh + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -245,11 +245,6 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   const size_t rows = (size_t)batch * num_q_heads;
   p.ws_ml = need ? ws : nullptr;
   p.ws_u = need ? ws + rows * parts * 2 : nullptr;
-  // counters live in the last `rows` ints of the buffer, so calls of different
-  // shapes sharing one buffer never write partials over each other's counters
-  p.ws_count = need ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (workspace_bytes & ~size_t(3))) -
-                          rows
-                    : nullptr;
   return hip_status(launch_decode(p, s), "pkv_attn_decode");
 }
 

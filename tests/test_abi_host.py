@@ -102,7 +102,7 @@ def test_decode_argument_validation(lib):
     assert call(scale=float("nan")) == pkv.PKV_EINVAL
     # split-KV needs workspace; sized by the query call
     need = lib.pkv_attn_decode_workspace_bytes(2, 32, 128, 64, 16)
-    assert need == (2 * 32 * 4 * 130 + 2 * 32) * 4
+    assert need == 2 * 32 * 4 * 130 * 4                     # (m, l) and u per partition
     assert call(pt=16) == pkv.PKV_EWORKSPACE
     assert call(pt=16, ws=0x90000, wsb=need - 4) == pkv.PKV_EWORKSPACE
     assert call(b=0) == pkv.PKV_OK                           # nothing to do, nothing launched

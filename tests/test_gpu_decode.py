@@ -178,10 +178,11 @@ def test_relabelled_blocks_give_bit_identical_output():
 
 
 def test_workspace_reuse_across_calls_and_shapes():
-    """The merge counters re-arm themselves: one zeroed workspace serves many
-    calls with different shapes."""
+    """The workspace needs no initialisation: one buffer, filled with NaN bytes
+    first, serves many calls with different shapes."""
     dev = device()
-    ws = torch.zeros(pkv.pkv_attn_decode_workspace_bytes(8, 32, 128, 4096, 16), dtype=torch.uint8, device=dev)
+    n = pkv.pkv_attn_decode_workspace_bytes(8, 32, 128, 4096, 16)
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device=dev).view(torch.uint8)
     for seed, lens_ in [(1, [4096, 100, 17]), (2, [50] * 8), (3, [4096])]:
         w = workloads.decode_inputs("reuse", seed, lens_, 32, 8, 128, "bf16", dev)
         cache = build_cache(w, dev)
@@ -191,5 +192,3 @@ def test_workspace_reuse_across_calls_and_shapes():
                                       partition_tokens=16, workspace=ws)
             torch.cuda.synchronize()
             assert_close(out.cpu().double().numpy(), oracle_decode(w), 2e-3, f"reuse {seed}")
-    counters = ws.view(torch.int32)[-8 * 32:]
-    assert int(counters.abs().sum()) == 0
