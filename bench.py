@@ -166,7 +166,7 @@ def main():
     slots = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty(B, hq, dh, dtype=torch.float32, device=dev)
     pt = args.partition
-    ws = pkv.decode_workspace(B, hq, dh, T, pt, dev)
+    ws = pkv.decode_workspace(B, hq, hkv, dh, T, pt, dev)
     lib = pkv.load()
     wsp = ws.data_ptr() if ws is not None else None
     wsb = ws.numel() if ws is not None else 0
@@ -260,7 +260,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": dh,
                    "seq_len": T, "block_size": 16, "layers": len(layers), "pool_copies": copies,
-                   "partition_tokens": pt or pkv.pkv_attn_decode_auto_partition(B, hq, T)},
+                   "partition_tokens": pt or pkv.pkv_attn_decode_auto_partition(B, hq, hkv, T)},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "new_tokens_per_s": round(B / (ms_step * 1e-3) if len(layers) == 1 else B / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w0.seq_lens.sum()) * len(layers) / (ms_step * 1e-3), 1),

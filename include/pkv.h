@@ -155,7 +155,8 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
  *   max_seq_len:  host bound on seq_lens (sizes the grid and the workspace)
  *   scale:        score scale (1/sqrt(head_dim) for standard attention)
  *   partition_tokens: tokens per split-KV partition, a multiple of
- *                 block_size in [16, 1024]; 0 picks one from the shape
+ *                 block_size in [16, 8192]; 0 picks one from the shape
+ *                 (pkv_attn_decode_auto_partition)
  *   out:          device fp32 [batch, num_q_heads, head_dim]
  *   workspace:    device, at least pkv_attn_decode_workspace_bytes(...)
  *                 bytes for the same arguments; may be NULL when that size
@@ -170,8 +171,8 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
  * partitions.
  * num_q_heads must be a multiple of num_kv_heads with Hq/Hkv <= 64. */
 PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
-                                               int32_t head_dim, int32_t max_seq_len,
-                                               int32_t partition_tokens);
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_seq_len, int32_t partition_tokens);
 
 PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype,
                             int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
@@ -179,9 +180,14 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
                             float scale, int32_t partition_tokens, float* out,
                             void* workspace, size_t workspace_bytes, pkv_stream stream);
 
-/* The partition size pkv_attn_decode uses when partition_tokens is 0. */
+/* The partition size pkv_attn_decode uses when partition_tokens is 0: with
+ * units = batch · num_kv_heads · (query-head chunks per KV head), every
+ * sequence is split into ceil(256 / units) partitions — one 8-wave workgroup
+ * per MI355X compute unit, no split when the units already fill the chip —
+ * rounded up to whole blocks, at least 256 tokens (or max_seq_len if
+ * shorter) and at most 8192. */
 PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads,
-                                               int32_t max_seq_len);
+                                               int32_t num_kv_heads, int32_t max_seq_len);
 
 /* ---------------------------------------------------------------------------
  * Causal chunked prefill over a cached prefix — [P3] 6.6 (long prefills are

@@ -10,29 +10,30 @@
 // at the last position, so nothing is masked but the unused tail of the last
 // block.
 //
-// One workgroup (4 waves) owns (sequence b, KV head g, a chunk of HC query
+// One workgroup (NW = 8 waves) owns (sequence b, KV head g, a chunk of HC query
 // heads of that group, partition π of part_tokens tokens). Each wave streams
 // the blocks w, w+4, w+8, … of π in a single pass:
 //   * the wave's block-table entries are loaded once, one per lane, and read
 //     back with a lane read into a scalar register;
-//   * K and V of the next block are loaded while the current one is used
-//     (16-byte loads; a token row of one head is read by row_bytes/16
-//     consecutive lanes, so every load instruction covers whole rows);
-//   * a lane holds an EPC-element column slice of several token rows; the
-//     score of a (token, head) is the sum over the row's lanes (DPP), so every
-//     lane of the row ends with it and multiplies its own V slice by p;
+//   * K and V of the next block are loaded while the current one is used,
+//     through raw buffer loads whose record limit masks what must not be read
+//     (non-temporal: every byte is read once);
+//   * K is held with few lanes per token row (LPK), so a score is a short DPP
+//     sum and each lane computes few exponentials; V is held with a row per
+//     RB/16 consecutive lanes (every load covers whole rows) and p moves from
+//     the K lanes to the V lanes through a small per-wave LDS slot;
 //   * online softmax per head in the log2 domain: the running max moves only
 //     when a block raises it, and only then are l and the accumulators
 //     rescaled (the wave-uniform branch is rarely taken once the max settles).
-// At the end the wave's accumulators are summed over its row groups, the four
+// At the end the wave's accumulators are summed over its lane groups, the
 // waves are merged through LDS, and either o = u / l is written (one
 // partition) or (m, l, u) go to the workspace for a second, small kernel that
 // merges the partitions. (Merging in the last workgroup to finish would need
 // a device-scope release per workgroup, which writes back the L2 of its XCD
 // every time; the kernel boundary does that once.)
-// Masked slots (past the sequence end) are selected out, never multiplied by
-// zero, and blocks whose id is outside the pool are skipped: pool slots may
-// hold NaN.
+// Masked slots (past the sequence end) are selected out or read as zeros,
+// never multiplied by zero, and blocks whose id is outside the pool are
+// skipped: pool slots may hold NaN.
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,20 +41,30 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kMergeThreads = 256;
 
-template <int KV, int DH>
+// Register layouts of one (block, head) tile of 16 token rows, RB bytes each.
+// K: a row is read by LPK lanes (4, 8 or 16); lane (tk = lane / LPK,
+//    jk = lane % LPK) holds rows tk + TPK·i (i < NTK) and, of each, the 16-byte
+//    chunks c·LPK + jk (c < NCK). A score is a sum over the LPK lanes of a row.
+// V: a row is read by LPV = RB/16 consecutive lanes, so each load covers whole
+//    rows; lane (rv, cv) holds rows rv + RPV·i (i < NIV), bytes cv·16 … +15.
+template <int KV, int DH, int LPK_>
 struct Geometry {
   static constexpr int ESZ = KV == kF32 ? 4 : KV == kBF16 ? 2 : 1;  // stored bytes per element
   static constexpr int RB = DH * ESZ;         // bytes of one token row of one head
-  static constexpr int LPR = RB / 16;         // lanes per row (16 bytes each)
-  static constexpr int RPI = kWave / LPR;     // rows covered by one wave load
-  static constexpr int NI = kBlockSize / RPI; // loads per block (per K or V)
-  static constexpr int EPC = 16 / ESZ;        // elements in a lane's 16-byte slice
-  // q dwords per head and lane: fp32 values, or packed bf16 pairs
-  static constexpr int QD = KV == kF32 ? EPC : EPC / 2;
-  static_assert(LPR >= 4 && LPR <= 32 && NI >= 1, "unsupported row size");
+  static constexpr int EPC = 16 / ESZ;        // elements in a 16-byte slice
+  // q dwords per 16-byte K slice: fp32 values, or packed bf16 pairs
+  static constexpr int QD = KV == kF32 ? 4 : EPC / 2;
+  static constexpr int LPK = LPK_ < RB / 16 ? LPK_ : RB / 16;
+  static constexpr int TPK = kWave / LPK;     // rows per K load
+  static constexpr int NTK = kBlockSize / TPK;
+  static constexpr int NCK = RB / (16 * LPK);
+  static constexpr int LPV = RB / 16;
+  static constexpr int RPV = kWave / LPV;
+  static constexpr int NIV = kBlockSize / RPV;
+  static_assert(LPK >= 4 && NTK >= 1 && NCK >= 1 && LPV >= 4 && LPV <= 32 && NIV >= 1,
+                "unsupported row size");
 };
 
 struct KernelArgs {
@@ -80,17 +91,38 @@ struct MergeArgs {
   int hq, head_dim, max_blocks, max_seq_len, part_tokens, num_parts;
 };
 
-// Sum over the LPR consecutive lanes of a row (LPR = 4, 8, 16 or 32); every
-// lane of the row receives the same bits (each step adds a commutative pair).
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
+// Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane
+// of a group receives the same bits (each step adds a commutative pair).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
   x += dpp_f32<kQuadXor1>(x);
   x += dpp_f32<kQuadXor2>(x);
-  if constexpr (LPR >= 8) x += dpp_f32<kRowHalfMirror>(x);
-  if constexpr (LPR >= 16) x += dpp_f32<kRowMirror>(x);
-  if constexpr (LPR >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (N >= 8) x += dpp_f32<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f32<kRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, kWave);
   return x;
 }
+
+// Combine x across the 64 / N lane groups of size N, keeping each lane's
+// position within its group (row rotations by 4 and 8 lanes, then exchanges
+// across rows); every lane receives the combination of its position's
+// values. The order of combination may differ between lanes, so a sum may
+// differ in its last bits from lane to lane; a max does not.
+template <int N, typename Op>
+__device__ __forceinline__ float across_groups(float x, Op op) {
+  if constexpr (N <= 4) x = op(x, dpp_f32<kRowRor4>(x));
+  if constexpr (N <= 8) x = op(x, dpp_f32<kRowRor8>(x));
+  if constexpr (N <= 16) x = op(x, __shfl_xor(x, 16, kWave));
+  x = op(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+
+struct MaxOp {
+  __device__ float operator()(float x, float y) const { return fmaxf(x, y); }
+};
+struct AddOp {
+  __device__ float operator()(float x, float y) const { return x + y; }
+};
 
 // Score contribution of one 16-byte K slice against one head's q slice.
 template <int KV, int QD>
@@ -141,18 +173,30 @@ __device__ __forceinline__ void slice_values(const uint4& v, float (&f)[EPC]) {
   }
 }
 
-// exp2 with exp2(−inf − x) taken as 0 also when x is −inf (an empty part).
+// exp2(m − mt), taken as 0 for an empty part (m = −inf), also when mt is −inf.
 __device__ __forceinline__ float part_weight(float m, float mt) {
   return m == -INFINITY ? 0.0f : fast_exp2(m - mt);
 }
 
-template <int KV, int DH, int HC>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
-  using G = Geometry<KV, DH>;
-  constexpr int NI = G::NI, EPC = G::EPC, QD = G::QD, LPR = G::LPR, RPI = G::RPI;
+// Order the compiler's LDS accesses of one wave around a lane exchange (the
+// hardware already executes one wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KV, int DH, int HC, int LPK_, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) {
+  constexpr int kWaves = NW, kThreads = NW * kWave;
+  using G = Geometry<KV, DH, LPK_>;
+  constexpr int EPC = G::EPC, QD = G::QD, LPK = G::LPK, TPK = G::TPK, NTK = G::NTK, NCK = G::NCK;
+  constexpr int LPV = G::LPV, RPV = G::RPV, NIV = G::NIV;
+  constexpr bool kSameLayout = LPK == LPV;    // p is already in the lanes that hold V
   __shared__ float sh_u[kWaves][HC][DH];
   __shared__ float sh_m[kWaves][HC];
   __shared__ float sh_l[kWaves][HC];
+  __shared__ __attribute__((aligned(16))) float sh_p[kWaves][kBlockSize][HC];   // K lanes → V lanes
 
   // ---- which (b, g, chunk, partition) ----------------------------------------
   const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
@@ -163,8 +207,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
   const int group = a.hq / a.hkv;
   const int h0 = g * group + chunk * HC;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int T = min(max(a.seq_lens[b], 0), min(a.max_seq_len, a.max_blocks * kBlockSize));
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform, and known to be
+  const int T = __builtin_amdgcn_readfirstlane(
+      min(max(a.seq_lens[b], 0), min(a.max_seq_len, a.max_blocks * kBlockSize)));
   const int nparts = (T + a.part_tokens - 1) / a.part_tokens;
   if (part >= nparts) {
     if (part == 0) {  // empty sequence: zeros
@@ -180,23 +226,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
   const int my_phys = lane < nbw ? bt[w + kWaves * lane] : -1;
   const size_t head_stride = (size_t)kBlockSize * G::RB;     // bytes of one (block, head)
 
-  const int r = lane / LPR, cc = lane % LPR;                  // row group, 16-byte column
-  const int lane_off = r * G::RB + cc * 16;                  // within a (block, head) tile
+  const int tk = lane / LPK, jk = lane % LPK;                 // K layout
+  const int rv = lane / LPV, cv = lane % LPV;                 // V layout
+  const int koff = tk * G::RB + jk * 16;
+  const int voff = rv * G::RB + cv * 16;
 
-  // q slices of the HC heads
-  uint32_t qreg[HC][QD];
+  // q slices matching the lane's K chunks
+  uint32_t qreg[HC][NCK][QD];
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
     const size_t row = (size_t)b * a.hq + h0 + h;
-    if constexpr (KV == kF32) {
-      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + row * DH + cc * EPC);
-      qreg[h][0] = x.x; qreg[h][1] = x.y; qreg[h][2] = x.z; qreg[h][3] = x.w;
-    } else {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * DH + cc * EPC;
 #pragma unroll
-      for (int c = 0; c < QD / 4; ++c) {
-        const uint4 x = *reinterpret_cast<const uint4*>(qp + 8 * c);
-        qreg[h][4 * c] = x.x; qreg[h][4 * c + 1] = x.y; qreg[h][4 * c + 2] = x.z; qreg[h][4 * c + 3] = x.w;
+    for (int c = 0; c < NCK; ++c) {
+      const int e0 = (c * LPK + jk) * EPC;   // first element of the chunk
+      if constexpr (KV == kF32) {
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + row * DH + e0);
+        qreg[h][c][0] = x.x; qreg[h][c][1] = x.y; qreg[h][c][2] = x.z; qreg[h][c][3] = x.w;
+      } else {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * DH + e0;
+#pragma unroll
+        for (int k = 0; k < QD / 4; ++k) {
+          const uint4 x = *reinterpret_cast<const uint4*>(qp + 8 * k);
+          qreg[h][c][4 * k] = x.x; qreg[h][c][4 * k + 1] = x.y;
+          qreg[h][c][4 * k + 2] = x.z; qreg[h][c][4 * k + 3] = x.w;
+        }
       }
     }
   }
@@ -212,56 +265,66 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
     for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
   }
 
-  // Buffer resources over the wave's j-th (block, head) tile of K and V. An id
-  // outside the pool, and j past the wave's last block, give zero records:
-  // their loads return zeros without touching memory, so loads need no branch.
-  auto tile_rsrc = [&](const uint8_t* pool, int phys) {
+  // Buffer resources over the wave's j-th (block, head) tile of K and V. The
+  // record limit is the block's valid rows: an id outside the pool, j past the
+  // wave's last block and rows past the sequence end read as zeros without a
+  // memory access, so loads need no branch and masked V rows are exact zeros.
+  auto tile_rsrc = [&](const uint8_t* pool, int phys, int rows) {
     const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
     const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, ok ? (int)head_stride : 0,
-                                             kBufferRsrcWord3);
+    // the record count is wave-uniform; reading it from the first lane keeps
+    // the resource in scalar registers (no per-lane loop around the loads)
+    const int records = __builtin_amdgcn_readfirstlane(ok ? rows * G::RB : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
   };
-  auto load_block = [&](int j, uint4 (&kb)[NI], uint4 (&vb)[NI]) {
+  auto rows_of = [&](int j) {   // valid rows of the wave's j-th block (wave-uniform)
+    return min(kBlockSize, max(0, ntok - (w + kWaves * j) * kBlockSize));
+  };
+  auto load_block = [&](int j, uint4 (&kb)[NTK][NCK], uint4 (&vb)[NIV]) {
     const int phys = __builtin_amdgcn_readlane(my_phys, j);
-    const auto rk = tile_rsrc(a.kc, phys);
-    const auto rv = tile_rsrc(a.vc, phys);
+    const int rows = rows_of(j);
+    const auto rk = tile_rsrc(a.kc, phys, rows);
+    const auto rvs = tile_rsrc(a.vc, phys, rows);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kb[i] = buffer_load16(rk, lane_off + i * RPI * G::RB);
+    for (int i = 0; i < NTK; ++i)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vb[i] = buffer_load16(rv, lane_off + i * RPI * G::RB);
+      for (int c = 0; c < NCK; ++c) kb[i][c] = buffer_load16_stream(rk, koff + i * TPK * G::RB + c * LPK * 16);
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) vb[i] = buffer_load16_stream(rvs, voff + i * RPV * G::RB);
   };
 
-  auto use_block = [&](int j, const uint4 (&kb)[NI], const uint4 (&vb)[NI]) {
+  auto use_block = [&](int j, const uint4 (&kb)[NTK][NCK], const uint4 (&vb)[NIV]) {
     const int phys = __builtin_amdgcn_readlane(my_phys, j);
     if ((unsigned)phys >= (unsigned)a.num_blocks) return;     // contributes nothing
-    const int lb = w + kWaves * j;                             // block within the partition
-    const int valid_rows = ntok - lb * kBlockSize;             // >= 1
-    // scores of the lane's NI tokens for the HC heads
-    float s[HC][NI];
+    const int rows = rows_of(j);                               // >= 1
+    // scores of the lane's NTK rows for the HC heads (rows past the end: −inf)
+    float s[HC][NTK];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      uint32_t kk[QD];
-      k_operand<KV, QD>(kb[i], kk);
+    for (int i = 0; i < NTK; ++i) {
+      float ps[HC];
 #pragma unroll
-      for (int h = 0; h < HC; ++h) s[h][i] = row_sum<LPR>(slice_dot<KV, QD>(qreg[h], kk, 0.0f)) * sc;
-    }
-    bool row_ok[NI];
+      for (int h = 0; h < HC; ++h) ps[h] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) row_ok[i] = r + RPI * i < valid_rows;
-    if (valid_rows < kBlockSize) {                             // tail block: select out
+      for (int c = 0; c < NCK; ++c) {
+        uint32_t kk[QD];
+        k_operand<KV, QD>(kb[i][c], kk);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+        for (int h = 0; h < HC; ++h) ps[h] = slice_dot<KV, QD>(qreg[h][c], kk, ps[h]);
+      }
+      const bool ok = tk + TPK * i < rows;
 #pragma unroll
-        for (int h = 0; h < HC; ++h) s[h][i] = row_ok[i] ? s[h][i] : -INFINITY;
+      for (int h = 0; h < HC; ++h) {
+        const float v = group_sum<LPK>(ps[h]) * sc;
+        s[h][i] = ok ? v : -INFINITY;
+      }
     }
     // block max per head; rescale only when it raises the running max
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
       float bm = s[h][0];
 #pragma unroll
-      for (int i = 1; i < NI; ++i) bm = fmaxf(bm, s[h][i]);
-#pragma unroll
-      for (int off = LPR; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off, kWave));
+      for (int i = 1; i < NTK; ++i) bm = fmaxf(bm, s[h][i]);
+      bm = across_groups<LPK>(bm, MaxOp());
       if (bm > m[h]) {
         const float alpha = m[h] == -INFINITY ? 0.0f : fast_exp2(m[h] - bm);
         l[h] *= alpha;
@@ -270,28 +333,62 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
         m[h] = bm;
       }
     }
-    // p = 2^(s − m); l += p; acc += p · v (rows past the end are zero-filled
-    // by the tile's record limit only for whole blocks, so select them out)
+    // p = 2^(s − m); every lane of a K row holds the same p, so l is summed
+    // across K rows only at the end
+    float p[HC][NTK];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int h = 0; h < HC; ++h)
+#pragma unroll
+      for (int i = 0; i < NTK; ++i) {
+        p[h][i] = fast_exp2(s[h][i] - m[h]);
+        l[h] += p[h][i];
+      }
+    // p of the lane's V rows
+    float pv[HC][NIV];
+    if constexpr (kSameLayout) {
+#pragma unroll
+      for (int h = 0; h < HC; ++h)
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) pv[h][i] = p[h][i];
+    } else {
+      // the LPK lanes of a K row share out the heads; the wave's own slot of
+      // sh_p is written and read back by that wave only
+#pragma unroll
+      for (int i = 0; i < NTK; ++i)
+#pragma unroll
+        for (int h = 0; h < HC; ++h)
+          if (h % LPK == jk) sh_p[w][tk + TPK * i][h] = p[h][i];
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) {
+        const float* src = sh_p[w][rv + RPV * i];
+        if constexpr (HC % 4 == 0) {
+#pragma unroll
+          for (int h4 = 0; h4 < HC; h4 += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(src + h4);
+            pv[h4][i] = x.x; pv[h4 + 1][i] = x.y; pv[h4 + 2][i] = x.z; pv[h4 + 3][i] = x.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < HC; ++h) pv[h][i] = src[h];
+        }
+      }
+      wave_lds_sync();
+    }
+    // acc += p · v (V rows past the end were read as zeros)
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
       float f[EPC];
       slice_values<KV, EPC>(vb[i], f);
-      if (valid_rows < kBlockSize) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) f[e] = row_ok[i] ? f[e] : 0.0f;
-      }
+      for (int h = 0; h < HC; ++h)
 #pragma unroll
-      for (int h = 0; h < HC; ++h) {
-        const float p = fast_exp2(s[h][i] - m[h]);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(p, f[e], acc[h][e]);
-      }
+        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(pv[h][i], f[e], acc[h][e]);
     }
   };
 
   {
-    uint4 k0[NI], v0[NI], k1[NI], v1[NI];
+    uint4 k0[NTK][NCK], v0[NIV], k1[NTK][NCK], v1[NIV];
     load_block(0, k0, v0);
     for (int j = 0; j < nbw; j += 2) {
       load_block(j + 1, k1, v1);
@@ -301,22 +398,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
     }
   }
 
-  // ---- the wave's totals: sum over its row groups ----------------------------
+  // ---- the wave's totals -----------------------------------------------------------
+  // l: one copy per K row group → combine across K row groups; acc: combine
+  // across V row groups. Afterwards every lane holds the wave's totals.
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
+  for (int h = 0; h < HC; ++h) l[h] = across_groups<LPK>(l[h], AddOp());
 #pragma unroll
-    for (int h = 0; h < HC; ++h) {
-      l[h] += __shfl_xor(l[h], off, kWave);
+  for (int h = 0; h < HC; ++h)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, kWave);
-    }
-  }
-  // every lane of a row now holds the totals of the wave's tokens
-  if (r == 0) {
+    for (int e = 0; e < EPC; ++e) acc[h][e] = across_groups<LPV>(acc[h][e], AddOp());
+  if (rv == 0) {
 #pragma unroll
     for (int h = 0; h < HC; ++h)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) sh_u[w][h][cc * EPC + e] = acc[h][e];
+      for (int e = 0; e < EPC; ++e) sh_u[w][h][cv * EPC + e] = acc[h][e];
   }
   if (lane == 0) {
 #pragma unroll
@@ -356,8 +451,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KernelArgs a) {
 // π left m_π (log2 domain), l_π and u_π; with m* = max m_π the output is
 // Σ 2^(m_π − m*) u_π / Σ 2^(m_π − m*) l_π. Rows of sequences that fit in one
 // partition were finished by the split kernel and are left alone.
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(MergeArgs a) {
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
+  const size_t idx = (size_t)blockIdx.x * kMergeThreads + threadIdx.x;
   if (idx >= a.total) return;
   const size_t row = idx / a.head_dim;
   const int d = (int)(idx % a.head_dim);
@@ -368,21 +463,45 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(MergeArgs a) {
   const int P = a.num_parts;
   const float* ml = a.ws_ml + row * P * 2;
   const float* u = a.ws_u + row * P * a.head_dim + d;
-  float mt = -INFINITY;
-  for (int pp = 0; pp < nparts; ++pp) mt = fmaxf(mt, ml[2 * pp]);
-  float lt = 0.0f, ut = 0.0f;
-  for (int pp = 0; pp < nparts; ++pp) {
-    const float wgt = part_weight(ml[2 * pp], mt);
-    lt = fmaf(wgt, ml[2 * pp + 1], lt);
-    ut = fmaf(wgt, u[(size_t)pp * a.head_dim], ut);
+  // online merge, eight partitions per round so their loads are in flight together
+  float mt = -INFINITY, lt = 0.0f, ut = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += 8) {
+    float pm[8], pl[8], pu[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = p0 + k < nparts;
+      pm[k] = ok ? ml[2 * (p0 + k)] : -INFINITY;
+      pl[k] = ok ? ml[2 * (p0 + k) + 1] : 0.0f;
+      pu[k] = ok ? u[(size_t)(p0 + k) * a.head_dim] : 0.0f;
+    }
+    float mr = mt;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mr = fmaxf(mr, pm[k]);
+    const float c = part_weight(mt, mr);
+    lt *= c;
+    ut *= c;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wgt = part_weight(pm[k], mr);
+      lt = fmaf(wgt, pl[k], lt);
+      ut = fmaf(wgt, pu[k], ut);
+    }
+    mt = mr;
   }
   a.out[idx] = lt > 0.0f ? ut / lt : 0.0f;
 }
 
+// Lanes per K row: 4 keeps the score reduction to two DPP steps and one
+// exponential per lane and head; eight heads per workgroup take 8 so that
+// their q slices fit in fewer registers.
+template <int HC>
+constexpr int k_lanes() { return HC >= 8 ? 8 : 4; }
+
 template <int KV, int DH, int HC>
 hipError_t launch_t(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
   const size_t n = (size_t)p.batch * p.cache.num_kv_heads * a.num_chunks * p.num_parts;
-  hipLaunchKernelGGL((decode_split_kernel<KV, DH, HC>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<KV, DH, HC, k_lanes<HC>(), kDecodeWaves>), dim3((unsigned)n),
+                     dim3(kDecodeWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -447,8 +566,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   m.max_seq_len = p.max_seq_len;
   m.part_tokens = p.part_tokens;
   m.num_parts = p.num_parts;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((m.total + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, m);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((m.total + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, s, m);
   return hipGetLastError();
 }
 

@@ -48,6 +48,8 @@ constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRowMirror = 0x140;      // lane i of a 16-lane row reads lane 15 - i
 constexpr int kRowHalfMirror = 0x141;  // lane i of an 8-lane half-row reads lane 7 - i
+constexpr int kRowRor4 = 0x124;        // rotate each 16-lane row by 4 lanes
+constexpr int kRowRor8 = 0x128;        // rotate each 16-lane row by 8 lanes
 
 // Sum over the four lanes of a quad; every lane of the quad receives it.
 __device__ __forceinline__ float quad_sum(float x) {
@@ -71,10 +73,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Raw buffer loads: a resource names a base address and a byte limit; a load
 // at or past the limit returns zeros and makes no memory access.
 constexpr int kBufferRsrcWord3 = 0x00020000;   // gfx9 raw-buffer format word
+constexpr int kCacheNonTemporal = 2;            // cache-policy operand: nt
 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
   typedef int v4i __attribute__((ext_vector_type(4)));
   const v4i x = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+  return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+}
+
+// The same load with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ uint4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kCacheNonTemporal);
   return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
 }
 

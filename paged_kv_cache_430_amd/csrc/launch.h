@@ -46,6 +46,11 @@ struct DecodeParams {
   float* ws_u;         // [batch, Hq, num_parts, head_dim]
 };
 
+// Waves of one split-KV decode workgroup. A wave reads its share of the
+// partition's table entries one per lane, so a partition holds at most
+// 64 * kDecodeWaves blocks.
+constexpr int kDecodeWaves = 8;
+
 // Heads of one KV group handled by one decode workgroup.
 int decode_heads_per_wg(int group);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include <string>
@@ -23,7 +24,13 @@ std::string& last_error() {
 
 namespace {
 
-constexpr int32_t kMaxPartition = 1024;
+// a wave reads its share of a partition's table entries one per lane
+constexpr int32_t kMaxPartition = 64 * 16 * kDecodeWaves;
+// MI355X compute units: the automatic partition size aims at one decode
+// workgroup (8 waves, a whole CU at the kernel's register use) per CU
+constexpr int32_t kComputeUnits = 256;
+// below this many tokens a partition is not split further
+constexpr int32_t kMinPartition = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -86,16 +93,25 @@ int check_tables(const std::vector<int32_t>& bt, int max_blocks, int seq, int to
   return PKV_OK;
 }
 
-int32_t auto_partition(int32_t batch, int32_t hq, int32_t max_seq_len) {
-  if (max_seq_len <= 512) return max_seq_len <= 16 ? 16 : (max_seq_len + 15) / 16 * 16;
-  int32_t pt = 512;
-  const int64_t units = (int64_t)batch * (hq >= 4 ? hq / 4 : 1);
-  while (pt > 128 && units * ((max_seq_len + pt - 1) / pt) < 1024) pt /= 2;
-  return pt;
+// Partition size for pkv_attn_decode when the caller passes 0. A workgroup
+// owns (sequence, KV head, chunk of up to 8 query heads, partition); with
+// units = batch · Hkv · chunks, split each sequence into ceil(256 / units)
+// partitions (one round of workgroups over the CUs, no split when the units
+// already fill the chip), never below 256 tokens and never above the
+// largest partition one workgroup can take.
+int32_t auto_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
+  const int32_t msl16 = (std::max(max_seq_len, 1) + 15) / 16 * 16;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return std::min(msl16, kMaxPartition);
+  const int group = hq / hkv;
+  const int64_t units = (int64_t)batch * hkv * (group / decode_heads_per_wg(group));
+  const int64_t parts = std::max<int64_t>(1, (kComputeUnits + units - 1) / units);
+  int32_t pt = (int32_t)(((max_seq_len + parts - 1) / parts + 15) / 16 * 16);
+  pt = std::max(pt, std::min(kMinPartition, msl16));
+  return std::min(pt, kMaxPartition);
 }
 
-int32_t effective_partition(int32_t batch, int32_t hq, int32_t max_seq_len, int32_t pt) {
-  return pt == 0 ? auto_partition(batch, hq, max_seq_len) : pt;
+int32_t effective_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len, int32_t pt) {
+  return pt == 0 ? auto_partition(batch, hq, hkv, max_seq_len) : pt;
 }
 
 size_t decode_ws_bytes(int32_t batch, int32_t hq, int32_t dh, int32_t max_seq_len, int32_t pt) {
@@ -178,14 +194,16 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
                     "pkv_kv_append");
 }
 
-PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                               int32_t max_seq_len, int32_t partition_tokens) {
-  const int32_t pt = effective_partition(batch, num_q_heads, max_seq_len, partition_tokens);
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_seq_len,
+                                               int32_t partition_tokens) {
+  const int32_t pt = effective_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
   return decode_ws_bytes(batch, num_q_heads, head_dim, max_seq_len, pt);
 }
 
-PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads, int32_t max_seq_len) {
-  return auto_partition(batch, num_q_heads, max_seq_len);
+PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t max_seq_len) {
+  return auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len);
 }
 
 PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
@@ -203,7 +221,7 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   if ((int64_t)max_seq_len > (int64_t)max_blocks * 16)
     return fail(PKV_EINVAL, "pkv_attn_decode: max_seq_len exceeds max_blocks * block_size");
   if (partition_tokens != 0 && (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16))
-    return fail(PKV_EINVAL, "pkv_attn_decode: partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
+    return fail(PKV_EINVAL, "pkv_attn_decode: partition_tokens must be 0 or a multiple of 16 in [16, " + std::to_string(kMaxPartition) + "]");
   const bool ok_q = (c.dtype == PKV_F32 && q_dtype == PKV_F32) ||
                     (c.dtype != PKV_F32 && q_dtype == PKV_BF16);
   if (!ok_q) return fail(PKV_EDTYPE, "pkv_attn_decode: q dtype must be F32 for an F32 cache, BF16 otherwise");
@@ -211,7 +229,7 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, "pkv_attn_decode: NULL pointer");
   if (!aligned16(q)) return fail(PKV_EINVAL, "pkv_attn_decode: q must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_decode: scale is not finite");
-  const int32_t pt = effective_partition(batch, num_q_heads, max_seq_len, partition_tokens);
+  const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens);
   const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
   if (need > 0 && (!workspace || workspace_bytes < need))

@@ -96,26 +96,36 @@ def test_decode_argument_validation(lib):
     assert call(hq=8 * 65) == pkv.PKV_EINVAL                 # group above 64
     assert call(msl=65) == pkv.PKV_EINVAL                    # beyond max_blocks * 16
     assert call(pt=24) == pkv.PKV_EINVAL                     # not a multiple of 16
-    assert call(pt=2048) == pkv.PKV_EINVAL
+    assert call(pt=8208) == pkv.PKV_EINVAL
     assert call(qd=pkv.PKV_F32) == pkv.PKV_EDTYPE            # bf16 cache wants bf16 q
     assert call(q=0x50004) == pkv.PKV_EINVAL                 # misaligned q
     assert call(scale=float("nan")) == pkv.PKV_EINVAL
     # split-KV needs workspace; sized by the query call
-    need = lib.pkv_attn_decode_workspace_bytes(2, 32, 128, 64, 16)
+    need = lib.pkv_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 16)
     assert need == 2 * 32 * 4 * 130 * 4                     # (m, l) and u per partition
     assert call(pt=16) == pkv.PKV_EWORKSPACE
     assert call(pt=16, ws=0x90000, wsb=need - 4) == pkv.PKV_EWORKSPACE
     assert call(b=0) == pkv.PKV_OK                           # nothing to do, nothing launched
-    assert lib.pkv_attn_decode_workspace_bytes(2, 32, 128, 64, 64) == 0
+    assert lib.pkv_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 64) == 0
 
 
 def test_auto_partition_rule(lib):
-    assert lib.pkv_attn_decode_auto_partition(1, 4, 36) == 48
-    assert lib.pkv_attn_decode_auto_partition(32, 32, 4096) == 512
-    assert lib.pkv_attn_decode_auto_partition(1, 32, 32768) == 256
-    for b, hq, t in [(1, 1, 100000), (8, 32, 8192), (64, 32, 2049)]:
-        p = lib.pkv_attn_decode_auto_partition(b, hq, t)
-        assert 16 <= p <= 1024 and p % 16 == 0
+    """ceil(256 / units) partitions of whole blocks, at least 256 tokens (or the
+    whole sequence), at most 8192; units = batch * Hkv * query-head chunks."""
+    ap = lib.pkv_attn_decode_auto_partition
+    assert ap(1, 4, 1, 36) == 48                 # short: one partition of whole blocks
+    assert ap(32, 32, 8, 4096) == 4096           # 256 units fill the chip: no split
+    assert ap(8, 32, 8, 8192) == 2048            # 64 units: 4 partitions
+    assert ap(1, 32, 8, 32768) == 1024           # 8 units: 32 partitions
+    assert ap(4, 32, 8, 32768) == 4096           # 32 units: 8 partitions
+    assert ap(8, 32, 32, 8192) == 8192           # MHA, 256 units
+    assert ap(8, 32, 1, 8192) == 1024            # MQA: 8 heads per workgroup, 4 chunks -> 32 units
+    assert ap(1, 1, 1, 100000) == 400            # 256 partitions of ceil(100000 / 256) -> 400 tokens
+    assert ap(64, 8, 8, 100000) == 8192          # no split wanted, but capped at the largest partition
+    assert ap(1, 8, 2, 300) == 256               # would be 16 tokens: floor of 256
+    for b, hq, hkv, t in [(1, 1, 1, 100000), (8, 32, 8, 8192), (64, 32, 8, 2049), (3, 12, 2, 777)]:
+        p = ap(b, hq, hkv, t)
+        assert 16 <= p <= 8192 and p % 16 == 0
 
 
 def test_append_and_prefill_validation(lib):

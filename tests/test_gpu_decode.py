@@ -181,7 +181,7 @@ def test_workspace_reuse_across_calls_and_shapes():
     """The workspace needs no initialisation: one buffer, filled with NaN bytes
     first, serves many calls with different shapes."""
     dev = device()
-    n = pkv.pkv_attn_decode_workspace_bytes(8, 32, 128, 4096, 16)
+    n = pkv.pkv_attn_decode_workspace_bytes(8, 32, 8, 128, 4096, 16)
     ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device=dev).view(torch.uint8)
     for seed, lens_ in [(1, [4096, 100, 17]), (2, [50] * 8), (3, [4096])]:
         w = workloads.decode_inputs("reuse", seed, lens_, 32, 8, 128, "bf16", dev)
