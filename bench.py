@@ -6,23 +6,35 @@ Hq=32, Hkv=8, Dh=128, every sequence 4096 tokens, bf16 cache, block size 16.
 One step is the whole decode hot path for the batch:
   1. slot mapping on the device for the 32 new tokens (position 4095),
   2. KV append of those tokens through the block table,
-  3. split-KV paged decode attention over all 4096 tokens (one kernel,
-     partitions merged in-kernel).
-Inputs are resident in HBM before timing. Four copies of the pool behind
-four block-table sets (2 GiB in total) are used in rotation so that the
+  3. split-KV paged decode attention over all 4096 tokens.
+Inputs are resident in HBM before timing. Copies of the pool behind separate
+block-table sets (at least 2 GiB in total) are used in rotation so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Prints one JSON line. `value` is algorithmic HBM bytes per step (KV read +
 q + out + tables + lengths + append traffic) divided by the step time;
-`roofline` reports the decode kernel alone, timed with HIP events on the
-stream it runs on; `cpu_baseline` times the float64 CPU oracle on the same
-batch on this host.
+`roofline` reports the decode call alone, timed with HIP events on the
+stream it runs on; `cpu_baseline` times the float64 CPU oracle on a sample of
+the same batch on this host.
 
-Other decode workloads are available with --workload for exploration; they
-print the same kind of line.
+--workload selects other decode workloads (same kind of line) or
+`cfg4-mixed`: one mixed step of the shared-prefix workload — a causal
+512-token prefill chunk on a 2048-token cache plus 64 single-token decodes —
+whose line reports the prefill chunk against the bf16 MFMA peak and the
+decodes against HBM.
+
+Counter summaries: `--calib-copy` adds, after the timed steps, one
+pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
+size). Run the bench under `rocprofv3 --pmc FETCH_SIZE` and again under
+`--pmc WRITE_SIZE` with that flag, then `python bench.py --counters
+FETCH_CSV WRITE_CSV --workload W` (no GPU needed) scales each counter by what
+it read for the copy and writes profiles/<kernel>_<workload>_traffic.json
+(picked up by later runs as roofline.traffic while the decode sources are
+unchanged) plus a text summary.
 """
 
 import argparse
+import csv
 import hashlib
 import json
 import math
@@ -35,9 +47,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV HBM GB/s (% of peak), B=32 Hkv=8 Dh=128 T=4096 bf16"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 MALL_BYTES = 2 * 2 ** 30          # rotate through at least this much pool memory
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h"]
+DECODE_WORKLOADS = ["cfg2-all4096", "cfg2-uniform", "cfg5-mha", "cfg5-gqa", "cfg5-mqa", "cfg5-gqa-fp8",
+                    "cfg3-b1", "cfg3-b4"]
 
 
 def parse():
@@ -45,14 +61,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="cfg2-all4096",
-                   choices=["cfg2-all4096", "cfg2-uniform", "cfg5-mha", "cfg5-gqa", "cfg5-mqa", "cfg5-gqa-fp8",
-                            "cfg3-b1", "cfg3-b4"])
+    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed"])
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle baseline")
-    p.add_argument("--calib-copy-mib", type=int, default=0,
-                   help="after timing, run a plain device copy of this size (for counter calibration)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="after timing, copy a 256 MiB scratch cache with pkv_copy_blocks (counter calibration)")
+    p.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this bench; no GPU needed")
     return p.parse_args()
 
 
@@ -79,6 +95,70 @@ def append_bytes(n_tokens, hkv, dh, in_elt, cache_elt):
     return n_tokens * hkv * dh * 2 * (in_elt + cache_elt) + n_tokens * 4
 
 
+def prefill_flops(prefix, chunk, hq, dh):
+    """4·Dh·Hq·Σ_i (P + i + 1): QKᵀ and PV over every visible (query, key) pair."""
+    pairs = chunk * prefix + chunk * (chunk + 1) // 2
+    return 4 * dh * hq * pairs
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, stream, n):
+        import torch
+        self.stream = stream
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.k = 0
+
+    def start(self):
+        self.ev[self.k][0].record(self.stream)
+
+    def stop(self):
+        self.ev[self.k][1].record(self.stream)
+        self.k += 1
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev[:self.k]]
+
+
+def stats_us(ms):
+    s = sorted(ms)
+    n = len(s)
+    return {"mean": round(sum(s) / n * 1e3, 2), "p10": round(s[n // 10] * 1e3, 2),
+            "p50": round(s[n // 2] * 1e3, 2), "p90": round(s[(9 * n) // 10] * 1e3, 2)}
+
+
+def calib_copy(dev):
+    """pkv_copy_blocks over a scratch cache: reads and writes CALIB_BYTES."""
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+    nb = CALIB_BYTES // (2 * 8 * 16 * 128 * 2)           # K and V blocks of [8, 16, 128] bf16
+    k = torch.zeros(2 * nb, 8, 16, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    cache = pkv.Cache(k, v)
+    src = torch.arange(nb, dtype=torch.int32, device=dev)
+    dst = src + nb
+    torch.cuda.synchronize()
+    pkv.pkv_copy_blocks(cache, src, dst)
+    torch.cuda.synchronize()
+
+
+def load_traffic(kernel, workload):
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("source_hash") != source_hash(DECODE_SOURCES):
+        return None
+    return tr.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# decode workloads
+# ---------------------------------------------------------------------------
+
 def make_decode_setup(name, dev):
     import numpy as np
     import torch
@@ -88,12 +168,9 @@ def make_decode_setup(name, dev):
 
     if name.startswith("cfg2"):
         make = lambda copies: workloads.cfg2(name.split("-", 1)[1], device=dev, copies=copies)  # noqa: E731
-        layers = 1
     elif name.startswith("cfg5"):
         make = lambda copies: workloads.cfg5(name.split("-", 1)[1], device=dev, copies=copies)  # noqa: E731
-        layers = 1
     else:
-        layers = 32
         make = None
     if make is not None:
         probe = make(1)
@@ -104,9 +181,9 @@ def make_decode_setup(name, dev):
         ws = [make(copies)]
     else:
         b = int(name.split("-b")[1])
-        ws = workloads.cfg3(batch=b, device=dev, layers=layers)
+        ws = workloads.cfg3(batch=b, device=dev, layers=32)
         copies = 1
-    caches, tables = [], []
+    layers = []
     for w in ws:
         shape = (w.num_blocks, w.hkv, 16, w.head_dim)
         if w.cache_dtype == "fp8":
@@ -126,32 +203,21 @@ def make_decode_setup(name, dev):
             pkv.pkv_kv_append(cache, w.k, w.v, torch.from_numpy(slots).to(dev), kinv, vinv)
         # the step's new tokens: each sequence's last position
         last = torch.from_numpy(w.cu_seqlens[1:] - 1).to(dev)
-        k_new = w.k.index_select(0, last).contiguous()
-        v_new = w.v.index_select(0, last).contiguous()
-        caches.append(dict(w=w, cache=cache, k_new=k_new, v_new=v_new, kinv=kinv, vinv=vinv,
+        layers.append(dict(w=w, cache=cache, kinv=kinv, vinv=vinv,
+                           k_new=w.k.index_select(0, last).contiguous(),
+                           v_new=w.v.index_select(0, last).contiguous(),
                            tables=[torch.from_numpy(np.ascontiguousarray(w.block_tables[c])).to(dev)
                                    for c in range(w.copies)]))
-        tables.append(None)
     torch.cuda.synchronize()
-    return caches, copies
+    return layers, copies
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(decode shards by sequence or KV head with no exchange; see the design notes).",
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_decode(args, dev):
     import numpy as np
     import torch
 
     import paged_kv_cache_430_amd as pkv
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    pkv.load()
     layers, copies = make_decode_setup(args.workload, dev)
     w0 = layers[0]["w"]
     B, hq, hkv, dh = w0.batch, w0.hq, w0.hkv, w0.head_dim
@@ -160,6 +226,7 @@ def main():
     kv_elt = 1 if fp8 else 2
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    lib = pkv.load()
     lens = torch.from_numpy(w0.seq_lens.astype(np.int32)).to(dev)
     cu_new = torch.arange(B + 1, dtype=torch.int32, device=dev)
     first_pos = (lens - 1).contiguous()
@@ -167,11 +234,10 @@ def main():
     out = torch.empty(B, hq, dh, dtype=torch.float32, device=dev)
     pt = args.partition
     ws = pkv.decode_workspace(B, hq, hkv, dh, T, pt, dev)
-    lib = pkv.load()
     wsp = ws.data_ptr() if ws is not None else None
     wsb = ws.numel() if ws is not None else 0
 
-    def step(i, ev=None):
+    def step(i, timer=None):
         c = i % copies
         for L in layers:
             tb = L["tables"][c]
@@ -181,70 +247,37 @@ def main():
                                          pkv.PKV_BF16, B, slots.data_ptr(),
                                          L["kinv"].data_ptr() if fp8 else None,
                                          L["vinv"].data_ptr() if fp8 else None, sh))
-            if ev is not None:
-                ev[0].record(stream)
+            if timer is not None:
+                timer.start()
             pkv._check(lib.pkv_attn_decode(L["cache"].ref(), L["w"].q.data_ptr(), pkv.PKV_BF16, B, hq,
                                            tb.data_ptr(), tb.shape[1], lens.data_ptr(), T, L["w"].scale, pt,
                                            out.data_ptr(), wsp, wsb, sh))
-            if ev is not None:
-                ev[1].record(stream)
+            if timer is not None:
+                timer.stop()
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    n_dec = args.steps * len(layers)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
+    timer = Timer(stream, args.steps * len(layers))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    k = 0
     for i in range(args.steps):
-        c = i % copies
-        for L in layers:
-            # per-layer events around the decode launch only
-            tb = L["tables"][c]
-            pkv._check(lib.pkv_slot_mapping_device(tb.data_ptr(), tb.shape[1], 16, B, cu_new.data_ptr(),
-                                                   first_pos.data_ptr(), B, slots.data_ptr(), sh))
-            pkv._check(lib.pkv_kv_append(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
-                                         pkv.PKV_BF16, B, slots.data_ptr(),
-                                         L["kinv"].data_ptr() if fp8 else None,
-                                         L["vinv"].data_ptr() if fp8 else None, sh))
-            evs[k][0].record(stream)
-            pkv._check(lib.pkv_attn_decode(L["cache"].ref(), L["w"].q.data_ptr(), pkv.PKV_BF16, B, hq,
-                                           tb.data_ptr(), tb.shape[1], lens.data_ptr(), T, L["w"].scale, pt,
-                                           out.data_ptr(), wsp, wsb, sh))
-            evs[k][1].record(stream)
-            k += 1
+        step(i, timer)
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = total_ms / args.steps
+    ms_step = t0.elapsed_time(t1) / args.steps
+    dec_ms = timer.ms()
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    dec_sorted = sorted(dec_ms)
-
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * 2 ** 20 // 4
-        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    if args.calib_copy:
+        calib_copy(dev)
 
     d_bytes = decode_bytes(w0.seq_lens, hq, hkv, dh, kv_elt, 2, fp8)
     a_bytes = append_bytes(B, hkv, dh, 2, kv_elt) + B * 4 * 3
     step_bytes = (d_bytes + a_bytes) * len(layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = d_bytes / (dec_avg_ms * 1e-3) / 1e9
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_hash") == source_hash(DECODE_SOURCES) and tr.get("workload") == args.workload:
-            traffic = tr.get("bytes_per_launch")
-
+    partition = pt or pkv.pkv_attn_decode_auto_partition(B, hq, hkv, T)
     line = {
         "metric": METRIC if args.workload == "cfg2-all4096" else f"decode-attn KV HBM GB/s ({args.workload})",
         "value": round(value, 2),
@@ -260,63 +293,323 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": dh,
                    "seq_len": T, "block_size": 16, "layers": len(layers), "pool_copies": copies,
-                   "partition_tokens": pt or pkv.pkv_attn_decode_auto_partition(B, hq, hkv, T)},
+                   "partition_tokens": partition, "partitions": -(-T // partition)},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "new_tokens_per_s": round(B / (ms_step * 1e-3) if len(layers) == 1 else B / (ms_step * 1e-3), 1),
+        "new_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w0.seq_lens.sum()) * len(layers) / (ms_step * 1e-3), 1),
-        "decode_kernel_us": {"mean": round(dec_avg_ms * 1e3, 2), "p10": round(dec_sorted[len(dec_sorted) // 10] * 1e3, 2),
-                             "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
-                             "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
+        "decode_call_us": stats_us(dec_ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel", "bytes_per_launch": d_bytes},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic("decode_split", args.workload),
+                     "kernel": "decode_split_kernel" + (" + decode_merge_kernel" if partition < T else ""),
+                     "bytes_per_launch": d_bytes},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds, d_bytes)
-    print(json.dumps(line), flush=True)
+        line["cpu_baseline"] = cpu_baseline_decode(w0, args.cpu_seconds, d_bytes)
+    return line
 
 
-def cpu_baseline(w, target_s, d_bytes):
-    """The float64 oracle on this host's cores, over the first layer's batch:
-    whole batches are repeated until target_s of compute has elapsed."""
+def cpu_baseline_decode(w, target_s, d_bytes):
+    """The float64 oracle on this host's cores over the first layer's batch:
+    whole sequences are attended until target_s of compute has elapsed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import fp8 as ofp8
+    threads = _blas_threads()
+    q = w.q.float().cpu().double().numpy()
+    per_seq_bytes = [d_bytes * int(t) / float(sum(int(x) for x in w.seq_lens)) for t in w.seq_lens]
+    done_bytes, seqs, el = 0.0, 0, 0.0
+    cache = {}
+    b = 0
+    while el < target_s:
+        if b not in cache:
+            k = w.seq_k(b).float().cpu().double().numpy().transpose(1, 0, 2).copy()
+            v = w.seq_v(b).float().cpu().double().numpy().transpose(1, 0, 2).copy()
+            if w.cache_dtype == "fp8":
+                kb = w.seq_k(b).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                vb = w.seq_v(b).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                k = np.stack([ofp8.dequantize(ofp8.quantize_bf16_bits(kb[:, h], w.k_inv_scale[h]), w.k_scale[h])
+                              for h in range(w.hkv)])
+                v = np.stack([ofp8.dequantize(ofp8.quantize_bf16_bits(vb[:, h], w.v_inv_scale[h]), w.v_scale[h])
+                              for h in range(w.hkv)])
+            cache[b] = (k, v)
+        k, v = cache[b]
+        t0 = time.perf_counter()
+        oracle.attention.decode(q[b:b + 1], [k], [v], w.scale)
+        el += time.perf_counter() - t0
+        done_bytes += per_seq_bytes[b]
+        seqs += 1
+        b = (b + 1) % w.batch
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{seqs} sequences of the batch (float64 numpy, materialised softmax over contiguous K/V), "
+                      f"{el:.1f} s of oracle compute; GB/s on the same algorithmic bytes"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+# ---------------------------------------------------------------------------
+# cfg4: mixed chunked prefill + decode with a shared prefix
+# ---------------------------------------------------------------------------
+
+def make_cfg4_setup(dev):
+    """Blocks come from the library's allocator with the workload's seeded free
+    order: 16 sequences share the prefix blocks (refcount 16) and own their
+    private blocks; S0 reserves its 512-token chunk; 64 decode sequences hold
+    their context plus the step's token."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+    import workloads
+
+    m = workloads.cfg4(device=dev)
+    bs, hkv, dh = 16, m.hkv, m.head_dim
+    alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
+    kp = torch.full((m.num_blocks, hkv, bs, dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    cache = pkv.Cache(kp, kp.clone())
+    max_blocks = (m.shared + m.private + m.chunk) // bs + 1
+
+    def append(table, first, k, v):
+        s = pkv.pkv_slot_mapping(table, bs, first, k.shape[0])
+        pkv.pkv_kv_append(cache, k.contiguous(), v.contiguous(), torch.from_numpy(s).to(dev))
+
+    prefix = np.full(max_blocks, -1, dtype=np.int32)
+    alloc.reserve_append(prefix, 0, m.shared)
+    append(prefix, 0, *m.prefix_kv)
+    n_pref = m.shared // bs
+    tables = []
+    for i in range(m.n_share):
+        t = prefix.copy()
+        if i > 0:
+            alloc.incref(prefix[:n_pref])
+        alloc.reserve_append(t, m.shared, m.private)
+        append(t, m.shared, *m.private_kv[i])
+        tables.append(t)
+    t0 = tables[0]
+    p0 = m.shared + m.private
+    alloc.reserve_append(t0, p0, m.chunk)
+    dtabs = np.full((len(m.decode_ctx), max_blocks), -1, dtype=np.int32)
+    for j, ctx in enumerate(m.decode_ctx):
+        ctx = int(ctx)
+        alloc.reserve_append(dtabs[j], 0, ctx + 1)
+        k, v = m.decode_kv[j]
+        append(dtabs[j], 0, k[:ctx], v[:ctx])
+    # the step's appends: the chunk's 512 tokens (S0) and one token per decode sequence
+    new_k = torch.cat([m.chunk_kv[0]] + [kv[0][-1:] for kv in m.decode_kv]).contiguous()
+    new_v = torch.cat([m.chunk_kv[1]] + [kv[1][-1:] for kv in m.decode_kv]).contiguous()
+    all_tables = torch.from_numpy(np.concatenate([t0[None], dtabs])).to(dev)
+    n_dec = len(m.decode_ctx)
+    cu_new = torch.tensor([0, m.chunk] + list(range(m.chunk + 1, m.chunk + n_dec + 1)), dtype=torch.int32,
+                          device=dev)
+    first_pos = torch.tensor([p0] + [int(c) for c in m.decode_ctx], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    return dict(m=m, cache=cache, p0=p0, max_blocks=max_blocks, all_tables=all_tables,
+                new_k=new_k, new_v=new_v, cu_new=cu_new, first_pos=first_pos,
+                dec_tables=all_tables[1:].contiguous(), chunk_table=all_tables[:1].contiguous(),
+                dec_lens=torch.from_numpy((m.decode_ctx + 1).astype(np.int32)).to(dev),
+                chunk_lens=torch.tensor([p0 + m.chunk], dtype=torch.int32, device=dev),
+                q_start=torch.tensor([0, m.chunk], dtype=torch.int32, device=dev))
+
+
+def run_cfg4(args, dev):
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    S = make_cfg4_setup(dev)
+    m = S["m"]
+    hq, hkv, dh = m.hq, m.hkv, m.head_dim
+    n_dec = len(m.decode_ctx)
+    n_new = m.chunk + n_dec
+    stream = torch.cuda.current_stream(dev)
+    lib = pkv.load()
+    sh = stream.cuda_stream
+    slots = torch.empty(n_new, dtype=torch.int32, device=dev)
+    out_p = torch.empty(m.chunk, hq, dh, dtype=torch.float32, device=dev)
+    out_d = torch.empty(n_dec, hq, dh, dtype=torch.float32, device=dev)
+    msl = S["max_blocks"] * 16
+    ws = pkv.decode_workspace(n_dec, hq, hkv, dh, msl, args.partition, dev)
+    wsp = ws.data_ptr() if ws is not None else None
+    wsb = ws.numel() if ws is not None else 0
+    at = S["all_tables"]
+
+    def step(tp=None, td=None):
+        pkv._check(lib.pkv_slot_mapping_device(at.data_ptr(), at.shape[1], 16, at.shape[0], S["cu_new"].data_ptr(),
+                                               S["first_pos"].data_ptr(), n_new, slots.data_ptr(), sh))
+        pkv._check(lib.pkv_kv_append(S["cache"].ref(), S["new_k"].data_ptr(), S["new_v"].data_ptr(), pkv.PKV_BF16,
+                                     n_new, slots.data_ptr(), None, None, sh))
+        if tp is not None:
+            tp.start()
+        pkv._check(lib.pkv_attn_prefill_chunk(S["cache"].ref(), m.chunk_q.data_ptr(), pkv.PKV_BF16, 1, hq,
+                                              S["q_start"].data_ptr(), S["chunk_table"].data_ptr(),
+                                              S["max_blocks"], S["chunk_lens"].data_ptr(), m.chunk, m.scale,
+                                              out_p.data_ptr(), None, 0, sh))
+        if tp is not None:
+            tp.stop()
+            td.start()
+        pkv._check(lib.pkv_attn_decode(S["cache"].ref(), m.decode_q.data_ptr(), pkv.PKV_BF16, n_dec, hq,
+                                       S["dec_tables"].data_ptr(), S["max_blocks"], S["dec_lens"].data_ptr(), msl,
+                                       m.scale, args.partition, out_d.data_ptr(), wsp, wsb, sh))
+        if td is not None:
+            td.stop()
+
+    for _ in range(args.warmup):
+        step()
+    tp, td = Timer(stream, args.steps), Timer(stream, args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(tp, td)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    p_ms, d_ms = tp.ms(), td.ms()
+    p_avg, d_avg = sum(p_ms) / len(p_ms), sum(d_ms) / len(d_ms)
+    if args.calib_copy:
+        calib_copy(dev)
+    flops = prefill_flops(S["p0"], m.chunk, hq, dh)
+    d_bytes = decode_bytes(m.decode_ctx + 1, hq, hkv, dh, 2, 2, False)
+    p_tflops = flops / (p_avg * 1e-3) / 1e12
+    line = {
+        "metric": "cfg4 mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + 64 decodes",
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "cfg4-mixed", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
+                   "prefix_tokens": S["p0"], "chunk": m.chunk, "shared_prefix_tokens": m.shared,
+                   "sharers": m.n_share, "decodes": n_dec,
+                   "decode_ctx_mean": float(np.mean(m.decode_ctx)) + 1.0},
+        "prefill_us": stats_us(p_ms),
+        "prefill_flops": flops,
+        "decode_us": stats_us(d_ms),
+        "decode_gbs": round(d_bytes / (d_avg * 1e-3) / 1e9, 2),
+        "decode_bytes": d_bytes,
+        "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "flops_per_launch": flops},
+        "decode_roofline": {"bound": "hbm", "achieved": round(d_bytes / (d_avg * 1e-3) / 1e9, 2),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(d_bytes / (d_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(m, S["p0"], flops)
+    return line
+
+
+def cpu_baseline_prefill(m, p0, flops):
+    """The float64 oracle's prefill chunk (materialised causal attention over
+    the contiguous 2560-token cache), once."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    cores = len(os.sched_getaffinity(0))
-    q = w.q.float().cpu().double().numpy()
-    ks, vs = [], []
-    nseq = w.batch
-    for b in range(nseq):
-        k = w.seq_k(b).float().cpu().double().numpy().transpose(1, 0, 2).copy()
-        v = w.seq_v(b).float().cpu().double().numpy().transpose(1, 0, 2).copy()
-        if w.cache_dtype == "fp8":
-            from oracle import fp8 as ofp8
-            kb = w.seq_k(b).contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-            vb = w.seq_v(b).contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-            k = np.stack([ofp8.dequantize(ofp8.quantize_bf16_bits(kb[:, h], w.k_inv_scale[h]), w.k_scale[h])
-                          for h in range(w.hkv)])
-            v = np.stack([ofp8.dequantize(ofp8.quantize_bf16_bits(vb[:, h], w.v_inv_scale[h]), w.v_scale[h])
-                          for h in range(w.hkv)])
-        ks.append(k)
-        vs.append(v)
-    reps = 0
+    f = lambda t: t.float().cpu().double().numpy()  # noqa: E731
+    k = np.concatenate([f(m.prefix_kv[0]), f(m.private_kv[0][0]), f(m.chunk_kv[0])]).transpose(1, 0, 2).copy()
+    v = np.concatenate([f(m.prefix_kv[1]), f(m.private_kv[0][1]), f(m.chunk_kv[1])]).transpose(1, 0, 2).copy()
+    q = f(m.chunk_q)
     t0 = time.perf_counter()
-    while True:
-        oracle.attention.decode(q, ks, vs, w.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 1000:
-            break
-    per_batch = el / reps
-    return {"value": round(d_bytes / per_batch / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "cores_available": cores, "kind": "oracle",
-            "sample": f"whole batch ({nseq} sequences, float64 numpy, materialised softmax), "
-                      f"{reps} repetitions in {el:.1f} s; {per_batch * 1e3:.1f} ms per batch"}
+    oracle.attention.prefill_chunk(q, k, v, m.scale)
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"the whole 512-query chunk on {p0 + m.chunk} cached tokens, once "
+                      f"(float64 numpy, materialised causal softmax), {el:.2f} s"}
+
+
+# ---------------------------------------------------------------------------
+# counter summaries
+# ---------------------------------------------------------------------------
+
+def summarize_counters(fetch_csv, write_csv, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernels, each
+    scaled by the factor that maps the calibration copy's reading onto the
+    bytes it is known to move."""
+    def load(path, counter):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                per.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+
+    def pick(per, key):
+        names = [n for n in per if key in n]
+        if not names:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        return names[0], per[names[0]]
+
+    _, cf = pick(fetch, "copy_blocks_kernel")
+    _, cw = pick(write, "copy_blocks_kernel")
+    f_scale = CALIB_BYTES / cf[-1]
+    w_scale = CALIB_BYTES / cw[-1]
+    out = {"workload": workload, "source_hash": source_hash(DECODE_SOURCES),
+           "calibration": {"kernel": "copy_blocks_kernel", "bytes": CALIB_BYTES,
+                           "fetch_bytes_read": cf[-1], "write_bytes_read": cw[-1],
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {}}
+    total = 0.0
+    for key in ("decode_split_kernel", "decode_merge_kernel"):
+        names = [n for n in fetch if key in n]
+        if not names:
+            continue
+        fv = fetch[names[0]]
+        wv = write[[n for n in write if key in n][0]]
+        fb = sum(fv) / len(fv) * f_scale
+        wb = sum(wv) / len(wv) * w_scale
+        out["kernels"][key] = {"name": names[0], "dispatches": len(fv), "fetch_bytes": fb, "write_bytes": wb}
+        total += fb + wb
+    out["bytes_per_launch"] = round(total)
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"decode_split_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return out
+
+
+def main():
+    args = parse()
+    if args.counters:
+        summarize_counters(args.counters[0], args.counters[1], args.workload)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence or KV head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    pkv.load()
+    line = run_cfg4(args, dev) if args.workload == "cfg4-mixed" else run_decode(args, dev)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
