@@ -10,17 +10,25 @@
 // mask includes the diagonal.
 //
 // Workgroup = (sequence, KV head g, a chunk of GW ≤ 4 query heads of g, a tile
-// of 64/GW queries); wave w takes head w % GW and 16 queries. Per 64-key tile:
-//   * K (row-major, padded) and V (transposed into groups of four keys per
-//     column) are gathered through the block table into LDS by all 256 threads;
-//     keys past the sequence end are stored as zeros;
+// of 64/GW queries); wave w takes head w % GW and 16 queries. Keys go in tiles
+// of 64 = four blocks; wave w gathers block w of each tile:
+//   * K and V of the block come in through raw buffer loads whose record limit
+//     is the block's rows before the workgroup's last visible key (rows past it
+//     and ids outside the pool read as zeros, with no memory access); the next
+//     tile's loads are in flight while the current tile is used, and its table
+//     entry is read a tile earlier still;
+//   * K is stored row-major and padded, V transposed into groups of four keys
+//     per column, so both feed MFMA operands with 16-byte LDS reads;
 //   * Sᵀ = K·Qᵀ on MFMA 16x16x32 bf16 (keys are the M dimension, so each lane's
 //     scores all belong to one query: lane % 16);
-//   * scale, inclusive causal mask (select to −inf), online softmax in the log2
-//     domain; the row sum stays lane-local until the end;
+//   * the causal mask (select to −inf) is applied only on tiles that reach past
+//     the wave's first query; online softmax in the log2 domain, with the scale
+//     folded into the exponent; O is rescaled only when some query's running
+//     max moved; the row sum stays lane-local until the end;
 //   * Oᵀ += Vᵀ·Pᵀ on MFMA, keys ordered as the score layout left them, so no
-//     shuffle of P is needed; P enters as a bf16 high part plus a bf16 low
-//     part (two MFMAs), which keeps the probabilities to ~16 bits.
+//     shuffle of P is needed; P enters as a bf16 high part (truncated) plus the
+//     bf16 rounding of the remainder (two MFMAs), which keeps the
+//     probabilities to ~16 bits.
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,11 +37,14 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKeys = 64;            // keys per tile
+constexpr int kWavesPf = kThreads / kWave;
+constexpr int kKeys = 64;                        // keys per tile
+constexpr int kTileBlocks = kKeys / kBlockSize;  // blocks per tile, one per wave
+static_assert(kTileBlocks == kWavesPf, "one block of each key tile per wave");
 
 struct Args {
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const uint8_t* kc;
+  const uint8_t* vc;
   const uint16_t* q;
   const int32_t* q_start;
   const int32_t* block_tables;
@@ -43,11 +54,6 @@ struct Args {
   float scale_log2;
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 template <int DH, int GW>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   constexpr int QT = 64 / GW;              // queries per workgroup
@@ -55,6 +61,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   constexpr int NDC = DH / 32;             // 32-wide k-steps for Q·Kᵀ
   constexpr int NDT = DH / 16;             // 16-row output tiles of Oᵀ
   constexpr int CPR = DH / 8;              // 16-byte chunks per row
+  constexpr int RB = DH * 2;               // bytes of one token row of one head
+  constexpr int NKL = kBlockSize * CPR / kWave;    // K chunks per lane per block
+  constexpr int NVL = kBlockSize / 4 * CPR;        // lanes that gather V (4 rows each)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeys * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[(kKeys / 4) * DH * 4];
 
@@ -64,10 +73,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   const int g = (L / a.num_qtiles / a.num_chunks) % a.hkv;
   const int s = L / a.num_qtiles / a.num_chunks / a.hkv;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int q_lo = a.q_start[s];
-  const int C = a.q_start[s + 1] - q_lo;                 // queries of this sequence
-  const int T = min(a.seq_lens[s], a.max_blocks * kBlockSize);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+  const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
+  const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;   // queries of this sequence
+  const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], a.max_blocks * kBlockSize));
   if (qtile * QT >= C || T <= 0) return;
   const int base_pos = T - C;                             // position of query 0
   const int group = a.hq / a.hkv;
@@ -77,11 +87,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   const int my_q = qi0 + col;                             // query whose scores this lane holds
   const bool q_valid = my_q < C;
   const int my_pos = q_valid ? base_pos + my_q : T - 1;
+  const int wave_first_pos = base_pos + qi0;              // smallest position of the wave's queries
   // last key any query of this workgroup sees
   const int wg_last_q = min(C, qtile * QT + QT) - 1;
   const int kend = min(T, base_pos + wg_last_q + 1);
   const int ntiles = (kend + kKeys - 1) / kKeys;
   const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t head_stride = (size_t)kBlockSize * RB;    // bytes of one (block, head)
 
   // Qᵀ operand: lane holds Q[my_q][dc*32 + kg*8 .. +7]
   bf16x8_t qreg[NDC];
@@ -96,40 +108,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   f32x4_t o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  const size_t head_stride = (size_t)kBlockSize * DH;    // elements of one (block, head)
+  float m_run = -INFINITY, l_run = 0.0f;   // m in raw-score units
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * kKeys;
-    // ---- gather K tile: 64 rows × CPR chunks ----
-    for (int c = tid; c < kKeys * CPR; c += kThreads) {
-      const int key = c / CPR, ch = c % CPR;
-      const int kabs = key0 + key;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (kabs < kend) {
-        const int phys = bt[kabs / kBlockSize];
-        if ((unsigned)phys < (unsigned)a.num_blocks)
-          x = *reinterpret_cast<const uint4*>(a.kc + ((size_t)phys * a.hkv + g) * head_stride +
-                                              (size_t)(kabs % kBlockSize) * DH + ch * 8);
-      }
-      *reinterpret_cast<uint4*>(&k_lds[key * KROW + ch * 8]) = x;
-    }
-    // ---- gather V tile: thread = (four keys, 8 columns), stored [key/4][col][key%4] ----
-    for (int c = tid; c < (kKeys / 4) * CPR; c += kThreads) {
-      const int kq = c / CPR, ch = c % CPR;
-      uint32_t rw[4][4];
+  // ---- gathers: wave w takes block w of each tile -------------------------------
+  // K: lane loads rows lane/CPR + (64/CPR)·i, chunk lane % CPR.
+  // V: lane < NVL loads rows 4·(lane/CPR) … +3 of chunk lane % CPR.
+  const int k_off = (lane / CPR) * RB + (lane % CPR) * 16;
+  const int v_off = (lane / CPR) * 4 * RB + (lane % CPR) * 16;
+  uint4 kst[NKL], vst[4];
+  auto table_entry = [&](int kt) -> int {
+    const int lb = kt * kTileBlocks + w;
+    return lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb]) : -1;
+  };
+  auto fetch = [&](int kt, int phys) {
+    const int rows = min(kBlockSize, max(0, kend - (kt * kTileBlocks + w) * kBlockSize));
+    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+    const size_t off = ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
+    const int records = __builtin_amdgcn_readfirstlane(ok ? rows * RB : 0);
+    const auto rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.kc + off), 0, records, kBufferRsrcWord3);
+    const auto rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.vc + off), 0, records, kBufferRsrcWord3);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kabs = key0 + kq * 4 + r;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (kabs < kend) {
-          const int phys = bt[kabs / kBlockSize];
-          if ((unsigned)phys < (unsigned)a.num_blocks)
-            x = *reinterpret_cast<const uint4*>(a.vc + ((size_t)phys * a.hkv + g) * head_stride +
-                                                (size_t)(kabs % kBlockSize) * DH + ch * 8);
-        }
-        rw[r][0] = x.x; rw[r][1] = x.y; rw[r][2] = x.z; rw[r][3] = x.w;
-      }
+    for (int i = 0; i < NKL; ++i) kst[i] = buffer_load16(rk, k_off + i * (kWave / CPR) * RB);
+    if (lane < NVL) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vst[r] = buffer_load16(rv, v_off + r * RB);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      const int key = w * kBlockSize + lane / CPR + i * (kWave / CPR);
+      *reinterpret_cast<uint4*>(&k_lds[key * KROW + (lane % CPR) * 8]) = kst[i];
+    }
+    if (lane < NVL) {
+      const int kq = w * (kBlockSize / 4) + lane / CPR, ch = lane % CPR;
+      const uint32_t rw[4][4] = {{vst[0].x, vst[0].y, vst[0].z, vst[0].w},
+                                 {vst[1].x, vst[1].y, vst[1].z, vst[1].w},
+                                 {vst[2].x, vst[2].y, vst[2].z, vst[2].w},
+                                 {vst[3].x, vst[3].y, vst[3].z, vst[3].w}};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {       // dword e holds columns 2e (low) and 2e+1 (high)
         const uint32_t lo01 = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x05040100u);
@@ -141,9 +159,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         *reinterpret_cast<uint2*>(&v_lds[(kq * DH + d + 1) * 4]) = make_uint2(hi01, hi23);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- Sᵀ = K·Qᵀ: four 16-key tiles ----
+  // ---- one tile's work on the K/V tile in LDS -----------------------------------
+  auto compute = [&](int kt) {
+    const int key0 = kt * kKeys;
+    // Sᵀ = K·Qᵀ: four 16-key tiles
     f32x4_t st[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -156,39 +177,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       }
       st[t4] = acc;
     }
-    // ---- scale, mask, online softmax (lane's scores all belong to my_q) ----
-    float mt = -INFINITY;
+    // inclusive causal mask, only where the tile reaches past the wave's first query
+    if (key0 + kKeys - 1 > wave_first_pos) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kabs = key0 + t4 * 16 + kg * 4 + i;
-        const float v = kabs <= my_pos ? st[t4][i] * a.scale_log2 : -INFINITY;
-        st[t4][i] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int i = 0; i < 4; ++i)
+          if (key0 + t4 * 16 + kg * 4 + i > my_pos) st[t4][i] = -INFINITY;
+    }
+    // online softmax: the lane's 16 scores all belong to query my_q
+    float mt = fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3]));
+#pragma unroll
+    for (int t4 = 1; t4 < 4; ++t4)
+      mt = fmaxf(mt, fmaxf(fmaxf(st[t4][0], st[t4][1]), fmaxf(st[t4][2], st[t4][3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
     const float m_new = fmaxf(m_run, mt);                 // finite: key 0 is visible to all
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    if (__any(m_new > m_run)) {                           // rescale only when a max moved
+      const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * a.scale_log2;
     float psum = 0.0f;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(st[t4][i] - m_new);
+        const float p = fast_exp2(fmaf(st[t4][i], a.scale_log2, -mc));
         st[t4][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    l_run += psum;
 
-    // ---- Oᵀ += Vᵀ·Pᵀ over two 32-key steps ----
-    // P is split into bf16 high and low parts (p = hi + lo to ~16 bits) and
-    // both go through the MFMA: V is exact in bf16, so the product keeps
-    // fp32-level accuracy instead of bf16's 2^-9 relative rounding of p.
+    // Oᵀ += Vᵀ·Pᵀ over two 32-key steps; P = hi + lo with hi the truncated
+    // bf16 of p and lo the bf16 rounding of p − hi, both through the MFMA (V is
+    // exact in bf16, so the product keeps ~16-bit probabilities instead of
+    // bf16's 2^-9 relative rounding)
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
       float pv[8];
@@ -197,9 +224,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 h0 = (__bf16)pv[2 * i], h1 = (__bf16)pv[2 * i + 1];
-        hw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{h0, h1});
-        lw[i] = pack_bf16x2(pv[2 * i] - (float)h0, pv[2 * i + 1] - (float)h1);
+        const uint32_t u0 = __float_as_uint(pv[2 * i]), u1 = __float_as_uint(pv[2 * i + 1]);
+        hw[i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        const float r0 = pv[2 * i] - __uint_as_float(u0 & 0xffff0000u);
+        const float r1 = pv[2 * i + 1] - __uint_as_float(u1 & 0xffff0000u);
+        lw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)r0, (__bf16)r1});
       }
       const bf16x8_t p_hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
       const bf16x8_t p_lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
@@ -215,13 +244,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, o[dt], 0, 0, 0);
       }
     }
+  };
+
+  int phys_next = table_entry(0);
+  fetch(0, phys_next);
+  phys_next = table_entry(1);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    store();
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      fetch(kt + 1, phys_next);
+      phys_next = table_entry(kt + 2);
+    }
+    compute(kt);
     __syncthreads();
   }
 
   // ---- finish: l over the four lanes of a query, o = u / l ----
   float lt = l_run;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  lt += __shfl_xor(lt, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
   if (!q_valid) return;
   const float inv = 1.0f / lt;
   float* op = a.out + ((size_t)(q_lo + my_q) * a.hq + head) * DH + kg * 4;
@@ -251,8 +293,8 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int gw = group >= 4 ? 4 : group;     // group is 1, 2 or a multiple of 4
   Args a;
-  a.kc = static_cast<const uint16_t*>(p.cache.k);
-  a.vc = static_cast<const uint16_t*>(p.cache.v);
+  a.kc = static_cast<const uint8_t*>(p.cache.k);
+  a.vc = static_cast<const uint8_t*>(p.cache.v);
   a.q = static_cast<const uint16_t*>(p.q);
   a.q_start = p.q_start;
   a.block_tables = p.block_tables;
