@@ -10,13 +10,16 @@
 // mask includes the diagonal.
 //
 // Workgroup = (sequence, KV head g, a chunk of GW ≤ 4 query heads of g, a tile
-// of 64/GW queries); wave w takes head w % GW and 16 queries. Keys go in tiles
-// of 64 = four blocks; wave w gathers block w of each tile:
+// of 64/GW queries), three streams of four waves: stream s takes key tiles
+// s, s+3, s+6, … (three waves per SIMD, so each hides the others' latencies),
+// and the streams' online-softmax states are merged into stream 0 at the end.
+// Within a stream, wave w takes head w % GW and 16 queries. Keys go in tiles
+// of 64 = four blocks; wave w of a stream gathers block w of its tiles:
 //   * K and V of the block come in through raw buffer loads whose record limit
 //     is the block's rows before the workgroup's last visible key (rows past it
-//     and ids outside the pool read as zeros, with no memory access); the next
-//     tile's loads are in flight while the current tile is used, and its table
-//     entry is read a tile earlier still;
+//     and ids outside the pool read as zeros, with no memory access); the
+//     stream's next tile's loads are in flight in registers while the current
+//     tile is used, and its table entry is read a tile earlier still;
 //   * K is stored row-major and padded, V transposed into groups of four keys
 //     per column, so both feed MFMA operands with 16-byte LDS reads;
 //   * Sᵀ = K·Qᵀ on MFMA 16x16x32 bf16 (keys are the M dimension, so each lane's
@@ -36,11 +39,12 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPf = kThreads / kWave;
+constexpr int kStreams = 3;                      // key streams: tiles s, s + 3, … (3 measured best)
+constexpr int kStreamWaves = 4;                  // waves of one stream
+constexpr int kThreads = kStreams * kStreamWaves * kWave;
 constexpr int kKeys = 64;                        // keys per tile
-constexpr int kTileBlocks = kKeys / kBlockSize;  // blocks per tile, one per wave
-static_assert(kTileBlocks == kWavesPf, "one block of each key tile per wave");
+constexpr int kTileBlocks = kKeys / kBlockSize;  // blocks per tile, one per wave of a stream
+static_assert(kTileBlocks == kStreamWaves, "one block of each key tile per wave");
 
 struct Args {
   const uint8_t* kc;
@@ -57,15 +61,23 @@ struct Args {
 template <int DH, int GW>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   constexpr int QT = 64 / GW;              // queries per workgroup
-  constexpr int KROW = DH + 8;             // padded K row in LDS (elements)
+  constexpr int KROW = DH + 16;            // padded K row in LDS (elements; +16 measured fewest conflicts)
   constexpr int NDC = DH / 32;             // 32-wide k-steps for Q·Kᵀ
   constexpr int NDT = DH / 16;             // 16-row output tiles of Oᵀ
   constexpr int CPR = DH / 8;              // 16-byte chunks per row
   constexpr int RB = DH * 2;               // bytes of one token row of one head
   constexpr int NKL = kBlockSize * CPR / kWave;    // K chunks per lane per block
   constexpr int NVL = kBlockSize / 4 * CPR;        // lanes that gather V (4 rows each)
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeys * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[(kKeys / 4) * DH * 4];
+  // V in LDS: [key quad][column][4 keys] bf16, 8 bytes per (quad, column),
+  // with 16 bytes of padding after every 8 columns (the transposing stores
+  // of neighbouring lanes are 64 bytes apart without it) and 128 bytes after
+  // every quad (the PV operand reads of lanes 0-15 and 16-31 use neighbouring
+  // quads; an odd multiple of 128 bytes puts them in opposite bank halves)
+  constexpr int VCOL = 4;                               // elements per (quad, column)
+  constexpr int VQ = DH * VCOL + (DH / 8) * 8 + 64;     // elements per key quad
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[kStreams][kKeys * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds_all[kStreams][(kKeys / 4) * VQ];
+  auto v_index = [](int kq, int d) { return kq * VQ + d * VCOL + (d / 8) * 8; };
 
   const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
   const int qtile = L % a.num_qtiles;
@@ -74,7 +86,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   const int s = L / a.num_qtiles / a.num_chunks / a.hkv;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+  const int stream = wave / kStreamWaves;                  // 0: even key tiles, 1: odd ones
+  const int w = wave % kStreamWaves;                       // wave within the stream
+  uint16_t* k_lds = k_lds_all[stream];
+  uint16_t* v_lds = v_lds_all[stream];
   const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
   const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;   // queries of this sequence
   const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], a.max_blocks * kBlockSize));
@@ -115,12 +131,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   // V: lane < NVL loads rows 4·(lane/CPR) … +3 of chunk lane % CPR.
   const int k_off = (lane / CPR) * RB + (lane % CPR) * 16;
   const int v_off = (lane / CPR) * 4 * RB + (lane % CPR) * 16;
-  uint4 kst[NKL], vst[4];
+  struct Stage {
+    uint4 k[NKL], v[4];
+  };
   auto table_entry = [&](int kt) -> int {
     const int lb = kt * kTileBlocks + w;
     return lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb]) : -1;
   };
-  auto fetch = [&](int kt, int phys) {
+  auto fetch = [&](int kt, int phys, Stage& st) {
     const int rows = min(kBlockSize, max(0, kend - (kt * kTileBlocks + w) * kBlockSize));
     const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
     const size_t off = ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
@@ -130,24 +148,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
     const auto rv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.vc + off), 0, records, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) kst[i] = buffer_load16(rk, k_off + i * (kWave / CPR) * RB);
+    for (int i = 0; i < NKL; ++i) st.k[i] = buffer_load16(rk, k_off + i * (kWave / CPR) * RB);
     if (lane < NVL) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vst[r] = buffer_load16(rv, v_off + r * RB);
+      for (int r = 0; r < 4; ++r) st.v[r] = buffer_load16(rv, v_off + r * RB);
     }
   };
-  auto store = [&]() {
+  auto store = [&](const Stage& st) {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
       const int key = w * kBlockSize + lane / CPR + i * (kWave / CPR);
-      *reinterpret_cast<uint4*>(&k_lds[key * KROW + (lane % CPR) * 8]) = kst[i];
+      *reinterpret_cast<uint4*>(&k_lds[key * KROW + (lane % CPR) * 8]) = st.k[i];
     }
     if (lane < NVL) {
       const int kq = w * (kBlockSize / 4) + lane / CPR, ch = lane % CPR;
-      const uint32_t rw[4][4] = {{vst[0].x, vst[0].y, vst[0].z, vst[0].w},
-                                 {vst[1].x, vst[1].y, vst[1].z, vst[1].w},
-                                 {vst[2].x, vst[2].y, vst[2].z, vst[2].w},
-                                 {vst[3].x, vst[3].y, vst[3].z, vst[3].w}};
+      const uint32_t rw[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
+                                 {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
+                                 {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},
+                                 {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w}};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {       // dword e holds columns 2e (low) and 2e+1 (high)
         const uint32_t lo01 = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x05040100u);
@@ -155,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         const uint32_t hi01 = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x07060302u);
         const uint32_t hi23 = __builtin_amdgcn_perm(rw[3][e], rw[2][e], 0x07060302u);
         const int d = ch * 8 + 2 * e;
-        *reinterpret_cast<uint2*>(&v_lds[(kq * DH + d) * 4]) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(&v_lds[(kq * DH + d + 1) * 4]) = make_uint2(hi01, hi23);
+        *reinterpret_cast<uint2*>(&v_lds[v_index(kq, d)]) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(&v_lds[v_index(kq, d + 1)]) = make_uint2(hi01, hi23);
       }
     }
   };
@@ -192,15 +210,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       mt = fmaxf(mt, fmaxf(fmaxf(st[t4][0], st[t4][1]), fmaxf(st[t4][2], st[t4][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);                 // finite: key 0 is visible to all
+    // m stays −inf while every key a query has met is masked (a later
+    // stream's first tile can lie wholly after an early query): the old state is then
+    // empty (weight 0) and the masked scores give p = 0
+    const float m_new = fmaxf(m_run, mt);
     if (__any(m_new > m_run)) {                           // rescale only when a max moved
-      const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);
+      const float alpha = m_run == -INFINITY ? 0.0f : fast_exp2((m_run - m_new) * a.scale_log2);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m_run = m_new;
     }
-    const float mc = m_run * a.scale_log2;
+    const float mc = m_run == -INFINITY ? 0.0f : m_run * a.scale_log2;
     float psum = 0.0f;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
@@ -237,8 +258,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int d = dt * 16 + col;
-        const uint2 va = *reinterpret_cast<const uint2*>(&v_lds[(quad_a * DH + d) * 4]);
-        const uint2 vb = *reinterpret_cast<const uint2*>(&v_lds[(quad_b * DH + d) * 4]);
+        const uint2 va = *reinterpret_cast<const uint2*>(&v_lds[v_index(quad_a, d)]);
+        const uint2 vb = *reinterpret_cast<const uint2*>(&v_lds[v_index(quad_b, d)]);
         const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, o[dt], 0, 0, 0);
@@ -246,18 +267,62 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
     }
   };
 
-  int phys_next = table_entry(0);
-  fetch(0, phys_next);
-  phys_next = table_entry(1);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    store();
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      fetch(kt + 1, phys_next);
-      phys_next = table_entry(kt + 2);
+  // Stream s takes tiles s, s+3, …, each stream with its own LDS tile and its
+  // next tile's loads in flight in registers; table entries are read a tile
+  // ahead of their gathers. All streams meet at every barrier.
+  {
+    Stage st;
+    int kt = stream;
+    fetch(kt, table_entry(kt), st);
+    int pn = table_entry(kt + kStreams);
+    const int iters = (ntiles + kStreams - 1) / kStreams;
+    for (int it = 0; it < iters; ++it, kt += kStreams) {
+      const bool active = kt < ntiles;
+      if (active) store(st);
+      __syncthreads();
+      if (kt + kStreams < ntiles) {
+        fetch(kt + kStreams, pn, st);
+        pn = table_entry(kt + 2 * kStreams);
+      }
+      if (active) compute(kt);
+      __syncthreads();
     }
-    compute(kt);
-    __syncthreads();
+  }
+
+  // ---- merge the other streams into stream 0 through LDS, one per round ----
+  // Each lane of a stream-r wave leaves m, its partial l and its 4·NDT output
+  // values; the stream-0 wave holding the same queries and head folds them in.
+  {
+    float* xch = reinterpret_cast<float*>(&k_lds_all[0][0]);
+    constexpr int NX = 2 + 4 * NDT;                        // floats per lane
+    static_assert(kStreamWaves * kWave * NX * 4 <= (int)sizeof(k_lds_all), "merge area");
+    float* mine = xch + ((size_t)w * kWave + lane) * NX;
+#pragma unroll
+    for (int r = 1; r < kStreams; ++r) {
+      if (stream == r) {
+        mine[0] = m_run;
+        mine[1] = l_run;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mine[2 + 4 * dt + j] = o[dt][j];
+      }
+      __syncthreads();
+      if (stream == 0) {
+        const float m1 = mine[0];
+        const float mt = fmaxf(m_run, m1);                 // finite: stream 0 saw key 0
+        const float a0 = fast_exp2((m_run - mt) * a.scale_log2);
+        const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2((m1 - mt) * a.scale_log2);
+        l_run = a0 * l_run + a1 * mine[1];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[dt][j] = a0 * o[dt][j] + a1 * mine[2 + 4 * dt + j];
+        m_run = mt;
+      }
+      __syncthreads();
+    }
+    if (stream != 0) return;
   }
 
   // ---- finish: l over the four lanes of a query, o = u / l ----
