@@ -4,9 +4,9 @@
 Default workload (the headline metric): GQA paged decode, B=32 sequences,
 Hq=32, Hkv=8, Dh=128, every sequence 4096 tokens, bf16 cache, block size 16.
 One step is the whole decode hot path for the batch:
-  1. slot mapping on the device for the 32 new tokens (position 4095),
-  2. KV append of those tokens through the block table,
-  3. split-KV paged decode attention over all 4096 tokens.
+  1. slot mapping and KV append of the 32 new tokens (position 4095) through
+     the block tables, in one launch (pkv_kv_append_paged),
+  2. split-KV paged decode attention over all 4096 tokens.
 Inputs are resident in HBM before timing. Copies of the pool behind separate
 block-table sets (at least 2 GiB in total) are used in rotation so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
@@ -14,8 +14,9 @@ block-table sets (at least 2 GiB in total) are used in rotation so that the
 Prints one JSON line. `value` is algorithmic HBM bytes per step (KV read +
 q + out + tables + lengths + append traffic) divided by the step time;
 `roofline` reports the decode call alone, timed with HIP events on the
-stream it runs on; `cpu_baseline` times the float64 CPU oracle on a sample of
-the same batch on this host.
+stream it runs on in a second pass over the same steps (so the K timed steps
+carry no per-call events); `cpu_baseline` times the float64 CPU oracle on a
+sample of the same batch on this host.
 
 --workload selects other decode workloads (same kind of line) or
 `cfg4-mixed`: one mixed step of the shared-prefix workload — a causal
@@ -230,7 +231,6 @@ def run_decode(args, dev):
     lens = torch.from_numpy(w0.seq_lens.astype(np.int32)).to(dev)
     cu_new = torch.arange(B + 1, dtype=torch.int32, device=dev)
     first_pos = (lens - 1).contiguous()
-    slots = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty(B, hq, dh, dtype=torch.float32, device=dev)
     pt = args.partition
     ws = pkv.decode_workspace(B, hq, hkv, dh, T, pt, dev)
@@ -241,12 +241,11 @@ def run_decode(args, dev):
         c = i % copies
         for L in layers:
             tb = L["tables"][c]
-            pkv._check(lib.pkv_slot_mapping_device(tb.data_ptr(), tb.shape[1], 16, B, cu_new.data_ptr(),
-                                                   first_pos.data_ptr(), B, slots.data_ptr(), sh))
-            pkv._check(lib.pkv_kv_append(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
-                                         pkv.PKV_BF16, B, slots.data_ptr(),
-                                         L["kinv"].data_ptr() if fp8 else None,
-                                         L["vinv"].data_ptr() if fp8 else None, sh))
+            # slot mapping and append of the step's tokens in one launch
+            pkv._check(lib.pkv_kv_append_paged(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
+                                               pkv.PKV_BF16, B, cu_new.data_ptr(), first_pos.data_ptr(), 1,
+                                               tb.data_ptr(), tb.shape[1], L["kinv"].data_ptr() if fp8 else None,
+                                               L["vinv"].data_ptr() if fp8 else None, None, sh))
             if timer is not None:
                 timer.start()
             pkv._check(lib.pkv_attn_decode(L["cache"].ref(), L["w"].q.data_ptr(), pkv.PKV_BF16, B, hq,
@@ -257,23 +256,28 @@ def run_decode(args, dev):
 
     for i in range(args.warmup):
         step(i)
-    timer = Timer(stream, args.steps * len(layers))
+    # the K timed steps: events only around the whole run
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i, timer)
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+    # then the same steps again with events around each decode call (roofline)
+    timer = Timer(stream, args.steps * len(layers))
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
     dec_ms = timer.ms()
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     if args.calib_copy:
         calib_copy(dev)
 
     d_bytes = decode_bytes(w0.seq_lens, hq, hkv, dh, kv_elt, 2, fp8)
-    a_bytes = append_bytes(B, hkv, dh, 2, kv_elt) + B * 4 * 3
+    a_bytes = append_bytes(B, hkv, dh, 2, kv_elt) + B * 4 * 2    # + table entry and first_pos per token
     step_bytes = (d_bytes + a_bytes) * len(layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = d_bytes / (dec_avg_ms * 1e-3) / 1e9
@@ -434,7 +438,6 @@ def run_cfg4(args, dev):
     stream = torch.cuda.current_stream(dev)
     lib = pkv.load()
     sh = stream.cuda_stream
-    slots = torch.empty(n_new, dtype=torch.int32, device=dev)
     out_p = torch.empty(m.chunk, hq, dh, dtype=torch.float32, device=dev)
     out_d = torch.empty(n_dec, hq, dh, dtype=torch.float32, device=dev)
     msl = S["max_blocks"] * 16
@@ -444,10 +447,9 @@ def run_cfg4(args, dev):
     at = S["all_tables"]
 
     def step(tp=None, td=None):
-        pkv._check(lib.pkv_slot_mapping_device(at.data_ptr(), at.shape[1], 16, at.shape[0], S["cu_new"].data_ptr(),
-                                               S["first_pos"].data_ptr(), n_new, slots.data_ptr(), sh))
-        pkv._check(lib.pkv_kv_append(S["cache"].ref(), S["new_k"].data_ptr(), S["new_v"].data_ptr(), pkv.PKV_BF16,
-                                     n_new, slots.data_ptr(), None, None, sh))
+        pkv._check(lib.pkv_kv_append_paged(S["cache"].ref(), S["new_k"].data_ptr(), S["new_v"].data_ptr(),
+                                           pkv.PKV_BF16, at.shape[0], S["cu_new"].data_ptr(), S["first_pos"].data_ptr(),
+                                           m.chunk, at.data_ptr(), at.shape[1], None, None, None, sh))
         if tp is not None:
             tp.start()
         pkv._check(lib.pkv_attn_prefill_chunk(S["cache"].ref(), m.chunk_q.data_ptr(), pkv.PKV_BF16, 1, hq,
@@ -465,16 +467,19 @@ def run_cfg4(args, dev):
 
     for _ in range(args.warmup):
         step()
-    tp, td = Timer(stream, args.steps), Timer(stream, args.steps)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        step(tp, td)
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+    tp, td = Timer(stream, args.steps), Timer(stream, args.steps)
+    for _ in range(args.steps):
+        step(tp, td)
+    torch.cuda.synchronize()
     p_ms, d_ms = tp.ms(), td.ms()
     p_avg, d_avg = sum(p_ms) / len(p_ms), sum(d_ms) / len(d_ms)
     if args.calib_copy:

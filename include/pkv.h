@@ -138,6 +138,26 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
                           const float* k_inv_scale, const float* v_inv_scale,
                           pkv_stream stream);
 
+/* Slot mapping and KV append in one launch, for a batch (the same pages):
+ * sequence s appends new tokens cu_new[s] … cu_new[s+1]−1 (rows of k_new /
+ * v_new) at logical positions first_pos[s], first_pos[s]+1, …; each token's
+ * slot is taken from the sequence's table row exactly as
+ * pkv_slot_mapping_device computes it (−1 when the block is beyond max_blocks
+ * or the entry is negative; such tokens are skipped), and stored values are
+ * those of pkv_kv_append.
+ *   cu_new:       device int32 [num_seqs + 1], nondecreasing, cu_new[0] = 0
+ *   first_pos:    device int32 [num_seqs]
+ *   max_new:      host bound on cu_new[s+1] − cu_new[s] (sizes the grid;
+ *                 tokens past it are not appended)
+ *   block_tables: device int32 [num_seqs, max_blocks]
+ *   out_slots:    device int32 [cu_new[num_seqs]] receiving the slots, or NULL
+ * Under PKV_CHECK=1 cu_new is copied back and checked against max_new. */
+PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const void* v_new,
+                                int32_t in_dtype, int32_t num_seqs, const int32_t* cu_new,
+                                const int32_t* first_pos, int32_t max_new, const int32_t* block_tables,
+                                int32_t max_blocks, const float* k_inv_scale, const float* v_inv_scale,
+                                int32_t* out_slots, pkv_stream stream);
+
 /* ---------------------------------------------------------------------------
  * Paged decode attention with split-KV — [P2] Q027 (online softmax: running
  * max m, sum l = Σ exp(s−m), weighted sum u = Σ exp(s−m)·v, output u/l, and

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "PKVError", "Cache", "BlockAllocator", "load",
-    "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append",
+    "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
     "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_debug_gather",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
@@ -52,6 +52,8 @@ _SIGS = {
     "pkv_slot_mapping": (ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP]),
     "pkv_slot_mapping_device": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "pkv_kv_append_paged": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP,
+                                           _I32, _VP, _VP, _VP, _VP]),
     "pkv_attn_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32, _I32]),
     "pkv_attn_decode": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32, _VP,
@@ -173,6 +175,16 @@ def pkv_kv_append(cache, k_new, v_new, slot_mapping, k_inv_scale=None, v_inv_sca
     _check(load().pkv_kv_append(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), k_new.shape[0],
                                 _ptr(slot_mapping), _ptr(k_inv_scale), _ptr(v_inv_scale),
                                 _stream(stream, cache.device)))
+
+
+def pkv_kv_append_paged(cache, k_new, v_new, block_tables, cu_new, first_pos, max_new, k_inv_scale=None,
+                        v_inv_scale=None, out_slots=None, stream=None):
+    """Slot mapping and append in one launch; returns out_slots (may be None)."""
+    _check(load().pkv_kv_append_paged(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), len(first_pos),
+                                      _ptr(cu_new), _ptr(first_pos), int(max_new), _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(k_inv_scale), _ptr(v_inv_scale), _ptr(out_slots),
+                                      _stream(stream, cache.device)))
+    return out_slots
 
 
 def pkv_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0):

@@ -14,6 +14,15 @@ namespace pkv {
 // ---------------------------------------------------------------------------
 // slot mapping: one workgroup per sequence, threads stride over its new tokens
 // ---------------------------------------------------------------------------
+// Slot of logical position pos through one sequence's table row; −1 when the
+// position's block is beyond max_blocks or its entry is negative.
+__device__ __forceinline__ int slot_of(const int32_t* __restrict__ bt, int max_blocks, int pos) {
+  const int lb = pos / kBlockSize;
+  if (pos < 0 || lb >= max_blocks) return -1;
+  const int phys = bt[lb];
+  return phys >= 0 ? phys * kBlockSize + pos % kBlockSize : -1;
+}
+
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ block_tables, int max_blocks,
                                     const int32_t* __restrict__ cu_new,
                                     const int32_t* __restrict__ first_pos, int n_tokens,
@@ -23,16 +32,7 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ block_tables, in
   const int hi = min(cu_new[s + 1], n_tokens);
   const int p0 = first_pos[s];
   const int32_t* bt = block_tables + (size_t)s * max_blocks;
-  for (int i = lo + (int)threadIdx.x; i < hi; i += blockDim.x) {
-    const int pos = p0 + (i - lo);
-    const int lb = pos / kBlockSize;
-    int slot = -1;
-    if (pos >= 0 && lb < max_blocks) {
-      const int phys = bt[lb];
-      if (phys >= 0) slot = phys * kBlockSize + pos % kBlockSize;
-    }
-    out[i] = slot;
-  }
+  for (int i = lo + (int)threadIdx.x; i < hi; i += blockDim.x) out[i] = slot_of(bt, max_blocks, p0 + (i - lo));
 }
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int num_seqs,
@@ -69,21 +69,22 @@ __device__ __forceinline__ uint32_t encode_e4m3(float y) {
   return sign | code;
 }
 
-// One workgroup per token; threads stride over 16-byte input chunks of K then V.
+// One token's K and V rows into its slot: threads of the workgroup stride
+// over 16-byte input chunks of K then V (copy, or e4m3 quantise per head).
 template <int IN, int OUT>
-__global__ void kv_append_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
-                                 const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
-                                 uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
-                                 const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
-  const int tok = blockIdx.x;
-  const int slot = slots[tok];
-  if (slot < 0 || slot >= num_blocks * kBlockSize) return;
+__device__ __forceinline__ void append_token(const uint8_t* __restrict__ k_new,
+                                             const uint8_t* __restrict__ v_new, int tok, int slot,
+                                             uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                             int num_blocks, int hkv, int dh,
+                                             const float* __restrict__ k_inv,
+                                             const float* __restrict__ v_inv, int t0, int nt) {
+  if (slot < 0 || slot >= num_blocks * kBlockSize) return;   // skipped token
   const int blk = slot / kBlockSize, off = slot % kBlockSize;
   constexpr int IN_B = IN == kF32 ? 4 : 2;
   constexpr int EPC = 16 / IN_B;                       // input elements per 16-byte chunk
   const int chunks_per_head = dh / EPC;
   const int chunks = hkv * chunks_per_head;
-  for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
+  for (int c = t0; c < 2 * chunks; c += nt) {
     const bool is_v = c >= chunks;
     const int cc = is_v ? c - chunks : c;
     const int h = cc / chunks_per_head;
@@ -123,6 +124,41 @@ __global__ void kv_append_kernel(const uint8_t* __restrict__ k_new, const uint8_
   }
 }
 
+// One workgroup per token.
+template <int IN, int OUT>
+__global__ void kv_append_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+                                 const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
+                                 uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
+                                 const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
+  const int tok = blockIdx.x;
+  append_token<IN, OUT>(k_new, v_new, tok, slots[tok], kc, vc, num_blocks, hkv, dh, k_inv, v_inv,
+                        threadIdx.x, blockDim.x);
+}
+
+// Slot mapping fused into the append: workgroup (s, j) takes sequence s's new
+// tokens j·kAppendTokensPerWg … +kAppendTokensPerWg−1, each handled by a
+// quarter of the workgroup; the slot comes from the table as in
+// slot_mapping_kernel and is optionally written out.
+constexpr int kAppendTokensPerWg = 4;
+template <int IN, int OUT>
+__global__ void kv_append_paged_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+                                       const int32_t* __restrict__ block_tables, int max_blocks,
+                                       const int32_t* __restrict__ cu_new,
+                                       const int32_t* __restrict__ first_pos, uint8_t* __restrict__ kc,
+                                       uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
+                                       const float* __restrict__ k_inv, const float* __restrict__ v_inv,
+                                       int32_t* __restrict__ out_slots) {
+  const int s = blockIdx.x;
+  const int lo = cu_new[s], hi = cu_new[s + 1];
+  const int part = threadIdx.x / (blockDim.x / kAppendTokensPerWg);
+  const int nt = blockDim.x / kAppendTokensPerWg;
+  const int i = lo + blockIdx.y * kAppendTokensPerWg + part;
+  if (i >= hi) return;
+  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, first_pos[s] + (i - lo));
+  if (out_slots && threadIdx.x % nt == 0) out_slots[i] = slot;
+  append_token<IN, OUT>(k_new, v_new, i, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x % nt, nt);
+}
+
 hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
                             int n_tokens, const int32_t* slots, const float* k_inv,
                             const float* v_inv, hipStream_t s) {
@@ -135,6 +171,28 @@ hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v
 #define PKV_APPEND(IN, OUT)                                                                      \
   hipLaunchKernelGGL((kv_append_kernel<IN, OUT>), grid, block, 0, s, kn, vn, slots, kc, vc,      \
                      c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv)
+  if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
+  else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
+  else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
+  else PKV_APPEND(kF32, kFP8);
+#undef PKV_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_paged(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
+                                  int num_seqs, const int32_t* cu_new, const int32_t* first_pos, int max_new,
+                                  const int32_t* block_tables, int max_blocks, const float* k_inv,
+                                  const float* v_inv, int32_t* out_slots, hipStream_t s) {
+  if (num_seqs == 0 || max_new == 0) return hipSuccess;
+  const dim3 grid(num_seqs, (max_new + kAppendTokensPerWg - 1) / kAppendTokensPerWg), block(256);
+  auto kn = static_cast<const uint8_t*>(k_new);
+  auto vn = static_cast<const uint8_t*>(v_new);
+  auto kc = static_cast<uint8_t*>(c.k);
+  auto vc = static_cast<uint8_t*>(c.v);
+#define PKV_APPEND(IN, OUT)                                                                             \
+  hipLaunchKernelGGL((kv_append_paged_kernel<IN, OUT>), grid, block, 0, s, kn, vn, block_tables, max_blocks, \
+                     cu_new, first_pos, kc, vc, c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv,   \
+                     out_slots)
   if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
   else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
   else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);

@@ -28,6 +28,11 @@ hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v
                             int n_tokens, const int32_t* slots, const float* k_inv,
                             const float* v_inv, hipStream_t s);
 
+hipError_t launch_kv_append_paged(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
+                                  int num_seqs, const int32_t* cu_new, const int32_t* first_pos, int max_new,
+                                  const int32_t* block_tables, int max_blocks, const float* k_inv,
+                                  const float* v_inv, int32_t* out_slots, hipStream_t s);
+
 hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int32_t* dst, int n,
                               hipStream_t s);
 

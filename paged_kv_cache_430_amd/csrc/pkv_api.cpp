@@ -122,6 +122,17 @@ size_t decode_ws_bytes(int32_t batch, int32_t hq, int32_t dh, int32_t max_seq_le
   return rows * parts * (dh + 2) * sizeof(float);
 }
 
+int check_append_dtypes(const CacheView& c, int32_t in_dtype, const float* k_inv, const float* v_inv,
+                        const char* fn) {
+  const bool ok_dtype = (c.dtype == PKV_F32 && in_dtype == PKV_F32) ||
+                        (c.dtype == PKV_BF16 && in_dtype == PKV_BF16) ||
+                        (c.dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32));
+  if (!ok_dtype) return fail(PKV_EDTYPE, std::string(fn) + ": input dtype does not match the cache");
+  if (c.dtype == PKV_FP8_E4M3 && (!k_inv || !v_inv))
+    return fail(PKV_EINVAL, std::string(fn) + ": fp8 cache needs k_inv_scale and v_inv_scale");
+  return PKV_OK;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -129,7 +140,7 @@ using namespace pkv;
 
 extern "C" {
 
-PKV_API int32_t pkv_version(void) { return 100; }
+PKV_API int32_t pkv_version(void) { return 200; }
 
 PKV_API const char* pkv_last_error(void) { return last_error().c_str(); }
 
@@ -175,12 +186,7 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
   if (n_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping) return fail(PKV_EINVAL, "pkv_kv_append: NULL pointer");
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(PKV_EINVAL, "pkv_kv_append: k_new / v_new must be 16-byte aligned");
-  const bool ok_dtype = (c.dtype == PKV_F32 && in_dtype == PKV_F32) ||
-                        (c.dtype == PKV_BF16 && in_dtype == PKV_BF16) ||
-                        (c.dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32));
-  if (!ok_dtype) return fail(PKV_EDTYPE, "pkv_kv_append: input dtype does not match the cache");
-  if (c.dtype == PKV_FP8_E4M3 && (!k_inv_scale || !v_inv_scale))
-    return fail(PKV_EINVAL, "pkv_kv_append: fp8 cache needs k_inv_scale and v_inv_scale");
+  if (int st = check_append_dtypes(c, in_dtype, k_inv_scale, v_inv_scale, "pkv_kv_append")) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (check_mode()) {
     std::vector<int32_t> slots;
@@ -192,6 +198,36 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
   return hip_status(launch_kv_append(c, k_new, v_new, in_dtype, n_tokens, slot_mapping, k_inv_scale,
                                      v_inv_scale, s),
                     "pkv_kv_append");
+}
+
+PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const void* v_new,
+                                int32_t in_dtype, int32_t num_seqs, const int32_t* cu_new,
+                                const int32_t* first_pos, int32_t max_new, const int32_t* block_tables,
+                                int32_t max_blocks, const float* k_inv_scale, const float* v_inv_scale,
+                                int32_t* out_slots, pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_kv_append_paged", &c)) return st;
+  if (num_seqs < 0 || max_new < 0 || max_blocks < 0) return fail(PKV_EINVAL, "pkv_kv_append_paged: negative size");
+  if (num_seqs == 0 || max_new == 0) return PKV_OK;
+  if (!k_new || !v_new || !cu_new || !first_pos || !block_tables)
+    return fail(PKV_EINVAL, "pkv_kv_append_paged: NULL pointer");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_EINVAL, "pkv_kv_append_paged: k_new / v_new must be 16-byte aligned");
+  if (int st = check_append_dtypes(c, in_dtype, k_inv_scale, v_inv_scale, "pkv_kv_append_paged")) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    std::vector<int32_t> cu;
+    if (int st = copy_to_host(cu, cu_new, (size_t)num_seqs + 1, s)) return st;
+    if (cu[0] != 0) return fail(PKV_EINVAL, "pkv_kv_append_paged: PKV_CHECK: cu_new[0] != 0");
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu[i + 1] < cu[i] || cu[i + 1] - cu[i] > max_new)
+        return fail(PKV_EINVAL, "pkv_kv_append_paged: PKV_CHECK: sequence " + std::to_string(i) +
+                                    " has a bad new-token count");
+  }
+  return hip_status(launch_kv_append_paged(c, k_new, v_new, in_dtype, num_seqs, cu_new, first_pos, max_new,
+                                           block_tables, max_blocks, k_inv_scale, v_inv_scale, out_slots, s),
+                    "pkv_kv_append_paged");
 }
 
 PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

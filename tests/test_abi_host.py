@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_error_string(lib):
-    assert pkv.pkv_version() == 100
+    assert pkv.pkv_version() == 200
     assert isinstance(lib.pkv_last_error(), bytes)
 
 
@@ -139,6 +139,14 @@ def test_append_and_prefill_validation(lib):
                                       None, 0, None) == pkv.PKV_EDTYPE
     assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 24, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
                                       None, 0, None) == pkv.PKV_EINVAL     # group 3
+    # fused slot mapping + append: same dtype rules, pointer and size checks
+    ap = lib.pkv_kv_append_paged
+    assert ap(ref, 0x50000, 0x60000, pkv.PKV_F32, 2, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EDTYPE
+    assert ap(ref, 0x50008, 0x60000, pkv.PKV_BF16, 2, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EINVAL
+    assert ap(ref, 0x50000, 0x60000, pkv.PKV_BF16, 2, None, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EINVAL
+    assert ap(ref, 0x50000, 0x60000, pkv.PKV_BF16, -1, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EINVAL
+    assert ap(ref8, 0x50000, 0x60000, pkv.PKV_BF16, 2, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EINVAL
+    assert ap(ref, 0x50000, 0x60000, pkv.PKV_BF16, 2, 0x1, 0x2, 0, 0x3, 4, None, None, None, None) == pkv.PKV_OK
     assert lib.pkv_copy_blocks(ref, None, None, 2, None) == pkv.PKV_EINVAL
     assert lib.pkv_debug_gather(ref, 0x1, 5, 0x50002, 0x60000, None) == pkv.PKV_EINVAL
 

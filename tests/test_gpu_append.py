@@ -155,3 +155,53 @@ def test_skip_slots_and_copy_blocks():
     assert torch.equal(kp[4].view(torch.int16), kp[1].view(torch.int16))
     assert torch.equal(vp[5].view(torch.int16), vp[2].view(torch.int16))
     assert torch.isnan(kp[0, :, 0:3].float()).all()
+
+
+@pytest.mark.parametrize("cache_dtype,in_dtype,dh", [("bf16", "bf16", 128), ("f32", "f32", 64), ("fp8", "bf16", 128),
+                                                      ("fp8", "f32", 64)])
+def test_fused_append_matches_slot_mapping_then_append(cache_dtype, in_dtype, dh):
+    """pkv_kv_append_paged writes the same slots and the same pool bytes as
+    pkv_slot_mapping_device followed by pkv_kv_append, including ragged
+    new-token counts (0 included), block crossings and unallocated entries."""
+    dev = device()
+    rng = np.random.default_rng(11 + dh)
+    s, mb, hkv = 9, 7, 2
+    nblocks = 80
+    tables = np.full((s, mb), -1, dtype=np.int32)
+    perm = rng.permutation(nblocks).astype(np.int32)
+    firsts, news, k = [], [], 0
+    for i in range(s):
+        nb = int(rng.integers(1, mb + 1))
+        tables[i, :nb] = perm[k:k + nb]
+        k += nb
+        first = int(rng.integers(0, nb * 16))
+        firsts.append(first)
+        news.append(int(rng.integers(0, 40)) if i != 3 else 0)   # may run past the allocated blocks
+    cu = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    n = int(cu[-1])
+    dt = torch.float32 if in_dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(3)
+    kn = torch.randn(n, hkv, dh, generator=g, device=dev).to(dt)
+    vn = torch.randn(n, hkv, dh, generator=g, device=dev).to(dt)
+    kinv = vinv = ksc = vsc = None
+    if cache_dtype == "fp8":
+        kinv = torch.tensor([1.7, 0.3], dtype=torch.float32, device=dev)
+        vinv = torch.tensor([0.9, 2.5], dtype=torch.float32, device=dev)
+        ksc, vsc = 1.0 / kinv, 1.0 / vinv
+    bt, cu_d = torch.from_numpy(tables).to(dev), torch.from_numpy(cu).to(dev)
+    fp = torch.tensor(firsts, dtype=torch.int32, device=dev)
+    ka, va = new_pools(nblocks, hkv, dh, cache_dtype, dev)
+    kb, vb = ka.clone(), va.clone()
+    slots = pkv.pkv_slot_mapping_device(bt, cu_d, fp, n)
+    pkv.pkv_kv_append(pkv.Cache(ka, va, ksc, vsc), kn, vn, slots, kinv, vinv)
+    out_slots = torch.full((n,), -7, dtype=torch.int32, device=dev)
+    pkv.pkv_kv_append_paged(pkv.Cache(kb, vb, ksc, vsc), kn, vn, bt, cu_d, fp, max(news), kinv, vinv, out_slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_slots.cpu().numpy(), slots.cpu().numpy())
+    assert np.array_equal(_bits(kb), _bits(ka))
+    assert np.array_equal(_bits(vb), _bits(va))
+    # without out_slots, and in a second pool, the same bytes again
+    kc, vc = new_pools(nblocks, hkv, dh, cache_dtype, dev)
+    pkv.pkv_kv_append_paged(pkv.Cache(kc, vc, ksc, vsc), kn, vn, bt, cu_d, fp, max(news), kinv, vinv)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kc), _bits(ka))
