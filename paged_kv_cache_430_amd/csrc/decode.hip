@@ -85,10 +85,9 @@ struct KernelArgs {
 struct MergeArgs {
   const float* ws_ml;
   const float* ws_u;
-  const int32_t* seq_lens;
   float* out;
   size_t total;   // batch · Hq · head_dim
-  int hq, head_dim, max_blocks, max_seq_len, part_tokens, num_parts;
+  int head_dim, num_parts;
 };
 
 // Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane
@@ -208,23 +207,33 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
   const int h0 = g * group + chunk * HC;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform, and known to be
-  const int T = __builtin_amdgcn_readfirstlane(
-      min(max(a.seq_lens[b], 0), min(a.max_seq_len, a.max_blocks * kBlockSize)));
-  const int nparts = (T + a.part_tokens - 1) / a.part_tokens;
-  if (part >= nparts) {
-    if (part == 0) {  // empty sequence: zeros
-      for (int i = tid; i < HC * DH; i += kThreads) a.out[((size_t)b * a.hq + h0) * DH + i] = 0.0f;
-    }
-    return;
-  }
+  // the wave index, read from the first lane so that the compiler knows it is
+  // wave-uniform (block ids and buffer resources derived from it stay scalar)
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int P = a.num_parts;
   const int tok0 = part * a.part_tokens;
-  const int ntok = min(a.part_tokens, T - tok0);
-  const int nblk = (ntok + kBlockSize - 1) / kBlockSize;
-  const int nbw = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;   // this wave's blocks
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + tok0 / kBlockSize;
-  const int my_phys = lane < nbw ? bt[w + kWaves * lane] : -1;
   const size_t head_stride = (size_t)kBlockSize * G::RB;     // bytes of one (block, head)
+  // Issued together with the length load rather than after it: the table
+  // entries the partition can hold (one per lane; entries past the sequence
+  // are masked once the length arrives).
+  const int lb0 = tok0 / kBlockSize;
+  const int cap = min(a.part_tokens / kBlockSize, a.max_blocks - lb0);   // blocks the partition can hold
+  const int cap_w = cap > w ? (cap - w + kWaves - 1) / kWaves : 0;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb0;
+  const int phys_all = lane < cap_w ? bt[w + kWaves * lane] : -1;
+  const int seq_len = a.seq_lens[b];
+  int ntok = 0;        // tokens of this partition, set once the length is known
+  int my_phys = -1;     // the wave's table entries, masked to the sequence
+  float sc = 0.0f;
+
+  float m[HC], l[HC], acc[HC][EPC];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
+  }
 
   const int tk = lane / LPK, jk = lane % LPK;                 // K layout
   const int rv = lane / LPV, cv = lane % LPV;                 // V layout
@@ -253,18 +262,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
       }
     }
   }
-  float sc = a.scale_log2;
-  if constexpr (KV == kFP8) sc *= a.k_scale[g];
-
-  float m[HC], l[HC], acc[HC][EPC];
-#pragma unroll
-  for (int h = 0; h < HC; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
-  }
-
   // Buffer resources over the wave's j-th (block, head) tile of K and V. The
   // record limit is the block's valid rows: an id outside the pool, j past the
   // wave's last block and rows past the sequence end read as zeros without a
@@ -387,9 +384,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
     }
   };
 
+  // Partitions past the sequence end (and every partition of an empty
+  // sequence) run through with no blocks: they leave m = −inf, l = 0 and u = 0,
+  // which the reduce kernel weighs 0 (or, with one partition, an output of 0).
+  // No early exit keeps the table load ahead of the length on every path.
+  const int T = __builtin_amdgcn_readfirstlane(min(max(seq_len, 0), min(a.max_seq_len, a.max_blocks * kBlockSize)));
+  ntok = min(a.part_tokens, T - tok0);
+  const int nblk = ntok > 0 ? (ntok + kBlockSize - 1) / kBlockSize : 0;
+  const int nbw = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;   // this wave's blocks
+  my_phys = lane < nbw ? phys_all : -1;
+  sc = a.scale_log2;
+  if constexpr (KV == kFP8) sc *= a.k_scale[g];
+
+  uint4 k0[NTK][NCK], v0[NIV], k1[NTK][NCK], v1[NIV];
+  load_block(0, k0, v0);
   {
-    uint4 k0[NTK][NCK], v0[NIV], k1[NTK][NCK], v1[NIV];
-    load_block(0, k0, v0);
     for (int j = 0; j < nbw; j += 2) {
       load_block(j + 1, k1, v1);
       use_block(j, k0, v0);
@@ -419,9 +428,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
   }
   __syncthreads();
 
-  // ---- merge the four waves -----------------------------------------------------
+  // ---- merge the waves ---------------------------------------------------------------
   const float vscale = KV == kFP8 ? a.v_scale[g] : 1.0f;
-  const int P = a.num_parts;
   for (int i = tid; i < HC * DH; i += kThreads) {
     const int h = i / DH, d = i % DH;
     float mt = sh_m[0][h];
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
       u = fmaf(wt, sh_u[ww][h][d], u);
       lt = fmaf(wt, sh_l[ww][h], lt);
     }
-    if (nparts == 1) {
+    if (P == 1) {
       a.out[((size_t)b * a.hq + h0 + h) * DH + d] = lt > 0.0f ? u * vscale / lt : 0.0f;
     } else {   // partials for the reduce kernel
       a.ws_u[(((size_t)b * a.hq + h0 + h) * P + part) * DH + d] = u * vscale;
@@ -448,21 +456,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
 }
 
 // Split-KV reduce: one thread per (sequence, query head, column). Partition
-// π left m_π (log2 domain), l_π and u_π; with m* = max m_π the output is
-// Σ 2^(m_π − m*) u_π / Σ 2^(m_π − m*) l_π. Rows of sequences that fit in one
-// partition were finished by the split kernel and are left alone.
+// π left m_π (log2 domain), l_π and u_π — an empty partition left m = −inf,
+// l = 0 and an unwritten u, which gets weight 0 and is never read into the
+// sum; with m* = max m_π the output is Σ 2^(m_π − m*) u_π / Σ 2^(m_π − m*) l_π
+// (0 for a sequence with no tokens).
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
   const size_t idx = (size_t)blockIdx.x * kMergeThreads + threadIdx.x;
   if (idx >= a.total) return;
   const size_t row = idx / a.head_dim;
   const int d = (int)(idx % a.head_dim);
-  const int b = (int)(row / a.hq);
-  const int T = min(max(a.seq_lens[b], 0), min(a.max_seq_len, a.max_blocks * kBlockSize));
-  const int nparts = (T + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;
-  const int P = a.num_parts;
-  const float* ml = a.ws_ml + row * P * 2;
-  const float* u = a.ws_u + row * P * a.head_dim + d;
+  const int nparts = a.num_parts;
+  const float* ml = a.ws_ml + row * nparts * 2;
+  const float* u = a.ws_u + row * nparts * a.head_dim + d;
   // online merge, eight partitions per round so their loads are in flight together
   float mt = -INFINITY, lt = 0.0f, ut = 0.0f;
   for (int p0 = 0; p0 < nparts; p0 += 8) {
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     for (int k = 0; k < 8; ++k) {
       const float wgt = part_weight(pm[k], mr);
       lt = fmaf(wgt, pl[k], lt);
-      ut = fmaf(wgt, pu[k], ut);
+      ut = wgt > 0.0f ? fmaf(wgt, pu[k], ut) : ut;   // an empty partition's u is never read
     }
     mt = mr;
   }
@@ -557,14 +562,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   MergeArgs m;
   m.ws_ml = p.ws_ml;
   m.ws_u = p.ws_u;
-  m.seq_lens = p.seq_lens;
   m.out = p.out;
   m.total = (size_t)p.batch * p.num_q_heads * dh;
-  m.hq = p.num_q_heads;
   m.head_dim = dh;
-  m.max_blocks = p.max_blocks;
-  m.max_seq_len = p.max_seq_len;
-  m.part_tokens = p.part_tokens;
   m.num_parts = p.num_parts;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((m.total + kMergeThreads - 1) / kMergeThreads)),
                      dim3(kMergeThreads), 0, s, m);
