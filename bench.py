@@ -233,7 +233,8 @@ def run_decode(args, dev):
     first_pos = (lens - 1).contiguous()
     out = torch.empty(B, hq, dh, dtype=torch.float32, device=dev)
     pt = args.partition
-    ws = pkv.decode_workspace(B, hq, hkv, dh, T, pt, dev)
+    cache_code = {"f32": pkv.PKV_F32, "bf16": pkv.PKV_BF16, "fp8": pkv.PKV_FP8_E4M3}[w0.cache_dtype]
+    ws = pkv.decode_workspace(cache_code, B, hq, hkv, dh, T, pt, dev)
     wsp = ws.data_ptr() if ws is not None else None
     wsb = ws.numel() if ws is not None else 0
 
@@ -281,7 +282,7 @@ def run_decode(args, dev):
     step_bytes = (d_bytes + a_bytes) * len(layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = d_bytes / (dec_avg_ms * 1e-3) / 1e9
-    partition = pt or pkv.pkv_attn_decode_auto_partition(B, hq, hkv, T)
+    partition = pt or pkv.pkv_attn_decode_auto_partition(cache_code, B, hq, hkv, T)
     line = {
         "metric": METRIC if args.workload == "cfg2-all4096" else f"decode-attn KV HBM GB/s ({args.workload})",
         "value": round(value, 2),
@@ -441,7 +442,7 @@ def run_cfg4(args, dev):
     out_p = torch.empty(m.chunk, hq, dh, dtype=torch.float32, device=dev)
     out_d = torch.empty(n_dec, hq, dh, dtype=torch.float32, device=dev)
     msl = S["max_blocks"] * 16
-    ws = pkv.decode_workspace(n_dec, hq, hkv, dh, msl, args.partition, dev)
+    ws = pkv.decode_workspace(pkv.PKV_BF16, n_dec, hq, hkv, dh, msl, args.partition, dev)
     wsp = ws.data_ptr() if ws is not None else None
     wsb = ws.numel() if ws is not None else 0
     at = S["all_tables"]

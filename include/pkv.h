@@ -188,9 +188,13 @@ PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const
  *                 overlap (one workspace per stream).
  * When more than one partition is needed the call launches two kernels on
  * the stream: the split kernel, then a small reduce kernel that merges the
- * partitions.
+ * partitions. BF16 and FP8 caches run the split on the matrix cores (the
+ * query heads of a KV group are one side of 16×16 products), F32 caches on
+ * the vector ALUs; see pkv_attn_decode_auto_partition for the override.
+ * The result does not depend on the physical block ids: relabelling blocks
+ * (with the same contents) gives bit-identical output.
  * num_q_heads must be a multiple of num_kv_heads with Hq/Hkv <= 64. */
-PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
                                                int32_t num_kv_heads, int32_t head_dim,
                                                int32_t max_seq_len, int32_t partition_tokens);
 
@@ -200,13 +204,18 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
                             float scale, int32_t partition_tokens, float* out,
                             void* workspace, size_t workspace_bytes, pkv_stream stream);
 
-/* The partition size pkv_attn_decode uses when partition_tokens is 0: with
- * units = batch · num_kv_heads · (query-head chunks per KV head), every
- * sequence is split into ceil(256 / units) partitions — one 8-wave workgroup
- * per MI355X compute unit, no split when the units already fill the chip —
- * rounded up to whole blocks, at least 256 tokens (or max_seq_len if
- * shorter) and at most 8192. */
-PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads,
+/* The partition size pkv_attn_decode uses when partition_tokens is 0 for a
+ * cache of cache_dtype: with units = batch · num_kv_heads · (query-head
+ * chunks per KV head), every sequence is split into ceil(256 / units)
+ * partitions — one 8-wave workgroup per MI355X compute unit, no split when
+ * the units already fill the chip — rounded up to whole blocks, at least 256
+ * tokens (or max_seq_len if shorter) and at most 8192. A chunk is up to 16
+ * query heads of one KV head for BF16 and FP8 caches (the matrix-core
+ * kernel) and the largest of 8, 4, 2, 1 dividing Hq/Hkv for F32 caches (the
+ * vector kernel). The environment variable PKV_DECODE_KERNEL=vector or
+ * =matrix, read at every call, selects the kernel for BF16 and FP8 caches
+ * instead (for tests and tuning; F32 always uses the vector kernel). */
+PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
                                                int32_t num_kv_heads, int32_t max_seq_len);
 
 /* ---------------------------------------------------------------------------

@@ -54,8 +54,8 @@ _SIGS = {
     "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP]),
     "pkv_kv_append_paged": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP,
                                            _I32, _VP, _VP, _VP, _VP]),
-    "pkv_attn_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
-    "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32, _I32]),
+    "pkv_attn_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_attn_decode": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32, _VP,
                                        _I32, ctypes.c_float, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
     "pkv_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _VP,
@@ -187,19 +187,22 @@ def pkv_kv_append_paged(cache, k_new, v_new, block_tables, cu_new, first_pos, ma
     return out_slots
 
 
-def pkv_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0):
-    return load().pkv_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                                  partition_tokens)
+def pkv_attn_decode_workspace_bytes(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                    partition_tokens=0):
+    return load().pkv_attn_decode_workspace_bytes(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim,
+                                                  max_seq_len, partition_tokens)
 
 
-def pkv_attn_decode_auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len):
-    return load().pkv_attn_decode_auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len)
+def pkv_attn_decode_auto_partition(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len):
+    return load().pkv_attn_decode_auto_partition(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len)
 
 
-def decode_workspace(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens, device):
+def decode_workspace(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens,
+                     device):
     """A workspace of the size pkv_attn_decode needs (or None); its contents
     need no initialisation."""
-    n = pkv_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens)
+    n = pkv_attn_decode_workspace_bytes(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                        partition_tokens)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -210,7 +213,7 @@ def pkv_attn_decode(cache, q, block_tables, seq_lens, max_seq_len, scale, partit
     if out is None:
         out = torch.empty(b, hq, dh, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = decode_workspace(b, hq, cache.num_kv_heads, dh, max_seq_len, partition_tokens, dev)
+        workspace = decode_workspace(cache.dtype, b, hq, cache.num_kv_heads, dh, max_seq_len, partition_tokens, dev)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().pkv_attn_decode(cache.ref(), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
                                   block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),

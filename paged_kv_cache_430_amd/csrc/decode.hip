@@ -10,9 +10,15 @@
 // at the last position, so nothing is masked but the unused tail of the last
 // block.
 //
-// One workgroup (NW = 8 waves) owns (sequence b, KV head g, a chunk of HC query
-// heads of that group, partition π of part_tokens tokens). Each wave streams
-// the blocks w, w+4, w+8, … of π in a single pass:
+// Two forms of the split kernel compute the same thing. The vector form
+// (below, any cache dtype; the only one for fp32 caches) does the products on
+// the vector ALUs; the matrix-core form (further down, bf16 and fp8 caches)
+// does them on MFMA with the query heads of a KV group as one side of 16×16
+// products. Both share the partial format and the reduce kernel.
+//
+// Vector form: one workgroup (NW = 8 waves) owns (sequence b, KV head g, a
+// chunk of HC query heads of that group, partition π of part_tokens tokens).
+// Each wave streams the blocks w, w+8, w+16, … of π in a single pass:
 //   * the wave's block-table entries are loaded once, one per lane, and read
 //     back with a lane read into a scalar register;
 //   * K and V of the next block are loaded while the current one is used,
@@ -496,6 +502,289 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   a.out[idx] = lt > 0.0f ? ut / lt : 0.0f;
 }
 
+// ---- matrix-core form -------------------------------------------------------------
+// The same (sequence, KV head, partition) work with the products on MFMA:
+// the query heads of a KV group are the N dimension of 16×16 products, so a
+// workgroup takes up to 16 heads of a group, and keys go 32 at a time (two
+// blocks). For a pair of blocks:
+//   Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32_bf16, keys as M (16 per block), Dh as the
+//   contraction: lane (col = lane % 16, kg = lane / 16) loads, for k-step dc,
+//   the 8 elements dc·32 + kg·8 … of key row col — the A operand as it lies in
+//   memory; q of head col is the B operand. The result leaves in lane (col, kg)
+//   the scores of head col for keys 4kg … 4kg+3 of each block.
+//   Oᵀ += Vᵀ·Pᵀ on the same instruction with the 32 keys as the contraction:
+//   those scores, as probabilities, are already the B operand (element j < 4
+//   ↔ key 4kg+j of the first block, j ≥ 4 ↔ key 4kg+j−4 of the second). For
+//   the A operand lane (col, kg) loads the NDT = Dh/16 consecutive elements
+//   col·NDT … of its 4 keys of each block and transposes them in registers,
+//   so output tile dt row m is column NDT·m + dt (a permutation of Dh that the
+//   final store undoes). P enters as a bf16 high part (truncated) plus the
+//   bf16 rounding of the remainder, two products, keeping ~16-bit
+//   probabilities; K, V (fp8 converted exactly) and q are exact in bf16.
+// The online softmax per head is the one above (log2 domain, lazy rescale,
+// wave-uniform decision); the waves merge through LDS and write the output
+// or the same partials for the reduce kernel.
+constexpr int kMfmaHeads = 16;   // query heads per workgroup (the MFMA N dimension)
+
+template <int KV, int DH>
+struct MfmaGeometry {
+  static constexpr int ESZ = KV == kBF16 ? 2 : 1;   // stored bytes per element
+  static constexpr int RB = DH * ESZ;               // bytes of one token row of one head
+  static constexpr int NDC = DH / 32;               // k-steps of Sᵀ = K·Qᵀ
+  static constexpr int NDT = DH / 16;               // 16-row tiles of Oᵀ = elements of a V slice
+  static constexpr int KW = 8 * ESZ / 4;            // stored dwords of one K operand slice
+  static constexpr int VW = NDT * ESZ / 4;          // stored dwords of one V slice (≥ 1)
+  static_assert(VW >= 1 && NDC >= 1, "unsupported head dimension");
+};
+
+// n stored dwords (n = 1, 2 or 4) at a byte offset, non-temporal.
+template <int N>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&d)[N]) {
+  if constexpr (N == 4) {
+    const uint4 x = buffer_load16_stream(r, off);
+    d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+  } else if constexpr (N == 2) {
+    const uint2 x = buffer_load8_stream(r, off);
+    d[0] = x.x; d[1] = x.y;
+  } else {
+    d[0] = buffer_load4_stream(r, off);
+  }
+}
+
+// Stored dwords of a slice → packed bf16 pairs (fp8: two pairs per dword, exact).
+template <int KV, int N>
+__device__ __forceinline__ void to_bf16_pairs(const uint32_t (&x)[N], uint32_t (&y)[KV == kFP8 ? 2 * N : N]) {
+  if constexpr (KV == kFP8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      y[2 * i] = fp8x2_to_bf16x2<false>(x[i]);
+      y[2 * i + 1] = fp8x2_to_bf16x2<true>(x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) y[i] = x[i];
+  }
+}
+
+template <int KV, int DH, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
+  constexpr int kWaves = NW, kThreads = NW * kWave;
+  constexpr int NH = kMfmaHeads;
+  using G = MfmaGeometry<KV, DH>;
+  constexpr int NDC = G::NDC, NDT = G::NDT, KW = G::KW, VW = G::VW;
+  __shared__ float sh_u[kWaves][NH][DH];
+  __shared__ float sh_m[kWaves][NH];
+  __shared__ float sh_l[kWaves][NH];
+
+  const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
+  const int chunk = L % a.num_chunks;
+  const int part = (L / a.num_chunks) % a.num_parts;
+  const int g = (L / a.num_chunks / a.num_parts) % a.hkv;
+  const int b = L / a.num_chunks / a.num_parts / a.hkv;
+  const int group = a.hq / a.hkv;
+  const int h0 = g * group + chunk * NH;
+  const int nh = min(NH, group - chunk * NH);                  // heads of this chunk
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane & 15, kg = lane >> 4;
+  const int P = a.num_parts;
+  const int tok0 = part * a.part_tokens;
+  const size_t head_stride = (size_t)kBlockSize * G::RB;
+  // Table entries, loaded beside the length: wave w takes block pairs
+  // (tiles) w, w + kWaves, …; lane j holds block 2·(w + kWaves·(j/2)) + j%2.
+  const int lb0 = tok0 / kBlockSize;
+  const int cap = min(a.part_tokens / kBlockSize, a.max_blocks - lb0);
+  const int jb = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb0;
+  const int phys_all = jb < cap ? bt[jb] : -1;
+  const int seq_len = a.seq_lens[b];
+
+  // q of head col as the B operand of each k-step (zeros past the chunk's heads)
+  bf16x8_t qb[NDC];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.hq + h0 + col) * DH;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const uint4 x = col < nh ? *reinterpret_cast<const uint4*>(qrow + dc * 32 + kg * 8) : make_uint4(0, 0, 0, 0);
+      qb[dc] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  const int T = __builtin_amdgcn_readfirstlane(min(max(seq_len, 0), min(a.max_seq_len, a.max_blocks * kBlockSize)));
+  const int ntok = min(a.part_tokens, T - tok0);
+  const int nblk = ntok > 0 ? (ntok + kBlockSize - 1) / kBlockSize : 0;
+  const int ntile = (nblk + 1) / 2;
+  const int ntw = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;   // this wave's tiles
+  const int my_phys = (lane >> 1) < ntw ? phys_all : -1;
+  float sc = a.scale_log2;
+  if constexpr (KV == kFP8) sc *= a.k_scale[g];
+
+  auto rows_of = [&](int idx) { return min(kBlockSize, max(0, ntok - idx * kBlockSize)); };
+  auto tile_rsrc = [&](const uint8_t* pool, int phys, int rows) {
+    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+    const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
+    const int records = __builtin_amdgcn_readfirstlane(ok ? rows * G::RB : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
+  };
+  struct Tile {
+    uint32_t k[2][NDC][KW];   // [block][k-step]
+    uint32_t v[2][4][VW];     // [block][key of the lane's quad]
+  };
+  // block e (0, 1) of the wave's j-th tile
+  auto block_phys = [&](int j, int e) { return j < ntw ? __builtin_amdgcn_readlane(my_phys, 2 * j + e) : -1; };
+  auto block_index = [&](int j, int e) { return 2 * (w + kWaves * j) + e; };
+  auto load_tile = [&](int j, Tile& t) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int phys = block_phys(j, e);
+      const int rows = rows_of(block_index(j, e));
+      const auto rk = tile_rsrc(a.kc, phys, rows);
+      const auto rv = tile_rsrc(a.vc, phys, rows);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) load_dwords<KW>(rk, col * G::RB + (dc * 4 + kg) * KW * 4, t.k[e][dc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;     // head col; l is this lane's share
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto use_tile = [&](int j, const Tile& t) {
+    int rows[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int phys = block_phys(j, e);
+      rows[e] = (unsigned)phys < (unsigned)a.num_blocks ? rows_of(block_index(j, e)) : 0;
+    }
+    // Sᵀ for both blocks
+    f32x4_t st[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        uint32_t kk[4];
+        to_bf16_pairs<KV, KW>(t.k[e][dc], kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(kk[0], kk[1], kk[2], kk[3])), qb[dc], acc, 0, 0, 0);
+      }
+      st[e] = acc;
+    }
+    // scale; keys past the valid rows (or of a block outside the pool) → −inf
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = 4 * kg + i < rows[e] ? st[e][i] * sc : -INFINITY;
+        st[e][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float m_new = fmaxf(m_run, mt);
+    if (__any(m_new > m_run)) {                          // rescale only when a max moved
+      const float alpha = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run == -INFINITY ? 0.0f : m_run;  // all keys so far masked: p = 0
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pp = fast_exp2(st[e][i] - mc);
+        pv[4 * e + i] = pp;
+        l_run += pp;
+      }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u0 = __float_as_uint(pv[2 * i]), u1 = __float_as_uint(pv[2 * i + 1]);
+      hw[i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      const float r0 = pv[2 * i] - __uint_as_float(u0 & 0xffff0000u);
+      const float r1 = pv[2 * i + 1] - __uint_as_float(u1 & 0xffff0000u);
+      lw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)r0, (__bf16)r1});
+    }
+    const bf16x8_t p_hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const bf16x8_t p_lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    // V slices as bf16 pairs: vp[block][key][pair]
+    constexpr int NP = NDT / 2;
+    uint32_t vp[2][4][NP];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) to_bf16_pairs<KV, VW>(t.v[e][i], vp[e][i]);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t sel = dt % 2 ? 0x07060302u : 0x05040100u;   // high or low element of the pair
+      uint32_t a4[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        a4[2 * e] = __builtin_amdgcn_perm(vp[e][1][dt / 2], vp[e][0][dt / 2], sel);
+        a4[2 * e + 1] = __builtin_amdgcn_perm(vp[e][3][dt / 2], vp[e][2][dt / 2], sel);
+      }
+      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(a4[0], a4[1], a4[2], a4[3]));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p_hi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p_lo, o[dt], 0, 0, 0);
+    }
+  };
+
+  {
+    Tile t0, t1;
+    load_tile(0, t0);
+    for (int j = 0; j < ntw; j += 2) {
+      load_tile(j + 1, t1);
+      use_tile(j, t0);
+      load_tile(j + 2, t0);
+      if (j + 1 < ntw) use_tile(j + 1, t1);
+    }
+  }
+
+  // ---- the wave's totals, then the waves' merge ------------------------------------
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (col < nh) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh_u[w][col][NDT * (4 * kg + i) + dt] = o[dt][i];
+    if (kg == 0) { sh_m[w][col] = m_run; sh_l[w][col] = l_run; }
+  }
+  __syncthreads();
+  const float vscale = KV == kFP8 ? a.v_scale[g] : 1.0f;
+  for (int i = tid; i < nh * DH; i += kThreads) {
+    const int h = i / DH, d = i % DH;
+    float mt = sh_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) mt = fmaxf(mt, sh_m[ww][h]);
+    float u = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float wt = part_weight(sh_m[ww][h], mt);
+      u = fmaf(wt, sh_u[ww][h][d], u);
+      lt = fmaf(wt, sh_l[ww][h], lt);
+    }
+    if (P == 1) {
+      a.out[((size_t)b * a.hq + h0 + h) * DH + d] = lt > 0.0f ? u * vscale / lt : 0.0f;
+    } else {
+      a.ws_u[(((size_t)b * a.hq + h0 + h) * P + part) * DH + d] = u * vscale;
+      if (d == 0) {
+        float* ml = a.ws_ml + (((size_t)b * a.hq + h0 + h) * P + part) * 2;
+        ml[0] = mt;
+        ml[1] = lt;
+      }
+    }
+  }
+}
+
 // Lanes per K row: 4 keeps the score reduction to two DPP steps and one
 // exponential per lane and head; eight heads per workgroup take 8 so that
 // their q slices fit in fewer registers.
@@ -511,6 +800,14 @@ hipError_t launch_t(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
 }
 
 template <int KV, int DH>
+hipError_t launch_mfma(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
+  const size_t n = (size_t)p.batch * p.cache.num_kv_heads * a.num_chunks * p.num_parts;
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves>), dim3((unsigned)n), dim3(kDecodeWaves * kWave), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <int KV, int DH>
 hipError_t launch_hc(const DecodeParams& p, const KernelArgs& a, int hc, hipStream_t s) {
   switch (hc) {
     case 1: return launch_t<KV, DH, 1>(p, a, s);
@@ -522,7 +819,8 @@ hipError_t launch_hc(const DecodeParams& p, const KernelArgs& a, int hc, hipStre
 
 }  // namespace
 
-int decode_heads_per_wg(int group) {
+int decode_heads_per_wg(int group, int kernel) {
+  if (kernel == kDecodeMatrix) return kMfmaHeads;
   if (group % 8 == 0) return 8;
   if (group % 4 == 0) return 4;
   if (group % 2 == 0) return 2;
@@ -532,7 +830,7 @@ int decode_heads_per_wg(int group) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const int group = p.num_q_heads / p.cache.num_kv_heads;
-  const int hc = decode_heads_per_wg(group);
+  const int hc = decode_heads_per_wg(group, p.kernel);
   KernelArgs a;
   a.kc = static_cast<const uint8_t*>(p.cache.k);
   a.vc = static_cast<const uint8_t*>(p.cache.v);
@@ -551,11 +849,14 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.max_seq_len = p.max_seq_len;
   a.part_tokens = p.part_tokens;
   a.num_parts = p.num_parts;
-  a.num_chunks = group / hc;
+  a.num_chunks = (group + hc - 1) / hc;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   const int dt = p.cache.dtype, dh = p.cache.head_dim;
   hipError_t e;
-  if (dt == kF32) e = dh == 64 ? launch_hc<kF32, 64>(p, a, hc, s) : launch_hc<kF32, 128>(p, a, hc, s);
+  if (p.kernel == kDecodeMatrix)
+    e = dt == kBF16 ? (dh == 64 ? launch_mfma<kBF16, 64>(p, a, s) : launch_mfma<kBF16, 128>(p, a, s))
+                    : (dh == 64 ? launch_mfma<kFP8, 64>(p, a, s) : launch_mfma<kFP8, 128>(p, a, s));
+  else if (dt == kF32) e = dh == 64 ? launch_hc<kF32, 64>(p, a, hc, s) : launch_hc<kF32, 128>(p, a, hc, s);
   else if (dt == kBF16) e = dh == 64 ? launch_hc<kBF16, 64>(p, a, hc, s) : launch_hc<kBF16, 128>(p, a, hc, s);
   else e = dh == 64 ? launch_hc<kFP8, 64>(p, a, hc, s) : launch_hc<kFP8, 128>(p, a, hc, s);
   if (e != hipSuccess || p.num_parts <= 1) return e;

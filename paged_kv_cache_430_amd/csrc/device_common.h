@@ -88,6 +88,17 @@ __device__ __forceinline__ uint4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, 
   return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
 }
 
+// 8- and 4-byte forms of the non-temporal load.
+__device__ __forceinline__ uint2 buffer_load8_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i x = __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, kCacheNonTemporal);
+  return make_uint2((uint32_t)x[0], (uint32_t)x[1]);
+}
+
+__device__ __forceinline__ uint32_t buffer_load4_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, kCacheNonTemporal);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Hardware hands consecutive workgroup ids to the XCDs round-robin. This

@@ -49,6 +49,7 @@ struct DecodeParams {
   float* out;
   float* ws_ml;        // [batch, Hq, num_parts, 2] (m, l) in log2 units
   float* ws_u;         // [batch, Hq, num_parts, head_dim]
+  int kernel;          // kDecodeVector or kDecodeMatrix
 };
 
 // Waves of one split-KV decode workgroup. A wave reads its share of the
@@ -56,8 +57,13 @@ struct DecodeParams {
 // 64 * kDecodeWaves blocks.
 constexpr int kDecodeWaves = 8;
 
-// Heads of one KV group handled by one decode workgroup.
-int decode_heads_per_wg(int group);
+// The two decode kernels: products on the vector ALUs (any cache dtype), or
+// on the matrix cores (bf16 and fp8 caches).
+constexpr int kDecodeVector = 0;
+constexpr int kDecodeMatrix = 1;
+
+// Heads of one KV group handled by one decode workgroup of the given kernel.
+int decode_heads_per_wg(int group, int kernel);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 struct PrefillParams {

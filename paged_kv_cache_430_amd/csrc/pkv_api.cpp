@@ -99,19 +99,29 @@ int check_tables(const std::vector<int32_t>& bt, int max_blocks, int seq, int to
 // partitions (one round of workgroups over the CUs, no split when the units
 // already fill the chip), never below 256 tokens and never above the
 // largest partition one workgroup can take.
-int32_t auto_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
+// Which decode kernel runs: PKV_DECODE_KERNEL=vector|matrix overrides the
+// default (the matrix kernel takes bf16 and fp8 caches only).
+int decode_kernel_for(int32_t dtype) {
+  if (dtype == PKV_F32) return kDecodeVector;
+  const char* e = getenv("PKV_DECODE_KERNEL");
+  if (e && std::string(e) == "vector") return kDecodeVector;
+  return kDecodeMatrix;
+}
+
+int32_t auto_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len, int kernel) {
   const int32_t msl16 = (std::max(max_seq_len, 1) + 15) / 16 * 16;
   if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return std::min(msl16, kMaxPartition);
   const int group = hq / hkv;
-  const int64_t units = (int64_t)batch * hkv * (group / decode_heads_per_wg(group));
+  const int hpw = decode_heads_per_wg(group, kernel);
+  const int64_t units = (int64_t)batch * hkv * ((group + hpw - 1) / hpw);
   const int64_t parts = std::max<int64_t>(1, (kComputeUnits + units - 1) / units);
   int32_t pt = (int32_t)(((max_seq_len + parts - 1) / parts + 15) / 16 * 16);
   pt = std::max(pt, std::min(kMinPartition, msl16));
   return std::min(pt, kMaxPartition);
 }
 
-int32_t effective_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len, int32_t pt) {
-  return pt == 0 ? auto_partition(batch, hq, hkv, max_seq_len) : pt;
+int32_t effective_partition(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len, int32_t pt, int kernel) {
+  return pt == 0 ? auto_partition(batch, hq, hkv, max_seq_len, kernel) : pt;
 }
 
 size_t decode_ws_bytes(int32_t batch, int32_t hq, int32_t dh, int32_t max_seq_len, int32_t pt) {
@@ -140,7 +150,7 @@ using namespace pkv;
 
 extern "C" {
 
-PKV_API int32_t pkv_version(void) { return 200; }
+PKV_API int32_t pkv_version(void) { return 300; }
 
 PKV_API const char* pkv_last_error(void) { return last_error().c_str(); }
 
@@ -230,16 +240,17 @@ PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const
                     "pkv_kv_append_paged");
 }
 
-PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                               int32_t head_dim, int32_t max_seq_len,
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                                int32_t partition_tokens) {
-  const int32_t pt = effective_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  const int32_t pt = effective_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens,
+                                         decode_kernel_for(cache_dtype));
   return decode_ws_bytes(batch, num_q_heads, head_dim, max_seq_len, pt);
 }
 
-PKV_API int32_t pkv_attn_decode_auto_partition(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                               int32_t max_seq_len) {
-  return auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len);
+PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_seq_len) {
+  return auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len, decode_kernel_for(cache_dtype));
 }
 
 PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
@@ -265,7 +276,8 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, "pkv_attn_decode: NULL pointer");
   if (!aligned16(q)) return fail(PKV_EINVAL, "pkv_attn_decode: q must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_decode: scale is not finite");
-  const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens);
+  const int kernel = decode_kernel_for(c.dtype);
+  const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
   const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -295,6 +307,7 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   p.seq_lens = seq_lens;
   p.scale = scale;
   p.out = out;
+  p.kernel = kernel;
   float* ws = static_cast<float*>(workspace);
   const size_t rows = (size_t)batch * num_q_heads;
   p.ws_ml = need ? ws : nullptr;

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_error_string(lib):
-    assert pkv.pkv_version() == 200
+    assert pkv.pkv_version() == 300
     assert isinstance(lib.pkv_last_error(), bytes)
 
 
@@ -101,31 +101,47 @@ def test_decode_argument_validation(lib):
     assert call(q=0x50004) == pkv.PKV_EINVAL                 # misaligned q
     assert call(scale=float("nan")) == pkv.PKV_EINVAL
     # split-KV needs workspace; sized by the query call
-    need = lib.pkv_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 16)
+    need = lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2, 32, 8, 128, 64, 16)
     assert need == 2 * 32 * 4 * 130 * 4                     # (m, l) and u per partition
     assert call(pt=16) == pkv.PKV_EWORKSPACE
     assert call(pt=16, ws=0x90000, wsb=need - 4) == pkv.PKV_EWORKSPACE
     assert call(b=0) == pkv.PKV_OK                           # nothing to do, nothing launched
-    assert lib.pkv_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 64) == 0
+    assert lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2, 32, 8, 128, 64, 64) == 0
 
 
-def test_auto_partition_rule(lib):
+def test_auto_partition_rule(lib, monkeypatch):
     """ceil(256 / units) partitions of whole blocks, at least 256 tokens (or the
-    whole sequence), at most 8192; units = batch * Hkv * query-head chunks."""
+    whole sequence), at most 8192; units = batch * Hkv * query-head chunks, a
+    chunk being up to 16 heads for bf16/fp8 caches (matrix-core kernel) and the
+    largest of 8, 4, 2, 1 dividing the group for f32 caches (vector kernel)."""
+    monkeypatch.delenv("PKV_DECODE_KERNEL", raising=False)
     ap = lib.pkv_attn_decode_auto_partition
-    assert ap(1, 4, 1, 36) == 48                 # short: one partition of whole blocks
-    assert ap(32, 32, 8, 4096) == 4096           # 256 units fill the chip: no split
-    assert ap(8, 32, 8, 8192) == 2048            # 64 units: 4 partitions
-    assert ap(1, 32, 8, 32768) == 1024           # 8 units: 32 partitions
-    assert ap(4, 32, 8, 32768) == 4096           # 32 units: 8 partitions
-    assert ap(8, 32, 32, 8192) == 8192           # MHA, 256 units
-    assert ap(8, 32, 1, 8192) == 1024            # MQA: 8 heads per workgroup, 4 chunks -> 32 units
-    assert ap(1, 1, 1, 100000) == 400            # 256 partitions of ceil(100000 / 256) -> 400 tokens
-    assert ap(64, 8, 8, 100000) == 8192          # no split wanted, but capped at the largest partition
-    assert ap(1, 8, 2, 300) == 256               # would be 16 tokens: floor of 256
-    for b, hq, hkv, t in [(1, 1, 1, 100000), (8, 32, 8, 8192), (64, 32, 8, 2049), (3, 12, 2, 777)]:
-        p = ap(b, hq, hkv, t)
-        assert 16 <= p <= 8192 and p % 16 == 0
+    bf, f32, fp8 = pkv.PKV_BF16, pkv.PKV_F32, pkv.PKV_FP8_E4M3
+    for dt in (bf, f32, fp8):
+        assert ap(dt, 1, 4, 1, 36) == 48             # short: one partition of whole blocks
+        assert ap(dt, 32, 32, 8, 4096) == 4096       # 256 units fill the chip: no split
+        assert ap(dt, 8, 32, 8, 8192) == 2048        # 64 units: 4 partitions
+        assert ap(dt, 1, 32, 8, 32768) == 1024       # 8 units: 32 partitions
+        assert ap(dt, 4, 32, 8, 32768) == 4096       # 32 units: 8 partitions
+        assert ap(dt, 8, 32, 32, 8192) == 8192       # MHA, 256 units
+        assert ap(dt, 1, 1, 1, 100000) == 400        # 256 partitions of ceil(100000 / 256) -> 400 tokens
+        assert ap(dt, 64, 8, 8, 100000) == 8192      # no split wanted, but capped at the largest partition
+        assert ap(dt, 1, 8, 2, 300) == 256           # would be 16 tokens: floor of 256
+    # MQA, 32 heads per KV head: two 16-head chunks (bf16, fp8) -> 16 units,
+    # or four 8-head chunks (f32) -> 32 units
+    assert ap(bf, 8, 32, 1, 8192) == 512 and ap(fp8, 8, 32, 1, 8192) == 512
+    assert ap(f32, 8, 32, 1, 8192) == 1024
+    # 24 heads per KV head: chunks of 16 and 8 (bf16) or three of 8 (f32)
+    assert ap(bf, 4, 24, 1, 32768) == 1024          # 8 units: 32 partitions
+    assert ap(f32, 4, 24, 1, 32768) == 1504         # 12 units: 22 partitions of ceil(32768 / 22) -> 1504
+    monkeypatch.setenv("PKV_DECODE_KERNEL", "vector")  # the override picks the vector kernel's chunks
+    assert ap(bf, 8, 32, 1, 8192) == 1024
+    monkeypatch.setenv("PKV_DECODE_KERNEL", "matrix")  # f32 caches always take the vector kernel
+    assert ap(f32, 8, 32, 1, 8192) == 1024
+    for dt in (bf, f32):
+        for b, hq, hkv, t in [(1, 1, 1, 100000), (8, 32, 8, 8192), (64, 32, 8, 2049), (3, 12, 2, 777)]:
+            p = ap(dt, b, hq, hkv, t)
+            assert 16 <= p <= 8192 and p % 16 == 0
 
 
 def test_append_and_prefill_validation(lib):

@@ -2,7 +2,11 @@
 
 Tolerances: max-abs 1e-5 for fp32 caches, 2e-3 for bf16 and fp8 caches.
 Pools are NaN-filled before the append, so a masked slot that leaks into a
-sum turns the output into NaN."""
+sum turns the output into NaN. bf16 and fp8 cases run both decode kernels
+(vector ALUs and matrix cores, chosen through PKV_DECODE_KERNEL)."""
+
+import contextlib
+import os
 
 import numpy as np
 import pytest
@@ -19,11 +23,29 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-3}
 
 
-def run_decode(w, cache, dev, partition_tokens=0, copy=0, max_seq_len=None):
+def kernels_for(cache_dtype):
+    return ["vector"] if cache_dtype == "f32" else ["vector", "matrix"]
+
+
+@contextlib.contextmanager
+def decode_kernel(kernel):
+    old = os.environ.get("PKV_DECODE_KERNEL")
+    os.environ["PKV_DECODE_KERNEL"] = kernel
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["PKV_DECODE_KERNEL"]
+        else:
+            os.environ["PKV_DECODE_KERNEL"] = old
+
+
+def run_decode(w, cache, dev, partition_tokens=0, copy=0, max_seq_len=None, kernel="vector"):
     msl = int(w.seq_lens.max()) if max_seq_len is None else max_seq_len
-    out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev, copy), lens(w, dev), msl, w.scale,
-                              partition_tokens=partition_tokens)
-    torch.cuda.synchronize()
+    with decode_kernel(kernel):
+        out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev, copy), lens(w, dev), msl, w.scale,
+                                  partition_tokens=partition_tokens)
+        torch.cuda.synchronize()
     return out.cpu().double().numpy()
 
 
@@ -74,17 +96,22 @@ def test_ragged_lengths_and_partitions(cache_dtype, hq, hkv, dh, pt):
     lens_ = [1, 2, 15, 16, 17, 63, 511, 513, 1000]
     w = workloads.decode_inputs("ragged", 1234 + hq + dh, lens_, hq, hkv, dh, cache_dtype, dev)
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev, partition_tokens=pt)
-    assert_close(got, oracle_decode(w), TOL[cache_dtype], f"{cache_dtype} {hq}/{hkv} dh{dh} pt{pt}")
+    ref = oracle_decode(w)
+    for kern in kernels_for(cache_dtype):
+        got = run_decode(w, cache, dev, partition_tokens=pt, kernel=kern)
+        assert_close(got, ref, TOL[cache_dtype], f"{kern} {cache_dtype} {hq}/{hkv} dh{dh} pt{pt}")
 
 
 def test_empty_sequence_and_clamped_length():
     dev = device()
     w = workloads.decode_inputs("empty", 7, [0, 40, 0, 5], 8, 2, 128, "bf16", dev)
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev, partition_tokens=16)
-    assert np.array_equal(got[0], np.zeros_like(got[0])) and np.array_equal(got[2], np.zeros_like(got[2]))
-    assert_close({1: got[1], 3: got[3]}, oracle_decode(w, [1, 3]), 2e-3, "mixed empty")
+    ref = oracle_decode(w, [1, 3])
+    for kern in kernels_for("bf16"):
+        for pt in (16, 0):
+            got = run_decode(w, cache, dev, partition_tokens=pt, kernel=kern)
+            assert np.array_equal(got[0], np.zeros_like(got[0])) and np.array_equal(got[2], np.zeros_like(got[2]))
+            assert_close({1: got[1], 3: got[3]}, ref, 2e-3, f"{kern} mixed empty pt{pt}")
     # a batch of zero sequences launches nothing
     out = pkv.pkv_attn_decode(cache, w.q[:0], tables(w, dev)[:0], lens(w, dev)[:0], 48, w.scale)
     assert out.shape == (0, 8, 128)
@@ -94,8 +121,10 @@ def test_cfg2_uniform_full_size():
     dev = device()
     w = workloads.cfg2("uniform", device=dev)
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev)
-    assert_close(got, oracle_decode(w), 2e-3, "cfg2 uniform")
+    ref = oracle_decode(w)
+    for kern in kernels_for("bf16"):
+        got = run_decode(w, cache, dev, kernel=kern)
+        assert_close(got, ref, 2e-3, f"{kern} cfg2 uniform")
 
 
 def test_cfg2_all4096_full_size_each_copy():
@@ -105,11 +134,12 @@ def test_cfg2_all4096_full_size_each_copy():
     cache = build_cache(w, dev)
     ref = oracle_decode(w)
     scale_ref = max(float(np.abs(r).max()) for r in ref.values())
-    for c in range(w.copies):
-        got = run_decode(w, cache, dev, copy=c)
-        assert_close(got, ref, 2e-3, f"cfg2 all4096 copy {c}")
-        rel = max(float(np.abs(got[b] - ref[b]).max()) for b in ref) / scale_ref
-        assert rel < 2e-2
+    for kern in kernels_for("bf16"):
+        for c in range(w.copies):
+            got = run_decode(w, cache, dev, copy=c, kernel=kern)
+            assert_close(got, ref, 2e-3, f"{kern} cfg2 all4096 copy {c}")
+            rel = max(float(np.abs(got[b] - ref[b]).max()) for b in ref) / scale_ref
+            assert rel < 2e-2
 
 
 @pytest.mark.parametrize("kind", ["mha", "gqa", "mqa", "gqa-fp8"])
@@ -117,8 +147,10 @@ def test_cfg5_head_layouts_full_size(kind):
     dev = device()
     w = workloads.cfg5(kind, device=dev)
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev)
-    assert_close(got, oracle_decode(w), 2e-3, f"cfg5 {kind}")
+    ref = oracle_decode(w)
+    for kern in kernels_for("bf16"):
+        got = run_decode(w, cache, dev, kernel=kern)
+        assert_close(got, ref, 2e-3, f"{kern} cfg5 {kind}")
 
 
 def test_cfg3_long_context_b1_layers_and_b4():
@@ -126,33 +158,42 @@ def test_cfg3_long_context_b1_layers_and_b4():
     layers = workloads.cfg3(batch=1, device=dev, layers=3)
     for li, w in enumerate(layers):
         cache = build_cache(w, dev)
-        got = run_decode(w, cache, dev, partition_tokens=512)
-        assert_close(got, oracle_decode(w), 2e-3, f"cfg3 B=1 layer {li}")
+        ref = oracle_decode(w)
+        for kern in kernels_for("bf16"):
+            got = run_decode(w, cache, dev, partition_tokens=512, kernel=kern)
+            assert_close(got, ref, 2e-3, f"{kern} cfg3 B=1 layer {li}")
         del cache
     w4 = workloads.cfg3(batch=4, device=dev, layers=1)[0]
     cache = build_cache(w4, dev)
-    got = run_decode(w4, cache, dev, partition_tokens=512)
-    assert_close(got, oracle_decode(w4), 2e-3, "cfg3 B=4")
+    ref = oracle_decode(w4)
+    for kern in kernels_for("bf16"):
+        got = run_decode(w4, cache, dev, partition_tokens=512, kernel=kern)
+        assert_close(got, ref, 2e-3, f"{kern} cfg3 B=4")
 
 
+@pytest.mark.parametrize("cache_dtype,kern", [("f32", "vector"), ("bf16", "vector"), ("bf16", "matrix")])
 @pytest.mark.parametrize("t,pt", [(37, 16), (4096, 0), (4096, 512), (32768, 512), (1, 0)])
-def test_position_probe(t, pt):
+def test_position_probe(t, pt, cache_dtype, kern):
     """q = 0 makes every weight exactly 1. V is one-hot, V[t, 1 + t % 127] = 1,
     so out[d] = #{t : 1 + t % 127 = d} / T in exact fp32 arithmetic: a dropped
     or doubled token moves one column by 1/T. Column 0 carries the ramp t/T,
-    whose mean is (T-1)/(2T)."""
+    whose mean is (T-1)/(2T) (checked for fp32 storage, where it is exact)."""
     dev = device()
-    w = workloads.decode_inputs("probe", 3, [t], 8, 2, 128, "f32", dev)
+    w = workloads.decode_inputs("probe", 3, [t], 8, 2, 128, cache_dtype, dev)
     w.q.zero_()
     w.v.zero_()
     tok = torch.arange(t, device=dev)
-    w.v[tok, :, 0] = (tok.float() / t)[:, None]
+    if cache_dtype == "f32":
+        w.v[tok, :, 0] = (tok.float() / t)[:, None]
     w.v[tok, :, 1 + tok % 127] = 1.0
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev, partition_tokens=pt)
+    got = run_decode(w, cache, dev, partition_tokens=pt, kernel=kern)
     counts = np.bincount(1 + np.arange(t) % 127, minlength=128)[1:] / t
     assert np.array_equal(got[0, :, 1:], np.broadcast_to(counts.astype(np.float32).astype(np.float64), (8, 127)))
-    assert np.abs(got[0, :, 0] - (t - 1) / (2 * t)).max() <= 1e-5
+    if cache_dtype == "f32":
+        assert np.abs(got[0, :, 0] - (t - 1) / (2 * t)).max() <= 1e-5
+    else:
+        assert np.array_equal(got[0, :, 0], np.zeros(8))
 
 
 def test_peaked_probe_bf16():
@@ -161,34 +202,41 @@ def test_peaked_probe_bf16():
     hit = 1777
     w.q[0] = (w.k[hit].repeat_interleave(4, dim=0).float() * 40.0).to(torch.bfloat16)
     cache = build_cache(w, dev)
-    got = run_decode(w, cache, dev)
     want = w.v[hit].repeat_interleave(4, dim=0).float().cpu().numpy()
-    assert np.abs(got[0] - want).max() <= 2e-3
-    assert_close({0: got[0]}, oracle_decode(w), 2e-3, "peaked")
+    ref = oracle_decode(w)
+    for kern in kernels_for("bf16"):
+        got = run_decode(w, cache, dev, kernel=kern)
+        assert np.abs(got[0] - want).max() <= 2e-3
+        assert_close({0: got[0]}, ref, 2e-3, f"{kern} peaked")
 
 
 def test_relabelled_blocks_give_bit_identical_output():
     dev = device()
     w = workloads.decode_inputs("relabel", 8, [700, 33, 4096], 32, 8, 128, "bf16", dev, copies=2)
     cache = build_cache(w, dev)
-    a = run_decode(w, cache, dev, copy=0)
-    b = run_decode(w, cache, dev, copy=1)
     assert not np.array_equal(w.block_tables[0], w.block_tables[1])
-    assert np.array_equal(a, b)
+    for kern in kernels_for("bf16"):
+        for pt in (0, 64):
+            a = run_decode(w, cache, dev, copy=0, partition_tokens=pt, kernel=kern)
+            b = run_decode(w, cache, dev, copy=1, partition_tokens=pt, kernel=kern)
+            assert np.array_equal(a, b), f"{kern} pt{pt}"
 
 
 def test_workspace_reuse_across_calls_and_shapes():
     """The workspace needs no initialisation: one buffer, filled with NaN bytes
     first, serves many calls with different shapes."""
     dev = device()
-    n = pkv.pkv_attn_decode_workspace_bytes(8, 32, 8, 128, 4096, 16)
+    n = pkv.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 8, 32, 8, 128, 4096, 16)
     ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device=dev).view(torch.uint8)
     for seed, lens_ in [(1, [4096, 100, 17]), (2, [50] * 8), (3, [4096])]:
         w = workloads.decode_inputs("reuse", seed, lens_, 32, 8, 128, "bf16", dev)
         cache = build_cache(w, dev)
         msl = w.max_blocks * 16
-        for _ in range(3):
-            out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev), lens(w, dev), msl, w.scale,
-                                      partition_tokens=16, workspace=ws)
-            torch.cuda.synchronize()
-            assert_close(out.cpu().double().numpy(), oracle_decode(w), 2e-3, f"reuse {seed}")
+        ref = oracle_decode(w)
+        for kern in kernels_for("bf16"):
+            for _ in range(2):
+                with decode_kernel(kern):
+                    out = pkv.pkv_attn_decode(cache, w.q, tables(w, dev), lens(w, dev), msl, w.scale,
+                                              partition_tokens=16, workspace=ws)
+                    torch.cuda.synchronize()
+                assert_close(out.cpu().double().numpy(), ref, 2e-3, f"{kern} reuse {seed}")
