@@ -509,9 +509,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
 // blocks). For a pair of blocks:
 //   Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32_bf16, keys as M (16 per block), Dh as the
 //   contraction: lane (col = lane % 16, kg = lane / 16) loads, for k-step dc,
-//   the 8 elements dc·32 + kg·8 … of key row col — the A operand as it lies in
-//   memory; q of head col is the B operand. The result leaves in lane (col, kg)
-//   the scores of head col for keys 4kg … 4kg+3 of each block.
+//   8 elements of key row col — the A operand as it lies in memory (which 8
+//   is MfmaGeometry::k_elem; the contraction may take Dh in any order as long
+//   as q follows it); q of head col is the B operand. The result leaves in
+//   lane (col, kg) the scores of head col for keys 4kg … 4kg+3 of each block.
 //   Oᵀ += Vᵀ·Pᵀ on the same instruction with the 32 keys as the contraction:
 //   those scores, as probabilities, are already the B operand (element j < 4
 //   ↔ key 4kg+j of the first block, j ≥ 4 ↔ key 4kg+j−4 of the second). For
@@ -534,7 +535,16 @@ struct MfmaGeometry {
   static constexpr int NDT = DH / 16;               // 16-row tiles of Oᵀ = elements of a V slice
   static constexpr int KW = 8 * ESZ / 4;            // stored dwords of one K operand slice
   static constexpr int VW = NDT * ESZ / 4;          // stored dwords of one V slice (≥ 1)
-  static_assert(VW >= 1 && NDC >= 1, "unsupported head dimension");
+  static_assert(VW >= 1 && NDC >= 2, "unsupported head dimension");
+  // First element of the 8 that lane group kg holds at k-step dc (the
+  // contraction over Dh may take its elements in any order, as long as q and
+  // K agree). Each K load covers 64 contiguous bytes of every row it touches:
+  // bf16 — k-step dc, group kg holds chunk 4dc + kg of 16 bytes (8 elements);
+  // fp8 — a 16-byte load of chunk 4·(dc/2) + kg holds 16 elements, the first
+  // 8 for even dc and the last 8 for odd dc.
+  static __device__ __forceinline__ int k_elem(int dc, int kg) {
+    return KV == kFP8 ? (dc / 2) * 64 + kg * 16 + (dc % 2) * 8 : dc * 32 + kg * 8;
+  }
 };
 
 // n stored dwords (n = 1, 2 or 4) at a byte offset, non-temporal.
@@ -606,7 +616,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.hq + h0 + col) * DH;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      const uint4 x = col < nh ? *reinterpret_cast<const uint4*>(qrow + dc * 32 + kg * 8) : make_uint4(0, 0, 0, 0);
+      const uint4 x = col < nh ? *reinterpret_cast<const uint4*>(qrow + G::k_elem(dc, kg)) : make_uint4(0, 0, 0, 0);
       qb[dc] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
@@ -641,8 +651,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       const int rows = rows_of(block_index(j, e));
       const auto rk = tile_rsrc(a.kc, phys, rows);
       const auto rv = tile_rsrc(a.vc, phys, rows);
+      if constexpr (KV == kFP8) {   // 16-byte loads, each feeding two k-steps
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) load_dwords<KW>(rk, col * G::RB + (dc * 4 + kg) * KW * 4, t.k[e][dc]);
+        for (int d2 = 0; d2 < NDC / 2; ++d2) {
+          const uint4 x = buffer_load16_stream(rk, col * G::RB + (d2 * 4 + kg) * 16);
+          t.k[e][2 * d2][0] = x.x; t.k[e][2 * d2][1] = x.y;
+          t.k[e][2 * d2 + 1][0] = x.z; t.k[e][2 * d2 + 1][1] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) load_dwords<KW>(rk, col * G::RB + (dc * 4 + kg) * 16, t.k[e][dc]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
     }
