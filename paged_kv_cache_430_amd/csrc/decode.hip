@@ -509,10 +509,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
 // blocks). For a pair of blocks:
 //   Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32_bf16, keys as M (16 per block), Dh as the
 //   contraction: lane (col = lane % 16, kg = lane / 16) loads, for k-step dc,
-//   8 elements of key row col — the A operand as it lies in memory (which 8
-//   is MfmaGeometry::k_elem; the contraction may take Dh in any order as long
-//   as q follows it); q of head col is the B operand. The result leaves in
-//   lane (col, kg) the scores of head col for keys 4kg … 4kg+3 of each block.
+//   8 elements of key row col (which 8 is MfmaGeometry::k_elem; the
+//   contraction may take Dh in any order as long as q follows it); q of head
+//   col is the B operand. K comes from memory in whole rows per load (CPR
+//   lanes per row, so every request covers full cache lines) and is restaged
+//   through a padded per-wave LDS area into that operand layout. The result
+//   leaves in lane (col, kg) the scores of head col for keys 4kg … 4kg+3 of
+//   each block.
 //   Oᵀ += Vᵀ·Pᵀ on the same instruction with the 32 keys as the contraction:
 //   those scores, as probabilities, are already the B operand (element j < 4
 //   ↔ key 4kg+j of the first block, j ≥ 4 ↔ key 4kg+j−4 of the second). For
@@ -534,6 +537,10 @@ struct MfmaGeometry {
   static constexpr int NDC = DH / 32;               // k-steps of Sᵀ = K·Qᵀ
   static constexpr int NDT = DH / 16;               // 16-row tiles of Oᵀ = elements of a V slice
   static constexpr int KW = 8 * ESZ / 4;            // stored dwords of one K operand slice
+  static constexpr int CPR = RB / 16;               // 16-byte chunks of a row
+  static constexpr int RPI = kWave / CPR;           // rows per whole-row K load
+  static constexpr int NKI = kBlockSize / RPI;      // whole-row K loads per block
+  static constexpr int KRS = RB + 16;               // padded K row in LDS (bytes)
   static constexpr int VW = NDT * ESZ / 4;          // stored dwords of one V slice (≥ 1)
   static_assert(VW >= 1 && NDC >= 2, "unsupported head dimension");
   // First element of the 8 that lane group kg holds at k-step dc (the
@@ -582,7 +589,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   constexpr int NH = kMfmaHeads;
   using G = MfmaGeometry<KV, DH>;
   constexpr int NDC = G::NDC, NDT = G::NDT, KW = G::KW, VW = G::VW;
-  __shared__ float sh_u[kWaves][NH][DH];
+  // Each wave's LDS region first stages its K blocks (two padded 16-row
+  // blocks), then, after its loop, holds its accumulators for the merge.
+  constexpr int kStage = 2 * kBlockSize * G::KRS;
+  constexpr int kRegion = kStage > NH * DH * 4 ? kStage : NH * DH * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t sh_region[kWaves][kRegion];
   __shared__ float sh_m[kWaves][NH];
   __shared__ float sh_l[kWaves][NH];
 
@@ -638,7 +649,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
   };
   struct Tile {
-    uint32_t k[2][NDC][KW];   // [block][k-step]
+    uint4 k[2][G::NKI];       // [block][whole-row load]
     uint32_t v[2][4][VW];     // [block][key of the lane's quad]
   };
   // block e (0, 1) of the wave's j-th tile
@@ -651,17 +662,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       const int rows = rows_of(block_index(j, e));
       const auto rk = tile_rsrc(a.kc, phys, rows);
       const auto rv = tile_rsrc(a.vc, phys, rows);
-      if constexpr (KV == kFP8) {   // 16-byte loads, each feeding two k-steps
+      // K: whole rows per load (CPR lanes per row), restaged through LDS
 #pragma unroll
-        for (int d2 = 0; d2 < NDC / 2; ++d2) {
-          const uint4 x = buffer_load16_stream(rk, col * G::RB + (d2 * 4 + kg) * 16);
-          t.k[e][2 * d2][0] = x.x; t.k[e][2 * d2][1] = x.y;
-          t.k[e][2 * d2 + 1][0] = x.z; t.k[e][2 * d2 + 1][1] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) load_dwords<KW>(rk, col * G::RB + (dc * 4 + kg) * 16, t.k[e][dc]);
-      }
+      for (int i = 0; i < G::NKI; ++i) t.k[e][i] = buffer_load16_stream(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
     }
@@ -679,15 +682,41 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       const int phys = block_phys(j, e);
       rows[e] = (unsigned)phys < (unsigned)a.num_blocks ? rows_of(block_index(j, e)) : 0;
     }
+    // K rows to the wave's LDS stage, then back as the A operand (row col)
+    uint8_t* stage = sh_region[w];
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < G::NKI; ++i)
+        *reinterpret_cast<uint4*>(stage + (e * kBlockSize + i * G::RPI + lane / G::CPR) * G::KRS +
+                                  (lane % G::CPR) * 16) = t.k[e][i];
+    wave_lds_sync();
     // Sᵀ for both blocks
     f32x4_t st[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
+      const uint8_t* krow = stage + (e * kBlockSize + col) * G::KRS;
+      uint32_t kd[NDC][KW];
+      if constexpr (KV == kFP8) {   // a 16-byte piece holds two k-steps
+#pragma unroll
+        for (int d2 = 0; d2 < NDC / 2; ++d2) {
+          const uint4 x = *reinterpret_cast<const uint4*>(krow + (d2 * 4 + kg) * 16);
+          kd[2 * d2][0] = x.x; kd[2 * d2][1] = x.y;
+          kd[2 * d2 + 1][0] = x.z; kd[2 * d2 + 1][1] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+          const uint4 x = *reinterpret_cast<const uint4*>(krow + (dc * 4 + kg) * 16);
+          kd[dc][0] = x.x; kd[dc][1] = x.y; kd[dc][2] = x.z; kd[dc][3] = x.w;
+        }
+      }
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
         uint32_t kk[4];
-        to_bf16_pairs<KV, KW>(t.k[e][dc], kk);
+        to_bf16_pairs<KV, KW>(kd[dc], kk);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8_t, make_uint4(kk[0], kk[1], kk[2], kk[3])), qb[dc], acc, 0, 0, 0);
       }
@@ -770,14 +799,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   // ---- the wave's totals, then the waves' merge ------------------------------------
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
+  typedef float HeadRow[DH];
+  wave_lds_sync();   // the wave's last stage reads are done before its region is reused
+  HeadRow* my_u = reinterpret_cast<HeadRow*>(sh_region[w]);
   if (col < nh) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sh_u[w][col][NDT * (4 * kg + i) + dt] = o[dt][i];
+      for (int i = 0; i < 4; ++i) my_u[col][NDT * (4 * kg + i) + dt] = o[dt][i];
     if (kg == 0) { sh_m[w][col] = m_run; sh_l[w][col] = l_run; }
   }
   __syncthreads();
+  auto sh_u = [&](int ww, int h, int d) { return reinterpret_cast<const HeadRow*>(sh_region[ww])[h][d]; };
   const float vscale = KV == kFP8 ? a.v_scale[g] : 1.0f;
   for (int i = tid; i < nh * DH; i += kThreads) {
     const int h = i / DH, d = i % DH;
@@ -788,7 +821,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const float wt = part_weight(sh_m[ww][h], mt);
-      u = fmaf(wt, sh_u[ww][h][d], u);
+      u = fmaf(wt, sh_u(ww, h, d), u);
       lt = fmaf(wt, sh_l[ww][h], lt);
     }
     if (P == 1) {
