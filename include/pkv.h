@@ -177,12 +177,13 @@ PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const
  *   partition_tokens: tokens per split-KV partition, a multiple of
  *                 block_size in [16, 8192]; 0 picks one from the shape
  *                 (pkv_attn_decode_auto_partition)
- *   out:          device fp32 [batch, num_q_heads, head_dim]
- *   workspace:    device, at least pkv_attn_decode_workspace_bytes(...)
- *                 bytes for the same arguments; may be NULL when that size
- *                 is 0 (a single partition covers max_seq_len). It holds the
- *                 partitions' fp32 (m, l) pairs [batch, Hq, P, 2] followed by
- *                 their weighted sums u [batch, Hq, P, head_dim], P =
+ *   out:          device fp32 [batch, num_q_heads, head_dim], 16-byte aligned
+ *   workspace:    device, 16-byte aligned, at least
+ *                 pkv_attn_decode_workspace_bytes(...) bytes for the same
+ *                 arguments; may be NULL when that size is 0 (a single
+ *                 partition covers max_seq_len). It holds the partitions'
+ *                 fp32 weighted sums u [batch, Hq, P, head_dim] followed by
+ *                 their (m, l) pairs [batch, Hq, P, 2], P =
  *                 ceil(max_seq_len / partition). Its contents need no
  *                 initialisation; calls that share a workspace must not
  *                 overlap (one workspace per stream).

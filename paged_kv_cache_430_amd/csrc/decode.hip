@@ -92,8 +92,7 @@ struct MergeArgs {
   const float* ws_ml;
   const float* ws_u;
   float* out;
-  size_t total;   // batch · Hq · head_dim
-  int head_dim, num_parts;
+  int num_parts;
 };
 
 // Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane
@@ -461,45 +460,73 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
   }
 }
 
-// Split-KV reduce: one thread per (sequence, query head, column). Partition
+// Split-KV reduce: one workgroup per (sequence, query head) row. Partition
 // π left m_π (log2 domain), l_π and u_π — an empty partition left m = −inf,
 // l = 0 and an unwritten u, which gets weight 0 and is never read into the
 // sum; with m* = max m_π the output is Σ 2^(m_π − m*) u_π / Σ 2^(m_π − m*) l_π
-// (0 for a sequence with no tokens).
+// (0 for a sequence with no tokens). Thread (d4, pg) merges, online, the
+// columns 4·d4 … 4·d4+3 of partitions pg, pg + NG, … (four partitions per
+// round, their loads in flight together); the NG groups are then combined
+// through LDS in a fixed order.
+template <int DH>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
-  const size_t idx = (size_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  if (idx >= a.total) return;
-  const size_t row = idx / a.head_dim;
-  const int d = (int)(idx % a.head_dim);
-  const int nparts = a.num_parts;
-  const float* ml = a.ws_ml + row * nparts * 2;
-  const float* u = a.ws_u + row * nparts * a.head_dim + d;
-  // online merge, eight partitions per round so their loads are in flight together
-  float mt = -INFINITY, lt = 0.0f, ut = 0.0f;
-  for (int p0 = 0; p0 < nparts; p0 += 8) {
-    float pm[8], pl[8], pu[8];
+  constexpr int D4 = DH / 4, NG = kMergeThreads / D4;
+  __shared__ float s_m[NG], s_l[NG];
+  __shared__ float4 s_u[NG][D4];
+  const size_t row = blockIdx.x;
+  const int t = threadIdx.x, d4 = t % D4, pg = t / D4;
+  const int P = a.num_parts;
+  const float* ml = a.ws_ml + row * P * 2;
+  const float4* u = reinterpret_cast<const float4*>(a.ws_u + row * P * DH) + d4;
+  float mt = -INFINITY, lt = 0.0f;
+  float4 ut = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = pg; p0 < P; p0 += 4 * NG) {
+    float pm[4], pl[4];
+    float4 pu[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool ok = p0 + k < nparts;
-      pm[k] = ok ? ml[2 * (p0 + k)] : -INFINITY;
-      pl[k] = ok ? ml[2 * (p0 + k) + 1] : 0.0f;
-      pu[k] = ok ? u[(size_t)(p0 + k) * a.head_dim] : 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + k * NG;
+      const bool ok = p < P;
+      pm[k] = ok ? ml[2 * p] : -INFINITY;
+      pl[k] = ok ? ml[2 * p + 1] : 0.0f;
+      pu[k] = ok ? u[(size_t)p * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float mr = mt;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mr = fmaxf(mr, pm[k]);
+    for (int k = 0; k < 4; ++k) mr = fmaxf(mr, pm[k]);
     const float c = part_weight(mt, mr);
     lt *= c;
-    ut *= c;
+    ut.x *= c; ut.y *= c; ut.z *= c; ut.w *= c;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       const float wgt = part_weight(pm[k], mr);
       lt = fmaf(wgt, pl[k], lt);
-      ut = wgt > 0.0f ? fmaf(wgt, pu[k], ut) : ut;   // an empty partition's u is never read
+      if (wgt > 0.0f) {   // an empty partition's u is never read into the sum
+        ut.x = fmaf(wgt, pu[k].x, ut.x); ut.y = fmaf(wgt, pu[k].y, ut.y);
+        ut.z = fmaf(wgt, pu[k].z, ut.z); ut.w = fmaf(wgt, pu[k].w, ut.w);
+      }
     }
     mt = mr;
   }
-  a.out[idx] = lt > 0.0f ? ut / lt : 0.0f;
+  s_u[pg][d4] = ut;
+  if (d4 == 0) { s_m[pg] = mt; s_l[pg] = lt; }
+  __syncthreads();
+  if (t < D4) {
+    float m = s_m[0];
+#pragma unroll
+    for (int q = 1; q < NG; ++q) m = fmaxf(m, s_m[q]);
+    float l = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float wgt = part_weight(s_m[q], m);
+      l = fmaf(wgt, s_l[q], l);
+      const float4 x = s_u[q][t];
+      o.x = fmaf(wgt, x.x, o.x); o.y = fmaf(wgt, x.y, o.y); o.z = fmaf(wgt, x.z, o.z); o.w = fmaf(wgt, x.w, o.w);
+    }
+    const float4 r = l > 0.0f ? make_float4(o.x / l, o.y / l, o.z / l, o.w / l) : make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(a.out + row * DH)[t] = r;
+  }
 }
 
 // ---- matrix-core form -------------------------------------------------------------
@@ -916,11 +943,10 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   m.ws_ml = p.ws_ml;
   m.ws_u = p.ws_u;
   m.out = p.out;
-  m.total = (size_t)p.batch * p.num_q_heads * dh;
-  m.head_dim = dh;
   m.num_parts = p.num_parts;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((m.total + kMergeThreads - 1) / kMergeThreads)),
-                     dim3(kMergeThreads), 0, s, m);
+  const unsigned rows = (unsigned)((size_t)p.batch * p.num_q_heads);
+  if (dh == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(rows), dim3(kMergeThreads), 0, s, m);
+  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(rows), dim3(kMergeThreads), 0, s, m);
   return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@ struct DecodeParams {
   const int32_t* seq_lens;
   float scale;
   float* out;
+  float* ws_u;         // [batch, Hq, num_parts, head_dim] (first in the workspace)
   float* ws_ml;        // [batch, Hq, num_parts, 2] (m, l) in log2 units
-  float* ws_u;         // [batch, Hq, num_parts, head_dim]
   int kernel;          // kDecodeVector or kDecodeMatrix
 };
 

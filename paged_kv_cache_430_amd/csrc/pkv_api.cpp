@@ -274,7 +274,7 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   if (!ok_q) return fail(PKV_EDTYPE, "pkv_attn_decode: q dtype must be F32 for an F32 cache, BF16 otherwise");
   if (batch == 0) return PKV_OK;
   if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, "pkv_attn_decode: NULL pointer");
-  if (!aligned16(q)) return fail(PKV_EINVAL, "pkv_attn_decode: q must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "pkv_attn_decode: q and out must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_decode: scale is not finite");
   const int kernel = decode_kernel_for(c.dtype);
   const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
@@ -282,6 +282,7 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "pkv_attn_decode: workspace needs " + std::to_string(need) + " bytes");
+  if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "pkv_attn_decode: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (check_mode()) {
     std::vector<int32_t> lens, bt;
@@ -310,8 +311,8 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   p.kernel = kernel;
   float* ws = static_cast<float*>(workspace);
   const size_t rows = (size_t)batch * num_q_heads;
-  p.ws_ml = need ? ws : nullptr;
-  p.ws_u = need ? ws + rows * parts * 2 : nullptr;
+  p.ws_u = need ? ws : nullptr;
+  p.ws_ml = need ? ws + rows * parts * c.head_dim : nullptr;
   return hip_status(launch_decode(p, s), "pkv_attn_decode");
 }
 

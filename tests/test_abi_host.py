@@ -90,7 +90,7 @@ def test_decode_argument_validation(lib):
     ref, _ = _fake_cache()
     call = lambda **kw: lib.pkv_attn_decode(  # noqa: E731
         ref, kw.get("q", 0x50000), kw.get("qd", pkv.PKV_BF16), kw.get("b", 2), kw.get("hq", 32), 0x60000,
-        kw.get("mb", 4), 0x70000, kw.get("msl", 64), kw.get("scale", 0.1), kw.get("pt", 0), 0x80000,
+        kw.get("mb", 4), 0x70000, kw.get("msl", 64), kw.get("scale", 0.1), kw.get("pt", 0), kw.get("out", 0x80000),
         kw.get("ws", None), kw.get("wsb", 0), None)
     assert call(hq=12) == pkv.PKV_EINVAL                     # not a multiple of Hkv
     assert call(hq=8 * 65) == pkv.PKV_EINVAL                 # group above 64
@@ -99,12 +99,14 @@ def test_decode_argument_validation(lib):
     assert call(pt=8208) == pkv.PKV_EINVAL
     assert call(qd=pkv.PKV_F32) == pkv.PKV_EDTYPE            # bf16 cache wants bf16 q
     assert call(q=0x50004) == pkv.PKV_EINVAL                 # misaligned q
+    assert call(out=0x80004) == pkv.PKV_EINVAL               # misaligned out
     assert call(scale=float("nan")) == pkv.PKV_EINVAL
     # split-KV needs workspace; sized by the query call
     need = lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2, 32, 8, 128, 64, 16)
     assert need == 2 * 32 * 4 * 130 * 4                     # (m, l) and u per partition
     assert call(pt=16) == pkv.PKV_EWORKSPACE
     assert call(pt=16, ws=0x90000, wsb=need - 4) == pkv.PKV_EWORKSPACE
+    assert call(pt=16, ws=0x90008, wsb=need) == pkv.PKV_EINVAL   # misaligned workspace
     assert call(b=0) == pkv.PKV_OK                           # nothing to do, nothing launched
     assert lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2, 32, 8, 128, 64, 64) == 0
 
