@@ -103,7 +103,7 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dpp_f32<kQuadXor2>(x);
   if constexpr (N >= 8) x += dpp_f32<kRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f32<kRowMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (N >= 32) x = pair_rows16(x, AddOp());
   return x;
 }
 
@@ -116,17 +116,10 @@ template <int N, typename Op>
 __device__ __forceinline__ float across_groups(float x, Op op) {
   if constexpr (N <= 4) x = op(x, dpp_f32<kRowRor4>(x));
   if constexpr (N <= 8) x = op(x, dpp_f32<kRowRor8>(x));
-  if constexpr (N <= 16) x = op(x, __shfl_xor(x, 16, kWave));
-  x = op(x, __shfl_xor(x, 32, kWave));
-  return x;
+  if constexpr (N <= 16) x = pair_rows16(x, op);
+  return pair_halves32(x, op);
 }
 
-struct MaxOp {
-  __device__ float operator()(float x, float y) const { return fmaxf(x, y); }
-};
-struct AddOp {
-  __device__ float operator()(float x, float y) const { return x + y; }
-};
 
 // Score contribution of one 16-byte K slice against one head's q slice.
 template <int KV, int QD>
@@ -759,8 +752,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
         st[e][i] = v;
         mt = fmaxf(mt, v);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = pair_halves32(pair_rows16(mt, MaxOp()), MaxOp());
     const float m_new = fmaxf(m_run, mt);
     if (__any(m_new > m_run)) {                          // rescale only when a max moved
       const float alpha = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new);
@@ -824,8 +816,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   }
 
   // ---- the wave's totals, then the waves' merge ------------------------------------
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = pair_halves32(pair_rows16(l_run, AddOp()), AddOp());
   typedef float HeadRow[DH];
   wave_lds_sync();   // the wave's last stage reads are done before its region is reused
   HeadRow* my_u = reinterpret_cast<HeadRow*>(sh_region[w]);

@@ -51,24 +51,27 @@ constexpr int kRowHalfMirror = 0x141;  // lane i of an 8-lane half-row reads lan
 constexpr int kRowRor4 = 0x124;        // rotate each 16-lane row by 4 lanes
 constexpr int kRowRor8 = 0x128;        // rotate each 16-lane row by 8 lanes
 
-// Sum over the four lanes of a quad; every lane of the quad receives it.
-__device__ __forceinline__ float quad_sum(float x) {
-  x += dpp_f32<kQuadXor1>(x);
-  x += dpp_f32<kQuadXor2>(x);
-  return x;
+// Cross-row exchanges on gfx950's lane-swap instructions (VALU, no LDS
+// round trip). pair_rows16: op(x of this 16-lane row, x of its partner row:
+// rows 0↔1 and 2↔3); pair_halves32: op(x of lanes 0-31, x of lanes 32-63).
+// Both lanes of a pair evaluate op on the same operands in the same order,
+// so they receive the same bits.
+template <typename Op>
+__device__ __forceinline__ float pair_rows16(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
+template <typename Op>
+__device__ __forceinline__ float pair_halves32(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
-}
+struct MaxOp {
+  __device__ float operator()(float x, float y) const { return fmaxf(x, y); }
+};
+struct AddOp {
+  __device__ float operator()(float x, float y) const { return x + y; }
+};
 
 // Raw buffer loads: a resource names a base address and a byte limit; a load
 // at or past the limit returns zeros and makes no memory access.

@@ -208,8 +208,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 #pragma unroll
     for (int t4 = 1; t4 < 4; ++t4)
       mt = fmaxf(mt, fmaxf(fmaxf(st[t4][0], st[t4][1]), fmaxf(st[t4][2], st[t4][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = pair_halves32(pair_rows16(mt, MaxOp()), MaxOp());
     // m stays −inf while every key a query has met is masked (a later
     // stream's first tile can lie wholly after an early query): the old state is then
     // empty (weight 0) and the masked scores give p = 0
@@ -326,9 +325,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   }
 
   // ---- finish: l over the four lanes of a query, o = u / l ----
-  float lt = l_run;
-  lt += __shfl_xor(lt, 16, kWave);
-  lt += __shfl_xor(lt, 32, kWave);
+  const float lt = pair_halves32(pair_rows16(l_run, AddOp()), AddOp());
   if (!q_valid) return;
   const float inv = 1.0f / lt;
   float* op = a.out + ((size_t)(q_lo + my_q) * a.hq + head) * DH + kg * 4;
