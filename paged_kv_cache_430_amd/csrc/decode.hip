@@ -612,7 +612,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   // Each wave's LDS region first stages its K blocks (two padded 16-row
   // blocks), then, after its loop, holds its accumulators for the merge.
   constexpr int kStage = 2 * kBlockSize * G::KRS;
-  constexpr int kRegion = kStage > NH * DH * 4 ? kStage : NH * DH * 4;
+  constexpr int kSlab = 4 * 4 * NH + 1;        // floats per dt slab of the accumulators (see the merge)
+  constexpr int kRegion = kStage > NDT * kSlab * 4 ? kStage : NDT * kSlab * 4;
   __shared__ __attribute__((aligned(16))) uint8_t sh_region[kWaves][kRegion];
   __shared__ float sh_m[kWaves][NH];
   __shared__ float sh_l[kWaves][NH];
@@ -817,18 +818,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
 
   // ---- the wave's totals, then the waves' merge ------------------------------------
   l_run = pair_halves32(pair_rows16(l_run, AddOp()), AddOp());
-  typedef float HeadRow[DH];
+  // The wave's accumulators go to its region as [dt][i][kg][head] with each dt
+  // slab padded by one float: a store instruction (fixed dt, i) then covers 64
+  // consecutive floats, and the merge's reads of consecutive columns d (dt
+  // fastest) land in different banks.
+  auto u_index = [](int dt, int i, int kgr, int h) { return dt * kSlab + (i * 4 + kgr) * NH + h; };
   wave_lds_sync();   // the wave's last stage reads are done before its region is reused
-  HeadRow* my_u = reinterpret_cast<HeadRow*>(sh_region[w]);
+  float* my_u = reinterpret_cast<float*>(sh_region[w]);
   if (col < nh) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) my_u[col][NDT * (4 * kg + i) + dt] = o[dt][i];
+      for (int i = 0; i < 4; ++i) my_u[u_index(dt, i, kg, col)] = o[dt][i];
     if (kg == 0) { sh_m[w][col] = m_run; sh_l[w][col] = l_run; }
   }
   __syncthreads();
-  auto sh_u = [&](int ww, int h, int d) { return reinterpret_cast<const HeadRow*>(sh_region[ww])[h][d]; };
+  auto sh_u = [&](int ww, int h, int d) {   // column d = NDT·(4kg + i) + dt
+    const int m = d / NDT;
+    return reinterpret_cast<const float*>(sh_region[ww])[u_index(d % NDT, m % 4, m / 4, h)];
+  };
   const float vscale = KV == kFP8 ? a.v_scale[g] : 1.0f;
   for (int i = tid; i < nh * DH; i += kThreads) {
     const int h = i / DH, d = i % DH;
