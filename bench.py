@@ -145,6 +145,15 @@ def calib_copy(dev):
     torch.cuda.synchronize()
 
 
+def decode_kernel_base(cache_dtype):
+    """The split kernel the library runs for a cache dtype: the matrix-core
+    form for bf16 and fp8 caches (unless PKV_DECODE_KERNEL=vector), the vector
+    form for fp32 caches."""
+    if cache_dtype == "f32" or os.environ.get("PKV_DECODE_KERNEL") == "vector":
+        return "decode_split"
+    return "decode_mfma"
+
+
 def load_traffic(kernel, workload):
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
@@ -305,8 +314,9 @@ def run_decode(args, dev):
         "decode_call_us": stats_us(dec_ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": load_traffic("decode_split", args.workload),
-                     "kernel": "decode_split_kernel" + (" + decode_merge_kernel" if partition < T else ""),
+                     "traffic": load_traffic(decode_kernel_base(w0.cache_dtype), args.workload),
+                     "kernel": decode_kernel_base(w0.cache_dtype) + "_kernel" +
+                               (" + decode_merge_kernel" if partition < T else ""),
                      "bytes_per_launch": d_bytes},
     }
     if not args.no_cpu_baseline:
@@ -577,7 +587,8 @@ def summarize_counters(fetch_csv, write_csv, workload):
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": {}}
     total = 0.0
-    for key in ("decode_split_kernel", "decode_merge_kernel"):
+    base = "decode_mfma" if any("decode_mfma_kernel" in n for n in fetch) else "decode_split"
+    for key in (base + "_kernel", "decode_merge_kernel"):
         names = [n for n in fetch if key in n]
         if not names:
             continue
@@ -589,7 +600,7 @@ def summarize_counters(fetch_csv, write_csv, workload):
         total += fb + wb
     out["bytes_per_launch"] = round(total)
     os.makedirs(PROFILES, exist_ok=True)
-    path = os.path.join(PROFILES, f"decode_split_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"{base}_{workload}_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
