@@ -640,16 +640,49 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   const int jb = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb0;
   const int phys_all = jb < cap ? bt[jb] : -1;
-  const int seq_len = a.seq_lens[b];
+  // the length through a vector-memory load: the scalar-cache wait for it
+  // would also hold back every other scalar load issued before the first tile
+  const int seq_len = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.seq_lens + b), 0, 4, kBufferRsrcWord3), 0, 0, 0);
+
+
+  auto tile_rsrc = [&](const uint8_t* pool, int phys, int rows) {
+    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+    const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
+    const int records = __builtin_amdgcn_readfirstlane(ok ? rows * G::RB : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
+  };
+  struct Tile {
+    uint4 k[2][G::NKI];       // [block][whole-row load]
+    uint32_t v[2][4][VW];     // [block][key of the lane's quad]
+  };
+  // block e of a tile from table entry phys, reading `rows` rows
+  auto load_blocks = [&](Tile& t, int e, int phys, int rows) {
+    const auto rk = tile_rsrc(a.kc, phys, rows);
+    const auto rv = tile_rsrc(a.vc, phys, rows);
+    // K: whole rows per load (CPR lanes per row), restaged through LDS
+#pragma unroll
+    for (int i = 0; i < G::NKI; ++i)
+      t.k[e][i] = buffer_load16_stream(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+  };
+
+  // The wave's first block pair is requested from its table entries alone,
+  // all 16 rows of each, before the length arrives; the rows past the
+  // sequence are masked when the pair is used.
+  Tile first;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), kBlockSize);
 
   // q of head col as the B operand of each k-step (zeros past the chunk's heads)
   bf16x8_t qb[NDC];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.hq + h0 + col) * DH;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.hq + h0 + (col < nh ? col : 0)) * DH;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      const uint4 x = col < nh ? *reinterpret_cast<const uint4*>(qrow + G::k_elem(dc, kg)) : make_uint4(0, 0, 0, 0);
-      qb[dc] = __builtin_bit_cast(bf16x8_t, x);
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow + G::k_elem(dc, kg));
+      qb[dc] = __builtin_bit_cast(bf16x8_t, col < nh ? x : make_uint4(0, 0, 0, 0));
     }
   }
 
@@ -663,32 +696,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   if constexpr (KV == kFP8) sc *= a.k_scale[g];
 
   auto rows_of = [&](int idx) { return min(kBlockSize, max(0, ntok - idx * kBlockSize)); };
-  auto tile_rsrc = [&](const uint8_t* pool, int phys, int rows) {
-    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
-    const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
-    const int records = __builtin_amdgcn_readfirstlane(ok ? rows * G::RB : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
-  };
-  struct Tile {
-    uint4 k[2][G::NKI];       // [block][whole-row load]
-    uint32_t v[2][4][VW];     // [block][key of the lane's quad]
-  };
   // block e (0, 1) of the wave's j-th tile
   auto block_phys = [&](int j, int e) { return j < ntw ? __builtin_amdgcn_readlane(my_phys, 2 * j + e) : -1; };
   auto block_index = [&](int j, int e) { return 2 * (w + kWaves * j) + e; };
   auto load_tile = [&](int j, Tile& t) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int phys = block_phys(j, e);
-      const int rows = rows_of(block_index(j, e));
-      const auto rk = tile_rsrc(a.kc, phys, rows);
-      const auto rv = tile_rsrc(a.vc, phys, rows);
-      // K: whole rows per load (CPR lanes per row), restaged through LDS
-#pragma unroll
-      for (int i = 0; i < G::NKI; ++i) t.k[e][i] = buffer_load16_stream(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
-    }
+    for (int e = 0; e < 2; ++e) load_blocks(t, e, block_phys(j, e), rows_of(block_index(j, e)));
   };
 
   float m_run = -INFINITY, l_run = 0.0f;     // head col; l is this lane's share
@@ -790,6 +803,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) to_bf16_pairs<KV, VW>(t.v[e][i], vp[e][i]);
+    if (j == 0) {   // the first tile was read whole before the length was known: rows past it → 0
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q2 = 0; q2 < NP; ++q2) vp[e][i][q2] = 4 * kg + i < rows[e] ? vp[e][i][q2] : 0u;
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const uint32_t sel = dt % 2 ? 0x07060302u : 0x05040100u;   // high or low element of the pair
@@ -806,9 +827,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   };
 
   {
-    Tile t0, t1;
-    load_tile(0, t0);
-    for (int j = 0; j < ntw; j += 2) {
+    // The first pair is used on every path (a wave with no blocks sees it
+    // fully masked, which adds nothing), so its loads stay ahead of the length.
+    Tile t0 = first, t1;
+    load_tile(1, t1);
+    use_tile(0, t0);
+    load_tile(2, t0);
+    if (1 < ntw) use_tile(1, t1);
+    for (int j = 2; j < ntw; j += 2) {
       load_tile(j + 1, t1);
       use_tile(j, t0);
       load_tile(j + 2, t0);
