@@ -89,6 +89,7 @@ def test_cfg1_fp32_before_and_after_append():
 @pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [
     ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 32, 1, 128), ("bf16", 6, 3, 64),
     ("f32", 4, 1, 64), ("f32", 8, 2, 128), ("fp8", 32, 8, 128), ("fp8", 16, 2, 64), ("bf16", 12, 2, 128),
+    ("bf16", 64, 1, 128), ("bf16", 24, 1, 64), ("fp8", 16, 1, 128), ("f32", 64, 2, 64),
 ])
 @pytest.mark.parametrize("pt", [0, 16, 64, 512])
 def test_ragged_lengths_and_partitions(cache_dtype, hq, hkv, dh, pt):
@@ -100,6 +101,34 @@ def test_ragged_lengths_and_partitions(cache_dtype, hq, hkv, dh, pt):
     for kern in kernels_for(cache_dtype):
         got = run_decode(w, cache, dev, partition_tokens=pt, kernel=kern)
         assert_close(got, ref, TOL[cache_dtype], f"{kern} {cache_dtype} {hq}/{hkv} dh{dh} pt{pt}")
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8", "f32"])
+def test_table_entries_past_the_sequence_point_at_nan_blocks(cache_dtype):
+    """Entries past each sequence's blocks hold ids of real pool blocks whose
+    slots are all NaN (the kernels may fetch a block pair before the length
+    is known, and partitions read their table slice whole): the output must
+    not see them."""
+    dev = device()
+    lens_ = [1, 17, 31, 32, 33, 200, 513, 1024]
+    w = workloads.decode_inputs("tail", 77, lens_, 16, 2, 128, cache_dtype, dev, extra_blocks=96)
+    rng = np.random.default_rng(5)
+    t0 = w.block_tables[0]
+    unused = np.setdiff1d(np.arange(w.num_blocks), t0[t0 >= 0]).astype(np.int32)   # never appended: NaN
+    assert len(unused) == 96
+    max_blocks = 96
+    bt = np.full((1, w.batch, max_blocks), -1, dtype=np.int32)
+    for b in range(w.batch):
+        nb = -(-int(w.seq_lens[b]) // 16)
+        bt[0, b, :nb] = t0[b, :nb]
+        bt[0, b, nb:] = rng.choice(unused, max_blocks - nb)
+    cache = build_cache(w, dev)            # appends through the original tables
+    w.block_tables = bt
+    ref = oracle_decode(w)
+    for kern in kernels_for(cache_dtype):
+        for pt in (0, 32, 256):
+            got = run_decode(w, cache, dev, partition_tokens=pt, max_seq_len=max_blocks * 16, kernel=kern)
+            assert_close(got, ref, TOL[cache_dtype], f"{kern} {cache_dtype} pt{pt}")
 
 
 def test_empty_sequence_and_clamped_length():
