@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed"])
+    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index"])
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
@@ -607,6 +607,89 @@ def summarize_counters(fetch_csv, write_csv, workload):
     return out
 
 
+# ---------------------------------------------------------------------------
+# prefix-cache index (host)
+# ---------------------------------------------------------------------------
+
+def run_prefix_index(args):
+    """Host workload for the prefix-cache index: 16 system prompts of 2048
+    tokens shared by 512 requests that each add 512 private tokens (16-token
+    blocks). All requests are indexed, then 512 new requests of the same mix
+    are matched; a step is matching those 512 prompts. Reported as blocks
+    looked up per second (each request walks its matched blocks plus the
+    first miss); the oracle's Python index is timed on the same lookups."""
+    import numpy as np
+
+    import paged_kv_cache_430_amd as pkv
+    from oracle import prefix as oprefix
+
+    page, n_sys, sys_len, n_req, priv = 16, 16, 2048, 512, 512
+    rng = np.random.default_rng(4306)
+    systems = [rng.integers(0, 32000, sys_len).astype(np.int32) for _ in range(n_sys)]
+
+    def prompts(n):
+        return [np.concatenate([systems[int(rng.integers(0, n_sys))],
+                                rng.integers(0, 32000, priv).astype(np.int32)]) for _ in range(n)]
+
+    cached, queries = prompts(n_req), prompts(n_req)
+    idx = pkv.PrefixIndex(page)
+    nid = 0
+    for t in cached:
+        nb = len(t) // page
+        idx.insert(t, np.arange(nid, nid + nb, dtype=np.int32))
+        nid += nb
+    lib = pkv.load()
+    qbufs = [np.ascontiguousarray(q) for q in queries]
+    out = np.empty((sys_len + priv) // page, dtype=np.int32)
+    n = pkv.ctypes.c_int32(0)
+    lookups = 0
+    for q in qbufs:
+        pkv._check(lib.pkv_prefix_match(idx._h, None, q.ctypes.data, len(q), 0, out.ctypes.data, len(out),
+                                        pkv.ctypes.addressof(n)))
+        lookups += n.value + (1 if n.value < len(q) // page else 0)
+    for _ in range(args.warmup):
+        for q in qbufs:
+            lib.pkv_prefix_match(idx._h, None, q.ctypes.data, len(q), 0, out.ctypes.data, len(out),
+                                 pkv.ctypes.addressof(n))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for q in qbufs:
+            lib.pkv_prefix_match(idx._h, None, q.ctypes.data, len(q), 0, out.ctypes.data, len(out),
+                                 pkv.ctypes.addressof(n))
+    el = time.perf_counter() - t0
+    value = lookups * args.steps / el
+    line = {
+        "metric": "prefix-index match, blocks looked up per second (host)",
+        "value": round(value, 1), "unit": "blocks/s", "n_gpus": 0, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "prefix-index", "block_size": page, "system_prompts": n_sys,
+                   "system_tokens": sys_len, "requests": n_req, "private_tokens": priv,
+                   "indexed_blocks": idx.stats()["entries"]},
+        "us_per_request": round(el / args.steps / n_req * 1e6, 3),
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        ref = oprefix.PrefixIndex(page)
+        nid = 0
+        for t in cached:
+            nb = len(t) // page
+            ref.insert(list(map(int, t)), list(range(nid, nid + nb)))
+            nid += nb
+        ql = [list(map(int, q)) for q in queries]
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            for q in ql:
+                ref.match(q)
+            reps += 1
+        el_o = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(lookups * reps / el_o, 1), "unit": "blocks/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{reps} passes over the 512 prompts (Python dict of "
+                                                            f"nested-tuple keys), {el_o:.2f} s"}
+    return line
+
+
 def main():
     args = parse()
     if args.counters:
@@ -617,6 +700,10 @@ def main():
               "(decode shards by sequence or KV head with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "prefix-index":   # host only
+        print(json.dumps(run_prefix_index(args)), flush=True)
+        return
 
     import torch
 

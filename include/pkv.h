@@ -310,6 +310,55 @@ PKV_API int pkv_alloc_reserve_append(pkv_alloc* a, int32_t* block_table, int32_t
                                      int32_t seq_len, int32_t n_new, int32_t* cow_src,
                                      int32_t* cow_dst, int32_t* n_cow);
 
+/* ---------------------------------------------------------------------------
+ * Prefix-cache index over full blocks — [P1] prefix-sharing section and its
+ * token demo (cached ABCDEFGHIJKL vs new ABCDEFGXIJKL: reuse stops at the
+ * first differing token and only whole pages count); [P1] engine section
+ * (a full block's key chains its parent's key, its tokens and extra identity
+ * such as model or adapter); [P3] 6.4 (chained hash of parent and block
+ * tokens; a partial block is not reused; token hit rate = hit tokens /
+ * compared prompt tokens; request hit rate = requests with any hit /
+ * requests). Host only; single-threaded like the allocator.
+ *
+ * Keys are compared exactly (parent entry, identity and the block's tokens);
+ * the chained 64-bit hash only selects candidates. When an allocator is
+ * passed, each block the index takes on holds one reference until
+ * pkv_prefix_clear, and each matched block gains one reference for the
+ * caller; pass NULL to leave reference counts alone.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_prefix pkv_prefix;
+
+/* block_size: tokens per block (the page) */
+PKV_API int pkv_prefix_create(int32_t block_size, pkv_prefix** out);
+PKV_API void pkv_prefix_destroy(pkv_prefix* idx);
+
+/* Index the full blocks of host tokens[0..n_tokens): block i (i <
+ * min(n_tokens / block_size, n_block_ids)) is held by block_ids[i]. A block
+ * whose key is already indexed keeps its first id. *n_new (nullable)
+ * receives how many blocks were newly indexed. All-or-nothing: with an
+ * allocator, PKV_EREF (nothing indexed) if a new block is free. */
+PKV_API int pkv_prefix_insert(pkv_prefix* idx, pkv_alloc* alloc, const int32_t* tokens, int32_t n_tokens,
+                              uint64_t identity, const int32_t* block_ids, int32_t n_block_ids,
+                              int32_t* n_new);
+
+/* The longest run of indexed full blocks that starts the prompt host
+ * tokens[0..n_tokens) under `identity`, stopping at the first block whose
+ * key is not indexed, and at most max_ids blocks: their ids go to host
+ * out_ids, their count to *n_match (so n_match·block_size prompt tokens need
+ * no prefill). Counts one request, n_tokens compared tokens and
+ * n_match·block_size hit tokens. */
+PKV_API int pkv_prefix_match(pkv_prefix* idx, pkv_alloc* alloc, const int32_t* tokens, int32_t n_tokens,
+                             uint64_t identity, int32_t* out_ids, int32_t max_ids, int32_t* n_match);
+
+/* Hit counters since creation and the number of indexed blocks (each
+ * pointer nullable). */
+PKV_API int pkv_prefix_stats(const pkv_prefix* idx, int64_t* hit_tokens, int64_t* compared_tokens,
+                             int64_t* requests, int64_t* hit_requests, int32_t* num_entries);
+
+/* Forget every indexed block (the counters stay). The allocator the index
+ * took references with must be passed to release them; PKV_EINVAL otherwise. */
+PKV_API int pkv_prefix_clear(pkv_prefix* idx, pkv_alloc* alloc);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "PKVError", "Cache", "BlockAllocator", "load",
+    "PKVError", "Cache", "BlockAllocator", "PrefixIndex", "load",
     "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
     "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_debug_gather",
@@ -70,6 +70,12 @@ _SIGS = {
     "pkv_alloc_refcount": (ctypes.c_int, [_VP, _I32]),
     "pkv_alloc_num_free": (_I32, [_VP]),
     "pkv_alloc_reserve_append": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "pkv_prefix_create": (ctypes.c_int, [_I32, ctypes.POINTER(_VP)]),
+    "pkv_prefix_destroy": (None, [_VP]),
+    "pkv_prefix_insert": (ctypes.c_int, [_VP, _VP, _VP, _I32, ctypes.c_uint64, _VP, _I32, _VP]),
+    "pkv_prefix_match": (ctypes.c_int, [_VP, _VP, _VP, _I32, ctypes.c_uint64, _VP, _I32, _VP]),
+    "pkv_prefix_stats": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_prefix_clear": (ctypes.c_int, [_VP, _VP]),
 }
 
 _lib = None
@@ -292,6 +298,53 @@ class BlockAllocator:
         _check(load().pkv_alloc_reserve_append(self._h, table.ctypes.data, len(table), seq_len, n_new,
                                                src.ctypes.data, dst.ctypes.data, ctypes.addressof(n)))
         return [(int(src[0]), int(dst[0]))] if n.value else []
+
+
+class PrefixIndex:
+    """Host prefix-cache index over full blocks (pkv_prefix_*). `alloc` (a
+    BlockAllocator or None) is passed to every call that can take or give
+    references."""
+
+    def __init__(self, block_size=16, alloc=None):
+        lib = load()
+        self._h = ctypes.c_void_p()
+        _check(lib.pkv_prefix_create(block_size, ctypes.byref(self._h)))
+        self.block_size, self.alloc = block_size, alloc
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_prefix_destroy(h)
+            self._h = None
+
+    def _a(self):
+        return None if self.alloc is None else self.alloc._h
+
+    def insert(self, tokens, block_ids, identity=0):
+        tok, ids = _i32_host(tokens), _i32_host(block_ids)
+        n = ctypes.c_int32(0)
+        _check(load().pkv_prefix_insert(self._h, self._a(), tok.ctypes.data, len(tok), identity, ids.ctypes.data,
+                                        len(ids), ctypes.addressof(n)))
+        return n.value
+
+    def match(self, tokens, identity=0, max_ids=None):
+        tok = _i32_host(tokens)
+        cap = len(tok) // self.block_size if max_ids is None else max_ids
+        out = np.empty(max(cap, 1), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(load().pkv_prefix_match(self._h, self._a(), tok.ctypes.data, len(tok), identity, out.ctypes.data,
+                                       cap, ctypes.addressof(n)))
+        return out[:n.value].copy()
+
+    def stats(self):
+        v = [ctypes.c_int64(0) for _ in range(4)]
+        e = ctypes.c_int32(0)
+        _check(load().pkv_prefix_stats(self._h, *[ctypes.addressof(x) for x in v], ctypes.addressof(e)))
+        return {"hit_tokens": v[0].value, "compared_tokens": v[1].value, "requests": v[2].value,
+                "hit_requests": v[3].value, "entries": e.value}
+
+    def clear(self):
+        _check(load().pkv_prefix_clear(self._h, self._a()))
 
 
 def _check_nonneg(v):
