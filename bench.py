@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn KV HBM GB/s (% of peak), B=32 Hkv=8 Dh=128 T=4096 bf16"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
 MALL_BYTES = 2 * 2 ** 30          # rotate through at least this much pool memory
 CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
@@ -62,7 +63,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index"])
+    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index", "swap"])
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
@@ -690,6 +691,60 @@ def run_prefix_index(args):
     return line
 
 
+# ---------------------------------------------------------------------------
+# swap-out / swap-in (pool <-> pinned host memory)
+# ---------------------------------------------------------------------------
+
+def run_swap(args, dev):
+    """4096 scattered blocks of a cfg2-shaped pool (Hkv=8, Dh=128, bf16: 64 KiB
+    of K+V per block, 256 MiB per call) out to pinned host memory and back in.
+    `value` is the swap-out rate; the line also carries the swap-in rate.
+    Both directions are bound by the host link, not by HBM."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    nb, hkv, dh, n = 8192, 8, 128, 4096
+    k = torch.randn(nb, hkv, 16, dh, device=dev).to(torch.bfloat16)
+    v = torch.randn(nb, hkv, 16, dh, device=dev).to(torch.bfloat16)
+    cache = pkv.Cache(k, v)
+    ids = torch.from_numpy(np.random.default_rng(4307).permutation(nb)[:n].astype(np.int32)).to(dev)
+    bb = hkv * 16 * dh * 2
+    host = torch.empty(n * 2 * bb, dtype=torch.uint8).pin_memory()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_out = timed(lambda: pkv.pkv_swap_out(cache, ids, host))
+    ms_in = timed(lambda: pkv.pkv_swap_in(cache, host, ids))
+    moved = n * 2 * bb
+    return {
+        "metric": "swap-out of 4096 KV blocks to pinned host memory, GB/s",
+        "value": round(moved / (ms_out * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_out, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap", "blocks": n, "pool_blocks": nb, "kv_heads": hkv, "head_dim": dh,
+                   "block_size": 16, "bytes_per_call": moved},
+        "swap_in_gbs": round(moved / (ms_in * 1e-3) / 1e9, 2), "swap_in_ms": round(ms_in, 4),
+        # the host link: PCIe 5.0 x16, 32 GT/s per lane with 128b/130b coding, per direction
+        "roofline": {"bound": "host-link", "achieved": round(moved / (ms_out * 1e-3) / 1e9, 2),
+                     "peak": PCIE5_X16_GBS, "unit": "GB/s",
+                     "frac": round(moved / (ms_out * 1e-3) / 1e9 / PCIE5_X16_GBS, 4), "traffic": None,
+                     "kernel": "swap_out_kernel", "bytes_per_launch": moved},
+    }
+
+
 def main():
     args = parse()
     if args.counters:
@@ -712,7 +767,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     pkv.load()
-    line = run_cfg4(args, dev) if args.workload == "cfg4-mixed" else run_decode(args, dev)
+    if args.workload == "swap":
+        line = run_swap(args, dev)
+    elif args.workload == "cfg4-mixed":
+        line = run_cfg4(args, dev)
+    else:
+        line = run_decode(args, dev)
     print(json.dumps(line), flush=True)
 
 

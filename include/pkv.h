@@ -253,6 +253,27 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
 PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const int32_t* dst,
                             int32_t n, pkv_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * Swap blocks out to host memory and back — [P4] closing section, table of
+ * the four remedies for a full cache, row "move it away for now" (KV not
+ * needed for a while goes to CPU memory and comes back when needed, at the
+ * cost of moving it); [P2] Q028 follow-up on what a server can do when
+ * memory runs short (preempt requests and move their state elsewhere).
+ * Whole blocks (K and V, every head) move between the pool and a pinned host
+ * buffer laid out [n][K block bytes, V block bytes] (block bytes =
+ * num_kv_heads · block_size · head_dim · element size).
+ *   ids:  device int32 [n]; slot i holds block ids[i]. Ids outside the pool
+ *         are skipped (their host slot, or nothing in the pool, is written).
+ *   host: pinned host memory (hipHostMalloc, or a torch pin_memory tensor),
+ *         16-byte aligned, at least host_bytes ≥ n · 2 · block bytes;
+ *         anything else is rejected (PKV_EINVAL) before any launch.
+ * Asynchronous on the stream; the host copy is complete once the stream is.
+ * Swap-in destinations must be distinct. */
+PKV_API int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, void* host, size_t host_bytes,
+                         pkv_stream stream);
+PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_bytes, const int32_t* ids, int32_t n,
+                        pkv_stream stream);
+
 /* Test aid: read one sequence back through its table into the semantic
  * layout [num_kv_heads, seq_len, head_dim] of the stored dtype ([P2] Q025:
  * K and V each [B, H_kv, T, Dh]; Q028: paging changes placement, not order).

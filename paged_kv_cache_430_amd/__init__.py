@@ -18,7 +18,7 @@ __all__ = [
     "PKVError", "Cache", "BlockAllocator", "PrefixIndex", "load",
     "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
-    "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_debug_gather",
+    "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]
 
@@ -62,6 +62,8 @@ _SIGS = {
                                               _I32, _VP, _I32, ctypes.c_float, _VP, _VP, ctypes.c_size_t, _VP]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP]),
     "pkv_debug_gather": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, _VP, _VP]),
+    "pkv_swap_out": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, ctypes.c_size_t, _VP]),
+    "pkv_swap_in": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, ctypes.c_size_t, _VP, _I32, _VP]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _VP, ctypes.POINTER(_VP)]),
     "pkv_alloc_destroy": (None, [_VP]),
     "pkv_alloc_allocate": (ctypes.c_int, [_VP, _I32, _VP]),
@@ -240,6 +242,19 @@ def pkv_attn_prefill_chunk(cache, q, q_start, block_tables, seq_lens, max_q_len,
 
 def pkv_copy_blocks(cache, src, dst, stream=None):
     _check(load().pkv_copy_blocks(cache.ref(), _ptr(src), _ptr(dst), src.numel(), _stream(stream, cache.device)))
+
+
+def pkv_swap_out(cache, ids, host, stream=None):
+    """Blocks ids (device int32) → host (a pinned uint8 tensor of n·2·block bytes)."""
+    _check(load().pkv_swap_out(cache.ref(), _ptr(ids), ids.numel(), _ptr(host), host.numel() * host.element_size(),
+                               _stream(stream, cache.device)))
+    return host
+
+
+def pkv_swap_in(cache, host, ids, stream=None):
+    """host (pinned, as written by pkv_swap_out) → blocks ids (device int32)."""
+    _check(load().pkv_swap_in(cache.ref(), _ptr(host), host.numel() * host.element_size(), _ptr(ids), ids.numel(),
+                              _stream(stream, cache.device)))
 
 
 def pkv_debug_gather(cache, block_table, seq_len, stream=None):

@@ -229,6 +229,57 @@ hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int3
 }
 
 // ---------------------------------------------------------------------------
+// swap-out / swap-in between the pool and pinned host memory: one workgroup
+// per listed block; host slot i holds block ids[i] as its K bytes then its V
+// bytes. The kernel itself moves the data across the host link (the host
+// buffer is pinned and device-addressable), so scattered ids need no staging.
+// ---------------------------------------------------------------------------
+__global__ void swap_out_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                const int32_t* __restrict__ ids, int num_blocks, size_t block_bytes,
+                                uint8_t* __restrict__ host) {
+  const int i = blockIdx.x;
+  const int b = ids[i];
+  if ((unsigned)b >= (unsigned)num_blocks) return;       // left untouched
+  const size_t n16 = block_bytes / 16;
+  uint4* dst = reinterpret_cast<uint4*>(host + (size_t)i * 2 * block_bytes);
+  const uint4* ks = reinterpret_cast<const uint4*>(kc + (size_t)b * block_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(vc + (size_t)b * block_bytes);
+  for (size_t c = threadIdx.x; c < n16; c += blockDim.x) {
+    dst[c] = ks[c];
+    dst[n16 + c] = vs[c];
+  }
+}
+
+__global__ void swap_in_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                               const int32_t* __restrict__ ids, int num_blocks, size_t block_bytes,
+                               const uint8_t* __restrict__ host) {
+  const int i = blockIdx.x;
+  const int b = ids[i];
+  if ((unsigned)b >= (unsigned)num_blocks) return;       // skipped
+  const size_t n16 = block_bytes / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(host + (size_t)i * 2 * block_bytes);
+  uint4* kd = reinterpret_cast<uint4*>(kc + (size_t)b * block_bytes);
+  uint4* vd = reinterpret_cast<uint4*>(vc + (size_t)b * block_bytes);
+  for (size_t c = threadIdx.x; c < n16; c += blockDim.x) {
+    kd[c] = src[c];
+    vd[c] = src[n16 + c];
+  }
+}
+
+hipError_t launch_swap(const CacheView& c, const int32_t* ids, int n, void* host, bool out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  if (out)
+    hipLaunchKernelGGL(swap_out_kernel, dim3(n), dim3(256), 0, s, static_cast<const uint8_t*>(c.k),
+                       static_cast<const uint8_t*>(c.v), ids, c.num_blocks, block_bytes, static_cast<uint8_t*>(host));
+  else
+    hipLaunchKernelGGL(swap_in_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k),
+                       static_cast<uint8_t*>(c.v), ids, c.num_blocks, block_bytes,
+                       static_cast<const uint8_t*>(host));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // test aid: paged → [Hkv, T, Dh] through the same slot arithmetic
 // ---------------------------------------------------------------------------
 __global__ void debug_gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,

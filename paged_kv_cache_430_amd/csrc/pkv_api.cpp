@@ -381,6 +381,49 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const in
   return hip_status(launch_copy_blocks(c, src, dst, n, static_cast<hipStream_t>(stream)), "pkv_copy_blocks");
 }
 
+// Host buffer checks for the swap calls: large enough, 16-byte aligned and
+// pinned (device-addressable) host memory, so the kernel never touches
+// pageable memory.
+static int check_swap_host(const CacheView& c, const void* host, size_t host_bytes, int32_t n, const char* what) {
+  const size_t block_bytes = (size_t)c.num_kv_heads * 16 * c.head_dim * dtype_bytes(c.dtype);
+  if (!host) return fail(PKV_EINVAL, std::string(what) + ": host is NULL");
+  if (!aligned16(host)) return fail(PKV_EINVAL, std::string(what) + ": host must be 16-byte aligned");
+  if (host_bytes < (size_t)n * 2 * block_bytes)
+    return fail(PKV_EINVAL, std::string(what) + ": host buffer needs " + std::to_string((size_t)n * 2 * block_bytes) +
+                                " bytes");
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(PKV_EINVAL, std::string(what) + ": host must be pinned host memory (hipHostMalloc)");
+  }
+  return PKV_OK;
+}
+
+PKV_API int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, void* host, size_t host_bytes,
+                         pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_swap_out", &c)) return st;
+  if (n < 0) return fail(PKV_EINVAL, "pkv_swap_out: n < 0");
+  if (n == 0) return PKV_OK;
+  if (!ids) return fail(PKV_EINVAL, "pkv_swap_out: ids is NULL");
+  if (int st = check_swap_host(c, host, host_bytes, n, "pkv_swap_out")) return st;
+  return hip_status(launch_swap(c, ids, n, host, true, static_cast<hipStream_t>(stream)), "pkv_swap_out");
+}
+
+PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_bytes, const int32_t* ids, int32_t n,
+                        pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, "pkv_swap_in", &c)) return st;
+  if (n < 0) return fail(PKV_EINVAL, "pkv_swap_in: n < 0");
+  if (n == 0) return PKV_OK;
+  if (!ids) return fail(PKV_EINVAL, "pkv_swap_in: ids is NULL");
+  if (int st = check_swap_host(c, host, host_bytes, n, "pkv_swap_in")) return st;
+  return hip_status(launch_swap(c, ids, n, const_cast<void*>(host), false, static_cast<hipStream_t>(stream)),
+                    "pkv_swap_in");
+}
+
 PKV_API int pkv_debug_gather(const pkv_cache* cache, const int32_t* block_table, int32_t seq_len,
                              void* k_out, void* v_out, pkv_stream stream) {
   clear_error();

@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 26
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
@@ -271,3 +271,16 @@ def test_allocator_matches_model_on_random_operations():
             assert nat.num_free() == mod.num_free()
             for bid in range(nb):
                 assert nat.refcount(bid) == mod.ref[bid]
+
+
+def test_swap_rejects_bad_host_buffers_before_any_launch(lib):
+    """Pageable, misaligned or short host buffers are refused on the host."""
+    ref, _ = _fake_cache()
+    bb = 8 * 16 * 128 * 2                        # the fake cache's block bytes (Hkv 8, Dh 128, bf16)
+    buf = np.zeros(4 * 2 * bb + 64, dtype=np.uint8)
+    base = buf.ctypes.data + (-buf.ctypes.data) % 16
+    assert lib.pkv_swap_out(ref, 0x60000, 4, base, 4 * 2 * bb, None) == pkv.PKV_EINVAL          # pageable
+    assert lib.pkv_swap_out(ref, 0x60000, 4, base + 4, 4 * 2 * bb, None) == pkv.PKV_EINVAL      # misaligned
+    assert lib.pkv_swap_in(ref, base, 4 * 2 * bb - 16, 0x60000, 4, None) == pkv.PKV_EINVAL      # too short
+    assert lib.pkv_swap_in(ref, base, 0, 0x60000, -1, None) == pkv.PKV_EINVAL                   # n < 0
+    assert lib.pkv_swap_out(ref, 0x60000, 0, None, 0, None) == pkv.PKV_OK                        # nothing to move
