@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index", "swap"])
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="decode workloads: append in its own launch before the decode (default: one launch)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
                    help="after timing, copy a 256 MiB scratch cache with pkv_copy_blocks (counter calibration)")
@@ -252,16 +254,26 @@ def run_decode(args, dev):
         c = i % copies
         for L in layers:
             tb = L["tables"][c]
-            # slot mapping and append of the step's tokens in one launch
-            pkv._check(lib.pkv_kv_append_paged(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
-                                               pkv.PKV_BF16, B, cu_new.data_ptr(), first_pos.data_ptr(), 1,
-                                               tb.data_ptr(), tb.shape[1], L["kinv"].data_ptr() if fp8 else None,
-                                               L["vinv"].data_ptr() if fp8 else None, None, sh))
-            if timer is not None:
-                timer.start()
-            pkv._check(lib.pkv_attn_decode(L["cache"].ref(), L["w"].q.data_ptr(), pkv.PKV_BF16, B, hq,
-                                           tb.data_ptr(), tb.shape[1], lens.data_ptr(), T, L["w"].scale, pt,
-                                           out.data_ptr(), wsp, wsb, sh))
+            kinv = L["kinv"].data_ptr() if fp8 else None
+            vinv = L["vinv"].data_ptr() if fp8 else None
+            if args.unfused:
+                # slot mapping and append of the step's tokens in one launch, then the decode
+                pkv._check(lib.pkv_kv_append_paged(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
+                                                   pkv.PKV_BF16, B, cu_new.data_ptr(), first_pos.data_ptr(), 1,
+                                                   tb.data_ptr(), tb.shape[1], kinv, vinv, None, sh))
+                if timer is not None:
+                    timer.start()
+                pkv._check(lib.pkv_attn_decode(L["cache"].ref(), L["w"].q.data_ptr(), pkv.PKV_BF16, B, hq,
+                                               tb.data_ptr(), tb.shape[1], lens.data_ptr(), T, L["w"].scale, pt,
+                                               out.data_ptr(), wsp, wsb, sh))
+            else:
+                # slot mapping, append and decode in one launch
+                if timer is not None:
+                    timer.start()
+                pkv._check(lib.pkv_attn_decode_append(L["cache"].ref(), L["k_new"].data_ptr(), L["v_new"].data_ptr(),
+                                                      pkv.PKV_BF16, kinv, vinv, L["w"].q.data_ptr(), pkv.PKV_BF16, B,
+                                                      hq, tb.data_ptr(), tb.shape[1], lens.data_ptr(), T,
+                                                      L["w"].scale, pt, out.data_ptr(), wsp, wsb, sh))
             if timer is not None:
                 timer.stop()
 
@@ -291,7 +303,8 @@ def run_decode(args, dev):
     a_bytes = append_bytes(B, hkv, dh, 2, kv_elt) + B * 4 * 2    # + table entry and first_pos per token
     step_bytes = (d_bytes + a_bytes) * len(layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = d_bytes / (dec_avg_ms * 1e-3) / 1e9
+    call_bytes = d_bytes if args.unfused else d_bytes + a_bytes   # the fused call also appends
+    achieved = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     partition = pt or pkv.pkv_attn_decode_auto_partition(cache_code, B, hq, hkv, T)
     line = {
         "metric": METRIC if args.workload == "cfg2-all4096" else f"decode-attn KV HBM GB/s ({args.workload})",
@@ -308,7 +321,8 @@ def run_decode(args, dev):
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": dh,
                    "seq_len": T, "block_size": 16, "layers": len(layers), "pool_copies": copies,
-                   "partition_tokens": partition, "partitions": -(-T // partition)},
+                   "partition_tokens": partition, "partitions": -(-T // partition),
+                   "step": "append launch + decode" if args.unfused else "append and decode in one launch"},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "new_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w0.seq_lens.sum()) * len(layers) / (ms_step * 1e-3), 1),
@@ -317,8 +331,9 @@ def run_decode(args, dev):
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": load_traffic(decode_kernel_base(w0.cache_dtype), args.workload),
                      "kernel": decode_kernel_base(w0.cache_dtype) + "_kernel" +
+                               ("" if args.unfused else " (append fused)") +
                                (" + decode_merge_kernel" if partition < T else ""),
-                     "bytes_per_launch": d_bytes},
+                     "bytes_per_launch": call_bytes},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w0, args.cpu_seconds, d_bytes)

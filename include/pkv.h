@@ -205,6 +205,24 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
                             float scale, int32_t partition_tokens, float* out,
                             void* workspace, size_t workspace_bytes, pkv_stream stream);
 
+/* The decode step's append and attention in one launch (BF16 and FP8
+ * caches): sequence b's new token k_new[b], v_new[b] ([batch, num_kv_heads,
+ * head_dim] in in_dtype, 16-byte aligned; BF16 for a BF16 cache, BF16 or F32
+ * for an FP8 cache, which stores e4m3(x · inv_scale) as pkv_kv_append does)
+ * is the token at position seq_lens[b] − 1 (its block already in the table;
+ * [P2] Q025 and [P3] 6.1: append, then attend). The split kernel writes it to
+ * that slot and attends to it from k_new / v_new, so the pool ends up as
+ * after pkv_kv_append_paged and the output equals pkv_attn_decode's on that
+ * pool. Other arguments as pkv_attn_decode. For an F32 cache, or with
+ * PKV_DECODE_KERNEL=vector, the call runs an append launch and then the
+ * decode. */
+PKV_API int pkv_attn_decode_append(const pkv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                                   const float* k_inv_scale, const float* v_inv_scale, const void* q,
+                                   int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                   int32_t max_seq_len, float scale, int32_t partition_tokens, float* out,
+                                   void* workspace, size_t workspace_bytes, pkv_stream stream);
+
 /* The partition size pkv_attn_decode uses when partition_tokens is 0 for a
  * cache of cache_dtype: with units = batch · num_kv_heads · (query-head
  * chunks per KV head), every sequence is split into ceil(256 / units)

@@ -18,6 +18,7 @@ __all__ = [
     "PKVError", "Cache", "BlockAllocator", "PrefixIndex", "load",
     "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
+    "pkv_attn_decode_append",
     "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]
@@ -58,6 +59,9 @@ _SIGS = {
     "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_attn_decode": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32, _VP,
                                        _I32, ctypes.c_float, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
+    "pkv_attn_decode_append": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP, _VP, _VP, _I32,
+                                              _I32, _I32, _VP, _I32, _VP, _I32, ctypes.c_float, _I32, _VP, _VP,
+                                              ctypes.c_size_t, _VP]),
     "pkv_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _VP,
                                               _I32, _VP, _I32, ctypes.c_float, _VP, _VP, ctypes.c_size_t, _VP]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP]),
@@ -226,6 +230,24 @@ def pkv_attn_decode(cache, q, block_tables, seq_lens, max_seq_len, scale, partit
     _check(load().pkv_attn_decode(cache.ref(), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
                                   block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
                                   partition_tokens, _ptr(out), _ptr(workspace), wbytes, _stream(stream, dev)))
+    return out
+
+
+def pkv_attn_decode_append(cache, k_new, v_new, q, block_tables, seq_lens, max_seq_len, scale, partition_tokens=0,
+                           k_inv_scale=None, v_inv_scale=None, out=None, workspace=None, stream=None):
+    """Append each sequence's new token (k_new, v_new: [B, Hkv, Dh]) at position
+    seq_lens[b] - 1 and decode, in one launch for bf16/fp8 caches."""
+    b, hq, dh = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty(b, hq, dh, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = decode_workspace(cache.dtype, b, hq, cache.num_kv_heads, dh, max_seq_len, partition_tokens, dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pkv_attn_decode_append(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_inv_scale),
+                                         _ptr(v_inv_scale), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
+                                         block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
+                                         partition_tokens, _ptr(out), _ptr(workspace), wbytes, _stream(stream, dev)))
     return out
 
 

@@ -86,6 +86,12 @@ struct KernelArgs {
   float* ws_u;
   int num_blocks, hkv, hq, max_blocks, max_seq_len, part_tokens, num_parts, num_chunks;
   float scale_log2;  // scale · log2(e)
+  // the fused append (matrix-core form): each sequence's new token
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const float* k_inv;
+  const float* v_inv;
+  int new_dtype;
 };
 
 struct MergeArgs {
@@ -603,7 +609,68 @@ __device__ __forceinline__ void to_bf16_pairs(const uint32_t (&x)[N], uint32_t (
   }
 }
 
-template <int KV, int DH, int NW>
+// n consecutive input elements (bf16 or fp32) from `base` as floats.
+template <int N>
+__device__ __forceinline__ void load_floats(const uint8_t* base, size_t elem, int dtype, float (&f)[N]) {
+  if (dtype == kF32) {
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + i);
+      f[i] = x.x; f[i + 1] = x.y; f[i + 2] = x.z; f[i + 3] = x.w;
+    }
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem;
+#pragma unroll
+    for (int i = 0; i < N; i += 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + i);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { f[i + 2 * k] = bf16_lo(w[k]); f[i + 2 * k + 1] = bf16_hi(w[k]); }
+    }
+  }
+}
+
+// The stored bytes of n elements of the new token, starting at element
+// `elem` of its row: a copy for bf16 caches (bf16 input), e4m3 of x·inv for
+// fp8 caches — the same bits the append kernels store. N_BYTES is 4, 8 or 16.
+template <int KV, int N_BYTES>
+__device__ __forceinline__ void new_token_bytes(const uint8_t* base, size_t elem, int dtype, float inv,
+                                                uint32_t (&out)[N_BYTES / 4]) {
+  if constexpr (KV == kBF16) {
+    const uint8_t* p = base + elem * 2;
+    if constexpr (N_BYTES == 16) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      out[0] = x.x; out[1] = x.y;
+    }
+  } else {
+    constexpr int N = N_BYTES;   // one byte per element
+    float f[N < 8 ? 8 : N];
+    if constexpr (N >= 8) {
+      load_floats<N>(base, elem, dtype, f);
+    } else {   // 4 elements
+      if (dtype == kF32) {
+        const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+        f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem);
+        f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x); f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b |= encode_e4m3(f[4 * i + j] * inv) << (8 * j);
+      out[i] = b;
+    }
+  }
+}
+
+template <int KV, int DH, int NW, bool APPEND>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   constexpr int kWaves = NW, kThreads = NW * kWave;
   constexpr int NH = kMfmaHeads;
@@ -695,6 +762,39 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   float sc = a.scale_log2;
   if constexpr (KV == kFP8) sc *= a.k_scale[g];
 
+  // Fused append: the sequence's new token sits at position T − 1. The
+  // partition holding it reads that row from k_new / v_new (the stored bytes
+  // the append writes) instead of the pool, and chunk 0's wave 0 writes it to
+  // its slot; nothing in this launch reads the pool's copy of that row.
+  int lb_new = -1, r_new = 0;
+  uint4 knew = make_uint4(0, 0, 0, 0);   // lane (chunk lane % CPR) of the new K row, stored form
+  uint32_t vnew[VW] = {};                // this lane's V slice (columns col·NDT …) of the new row
+  if constexpr (APPEND) {
+    const int pos = T - 1;
+    if (pos >= tok0 && pos < tok0 + a.part_tokens) { lb_new = pos / kBlockSize - lb0; r_new = pos % kBlockSize; }
+    if (T > 0) {
+      const size_t row = ((size_t)b * a.hkv + g) * DH;   // element index of the new token's head-g row
+      const float kinv = KV == kFP8 ? a.k_inv[g] : 1.0f, vinv = KV == kFP8 ? a.v_inv[g] : 1.0f;
+      uint32_t kq[4];
+      new_token_bytes<KV, 16>(a.k_new, row + (lane % G::CPR) * (16 / G::ESZ), a.new_dtype, kinv, kq);
+      knew = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+      new_token_bytes<KV, VW * 4>(a.v_new, row + col * NDT, a.new_dtype, vinv, vnew);
+    }
+    if (lb_new >= 0 && chunk == 0 && w == 0) {
+      const int phys = bt[lb_new];
+      if ((unsigned)phys < (unsigned)a.num_blocks) {
+        const size_t off = ((size_t)phys * a.hkv + g) * head_stride + (size_t)r_new * G::RB;
+        if (lane < G::CPR) *reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.kc) + off + lane * 16) = knew;
+        if (kg == 0) {
+          uint8_t* vd = const_cast<uint8_t*>(a.vc) + off + col * VW * 4;
+          if constexpr (VW == 4) *reinterpret_cast<uint4*>(vd) = make_uint4(vnew[0], vnew[1], vnew[2], vnew[3]);
+          else if constexpr (VW == 2) *reinterpret_cast<uint2*>(vd) = make_uint2(vnew[0], vnew[1]);
+          else *reinterpret_cast<uint32_t*>(vd) = vnew[0];
+        }
+      }
+    }
+  }
+
   auto rows_of = [&](int idx) { return min(kBlockSize, max(0, ntok - idx * kBlockSize)); };
   // block e (0, 1) of the wave's j-th tile
   auto block_phys = [&](int j, int e) { return j < ntw ? __builtin_amdgcn_readlane(my_phys, 2 * j + e) : -1; };
@@ -725,6 +825,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       for (int i = 0; i < G::NKI; ++i)
         *reinterpret_cast<uint4*>(stage + (e * kBlockSize + i * G::RPI + lane / G::CPR) * G::KRS +
                                   (lane % G::CPR) * 16) = t.k[e][i];
+    if constexpr (APPEND) {   // the new token's K row from k_new
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (block_index(j, e) == lb_new && lane < G::CPR)
+          *reinterpret_cast<uint4*>(stage + (e * kBlockSize + r_new) * G::KRS + lane * 16) = knew;
+    }
     wave_lds_sync();
     // Sᵀ for both blocks
     f32x4_t st[2];
@@ -810,6 +916,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q2 = 0; q2 < NP; ++q2) vp[e][i][q2] = 4 * kg + i < rows[e] ? vp[e][i][q2] : 0u;
+    }
+    if constexpr (APPEND) {   // the new token's V slice from v_new
+      uint32_t vn[NP];
+      to_bf16_pairs<KV, VW>(vnew, vn);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (block_index(j, e) == lb_new)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q2 = 0; q2 < NP; ++q2) vp[e][i][q2] = 4 * kg + i == r_new ? vn[q2] : vp[e][i][q2];
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -906,8 +1023,12 @@ hipError_t launch_t(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
 template <int KV, int DH>
 hipError_t launch_mfma(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
   const size_t n = (size_t)p.batch * p.cache.num_kv_heads * a.num_chunks * p.num_parts;
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves>), dim3((unsigned)n), dim3(kDecodeWaves * kWave), 0,
-                     s, a);
+  if (a.k_new)
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true>), dim3((unsigned)n),
+                       dim3(kDecodeWaves * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, false>), dim3((unsigned)n),
+                       dim3(kDecodeWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -955,6 +1076,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.num_parts = p.num_parts;
   a.num_chunks = (group + hc - 1) / hc;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.k_new = p.kernel == kDecodeMatrix ? static_cast<const uint8_t*>(p.k_new) : nullptr;
+  a.v_new = static_cast<const uint8_t*>(p.v_new);
+  a.k_inv = p.k_inv;
+  a.v_inv = p.v_inv;
+  a.new_dtype = p.new_dtype;
   const int dt = p.cache.dtype, dh = p.cache.head_dim;
   hipError_t e;
   if (p.kernel == kDecodeMatrix)

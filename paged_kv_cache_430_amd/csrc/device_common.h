@@ -39,6 +39,29 @@ __device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
 
+// OCP e4m3fn encode, round to nearest even, saturating at ±448, NaN kept.
+// Integer formulation on the fp32 bit pattern (the round-half-even carry
+// trick on the 3 kept mantissa bits); subnormal outputs use the exact
+// scaling by 2^9 followed by an ties-to-even integer rounding.
+__device__ __forceinline__ uint32_t encode_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;            // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;           // >= 448 (and inf): saturate
+  if (a < 0x3c800000u) {                               // below 2^-6: spacing 2^-9
+    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)q;                         // 0..8; 8 is the first normal
+  }
+  // keep 3 mantissa bits with ties to even
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) & 0xfff00000u;
+  const int e = (int)(r >> 23) - 127;                  // -6 … 8 (9 only past 448)
+  const uint32_t m = (r >> 20) & 7u;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | m;
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
 // Lane exchange inside a row of 16 lanes (DPP).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {

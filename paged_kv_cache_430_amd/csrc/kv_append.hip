@@ -44,31 +44,6 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int 
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// e4m3fn encode, round to nearest even, saturating at ±448, NaN kept.
-// Integer formulation on the fp32 bit pattern (the round-half-even carry
-// trick on the 3 kept mantissa bits); subnormal outputs use the exact
-// scaling by 2^9 followed by an ties-to-even integer rounding.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t encode_e4m3(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7fu;            // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;           // >= 448 (and inf): saturate
-  if (a < 0x3c800000u) {                               // below 2^-6: spacing 2^-9
-    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | (uint32_t)q;                         // 0..8; 8 is the first normal
-  }
-  // keep 3 mantissa bits with ties to even
-  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) & 0xfff00000u;
-  const int e = (int)(r >> 23) - 127;                  // -6 … 8 (9 only past 448)
-  const uint32_t m = (r >> 20) & 7u;
-  uint32_t code = ((uint32_t)(e + 7) << 3) | m;
-  if (code > 0x7eu) code = 0x7eu;
-  return sign | code;
-}
-
 // One token's K and V rows into its slot: threads of the workgroup stride
 // over 16-byte input chunks of K then V (copy, or e4m3 quantise per head).
 template <int IN, int OUT>
@@ -171,6 +146,41 @@ hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v
 #define PKV_APPEND(IN, OUT)                                                                      \
   hipLaunchKernelGGL((kv_append_kernel<IN, OUT>), grid, block, 0, s, kn, vn, slots, kc, vc,      \
                      c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv)
+  if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
+  else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
+  else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
+  else PKV_APPEND(kF32, kFP8);
+#undef PKV_APPEND
+  return hipGetLastError();
+}
+
+// One new token per sequence at position T − 1 (T = seq_lens[s] clamped as
+// the decode clamps it): workgroup s appends k_new[s], v_new[s].
+template <int IN, int OUT>
+__global__ void kv_append_last_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+                                      const int32_t* __restrict__ block_tables, int max_blocks,
+                                      const int32_t* __restrict__ seq_lens, int max_seq_len,
+                                      uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, int num_blocks, int hkv,
+                                      int dh, const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
+  const int s = blockIdx.x;
+  const int T = min(max(seq_lens[s], 0), min(max_seq_len, max_blocks * kBlockSize));
+  if (T <= 0) return;
+  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, T - 1);
+  append_token<IN, OUT>(k_new, v_new, s, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x, blockDim.x);
+}
+
+hipError_t launch_kv_append_last(const CacheView& c, const void* k_new, const void* v_new, int in_dtype, int batch,
+                                 const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                                 int max_seq_len, const float* k_inv, const float* v_inv, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  auto kn = static_cast<const uint8_t*>(k_new);
+  auto vn = static_cast<const uint8_t*>(v_new);
+  auto kc = static_cast<uint8_t*>(c.k);
+  auto vc = static_cast<uint8_t*>(c.v);
+#define PKV_APPEND(IN, OUT)                                                                                   \
+  hipLaunchKernelGGL((kv_append_last_kernel<IN, OUT>), dim3(batch), dim3(128), 0, s, kn, vn, block_tables,    \
+                     max_blocks, seq_lens, max_seq_len, kc, vc, c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, \
+                     v_inv)
   if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
   else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
   else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);

@@ -41,6 +41,11 @@ hipError_t launch_swap(const CacheView& c, const int32_t* ids, int n, void* host
 hipError_t launch_debug_gather(const CacheView& c, const int32_t* table, int seq_len, void* k_out,
                                void* v_out, hipStream_t s);
 
+// One new token per sequence appended at position seq_lens[s] − 1.
+hipError_t launch_kv_append_last(const CacheView& c, const void* k_new, const void* v_new, int in_dtype, int batch,
+                                 const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                                 int max_seq_len, const float* k_inv, const float* v_inv, hipStream_t s);
+
 struct DecodeParams {
   CacheView cache;
   const void* q;
@@ -52,6 +57,14 @@ struct DecodeParams {
   float* ws_u;         // [batch, Hq, num_parts, head_dim] (first in the workspace)
   float* ws_ml;        // [batch, Hq, num_parts, 2] (m, l) in log2 units
   int kernel;          // kDecodeVector or kDecodeMatrix
+  // With k_new set (matrix kernel only), each sequence's new token k_new[b],
+  // v_new[b] ([Hkv, head_dim] of new_dtype) is written to position
+  // seq_lens[b] − 1 by the split kernel itself and attended to from k_new.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int new_dtype = 0;
+  const float* k_inv = nullptr;
+  const float* v_inv = nullptr;
 };
 
 // Waves of one split-KV decode workgroup. A wave reads its share of the

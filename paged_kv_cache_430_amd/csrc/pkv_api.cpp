@@ -253,36 +253,51 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
   return auto_partition(batch, num_q_heads, num_kv_heads, max_seq_len, decode_kernel_for(cache_dtype));
 }
 
-PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
-                            int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
-                            const int32_t* seq_lens, int32_t max_seq_len, float scale,
-                            int32_t partition_tokens, float* out, void* workspace,
-                            size_t workspace_bytes, pkv_stream stream) {
+}  // extern "C"
+
+struct NewTokens {   // the fused append's inputs
+  const void* k_new;
+  const void* v_new;
+  int32_t in_dtype;
+  const float* k_inv;
+  const float* v_inv;
+};
+
+static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* app, const void* q, int32_t q_dtype,
+                       int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
+                       float* out, void* workspace, size_t workspace_bytes, pkv_stream stream) {
   clear_error();
   CacheView c;
-  if (int st = validate_cache(cache, "pkv_attn_decode", &c)) return st;
+  if (int st = validate_cache(cache, fn, &c)) return st;
   if (batch < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_seq_len < 0)
-    return fail(PKV_EINVAL, "pkv_attn_decode: bad size");
-  if (num_q_heads % c.num_kv_heads != 0) return fail(PKV_EINVAL, "pkv_attn_decode: num_q_heads must be a multiple of num_kv_heads");
-  if (num_q_heads / c.num_kv_heads > 64) return fail(PKV_EINVAL, "pkv_attn_decode: more than 64 query heads per KV head");
+    return fail(PKV_EINVAL, std::string(fn) + ": bad size");
+  if (num_q_heads % c.num_kv_heads != 0) return fail(PKV_EINVAL, std::string(fn) + ": num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / c.num_kv_heads > 64) return fail(PKV_EINVAL, std::string(fn) + ": more than 64 query heads per KV head");
   if ((int64_t)max_seq_len > (int64_t)max_blocks * 16)
-    return fail(PKV_EINVAL, "pkv_attn_decode: max_seq_len exceeds max_blocks * block_size");
+    return fail(PKV_EINVAL, std::string(fn) + ": max_seq_len exceeds max_blocks * block_size");
   if (partition_tokens != 0 && (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16))
-    return fail(PKV_EINVAL, "pkv_attn_decode: partition_tokens must be 0 or a multiple of 16 in [16, " + std::to_string(kMaxPartition) + "]");
+    return fail(PKV_EINVAL, std::string(fn) + ": partition_tokens must be 0 or a multiple of 16 in [16, " + std::to_string(kMaxPartition) + "]");
   const bool ok_q = (c.dtype == PKV_F32 && q_dtype == PKV_F32) ||
                     (c.dtype != PKV_F32 && q_dtype == PKV_BF16);
-  if (!ok_q) return fail(PKV_EDTYPE, "pkv_attn_decode: q dtype must be F32 for an F32 cache, BF16 otherwise");
+  if (!ok_q) return fail(PKV_EDTYPE, std::string(fn) + ": q dtype must be F32 for an F32 cache, BF16 otherwise");
   if (batch == 0) return PKV_OK;
-  if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, "pkv_attn_decode: NULL pointer");
-  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "pkv_attn_decode: q and out must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_decode: scale is not finite");
+  if (!q || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, std::string(fn) + ": q and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, std::string(fn) + ": scale is not finite");
+  if (app) {
+    if (int st = check_append_dtypes(c, app->in_dtype, app->k_inv, app->v_inv, fn)) return st;
+    if (!app->k_new || !app->v_new) return fail(PKV_EINVAL, std::string(fn) + ": k_new / v_new is NULL");
+    if (!aligned16(app->k_new) || !aligned16(app->v_new))
+      return fail(PKV_EINVAL, std::string(fn) + ": k_new / v_new must be 16-byte aligned");
+  }
   const int kernel = decode_kernel_for(c.dtype);
   const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
   const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
   if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_EWORKSPACE, "pkv_attn_decode: workspace needs " + std::to_string(need) + " bytes");
-  if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, "pkv_attn_decode: workspace must be 16-byte aligned");
+    return fail(PKV_EWORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) + " bytes");
+  if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, std::string(fn) + ": workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (check_mode()) {
     std::vector<int32_t> lens, bt;
@@ -290,9 +305,9 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
     if (int st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks, s)) return st;
     for (int b = 0; b < batch; ++b) {
       if (lens[b] < 0 || lens[b] > max_seq_len)
-        return fail(PKV_EINVAL, "pkv_attn_decode: PKV_CHECK: seq_lens[" + std::to_string(b) + "] = " +
+        return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: seq_lens[" + std::to_string(b) + "] = " +
                                     std::to_string(lens[b]) + " outside [0, max_seq_len]");
-      if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, "pkv_attn_decode")) return st;
+      if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, fn)) return st;
     }
   }
   DecodeParams p;
@@ -313,7 +328,42 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
   const size_t rows = (size_t)batch * num_q_heads;
   p.ws_u = need ? ws : nullptr;
   p.ws_ml = need ? ws + rows * parts * c.head_dim : nullptr;
-  return hip_status(launch_decode(p, s), "pkv_attn_decode");
+  if (app) {
+    if (kernel == kDecodeMatrix) {   // the split kernel writes and reads the new tokens itself
+      p.k_new = app->k_new;
+      p.v_new = app->v_new;
+      p.new_dtype = app->in_dtype;
+      p.k_inv = app->k_inv;
+      p.v_inv = app->v_inv;
+    } else if (hipError_t e = launch_kv_append_last(c, app->k_new, app->v_new, app->in_dtype, batch, block_tables,
+                                                    max_blocks, seq_lens, max_seq_len, app->k_inv, app->v_inv, s)) {
+      return hip_status(e, fn);
+    }
+  }
+  return hip_status(launch_decode(p, s), fn);
+}
+
+extern "C" {
+
+PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
+                            int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                            int32_t partition_tokens, float* out, void* workspace,
+                            size_t workspace_bytes, pkv_stream stream) {
+  return decode_impl("pkv_attn_decode", cache, nullptr, q, q_dtype, batch, num_q_heads, block_tables, max_blocks,
+                     seq_lens, max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes, stream);
+}
+
+PKV_API int pkv_attn_decode_append(const pkv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                                   const float* k_inv_scale, const float* v_inv_scale, const void* q,
+                                   int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                   int32_t max_seq_len, float scale, int32_t partition_tokens, float* out,
+                                   void* workspace, size_t workspace_bytes, pkv_stream stream) {
+  const NewTokens app{k_new, v_new, in_dtype, k_inv_scale, v_inv_scale};
+  return decode_impl("pkv_attn_decode_append", cache, &app, q, q_dtype, batch, num_q_heads, block_tables,
+                     max_blocks, seq_lens, max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes,
+                     stream);
 }
 
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,

@@ -269,3 +269,53 @@ def test_workspace_reuse_across_calls_and_shapes():
                                               partition_tokens=16, workspace=ws)
                     torch.cuda.synchronize()
                 assert_close(out.cpu().double().numpy(), ref, 2e-3, f"{kern} reuse {seed}")
+
+
+@pytest.mark.parametrize("cache_dtype,in_dtype,hq,hkv,dh", [
+    ("bf16", "bf16", 32, 8, 128), ("bf16", "bf16", 8, 2, 64), ("bf16", "bf16", 32, 1, 128),
+    ("fp8", "bf16", 32, 8, 128), ("fp8", "f32", 16, 2, 64), ("f32", "f32", 8, 2, 128),
+])
+@pytest.mark.parametrize("pt", [0, 64])
+def test_decode_append_in_one_launch(cache_dtype, in_dtype, hq, hkv, dh, pt):
+    """pkv_attn_decode_append leaves the pool exactly as pkv_kv_append_paged
+    does and returns exactly pkv_attn_decode's output on that pool (and the
+    oracle's within tolerance). The new token's slot holds NaN before the call."""
+    from gpu_helpers import NAN_FP8
+    dev = device()
+    lens_ = [1, 2, 16, 17, 33, 500, 1024]
+    w = workloads.decode_inputs("fused", 91 + dh + hq, lens_, hq, hkv, dh, cache_dtype, dev)
+    cache = build_cache(w, dev)
+    cu = w.cu_seqlens
+    last = torch.tensor([int(c) - 1 for c in cu[1:]], device=dev)
+    dt = torch.float32 if in_dtype == "f32" else w.k.dtype
+    k_new, v_new = w.k[last].to(dt).contiguous(), w.v[last].to(dt).contiguous()
+    nan = NAN_FP8 if cache_dtype == "fp8" else float("nan")
+    for b, t in enumerate(lens_):              # the new token's slot: not yet written
+        phys, off = int(w.block_tables[0, b, (t - 1) // 16]), (t - 1) % 16
+        cache.k[phys, :, off, :] = nan
+        cache.v[phys, :, off, :] = nan
+    kinv = vinv = None
+    if cache_dtype == "fp8":
+        kinv = torch.from_numpy(w.k_inv_scale).to(dev)
+        vinv = torch.from_numpy(w.v_inv_scale).to(dev)
+    bt, ln = tables(w, dev), lens(w, dev)
+    msl = int(max(lens_))
+    # reference: the append launch, then the decode
+    ref = pkv.Cache(cache.k.clone(), cache.v.clone(), cache.k_scale, cache.v_scale)
+    cu_new = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
+    pkv.pkv_kv_append_paged(ref, k_new, v_new, bt, cu_new, (ln - 1).contiguous(), 1, kinv, vinv)
+    out_ref = pkv.pkv_attn_decode(ref, w.q, bt, ln, msl, w.scale, partition_tokens=pt)
+    torch.cuda.synchronize()
+    want = oracle_decode(w)
+    for kern in kernels_for(cache_dtype):
+        fused = pkv.Cache(cache.k.clone(), cache.v.clone(), cache.k_scale, cache.v_scale)
+        with decode_kernel(kern):
+            out = pkv.pkv_attn_decode_append(fused, k_new, v_new, w.q, bt, ln, msl, w.scale, partition_tokens=pt,
+                                             k_inv_scale=kinv, v_inv_scale=vinv)
+            out_unfused = pkv.pkv_attn_decode(ref, w.q, bt, ln, msl, w.scale, partition_tokens=pt)
+            torch.cuda.synchronize()
+        assert torch.equal(fused.k.view(torch.uint8), ref.k.view(torch.uint8)), kern
+        assert torch.equal(fused.v.view(torch.uint8), ref.v.view(torch.uint8)), kern
+        assert torch.equal(out, out_unfused), kern
+        assert_close(out.cpu().double().numpy(), want, TOL[cache_dtype], f"{kern} fused {cache_dtype}/{in_dtype}")
+    assert torch.isfinite(out_ref).all()
