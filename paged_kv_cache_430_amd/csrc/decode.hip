@@ -74,8 +74,8 @@ struct Geometry {
 };
 
 struct KernelArgs {
-  const uint8_t* kc;
-  const uint8_t* vc;
+  uint8_t* kc;         // pools: read, and written only by the fused append
+  uint8_t* vc;
   const float* k_scale;
   const float* v_scale;
   const void* q;
@@ -784,9 +784,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       const int phys = bt[lb_new];
       if ((unsigned)phys < (unsigned)a.num_blocks) {
         const size_t off = ((size_t)phys * a.hkv + g) * head_stride + (size_t)r_new * G::RB;
-        if (lane < G::CPR) *reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.kc) + off + lane * 16) = knew;
+        if (lane < G::CPR) *reinterpret_cast<uint4*>(a.kc + off + lane * 16) = knew;
         if (kg == 0) {
-          uint8_t* vd = const_cast<uint8_t*>(a.vc) + off + col * VW * 4;
+          uint8_t* vd = a.vc + off + col * VW * 4;
           if constexpr (VW == 4) *reinterpret_cast<uint4*>(vd) = make_uint4(vnew[0], vnew[1], vnew[2], vnew[3]);
           else if constexpr (VW == 2) *reinterpret_cast<uint2*>(vd) = make_uint2(vnew[0], vnew[1]);
           else *reinterpret_cast<uint32_t*>(vd) = vnew[0];
@@ -1057,8 +1057,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int hc = decode_heads_per_wg(group, p.kernel);
   KernelArgs a;
-  a.kc = static_cast<const uint8_t*>(p.cache.k);
-  a.vc = static_cast<const uint8_t*>(p.cache.v);
+  a.kc = static_cast<uint8_t*>(p.cache.k);
+  a.vc = static_cast<uint8_t*>(p.cache.v);
   a.k_scale = p.cache.k_scale;
   a.v_scale = p.cache.v_scale;
   a.q = p.q;

@@ -276,16 +276,19 @@ __global__ void swap_in_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ v
   }
 }
 
-hipError_t launch_swap(const CacheView& c, const int32_t* ids, int n, void* host, bool out, hipStream_t s) {
+hipError_t launch_swap_out(const CacheView& c, const int32_t* ids, int n, void* host, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
-  if (out)
-    hipLaunchKernelGGL(swap_out_kernel, dim3(n), dim3(256), 0, s, static_cast<const uint8_t*>(c.k),
-                       static_cast<const uint8_t*>(c.v), ids, c.num_blocks, block_bytes, static_cast<uint8_t*>(host));
-  else
-    hipLaunchKernelGGL(swap_in_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k),
-                       static_cast<uint8_t*>(c.v), ids, c.num_blocks, block_bytes,
-                       static_cast<const uint8_t*>(host));
+  hipLaunchKernelGGL(swap_out_kernel, dim3(n), dim3(256), 0, s, static_cast<const uint8_t*>(c.k),
+                     static_cast<const uint8_t*>(c.v), ids, c.num_blocks, block_bytes, static_cast<uint8_t*>(host));
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_in(const CacheView& c, const int32_t* ids, int n, const void* host, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  hipLaunchKernelGGL(swap_in_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v),
+                     ids, c.num_blocks, block_bytes, static_cast<const uint8_t*>(host));
   return hipGetLastError();
 }
 

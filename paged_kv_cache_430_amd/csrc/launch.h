@@ -36,8 +36,9 @@ hipError_t launch_kv_append_paged(const CacheView& c, const void* k_new, const v
 hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int32_t* dst, int n,
                               hipStream_t s);
 
-// Swap whole blocks between the pool and pinned host memory (out: pool → host).
-hipError_t launch_swap(const CacheView& c, const int32_t* ids, int n, void* host, bool out, hipStream_t s);
+// Swap whole blocks between the pool and pinned host memory.
+hipError_t launch_swap_out(const CacheView& c, const int32_t* ids, int n, void* host, hipStream_t s);
+hipError_t launch_swap_in(const CacheView& c, const int32_t* ids, int n, const void* host, hipStream_t s);
 hipError_t launch_debug_gather(const CacheView& c, const int32_t* table, int seq_len, void* k_out,
                                void* v_out, hipStream_t s);
 

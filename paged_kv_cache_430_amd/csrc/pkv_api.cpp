@@ -458,7 +458,7 @@ PKV_API int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, 
   if (n == 0) return PKV_OK;
   if (!ids) return fail(PKV_EINVAL, "pkv_swap_out: ids is NULL");
   if (int st = check_swap_host(c, host, host_bytes, n, "pkv_swap_out")) return st;
-  return hip_status(launch_swap(c, ids, n, host, true, static_cast<hipStream_t>(stream)), "pkv_swap_out");
+  return hip_status(launch_swap_out(c, ids, n, host, static_cast<hipStream_t>(stream)), "pkv_swap_out");
 }
 
 PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_bytes, const int32_t* ids, int32_t n,
@@ -470,7 +470,7 @@ PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_by
   if (n == 0) return PKV_OK;
   if (!ids) return fail(PKV_EINVAL, "pkv_swap_in: ids is NULL");
   if (int st = check_swap_host(c, host, host_bytes, n, "pkv_swap_in")) return st;
-  return hip_status(launch_swap(c, ids, n, const_cast<void*>(host), false, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_swap_in(c, ids, n, host, static_cast<hipStream_t>(stream)),
                     "pkv_swap_in");
 }
 
