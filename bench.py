@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index", "swap"])
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
+    p.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64],
+                   help="tokens per pool block for the cfg2/cfg5 decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--unfused", action="store_true",
                    help="decode workloads: append in its own launch before the decode (default: one launch)")
@@ -84,15 +86,23 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def decode_bytes(seq_lens, hq, hkv, dh, kv_elt, q_elt, fp8):
+def decode_bytes(seq_lens, hq, hkv, dh, kv_elt, q_elt, fp8, block_size=16):
     """Algorithmic bytes of one decode call: every visible K and V element
     once, q, the fp32 output, the block-table entries and lengths read."""
     kv = sum(int(t) for t in seq_lens) * hkv * dh * 2 * kv_elt
     b = len(seq_lens)
-    extra = b * hq * dh * q_elt + b * hq * dh * 4 + sum(-(-int(t) // 16) for t in seq_lens) * 4 + 4 * b
+    extra = (b * hq * dh * q_elt + b * hq * dh * 4 + sum(-(-int(t) // block_size) for t in seq_lens) * 4
+             + 4 * b)
     if fp8:
         extra += 2 * hkv * 4
     return kv + extra
+
+
+def tail_waste(seq_lens, block_size):
+    """Slots allocated but empty: Σ ⌈T/bs⌉·bs − T, and its share of the slots."""
+    slots = sum(-(-int(t) // block_size) * block_size for t in seq_lens)
+    waste = slots - sum(int(t) for t in seq_lens)
+    return {"slots": waste, "frac": round(waste / slots, 5) if slots else 0.0}
 
 
 def append_bytes(n_tokens, hkv, dh, in_elt, cache_elt):
@@ -172,7 +182,7 @@ def load_traffic(kernel, workload):
 # decode workloads
 # ---------------------------------------------------------------------------
 
-def make_decode_setup(name, dev):
+def make_decode_setup(name, dev, block_size=16):
     import numpy as np
     import torch
 
@@ -180,25 +190,29 @@ def make_decode_setup(name, dev):
     import workloads
 
     if name.startswith("cfg2"):
-        make = lambda copies: workloads.cfg2(name.split("-", 1)[1], device=dev, copies=copies)  # noqa: E731
+        make = lambda copies: workloads.cfg2(name.split("-", 1)[1], device=dev, copies=copies,  # noqa: E731
+                                             block_size=block_size)
     elif name.startswith("cfg5"):
-        make = lambda copies: workloads.cfg5(name.split("-", 1)[1], device=dev, copies=copies)  # noqa: E731
+        make = lambda copies: workloads.cfg5(name.split("-", 1)[1], device=dev, copies=copies,  # noqa: E731
+                                             block_size=block_size)
     else:
         make = None
     if make is not None:
         probe = make(1)
         elt = 1 if probe.cache_dtype == "fp8" else 2
-        pool_bytes = probe.num_blocks * probe.hkv * 16 * probe.head_dim * elt * 2
+        pool_bytes = probe.num_blocks * probe.hkv * probe.block_size * probe.head_dim * elt * 2
         copies = max(1, min(64, math.ceil(MALL_BYTES / pool_bytes)))
         del probe
         ws = [make(copies)]
     else:
+        if block_size != 16:
+            raise SystemExit("bench.py: the long-context workloads use 16-token blocks")
         b = int(name.split("-b")[1])
         ws = workloads.cfg3(batch=b, device=dev, layers=32)
         copies = 1
     layers = []
     for w in ws:
-        shape = (w.num_blocks, w.hkv, 16, w.head_dim)
+        shape = (w.num_blocks, w.hkv, w.block_size, w.head_dim)
         if w.cache_dtype == "fp8":
             kp = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
             ks = torch.from_numpy(w.k_scale).to(dev)
@@ -211,7 +225,7 @@ def make_decode_setup(name, dev):
         vp = kp.clone()
         cache = pkv.Cache(kp, vp, ks, vs)
         for c in range(w.copies):
-            slots = np.concatenate([pkv.pkv_slot_mapping(w.block_tables[c, i], 16, 0, int(w.seq_lens[i]))
+            slots = np.concatenate([pkv.pkv_slot_mapping(w.block_tables[c, i], w.block_size, 0, int(w.seq_lens[i]))
                                     for i in range(w.batch)])
             pkv.pkv_kv_append(cache, w.k, w.v, torch.from_numpy(slots).to(dev), kinv, vinv)
         # the step's new tokens: each sequence's last position
@@ -231,7 +245,7 @@ def run_decode(args, dev):
 
     import paged_kv_cache_430_amd as pkv
 
-    layers, copies = make_decode_setup(args.workload, dev)
+    layers, copies = make_decode_setup(args.workload, dev, args.block_size)
     w0 = layers[0]["w"]
     B, hq, hkv, dh = w0.batch, w0.hq, w0.hkv, w0.head_dim
     T = int(w0.seq_lens.max())
@@ -299,7 +313,7 @@ def run_decode(args, dev):
     if args.calib_copy:
         calib_copy(dev)
 
-    d_bytes = decode_bytes(w0.seq_lens, hq, hkv, dh, kv_elt, 2, fp8)
+    d_bytes = decode_bytes(w0.seq_lens, hq, hkv, dh, kv_elt, 2, fp8, w0.block_size)
     a_bytes = append_bytes(B, hkv, dh, 2, kv_elt) + B * 4 * 2    # + table entry and first_pos per token
     step_bytes = (d_bytes + a_bytes) * len(layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -307,7 +321,8 @@ def run_decode(args, dev):
     achieved = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     partition = pt or pkv.pkv_attn_decode_auto_partition(cache_code, B, hq, hkv, T)
     line = {
-        "metric": METRIC if args.workload == "cfg2-all4096" else f"decode-attn KV HBM GB/s ({args.workload})",
+        "metric": (METRIC if args.workload == "cfg2-all4096" and w0.block_size == 16 else
+                   f"decode-attn KV HBM GB/s ({args.workload}, {w0.block_size}-token blocks)"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -320,10 +335,11 @@ def run_decode(args, dev):
         "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": dh,
-                   "seq_len": T, "block_size": 16, "layers": len(layers), "pool_copies": copies,
+                   "seq_len": T, "block_size": w0.block_size, "layers": len(layers), "pool_copies": copies,
                    "partition_tokens": partition, "partitions": -(-T // partition),
                    "step": "append launch + decode" if args.unfused else "append and decode in one launch"},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "tail_waste": tail_waste(w0.seq_lens, w0.block_size),
         "new_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w0.seq_lens.sum()) * len(layers) / (ms_step * 1e-3), 1),
         "decode_call_us": stats_us(dec_ms),

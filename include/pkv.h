@@ -65,7 +65,12 @@ typedef enum pkv_dtype {
 typedef void* pkv_stream;   /* a hipStream_t */
 
 /* One layer's paged cache. Borrowed: the library keeps no pointer past a call.
- * Supported: block_size 16; head_dim 64 or 128; dtype F32, BF16 or FP8_E4M3.
+ * Supported: block_size 16, 32 or 64; head_dim 64 or 128; dtype F32, BF16 or
+ * FP8_E4M3. Every call takes 16-, 32- and 64-token blocks except the F32
+ * decode (its vector-ALU kernel) and pkv_attn_prefill, which take 16. [P2]
+ * Q028 leaves the block size to the implementation and, in its follow-up on
+ * smaller blocks, names the trade: a larger block wastes more tail slots
+ * (blocks·bs − T) but needs fewer table entries and lookups.
  * k_scale/v_scale: device fp32 [num_kv_heads], the dequantisation scale of
  * each KV head (stored byte decoded, times scale, is the value attended to);
  * required for FP8_E4M3, ignored otherwise. */
@@ -174,8 +179,9 @@ PKV_API int pkv_kv_append_paged(const pkv_cache* cache, const void* k_new, const
  *   seq_lens:     device int32 [batch]; values above max_seq_len are clamped
  *   max_seq_len:  host bound on seq_lens (sizes the grid and the workspace)
  *   scale:        score scale (1/sqrt(head_dim) for standard attention)
- *   partition_tokens: tokens per split-KV partition, a multiple of
- *                 block_size in [16, 8192]; 0 picks one from the shape
+ *   partition_tokens: tokens per split-KV partition, a multiple of 16 in
+ *                 [16, 8192] (a partition may end inside a 32- or 64-token
+ *                 block); 0 picks one from the shape
  *                 (pkv_attn_decode_auto_partition)
  *   out:          device fp32 [batch, num_q_heads, head_dim], 16-byte aligned
  *   workspace:    device, 16-byte aligned, at least
@@ -227,7 +233,7 @@ PKV_API int pkv_attn_decode_append(const pkv_cache* cache, const void* k_new, co
  * cache of cache_dtype: with units = batch · num_kv_heads · (query-head
  * chunks per KV head), every sequence is split into ceil(256 / units)
  * partitions — one 8-wave workgroup per MI355X compute unit, no split when
- * the units already fill the chip — rounded up to whole blocks, at least 256
+ * the units already fill the chip — rounded up to 16 tokens, at least 256
  * tokens (or max_seq_len if shorter) and at most 8192. A chunk is up to 16
  * query heads of one KV head for BF16 and FP8 caches (the matrix-core
  * kernel) and the largest of 8, 4, 2, 1 dividing Hq/Hkv for F32 caches (the

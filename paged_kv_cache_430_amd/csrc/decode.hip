@@ -92,6 +92,7 @@ struct KernelArgs {
   const float* k_inv;
   const float* v_inv;
   int new_dtype;
+  int block_size;    // pool block: 16, 32 or 64 tokens (the matrix-core form; 16 for the vector form)
 };
 
 struct MergeArgs {
@@ -699,23 +700,30 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   const int col = lane & 15, kg = lane >> 4;
   const int P = a.num_parts;
   const int tok0 = part * a.part_tokens;
-  const size_t head_stride = (size_t)kBlockSize * G::RB;
-  // Table entries, loaded beside the length: wave w takes block pairs
-  // (tiles) w, w + kWaves, …; lane j holds block 2·(w + kWaves·(j/2)) + j%2.
-  const int lb0 = tok0 / kBlockSize;
-  const int cap = min(a.part_tokens / kBlockSize, a.max_blocks - lb0);
+  // The kernel works in 16-row units ("blocks" below); a pool block of
+  // bs = 16, 32 or 64 tokens holds bs/16 of them, unit u at rows
+  // (u mod bs/16)·16 … of table entry u / (bs/16).
+  const int bs = a.block_size;
+  const int unit_shift = __builtin_amdgcn_readfirstlane(__builtin_ctz((unsigned)bs / kBlockSize));   // log2(bs/16)
+  const int unit_mask = (1 << unit_shift) - 1;
+  const size_t head_stride = (size_t)bs * G::RB;              // bytes of one (pool block, head)
+  // Table entries, loaded beside the length: wave w takes unit pairs
+  // (tiles) w, w + kWaves, …; lane j holds unit 2·(w + kWaves·(j/2)) + j%2.
+  const int lb0 = tok0 / kBlockSize;                         // the partition's first unit
+  const int cap = min(a.part_tokens / kBlockSize, (a.max_blocks << unit_shift) - lb0);
   const int jb = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb0;
-  const int phys_all = jb < cap ? bt[jb] : -1;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+  const int phys_all = jb < cap ? bt[(lb0 + jb) >> unit_shift] : -1;
+  auto unit_row0 = [&](int idx) { return ((lb0 + idx) & unit_mask) * kBlockSize; };   // first pool row of unit idx
   // the length through a vector-memory load: the scalar-cache wait for it
   // would also hold back every other scalar load issued before the first tile
   const int seq_len = (int)__builtin_amdgcn_raw_buffer_load_b32(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.seq_lens + b), 0, 4, kBufferRsrcWord3), 0, 0, 0);
 
 
-  auto tile_rsrc = [&](const uint8_t* pool, int phys, int rows) {
+  auto tile_rsrc = [&](const uint8_t* pool, int phys, int row0, int rows) {
     const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
-    const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
+    const uint8_t* base = pool + ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride + (size_t)row0 * G::RB;
     const int records = __builtin_amdgcn_readfirstlane(ok ? rows * G::RB : 0);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, records, kBufferRsrcWord3);
   };
@@ -723,10 +731,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     uint4 k[2][G::NKI];       // [block][whole-row load]
     uint32_t v[2][4][VW];     // [block][key of the lane's quad]
   };
-  // block e of a tile from table entry phys, reading `rows` rows
-  auto load_blocks = [&](Tile& t, int e, int phys, int rows) {
-    const auto rk = tile_rsrc(a.kc, phys, rows);
-    const auto rv = tile_rsrc(a.vc, phys, rows);
+  // unit e of a tile: `rows` rows from row0 of table entry phys
+  auto load_blocks = [&](Tile& t, int e, int phys, int row0, int rows) {
+    const auto rk = tile_rsrc(a.kc, phys, row0, rows);
+    const auto rv = tile_rsrc(a.vc, phys, row0, rows);
     // K: whole rows per load (CPR lanes per row), restaged through LDS
 #pragma unroll
     for (int i = 0; i < G::NKI; ++i)
@@ -740,7 +748,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   // sequence are masked when the pair is used.
   Tile first;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), kBlockSize);
+  for (int e = 0; e < 2; ++e)
+    load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), unit_row0(2 * w + e), kBlockSize);
 
   // q of head col as the B operand of each k-step (zeros past the chunk's heads)
   bf16x8_t qb[NDC];
@@ -753,7 +762,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     }
   }
 
-  const int T = __builtin_amdgcn_readfirstlane(min(max(seq_len, 0), min(a.max_seq_len, a.max_blocks * kBlockSize)));
+  const int T = __builtin_amdgcn_readfirstlane(min(max(seq_len, 0), min(a.max_seq_len, a.max_blocks * bs)));
   const int ntok = min(a.part_tokens, T - tok0);
   const int nblk = ntok > 0 ? (ntok + kBlockSize - 1) / kBlockSize : 0;
   const int ntile = (nblk + 1) / 2;
@@ -781,9 +790,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       new_token_bytes<KV, VW * 4>(a.v_new, row + col * NDT, a.new_dtype, vinv, vnew);
     }
     if (lb_new >= 0 && chunk == 0 && w == 0) {
-      const int phys = bt[lb_new];
+      const int phys = bt[pos / bs];
       if ((unsigned)phys < (unsigned)a.num_blocks) {
-        const size_t off = ((size_t)phys * a.hkv + g) * head_stride + (size_t)r_new * G::RB;
+        const size_t off = ((size_t)phys * a.hkv + g) * head_stride + (size_t)(pos % bs) * G::RB;
         if (lane < G::CPR) *reinterpret_cast<uint4*>(a.kc + off + lane * 16) = knew;
         if (kg == 0) {
           uint8_t* vd = a.vc + off + col * VW * 4;
@@ -801,7 +810,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   auto block_index = [&](int j, int e) { return 2 * (w + kWaves * j) + e; };
   auto load_tile = [&](int j, Tile& t) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) load_blocks(t, e, block_phys(j, e), rows_of(block_index(j, e)));
+    for (int e = 0; e < 2; ++e)
+      load_blocks(t, e, block_phys(j, e), unit_row0(block_index(j, e)), rows_of(block_index(j, e)));
   };
 
   float m_run = -INFINITY, l_run = 0.0f;     // head col; l is this lane's share
@@ -1081,6 +1091,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.k_inv = p.k_inv;
   a.v_inv = p.v_inv;
   a.new_dtype = p.new_dtype;
+  a.block_size = p.cache.block_size;
   const int dt = p.cache.dtype, dh = p.cache.head_dim;
   hipError_t e;
   if (p.kernel == kDecodeMatrix)

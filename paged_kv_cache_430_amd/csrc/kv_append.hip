@@ -16,31 +16,31 @@ namespace pkv {
 // ---------------------------------------------------------------------------
 // Slot of logical position pos through one sequence's table row; −1 when the
 // position's block is beyond max_blocks or its entry is negative.
-__device__ __forceinline__ int slot_of(const int32_t* __restrict__ bt, int max_blocks, int pos) {
-  const int lb = pos / kBlockSize;
+__device__ __forceinline__ int slot_of(const int32_t* __restrict__ bt, int max_blocks, int pos, int bs) {
+  const int lb = pos / bs;
   if (pos < 0 || lb >= max_blocks) return -1;
   const int phys = bt[lb];
-  return phys >= 0 ? phys * kBlockSize + pos % kBlockSize : -1;
+  return phys >= 0 ? phys * bs + pos % bs : -1;
 }
 
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ block_tables, int max_blocks,
                                     const int32_t* __restrict__ cu_new,
-                                    const int32_t* __restrict__ first_pos, int n_tokens,
+                                    const int32_t* __restrict__ first_pos, int n_tokens, int bs,
                                     int32_t* __restrict__ out) {
   const int s = blockIdx.x;
   const int lo = cu_new[s];
   const int hi = min(cu_new[s + 1], n_tokens);
   const int p0 = first_pos[s];
   const int32_t* bt = block_tables + (size_t)s * max_blocks;
-  for (int i = lo + (int)threadIdx.x; i < hi; i += blockDim.x) out[i] = slot_of(bt, max_blocks, p0 + (i - lo));
+  for (int i = lo + (int)threadIdx.x; i < hi; i += blockDim.x) out[i] = slot_of(bt, max_blocks, p0 + (i - lo), bs);
 }
 
-hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int num_seqs,
+hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int block_size, int num_seqs,
                                const int32_t* cu_new, const int32_t* first_pos, int n_tokens,
                                int32_t* out_slots, hipStream_t s) {
   if (num_seqs == 0 || n_tokens == 0) return hipSuccess;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(128), 0, s, block_tables,
-                     max_blocks, cu_new, first_pos, n_tokens, out_slots);
+                     max_blocks, cu_new, first_pos, n_tokens, block_size, out_slots);
   return hipGetLastError();
 }
 
@@ -52,9 +52,9 @@ __device__ __forceinline__ void append_token(const uint8_t* __restrict__ k_new,
                                              uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                              int num_blocks, int hkv, int dh,
                                              const float* __restrict__ k_inv,
-                                             const float* __restrict__ v_inv, int t0, int nt) {
-  if (slot < 0 || slot >= num_blocks * kBlockSize) return;   // skipped token
-  const int blk = slot / kBlockSize, off = slot % kBlockSize;
+                                             const float* __restrict__ v_inv, int t0, int nt, int bs) {
+  if (slot < 0 || slot >= num_blocks * bs) return;   // skipped token
+  const int blk = slot / bs, off = slot % bs;
   constexpr int IN_B = IN == kF32 ? 4 : 2;
   constexpr int EPC = 16 / IN_B;                       // input elements per 16-byte chunk
   const int chunks_per_head = dh / EPC;
@@ -65,7 +65,7 @@ __device__ __forceinline__ void append_token(const uint8_t* __restrict__ k_new,
     const int h = cc / chunks_per_head;
     const int e0 = (cc % chunks_per_head) * EPC;
     const uint8_t* src = (is_v ? v_new : k_new) + ((size_t)tok * hkv * dh + (size_t)h * dh + e0) * IN_B;
-    const size_t dst_elem = (((size_t)blk * hkv + h) * kBlockSize + off) * dh + e0;
+    const size_t dst_elem = (((size_t)blk * hkv + h) * bs + off) * dh + e0;
     uint8_t* dst_base = is_v ? vc : kc;
     const uint4 x = *reinterpret_cast<const uint4*>(src);
     if constexpr (OUT != kFP8) {
@@ -104,10 +104,10 @@ template <int IN, int OUT>
 __global__ void kv_append_kernel(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
                                  const int32_t* __restrict__ slots, uint8_t* __restrict__ kc,
                                  uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
-                                 const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
+                                 const float* __restrict__ k_inv, const float* __restrict__ v_inv, int bs) {
   const int tok = blockIdx.x;
   append_token<IN, OUT>(k_new, v_new, tok, slots[tok], kc, vc, num_blocks, hkv, dh, k_inv, v_inv,
-                        threadIdx.x, blockDim.x);
+                        threadIdx.x, blockDim.x, bs);
 }
 
 // Slot mapping fused into the append: workgroup (s, j) takes sequence s's new
@@ -122,16 +122,16 @@ __global__ void kv_append_paged_kernel(const uint8_t* __restrict__ k_new, const 
                                        const int32_t* __restrict__ first_pos, uint8_t* __restrict__ kc,
                                        uint8_t* __restrict__ vc, int num_blocks, int hkv, int dh,
                                        const float* __restrict__ k_inv, const float* __restrict__ v_inv,
-                                       int32_t* __restrict__ out_slots) {
+                                       int32_t* __restrict__ out_slots, int bs) {
   const int s = blockIdx.x;
   const int lo = cu_new[s], hi = cu_new[s + 1];
   const int part = threadIdx.x / (blockDim.x / kAppendTokensPerWg);
   const int nt = blockDim.x / kAppendTokensPerWg;
   const int i = lo + blockIdx.y * kAppendTokensPerWg + part;
   if (i >= hi) return;
-  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, first_pos[s] + (i - lo));
+  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, first_pos[s] + (i - lo), bs);
   if (out_slots && threadIdx.x % nt == 0) out_slots[i] = slot;
-  append_token<IN, OUT>(k_new, v_new, i, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x % nt, nt);
+  append_token<IN, OUT>(k_new, v_new, i, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x % nt, nt, bs);
 }
 
 hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v_new, int in_dtype,
@@ -145,7 +145,7 @@ hipError_t launch_kv_append(const CacheView& c, const void* k_new, const void* v
   auto vc = static_cast<uint8_t*>(c.v);
 #define PKV_APPEND(IN, OUT)                                                                      \
   hipLaunchKernelGGL((kv_append_kernel<IN, OUT>), grid, block, 0, s, kn, vn, slots, kc, vc,      \
-                     c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv)
+                     c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv, c.block_size)
   if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
   else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
   else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
@@ -161,12 +161,14 @@ __global__ void kv_append_last_kernel(const uint8_t* __restrict__ k_new, const u
                                       const int32_t* __restrict__ block_tables, int max_blocks,
                                       const int32_t* __restrict__ seq_lens, int max_seq_len,
                                       uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, int num_blocks, int hkv,
-                                      int dh, const float* __restrict__ k_inv, const float* __restrict__ v_inv) {
+                                      int dh, const float* __restrict__ k_inv, const float* __restrict__ v_inv,
+                                      int bs) {
   const int s = blockIdx.x;
-  const int T = min(max(seq_lens[s], 0), min(max_seq_len, max_blocks * kBlockSize));
+  const int T = min(max(seq_lens[s], 0), min(max_seq_len, max_blocks * bs));
   if (T <= 0) return;
-  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, T - 1);
-  append_token<IN, OUT>(k_new, v_new, s, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x, blockDim.x);
+  const int slot = slot_of(block_tables + (size_t)s * max_blocks, max_blocks, T - 1, bs);
+  append_token<IN, OUT>(k_new, v_new, s, slot, kc, vc, num_blocks, hkv, dh, k_inv, v_inv, threadIdx.x, blockDim.x,
+                        bs);
 }
 
 hipError_t launch_kv_append_last(const CacheView& c, const void* k_new, const void* v_new, int in_dtype, int batch,
@@ -180,7 +182,7 @@ hipError_t launch_kv_append_last(const CacheView& c, const void* k_new, const vo
 #define PKV_APPEND(IN, OUT)                                                                                   \
   hipLaunchKernelGGL((kv_append_last_kernel<IN, OUT>), dim3(batch), dim3(128), 0, s, kn, vn, block_tables,    \
                      max_blocks, seq_lens, max_seq_len, kc, vc, c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, \
-                     v_inv)
+                     v_inv, c.block_size)
   if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
   else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
   else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
@@ -202,7 +204,7 @@ hipError_t launch_kv_append_paged(const CacheView& c, const void* k_new, const v
 #define PKV_APPEND(IN, OUT)                                                                             \
   hipLaunchKernelGGL((kv_append_paged_kernel<IN, OUT>), grid, block, 0, s, kn, vn, block_tables, max_blocks, \
                      cu_new, first_pos, kc, vc, c.num_blocks, c.num_kv_heads, c.head_dim, k_inv, v_inv,   \
-                     out_slots)
+                     out_slots, c.block_size)
   if (c.dtype == kF32) PKV_APPEND(kF32, kF32);
   else if (c.dtype == kBF16) PKV_APPEND(kBF16, kBF16);
   else if (in_dtype == kBF16) PKV_APPEND(kBF16, kFP8);
@@ -232,7 +234,7 @@ __global__ void copy_blocks_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict
 hipError_t launch_copy_blocks(const CacheView& c, const int32_t* src, const int32_t* dst, int n,
                               hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  const size_t block_bytes = (size_t)c.num_kv_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k),
                      static_cast<uint8_t*>(c.v), src, dst, c.num_blocks, block_bytes);
   return hipGetLastError();
@@ -278,7 +280,7 @@ __global__ void swap_in_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ v
 
 hipError_t launch_swap_out(const CacheView& c, const int32_t* ids, int n, void* host, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  const size_t block_bytes = (size_t)c.num_kv_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   hipLaunchKernelGGL(swap_out_kernel, dim3(n), dim3(256), 0, s, static_cast<const uint8_t*>(c.k),
                      static_cast<const uint8_t*>(c.v), ids, c.num_blocks, block_bytes, static_cast<uint8_t*>(host));
   return hipGetLastError();
@@ -286,7 +288,7 @@ hipError_t launch_swap_out(const CacheView& c, const int32_t* ids, int n, void* 
 
 hipError_t launch_swap_in(const CacheView& c, const int32_t* ids, int n, const void* host, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const size_t block_bytes = (size_t)c.num_kv_heads * kBlockSize * c.head_dim * dtype_bytes(c.dtype);
+  const size_t block_bytes = (size_t)c.num_kv_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   hipLaunchKernelGGL(swap_in_kernel, dim3(n), dim3(256), 0, s, static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v),
                      ids, c.num_blocks, block_bytes, static_cast<const uint8_t*>(host));
   return hipGetLastError();
@@ -298,12 +300,12 @@ hipError_t launch_swap_in(const CacheView& c, const int32_t* ids, int n, const v
 __global__ void debug_gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                                     const int32_t* __restrict__ table, int seq_len, int num_blocks,
                                     int hkv, int row_bytes, uint8_t* __restrict__ k_out,
-                                    uint8_t* __restrict__ v_out) {
+                                    uint8_t* __restrict__ v_out, int bs) {
   const int p = blockIdx.x;
   const int h = blockIdx.y;
-  const int phys = table[p / kBlockSize];
+  const int phys = table[p / bs];
   if ((unsigned)phys >= (unsigned)num_blocks) return;
-  const size_t src = (((size_t)phys * hkv + h) * kBlockSize + p % kBlockSize) * row_bytes;
+  const size_t src = (((size_t)phys * hkv + h) * bs + p % bs) * row_bytes;
   const size_t dst = ((size_t)h * seq_len + p) * row_bytes;
   for (int b = threadIdx.x * 4; b < row_bytes; b += blockDim.x * 4) {
     *reinterpret_cast<uint32_t*>(k_out + dst + b) = *reinterpret_cast<const uint32_t*>(kc + src + b);
@@ -318,7 +320,7 @@ hipError_t launch_debug_gather(const CacheView& c, const int32_t* table, int seq
   hipLaunchKernelGGL(debug_gather_kernel, dim3(seq_len, c.num_kv_heads), dim3(64), 0, s,
                      static_cast<const uint8_t*>(c.k), static_cast<const uint8_t*>(c.v), table,
                      seq_len, c.num_blocks, c.num_kv_heads, row_bytes,
-                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
+                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), c.block_size);
   return hipGetLastError();
 }
 

@@ -14,13 +14,14 @@ inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
 
 struct CacheView {
   int num_blocks, num_kv_heads, head_dim, dtype;
+  int block_size;   // tokens per block: 16, 32 or 64
   void* k;
   void* v;
   const float* k_scale;
   const float* v_scale;
 };
 
-hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int num_seqs,
+hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks, int block_size, int num_seqs,
                                const int32_t* cu_new, const int32_t* first_pos, int n_tokens,
                                int32_t* out_slots, hipStream_t s);
 

@@ -47,10 +47,11 @@ int hip_status(hipError_t e, const char* what) {
 int validate_cache(const pkv_cache* c, const char* fn, CacheView* view) {
   const std::string f(fn);
   if (!c) return fail(PKV_EINVAL, f + ": cache is NULL");
-  if (c->block_size != 16) return fail(PKV_EINVAL, f + ": block_size must be 16");
+  if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PKV_EINVAL, f + ": block_size must be 16, 32 or 64");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(PKV_EINVAL, f + ": head_dim must be 64 or 128");
   if (c->num_kv_heads <= 0) return fail(PKV_EINVAL, f + ": num_kv_heads must be positive");
-  if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX / 16)
+  if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX / c->block_size)
     return fail(PKV_EINVAL, f + ": num_blocks out of range");
   if (c->dtype != PKV_F32 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)
     return fail(PKV_EDTYPE, f + ": unknown cache dtype");
@@ -63,6 +64,7 @@ int validate_cache(const pkv_cache* c, const char* fn, CacheView* view) {
   view->num_kv_heads = c->num_kv_heads;
   view->head_dim = c->head_dim;
   view->dtype = c->dtype;
+  view->block_size = c->block_size;
   view->k = c->k_cache;
   view->v = c->v_cache;
   view->k_scale = c->k_scale;
@@ -81,8 +83,8 @@ int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
 
 // PKV_CHECK: every table entry a sequence will read names a pool block.
 int check_tables(const std::vector<int32_t>& bt, int max_blocks, int seq, int tokens,
-                 int num_blocks, const char* fn) {
-  const int nb = (tokens + 15) / 16;
+                 int num_blocks, const char* fn, int bs = 16) {
+  const int nb = (tokens + bs - 1) / bs;
   if (nb > max_blocks) return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: sequence longer than its table");
   for (int i = 0; i < nb; ++i) {
     const int32_t id = bt[(size_t)seq * max_blocks + i];
@@ -177,11 +179,12 @@ PKV_API int pkv_slot_mapping_device(const int32_t* block_tables, int32_t max_blo
                                     const int32_t* first_pos, int32_t n_tokens, int32_t* out_slots,
                                     pkv_stream stream) {
   clear_error();
-  if (block_size != 16) return fail(PKV_EINVAL, "pkv_slot_mapping_device: block_size must be 16");
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PKV_EINVAL, "pkv_slot_mapping_device: block_size must be 16, 32 or 64");
   if (num_seqs < 0 || n_tokens < 0 || max_blocks < 0) return fail(PKV_EINVAL, "pkv_slot_mapping_device: negative size");
   if (num_seqs > 0 && n_tokens > 0 && (!block_tables || !cu_new || !first_pos || !out_slots))
     return fail(PKV_EINVAL, "pkv_slot_mapping_device: NULL pointer");
-  return hip_status(launch_slot_mapping(block_tables, max_blocks, num_seqs, cu_new, first_pos,
+  return hip_status(launch_slot_mapping(block_tables, max_blocks, block_size, num_seqs, cu_new, first_pos,
                                         n_tokens, out_slots, static_cast<hipStream_t>(stream)),
                     "pkv_slot_mapping_device");
 }
@@ -202,7 +205,7 @@ PKV_API int pkv_kv_append(const pkv_cache* cache, const void* k_new, const void*
     std::vector<int32_t> slots;
     if (int st = copy_to_host(slots, slot_mapping, (size_t)n_tokens, s)) return st;
     for (int32_t v : slots)
-      if (v < -1 || (int64_t)v >= (int64_t)c.num_blocks * 16)
+      if (v < -1 || (int64_t)v >= (int64_t)c.num_blocks * c.block_size)
         return fail(PKV_EINVAL, "pkv_kv_append: PKV_CHECK: slot " + std::to_string(v) + " outside the pool");
   }
   return hip_status(launch_kv_append(c, k_new, v_new, in_dtype, n_tokens, slot_mapping, k_inv_scale,
@@ -274,7 +277,7 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
     return fail(PKV_EINVAL, std::string(fn) + ": bad size");
   if (num_q_heads % c.num_kv_heads != 0) return fail(PKV_EINVAL, std::string(fn) + ": num_q_heads must be a multiple of num_kv_heads");
   if (num_q_heads / c.num_kv_heads > 64) return fail(PKV_EINVAL, std::string(fn) + ": more than 64 query heads per KV head");
-  if ((int64_t)max_seq_len > (int64_t)max_blocks * 16)
+  if ((int64_t)max_seq_len > (int64_t)max_blocks * c.block_size)
     return fail(PKV_EINVAL, std::string(fn) + ": max_seq_len exceeds max_blocks * block_size");
   if (partition_tokens != 0 && (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16))
     return fail(PKV_EINVAL, std::string(fn) + ": partition_tokens must be 0 or a multiple of 16 in [16, " + std::to_string(kMaxPartition) + "]");
@@ -292,6 +295,8 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
       return fail(PKV_EINVAL, std::string(fn) + ": k_new / v_new must be 16-byte aligned");
   }
   const int kernel = decode_kernel_for(c.dtype);
+  if (c.block_size != 16 && kernel != kDecodeMatrix)
+    return fail(PKV_EINVAL, std::string(fn) + ": block sizes other than 16 need the matrix-core decode (bf16 or fp8 cache)");
   const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
   const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
@@ -307,7 +312,7 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
       if (lens[b] < 0 || lens[b] > max_seq_len)
         return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: seq_lens[" + std::to_string(b) + "] = " +
                                     std::to_string(lens[b]) + " outside [0, max_seq_len]");
-      if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, fn)) return st;
+      if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, fn, c.block_size)) return st;
     }
   }
   DecodeParams p;
@@ -379,6 +384,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
   if (int st = validate_cache(cache, "pkv_attn_prefill_chunk", &c)) return st;
   if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16)
     return fail(PKV_EDTYPE, "pkv_attn_prefill_chunk: cache and q must be BF16");
+  if (c.block_size != 16) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: block_size must be 16");
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
     return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: bad size");
   if (num_q_heads % c.num_kv_heads != 0)
@@ -435,7 +441,7 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const in
 // pinned (device-addressable) host memory, so the kernel never touches
 // pageable memory.
 static int check_swap_host(const CacheView& c, const void* host, size_t host_bytes, int32_t n, const char* what) {
-  const size_t block_bytes = (size_t)c.num_kv_heads * 16 * c.head_dim * dtype_bytes(c.dtype);
+  const size_t block_bytes = (size_t)c.num_kv_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   if (!host) return fail(PKV_EINVAL, std::string(what) + ": host is NULL");
   if (!aligned16(host)) return fail(PKV_EINVAL, std::string(what) + ": host must be 16-byte aligned");
   if (host_bytes < (size_t)n * 2 * block_bytes)

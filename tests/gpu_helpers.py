@@ -17,8 +17,8 @@ def device():
     return torch.device("cuda:0")
 
 
-def new_pools(num_blocks, hkv, dh, cache_dtype, dev):
-    shape = (num_blocks, hkv, 16, dh)
+def new_pools(num_blocks, hkv, dh, cache_dtype, dev, block_size=16):
+    shape = (num_blocks, hkv, block_size, dh)
     if cache_dtype == "fp8":
         k = torch.full(shape, NAN_FP8, dtype=torch.uint8, device=dev)
     else:
@@ -30,7 +30,7 @@ def new_pools(num_blocks, hkv, dh, cache_dtype, dev):
 def build_cache(w, dev, copies=None):
     """Pools for a DecodeInputs workload, every sequence appended through the
     library at positions 0..T-1 (once per table copy)."""
-    kp, vp = new_pools(w.num_blocks, w.hkv, w.head_dim, w.cache_dtype, dev)
+    kp, vp = new_pools(w.num_blocks, w.hkv, w.head_dim, w.cache_dtype, dev, w.block_size)
     ks = vs = kinv = vinv = None
     if w.cache_dtype == "fp8":
         ks = torch.from_numpy(w.k_scale).to(dev)
@@ -39,7 +39,7 @@ def build_cache(w, dev, copies=None):
         vinv = torch.from_numpy(w.v_inv_scale).to(dev)
     cache = pkv.Cache(kp, vp, ks, vs)
     for c in range(w.copies if copies is None else copies):
-        slots = np.concatenate([pkv.pkv_slot_mapping(w.block_tables[c, b], 16, 0, int(w.seq_lens[b]))
+        slots = np.concatenate([pkv.pkv_slot_mapping(w.block_tables[c, b], w.block_size, 0, int(w.seq_lens[b]))
                                 for b in range(w.batch)] or [np.zeros(0, np.int32)])
         if len(slots):
             pkv.pkv_kv_append(cache, w.k, w.v, torch.from_numpy(slots).to(dev), kinv, vinv)

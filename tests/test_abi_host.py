@@ -146,6 +146,27 @@ def test_auto_partition_rule(lib, monkeypatch):
             assert 16 <= p <= 8192 and p % 16 == 0
 
 
+def test_block_size_rules(lib, monkeypatch):
+    """16-, 32- and 64-token blocks; the F32 (vector) decode and the prefill take 16 only."""
+    def decode(ref, b=1, msl=64, dtype=pkv.PKV_BF16):
+        return lib.pkv_attn_decode(ref, 0x50000, dtype, b, 8, 0x60000, 4, 0x70000, msl, 0.1, 0, 0x80000,
+                                   None, 0, None)
+    for bs in (8, 24, 48, 128):
+        assert decode(_fake_cache(bs=bs)[0], b=0) == pkv.PKV_EINVAL, bs
+    for bs in (32, 64):
+        ref, _ = _fake_cache(bs=bs)
+        assert decode(ref, b=0, msl=4 * bs) == pkv.PKV_OK
+        assert decode(ref, b=0, msl=4 * bs + 1) == pkv.PKV_EINVAL          # beyond max_blocks · bs
+        ref32, _ = _fake_cache(dtype=pkv.PKV_F32, bs=bs)
+        assert decode(ref32, dtype=pkv.PKV_F32) == pkv.PKV_EINVAL          # vector kernel: 16 only
+        monkeypatch.setenv("PKV_DECODE_KERNEL", "vector")
+        assert decode(ref) == pkv.PKV_EINVAL
+        monkeypatch.delenv("PKV_DECODE_KERNEL")
+        assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
+                                          None, 0, None) == pkv.PKV_EINVAL
+        assert "block_size" in lib.pkv_last_error().decode()
+
+
 def test_append_and_prefill_validation(lib):
     ref, _ = _fake_cache()
     assert lib.pkv_kv_append(ref, 0x50000, 0x60000, pkv.PKV_F32, 4, 0x70000, None, None, None) == pkv.PKV_EDTYPE

@@ -205,3 +205,38 @@ def test_fused_append_matches_slot_mapping_then_append(cache_dtype, in_dtype, dh
     pkv.pkv_kv_append_paged(pkv.Cache(kc, vc, ksc, vsc), kn, vn, bt, cu_d, fp, max(news), kinv, vinv)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(kc), _bits(ka))
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_append_and_slots_at_larger_block_sizes(bs):
+    """Slot mapping (host and device), append and gather with 32- and 64-token
+    blocks, bit-exact against the oracle's scatter."""
+    dev = device()
+    rng = np.random.default_rng(40 + bs)
+    nblocks, hkv, dh = 24, 2, 64
+    table = [int(x) for x in rng.permutation(nblocks)[:5]]
+    n = 5 * bs - 3
+    kn = torch.randn(n, hkv, dh, device=dev).to(torch.bfloat16)
+    vn = torch.randn(n, hkv, dh, device=dev).to(torch.bfloat16)
+    kp, vp = new_pools(nblocks, hkv, dh, "bf16", dev, block_size=bs)
+    cache = pkv.Cache(kp, vp)
+    slots = pkv.pkv_slot_mapping(table, bs, 0, n)
+    assert list(slots) == paging.slot_mapping(table, 0, n, bs)
+    bt = torch.tensor([table + [-1, -1]], dtype=torch.int32, device=dev)
+    dev_slots = pkv.pkv_slot_mapping_device(bt, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                                            torch.tensor([0], dtype=torch.int32, device=dev), n, block_size=bs)
+    assert np.array_equal(dev_slots.cpu().numpy(), slots)
+    pkv.pkv_kv_append_paged(cache, kn, vn, bt, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                            torch.tensor([0], dtype=torch.int32, device=dev), n)
+    nan_bits = int(bf16_bits(torch.tensor([float("nan")], dtype=torch.bfloat16))[0])   # the pools' fill
+    ref_k = np.full((nblocks, hkv, bs, dh), nan_bits, dtype=np.uint16)
+    ref_v = ref_k.copy()
+    paging.scatter(ref_k, bf16_bits(kn), table, bs)
+    paging.scatter(ref_v, bf16_bits(vn), table, bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(kp), ref_k)
+    assert np.array_equal(bf16_bits(vp), ref_v)
+    gk, gv = pkv.pkv_debug_gather(cache, bt[0], n)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(gk), bf16_bits(kn.permute(1, 0, 2)))
+    assert np.array_equal(bf16_bits(gv), bf16_bits(vn.permute(1, 0, 2)))

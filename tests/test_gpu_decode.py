@@ -319,3 +319,44 @@ def test_decode_append_in_one_launch(cache_dtype, in_dtype, hq, hkv, dh, pt):
         assert torch.equal(out, out_unfused), kern
         assert_close(out.cpu().double().numpy(), want, TOL[cache_dtype], f"{kern} fused {cache_dtype}/{in_dtype}")
     assert torch.isfinite(out_ref).all()
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [("bf16", 32, 8, 128), ("fp8", 16, 2, 64), ("bf16", 32, 1, 64)])
+def test_block_sizes_32_and_64(bs, cache_dtype, hq, hkv, dh):
+    """Pools of 32- and 64-token blocks (matrix-core decode): ragged lengths,
+    partitions that split a block, the fused append, NaN slots elsewhere."""
+    from gpu_helpers import NAN_FP8
+    dev = device()
+    lens_ = [1, 15, 16, 31, 33, 64, 65, 500, 1031]
+    w = workloads.decode_inputs("bs", 7 + bs + dh, lens_, hq, hkv, dh, cache_dtype, dev, block_size=bs)
+    cache = build_cache(w, dev)
+    assert cache.block_size == bs
+    ref = oracle_decode(w)
+    msl = int(max(lens_))
+    for pt in (0, 16, 48, 512):
+        got = run_decode(w, cache, dev, partition_tokens=pt, kernel="matrix")
+        assert_close(got, ref, TOL[cache_dtype], f"bs{bs} {cache_dtype} pt{pt}")
+    with pytest.raises(pkv.PKVError):                  # the vector form takes 16-token blocks only
+        run_decode(w, cache, dev, kernel="vector")
+    # the fused append at these block sizes: the last token's slot starts as NaN
+    bt, ln = tables(w, dev), lens(w, dev)
+    last = torch.tensor([int(c) - 1 for c in w.cu_seqlens[1:]], device=dev)
+    k_new, v_new = w.k[last].contiguous(), w.v[last].contiguous()
+    want_k, want_v = cache.k.clone(), cache.v.clone()
+    nan = NAN_FP8 if cache_dtype == "fp8" else float("nan")
+    for b, t in enumerate(lens_):
+        phys, off = int(w.block_tables[0, b, (t - 1) // bs]), (t - 1) % bs
+        cache.k[phys, :, off, :] = nan
+        cache.v[phys, :, off, :] = nan
+    kinv = vinv = None
+    if cache_dtype == "fp8":
+        kinv = torch.from_numpy(w.k_inv_scale).to(dev)
+        vinv = torch.from_numpy(w.v_inv_scale).to(dev)
+    with decode_kernel("matrix"):
+        out = pkv.pkv_attn_decode_append(cache, k_new, v_new, w.q, bt, ln, msl, w.scale, partition_tokens=48,
+                                         k_inv_scale=kinv, v_inv_scale=vinv)
+        torch.cuda.synchronize()
+    assert torch.equal(cache.k.view(torch.uint8), want_k.view(torch.uint8))
+    assert torch.equal(cache.v.view(torch.uint8), want_v.view(torch.uint8))
+    assert_close(out.cpu().double().numpy(), ref, TOL[cache_dtype], f"bs{bs} fused")

@@ -12,16 +12,16 @@ from gpu_helpers import device
 pytestmark = pytest.mark.gpu
 
 
-def _pool(dtype, nb, hkv, dh, dev, seed):
+def _pool(dtype, nb, hkv, dh, dev, seed, bs=16):
     g = torch.Generator(device=dev).manual_seed(seed)
     if dtype == "fp8":
-        k = torch.randint(0, 256, (nb, hkv, 16, dh), generator=g, dtype=torch.uint8, device=dev)
-        v = torch.randint(0, 256, (nb, hkv, 16, dh), generator=g, dtype=torch.uint8, device=dev)
+        k = torch.randint(0, 256, (nb, hkv, bs, dh), generator=g, dtype=torch.uint8, device=dev)
+        v = torch.randint(0, 256, (nb, hkv, bs, dh), generator=g, dtype=torch.uint8, device=dev)
         sc = torch.ones(hkv, device=dev)
         return pkv.Cache(k, v, sc, sc)
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
-    k = torch.randn(nb, hkv, 16, dh, generator=g, device=dev).to(dt)
-    v = torch.randn(nb, hkv, 16, dh, generator=g, device=dev).to(dt)
+    k = torch.randn(nb, hkv, bs, dh, generator=g, device=dev).to(dt)
+    v = torch.randn(nb, hkv, bs, dh, generator=g, device=dev).to(dt)
     return pkv.Cache(k, v)
 
 
@@ -29,11 +29,12 @@ def _bytes(t):
     return t.contiguous().view(torch.uint8).cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,hkv,dh", [("bf16", 8, 128), ("fp8", 8, 128), ("f32", 2, 64)])
-def test_swap_round_trip_is_bit_exact(dtype, hkv, dh):
+@pytest.mark.parametrize("dtype,hkv,dh,bs", [("bf16", 8, 128, 16), ("fp8", 8, 128, 16), ("f32", 2, 64, 16),
+                                             ("bf16", 2, 64, 32), ("fp8", 4, 128, 64)])
+def test_swap_round_trip_is_bit_exact(dtype, hkv, dh, bs):
     dev = device()
     nb = 64
-    cache = _pool(dtype, nb, hkv, dh, dev, 11)
+    cache = _pool(dtype, nb, hkv, dh, dev, 11, bs)
     k0, v0 = _bytes(cache.k), _bytes(cache.v)
     out_ids = [3, 17, 60, 99, 5, -1, 0]               # 99 and -1 are outside the pool: skipped
     n = len(out_ids)

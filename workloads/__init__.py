@@ -147,7 +147,7 @@ def cfg1(device="cpu"):
                         tables, 8, q, k, v, scale=1.0 / 8.0)
 
 
-def cfg2(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096):
+def cfg2(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096, block_size=BLOCK_SIZE):
     """GQA decode, bf16: B=32, Hq=32, Hkv=8, Dh=128; lengths all 4096 or
     uniform in [1, 4096]."""
     seed = SEEDS["cfg2"]
@@ -159,7 +159,7 @@ def cfg2(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096):
     else:
         raise ValueError(variant)
     return decode_inputs(f"cfg2-{variant}", seed, lens, 32, 8, 128, "bf16", device,
-                         copies=copies, rng=rng)
+                         block_size=block_size, copies=copies, rng=rng)
 
 
 def cfg3(batch=1, device="cpu", tokens=32768, layers=32):
@@ -181,7 +181,7 @@ def cfg3(batch=1, device="cpu", tokens=32768, layers=32):
     return out
 
 
-def cfg5(kind, device="cpu", batch=8, tokens=8192, copies=1):
+def cfg5(kind, device="cpu", batch=8, tokens=8192, copies=1, block_size=BLOCK_SIZE):
     """Head-layout / KV-dtype sweep at T=8192, B=8, Dh=128: "mha" 32/32,
     "gqa" 32/8, "mqa" 32/1 in bf16, "gqa-fp8" 32/8 with e4m3 storage."""
     seed = SEEDS["cfg5"]
@@ -190,7 +190,7 @@ def cfg5(kind, device="cpu", batch=8, tokens=8192, copies=1):
     rng = np.random.default_rng(seed)
     lens = np.full(batch, tokens, dtype=np.int32)
     return decode_inputs(f"cfg5-{kind}", seed, lens, 32, hkv, 128, dt, device,
-                         copies=copies, rng=rng)
+                         block_size=block_size, copies=copies, rng=rng)
 
 
 @dataclass
