@@ -36,6 +36,7 @@ unchanged) plus a text summary.
 
 import argparse
 import csv
+import ctypes
 import hashlib
 import json
 import math
@@ -53,7 +54,8 @@ PCIE5_X16_GBS = 32.0 * 16 * 128 / 130 / 8   # 63.0 GB/s per direction
 MALL_BYTES = 2 * 2 ** 30          # rotate through at least this much pool memory
 CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h"]
+DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h",
+                  "paged_kv_cache_430_amd/csrc/append_common.h"]
 DECODE_WORKLOADS = ["cfg2-all4096", "cfg2-uniform", "cfg5-mha", "cfg5-gqa", "cfg5-mqa", "cfg5-gqa-fp8",
                     "cfg3-b1", "cfg3-b4"]
 
@@ -69,7 +71,8 @@ def parse():
                    help="tokens per pool block for the cfg2/cfg5 decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--unfused", action="store_true",
-                   help="decode workloads: append in its own launch before the decode (default: one launch)")
+                   help="decode workloads: append in its own launch before the decode (default: one launch); "
+                        "cfg4-mixed: append, prefill and decode as three calls (default: pkv_attn_mixed_step)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
                    help="after timing, copy a 256 MiB scratch cache with pkv_copy_blocks (counter calibration)")
@@ -489,6 +492,22 @@ def run_cfg4(args, dev):
     wsb = ws.numel() if ws is not None else 0
     at = S["all_tables"]
 
+    # the mixed step: one decode launch whose last workgroups append the
+    # chunk's 512 tokens (each decode appends its own), then the prefill
+    r = m.chunk
+    k_ch, v_ch = S["new_k"][:r], S["new_v"][:r]
+    k_dec, v_dec = S["new_k"][r:], S["new_v"][r:]
+    chunk_b = pkv._ChunkBatch(1, m.chunk_q.data_ptr(), S["q_start"].data_ptr(), k_ch.data_ptr(), v_ch.data_ptr(),
+                              S["chunk_table"].data_ptr(), S["max_blocks"], S["chunk_lens"].data_ptr(), m.chunk,
+                              out_p.data_ptr())
+    dec_b = pkv._DecodeBatch(n_dec, m.decode_q.data_ptr(), k_dec.data_ptr(), v_dec.data_ptr(),
+                             S["dec_tables"].data_ptr(), S["max_blocks"], S["dec_lens"].data_ptr(), msl,
+                             args.partition, out_d.data_ptr(), wsp, wsb)
+
+    def mixed_step():
+        pkv._check(lib.pkv_attn_mixed_step(S["cache"].ref(), hq, m.scale, ctypes.byref(chunk_b),
+                                           ctypes.byref(dec_b), sh))
+
     def step(tp=None, td=None):
         pkv._check(lib.pkv_kv_append_paged(S["cache"].ref(), S["new_k"].data_ptr(), S["new_v"].data_ptr(),
                                            pkv.PKV_BF16, at.shape[0], S["cu_new"].data_ptr(), S["first_pos"].data_ptr(),
@@ -508,17 +527,19 @@ def run_cfg4(args, dev):
         if td is not None:
             td.stop()
 
+    timed_step = step if args.unfused else mixed_step
     for _ in range(args.warmup):
-        step()
+        timed_step()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        timed_step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+    # the kernels one by one (separate calls) with events around each
     tp, td = Timer(stream, args.steps), Timer(stream, args.steps)
     for _ in range(args.steps):
         step(tp, td)
@@ -546,7 +567,9 @@ def run_cfg4(args, dev):
         "config": {"workload": "cfg4-mixed", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
                    "prefix_tokens": S["p0"], "chunk": m.chunk, "shared_prefix_tokens": m.shared,
                    "sharers": m.n_share, "decodes": n_dec,
-                   "decode_ctx_mean": float(np.mean(m.decode_ctx)) + 1.0},
+                   "decode_ctx_mean": float(np.mean(m.decode_ctx)) + 1.0,
+                   "step": ("append launch + prefill + decode" if args.unfused else
+                            "pkv_attn_mixed_step: decode launch that also appends the chunk, then the prefill")},
         "prefill_us": stats_us(p_ms),
         "prefill_flops": flops,
         "decode_us": stats_us(d_ms),

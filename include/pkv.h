@@ -258,14 +258,65 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   seq_lens: device int32 [num_seqs], T_s >= C_s
  *   max_q_len: host bound on C_s (sizes the grid)
  *   out:      device fp32, same shape as q
- * Cache dtype BF16; head_dim 64 or 128; Hq/Hkv in {1, 2, 4, 8, 16, 32}.
- * No workspace is needed (pass NULL, 0). */
+ * Cache dtype BF16, block_size 16; head_dim 64 or 128; Hq/Hkv 1, 2 or a
+ * multiple of 4 up to 64. No workspace is needed (pass NULL, 0). */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,
                                    const int32_t* seq_lens, int32_t max_q_len, float scale,
                                    float* out, void* workspace, size_t workspace_bytes,
                                    pkv_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * One continuous-batching step over a mixed batch — [P3] 6.6 (at an
+ * iteration boundary some sequences run a prefill chunk while the others
+ * decode one token; chunked prefill keeps long prompts from starving the
+ * decodes); [P2] Q025 and [P3] 6.1 (append a token's K/V, then attend).
+ *
+ * The chunk sequences' new K/V are appended and their chunks attend causally
+ * (as pkv_kv_append_paged followed by pkv_attn_prefill_chunk), and every
+ * decode sequence appends its token and attends (as pkv_attn_decode_append).
+ * Two launches on the stream instead of three: the decode kernel, whose
+ * last workgroups write the chunks' tokens, then the prefill kernel (a third,
+ * the split-KV reduce, when the decodes use more than one partition). The
+ * pool bytes and both outputs are bit-identical to the separate calls'.
+ *   chunks:  see pkv_chunk_batch; num_seqs may be 0
+ *   decodes: see pkv_decode_batch; batch may be 0
+ * BF16 cache and inputs, block_size 16, the matrix-core decode whatever
+ * PKV_DECODE_KERNEL says. A chunk's new positions must not lie in blocks the
+ * decodes read (shared prefix blocks are full, so copy-on-write of a shared
+ * tail keeps this). */
+typedef struct pkv_chunk_batch {
+  int32_t num_seqs;
+  const void* q;                 /* as pkv_attn_prefill_chunk                    */
+  const int32_t* q_start;
+  const void* k_new;             /* device [q_start[num_seqs], Hkv, head_dim]:  */
+  const void* v_new;             /*   rows of sequence s are its last C_s tokens */
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* seq_lens;       /* T_s, the chunk's tokens included           */
+  int32_t max_q_len;
+  float* out;
+} pkv_chunk_batch;
+
+typedef struct pkv_decode_batch {   /* as pkv_attn_decode_append              */
+  int32_t batch;
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  int32_t max_blocks;               /* >= 1 even when batch is 0             */
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t partition_tokens;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_decode_batch;
+
+PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, float scale,
+                                const pkv_chunk_batch* chunks, const pkv_decode_batch* decodes,
+                                pkv_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Copy-on-write block copy — [P2] Q028 (sharing a partly filled last block

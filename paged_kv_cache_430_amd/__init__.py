@@ -19,7 +19,7 @@ __all__ = [
     "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
     "pkv_attn_decode_append",
-    "pkv_attn_prefill_chunk", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
+    "pkv_attn_prefill_chunk", "pkv_attn_mixed_step", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]
 
@@ -47,6 +47,21 @@ class _CacheStruct(ctypes.Structure):
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
+class _ChunkBatch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("q", ctypes.c_void_p), ("q_start", ctypes.c_void_p),
+                ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+                ("max_blocks", ctypes.c_int32), ("seq_lens", ctypes.c_void_p), ("max_q_len", ctypes.c_int32),
+                ("out", ctypes.c_void_p)]
+
+
+class _DecodeBatch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("max_seq_len", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _SIGS = {
     "pkv_version": (_I32, []),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -64,6 +79,8 @@ _SIGS = {
                                               ctypes.c_size_t, _VP]),
     "pkv_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _VP,
                                               _I32, _VP, _I32, ctypes.c_float, _VP, _VP, ctypes.c_size_t, _VP]),
+    "pkv_attn_mixed_step": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _I32, ctypes.c_float,
+                                           ctypes.POINTER(_ChunkBatch), ctypes.POINTER(_DecodeBatch), _VP]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP]),
     "pkv_debug_gather": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, _VP, _VP]),
     "pkv_swap_out": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, ctypes.c_size_t, _VP]),
@@ -249,6 +266,31 @@ def pkv_attn_decode_append(cache, k_new, v_new, q, block_tables, seq_lens, max_s
                                          block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
                                          partition_tokens, _ptr(out), _ptr(workspace), wbytes, _stream(stream, dev)))
     return out
+
+
+def pkv_attn_mixed_step(cache, scale, chunk_q, chunk_k_new, chunk_v_new, q_start, chunk_tables, chunk_lens, max_q_len,
+                        dec_q, dec_k_new, dec_v_new, dec_tables, dec_lens, max_seq_len, partition_tokens=0,
+                        chunk_out=None, dec_out=None, workspace=None, stream=None):
+    """One mixed continuous-batching step (bf16 cache): the chunks' tokens are
+    appended and their chunks attend causally; each decode sequence appends its
+    token and attends. Returns (chunk_out, dec_out)."""
+    dev = dec_q.device
+    b, hq, dh = dec_q.shape
+    n_chunks = len(chunk_lens)
+    if chunk_out is None:
+        chunk_out = torch.empty(chunk_q.shape[0], hq, dh, dtype=torch.float32, device=dev)
+    if dec_out is None:
+        dec_out = torch.empty(b, hq, dh, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = decode_workspace(cache.dtype, b, hq, cache.num_kv_heads, dh, max_seq_len, partition_tokens, dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ch = _ChunkBatch(n_chunks, _ptr(chunk_q), _ptr(q_start), _ptr(chunk_k_new), _ptr(chunk_v_new), _ptr(chunk_tables),
+                     chunk_tables.shape[1], _ptr(chunk_lens), max_q_len, _ptr(chunk_out))
+    de = _DecodeBatch(b, _ptr(dec_q), _ptr(dec_k_new), _ptr(dec_v_new), _ptr(dec_tables), dec_tables.shape[1],
+                      _ptr(dec_lens), max_seq_len, partition_tokens, _ptr(dec_out), _ptr(workspace), wbytes)
+    _check(load().pkv_attn_mixed_step(cache.ref(), hq, float(scale), ctypes.byref(ch), ctypes.byref(de),
+                                      _stream(stream, dev)))
+    return chunk_out, dec_out
 
 
 def pkv_attn_prefill_chunk(cache, q, q_start, block_tables, seq_lens, max_q_len, scale, out=None, stream=None):

@@ -40,6 +40,7 @@
 // Masked slots (past the sequence end) are selected out or read as zeros,
 // never multiplied by zero, and blocks whose id is outside the pool are
 // skipped: pool slots may hold NaN.
+#include "append_common.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -93,6 +94,17 @@ struct KernelArgs {
   const float* v_inv;
   int new_dtype;
   int block_size;    // pool block: 16, 32 or 64 tokens (the matrix-core form; 16 for the vector form)
+  // Further appends done by the last x_wgs workgroups of the matrix-core
+  // form, kExtraTokens tokens each (a mixed step's prefill chunks): sequence
+  // s's rows x_cu[s] … x_cu[s+1]−1 of x_k / x_v (new_dtype) are its last
+  // C_s = x_cu[s+1] − x_cu[s] positions, x_lens[s] − C_s …, placed through
+  // row s of x_tables.
+  const uint8_t* x_k;
+  const uint8_t* x_v;
+  const int32_t* x_cu;
+  const int32_t* x_lens;
+  const int32_t* x_tables;
+  int x_max_blocks, x_seqs, x_wgs_per_seq, x_wgs;
 };
 
 struct MergeArgs {
@@ -671,7 +683,33 @@ __device__ __forceinline__ void new_token_bytes(const uint8_t* base, size_t elem
   }
 }
 
-template <int KV, int DH, int NW, bool APPEND>
+// A mixed step's further appends: extra workgroup idx takes kExtraTokens
+// tokens of one sequence, NTH / kExtraTokens threads per token, each token
+// stored exactly as the append kernels store it.
+constexpr int kExtraTokens = 16;
+template <int KV, int DH, int NTH>
+__device__ __forceinline__ void extra_append(const KernelArgs& a, int idx) {
+  constexpr int per = NTH / kExtraTokens;
+  const int s = idx / a.x_wgs_per_seq, j = idx % a.x_wgs_per_seq;
+  if (s >= a.x_seqs) return;
+  const int lo = a.x_cu[s], C = a.x_cu[s + 1] - lo;
+  const int i = j * kExtraTokens + (int)threadIdx.x / per;
+  if (i >= C) return;
+  const int slot = slot_of(a.x_tables + (size_t)s * a.x_max_blocks, a.x_max_blocks, a.x_lens[s] - C + i,
+                           a.block_size);
+  const int t0 = (int)threadIdx.x % per;
+  if constexpr (KV == kFP8) {
+    if (a.new_dtype == kF32) {
+      append_token<kF32, KV>(a.x_k, a.x_v, lo + i, slot, a.kc, a.vc, a.num_blocks, a.hkv, DH, a.k_inv, a.v_inv,
+                             t0, per, a.block_size);
+      return;
+    }
+  }
+  append_token<kBF16, KV>(a.x_k, a.x_v, lo + i, slot, a.kc, a.vc, a.num_blocks, a.hkv, DH, a.k_inv, a.v_inv, t0,
+                          per, a.block_size);
+}
+
+template <int KV, int DH, int NW, bool APPEND, bool EXTRA>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   constexpr int kWaves = NW, kThreads = NW * kWave;
   constexpr int NH = kMfmaHeads;
@@ -686,7 +724,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   __shared__ float sh_m[kWaves][NH];
   __shared__ float sh_l[kWaves][NH];
 
-  const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
+  uint32_t flat = flat_block_id(), nflat = flat_grid_size();
+  if constexpr (EXTRA) {   // the last x_wgs workgroups only append; they fill the decode's ragged tail
+    nflat -= a.x_wgs;
+    if (flat >= nflat) {
+      extra_append<KV, DH, kThreads>(a, (int)(flat - nflat));
+      return;
+    }
+  }
+  const uint32_t L = xcd_logical_index(flat, nflat);
   const int chunk = L % a.num_chunks;
   const int part = (L / a.num_chunks) % a.num_parts;
   const int g = (L / a.num_chunks / a.num_parts) % a.hkv;
@@ -1033,12 +1079,19 @@ hipError_t launch_t(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
 template <int KV, int DH>
 hipError_t launch_mfma(const DecodeParams& p, const KernelArgs& a, hipStream_t s) {
   const size_t n = (size_t)p.batch * p.cache.num_kv_heads * a.num_chunks * p.num_parts;
+  const dim3 block(kDecodeWaves * kWave);
+  if (a.x_wgs > 0) {
+    if constexpr (KV == kBF16) {
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, true>), dim3((unsigned)(n + a.x_wgs)),
+                         block, 0, s, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;   // the mixed step takes bf16 caches only
+  }
   if (a.k_new)
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true>), dim3((unsigned)n),
-                       dim3(kDecodeWaves * kWave), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, false>), dim3((unsigned)n), block, 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, false>), dim3((unsigned)n),
-                       dim3(kDecodeWaves * kWave), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, false, false>), dim3((unsigned)n), block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1063,7 +1116,7 @@ int decode_heads_per_wg(int group, int kernel) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  if (p.batch == 0) return hipSuccess;
+  if (p.batch == 0 && p.x_seqs == 0) return hipSuccess;
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int hc = decode_heads_per_wg(group, p.kernel);
   KernelArgs a;
@@ -1092,6 +1145,16 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.v_inv = p.v_inv;
   a.new_dtype = p.new_dtype;
   a.block_size = p.cache.block_size;
+  a.x_k = static_cast<const uint8_t*>(p.x_k);
+  a.x_v = static_cast<const uint8_t*>(p.x_v);
+  a.x_cu = p.x_cu;
+  a.x_lens = p.x_lens;
+  a.x_tables = p.x_tables;
+  a.x_max_blocks = p.x_max_blocks;
+  a.x_seqs = p.x_seqs;
+  a.x_wgs_per_seq = (p.x_max_q + kExtraTokens - 1) / kExtraTokens;
+  a.x_wgs = p.x_seqs > 0 && a.x_wgs_per_seq > 0 ? (p.x_seqs * a.x_wgs_per_seq + 7) / 8 * 8 : 0;
+  if (a.x_wgs > 0 && p.kernel != kDecodeMatrix) return hipErrorInvalidValue;
   const int dt = p.cache.dtype, dh = p.cache.head_dim;
   hipError_t e;
   if (p.kernel == kDecodeMatrix)
@@ -1100,7 +1163,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   else if (dt == kF32) e = dh == 64 ? launch_hc<kF32, 64>(p, a, hc, s) : launch_hc<kF32, 128>(p, a, hc, s);
   else if (dt == kBF16) e = dh == 64 ? launch_hc<kBF16, 64>(p, a, hc, s) : launch_hc<kBF16, 128>(p, a, hc, s);
   else e = dh == 64 ? launch_hc<kFP8, 64>(p, a, hc, s) : launch_hc<kFP8, 128>(p, a, hc, s);
-  if (e != hipSuccess || p.num_parts <= 1) return e;
+  if (e != hipSuccess || p.batch == 0 || p.num_parts <= 1) return e;
   MergeArgs m;
   m.ws_ml = p.ws_ml;
   m.ws_u = p.ws_u;

@@ -7,7 +7,7 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;   // tokens per KV block (the only size the kernels take)
+constexpr int kBlockSize = 16;   // the kernels' unit of 16 token rows (a pool block of bs holds bs/16)
 constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kNumXcd = 8;       // MI355X: 8 accelerator dies, each with its own L2
 

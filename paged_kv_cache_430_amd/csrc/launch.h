@@ -67,6 +67,17 @@ struct DecodeParams {
   int new_dtype = 0;
   const float* k_inv = nullptr;
   const float* v_inv = nullptr;
+  // A mixed step's prefill-chunk tokens, appended by extra workgroups of the
+  // same launch (matrix kernel, bf16 cache): sequence s's rows x_cu[s] …
+  // x_cu[s+1]−1 of x_k / x_v go to its last x_cu[s+1] − x_cu[s] positions
+  // (before x_lens[s]) through row s of x_tables; x_max_q bounds the rows
+  // per sequence.
+  const void* x_k = nullptr;
+  const void* x_v = nullptr;
+  const int32_t* x_cu = nullptr;
+  const int32_t* x_lens = nullptr;
+  const int32_t* x_tables = nullptr;
+  int x_max_blocks = 0, x_seqs = 0, x_max_q = 0;
 };
 
 // Waves of one split-KV decode workgroup. A wave reads its share of the

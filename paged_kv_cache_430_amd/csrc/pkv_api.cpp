@@ -266,13 +266,20 @@ struct NewTokens {   // the fused append's inputs
   const float* v_inv;
 };
 
-static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* app, const void* q, int32_t q_dtype,
-                       int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
-                       const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
-                       float* out, void* workspace, size_t workspace_bytes, pkv_stream stream) {
-  clear_error();
-  CacheView c;
-  if (int st = validate_cache(cache, fn, &c)) return st;
+// Checks a decode call's arguments and fills *p (kernel chosen by the
+// caller); p->batch == 0 means nothing to launch.
+static int decode_prepare(const char* fn, const CacheView& c, const NewTokens* app, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
+                          float* out, void* workspace, size_t workspace_bytes, int kernel, hipStream_t s,
+                          DecodeParams* p) {
+  p->cache = c;
+  p->batch = 0;
+  p->num_q_heads = num_q_heads;
+  p->max_blocks = max_blocks;
+  p->kernel = kernel;
+  p->num_parts = 1;
+  p->part_tokens = 16;
   if (batch < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_seq_len < 0)
     return fail(PKV_EINVAL, std::string(fn) + ": bad size");
   if (num_q_heads % c.num_kv_heads != 0) return fail(PKV_EINVAL, std::string(fn) + ": num_q_heads must be a multiple of num_kv_heads");
@@ -294,7 +301,6 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
     if (!aligned16(app->k_new) || !aligned16(app->v_new))
       return fail(PKV_EINVAL, std::string(fn) + ": k_new / v_new must be 16-byte aligned");
   }
-  const int kernel = decode_kernel_for(c.dtype);
   if (c.block_size != 16 && kernel != kDecodeMatrix)
     return fail(PKV_EINVAL, std::string(fn) + ": block sizes other than 16 need the matrix-core decode (bf16 or fp8 cache)");
   const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
@@ -303,7 +309,6 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) + " bytes");
   if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, std::string(fn) + ": workspace must be 16-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (check_mode()) {
     std::vector<int32_t> lens, bt;
     if (int st = copy_to_host(lens, seq_lens, (size_t)batch, s)) return st;
@@ -315,37 +320,96 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
       if (int st = check_tables(bt, max_blocks, b, lens[b], c.num_blocks, fn, c.block_size)) return st;
     }
   }
-  DecodeParams p;
-  p.cache = c;
-  p.q = q;
-  p.batch = batch;
-  p.num_q_heads = num_q_heads;
-  p.max_blocks = max_blocks;
-  p.max_seq_len = max_seq_len;
-  p.part_tokens = pt;
-  p.num_parts = parts;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  p.scale = scale;
-  p.out = out;
-  p.kernel = kernel;
+  p->q = q;
+  p->batch = batch;
+  p->max_seq_len = max_seq_len;
+  p->part_tokens = pt;
+  p->num_parts = parts;
+  p->block_tables = block_tables;
+  p->seq_lens = seq_lens;
+  p->scale = scale;
+  p->out = out;
   float* ws = static_cast<float*>(workspace);
   const size_t rows = (size_t)batch * num_q_heads;
-  p.ws_u = need ? ws : nullptr;
-  p.ws_ml = need ? ws + rows * parts * c.head_dim : nullptr;
-  if (app) {
-    if (kernel == kDecodeMatrix) {   // the split kernel writes and reads the new tokens itself
-      p.k_new = app->k_new;
-      p.v_new = app->v_new;
-      p.new_dtype = app->in_dtype;
-      p.k_inv = app->k_inv;
-      p.v_inv = app->v_inv;
-    } else if (hipError_t e = launch_kv_append_last(c, app->k_new, app->v_new, app->in_dtype, batch, block_tables,
-                                                    max_blocks, seq_lens, max_seq_len, app->k_inv, app->v_inv, s)) {
+  p->ws_u = need ? ws : nullptr;
+  p->ws_ml = need ? ws + rows * parts * c.head_dim : nullptr;
+  if (app && kernel == kDecodeMatrix) {   // the split kernel writes and reads the new tokens itself
+    p->k_new = app->k_new;
+    p->v_new = app->v_new;
+    p->new_dtype = app->in_dtype;
+    p->k_inv = app->k_inv;
+    p->v_inv = app->v_inv;
+  }
+  return PKV_OK;
+}
+
+static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* app, const void* q, int32_t q_dtype,
+                       int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
+                       float* out, void* workspace, size_t workspace_bytes, pkv_stream stream) {
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, fn, &c)) return st;
+  const int kernel = decode_kernel_for(c.dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  if (int st = decode_prepare(fn, c, app, q, q_dtype, batch, num_q_heads, block_tables, max_blocks, seq_lens,
+                              max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes, kernel, s, &p))
+    return st;
+  if (p.batch == 0) return PKV_OK;
+  if (app && kernel != kDecodeMatrix) {   // the vector form: an append launch first
+    if (hipError_t e = launch_kv_append_last(c, app->k_new, app->v_new, app->in_dtype, batch, block_tables,
+                                             max_blocks, seq_lens, max_seq_len, app->k_inv, app->v_inv, s))
       return hip_status(e, fn);
-    }
   }
   return hip_status(launch_decode(p, s), fn);
+}
+
+// Checks a prefill call's arguments and fills *p; p->num_seqs == 0 means
+// nothing to launch.
+static int prefill_prepare(const char* fn, const CacheView& c, const void* q, int32_t q_dtype, int32_t num_seqs,
+                           int32_t num_q_heads, const int32_t* q_start, const int32_t* block_tables,
+                           int32_t max_blocks, const int32_t* seq_lens, int32_t max_q_len, float scale, float* out,
+                           hipStream_t s, PrefillParams* p) {
+  p->num_seqs = 0;
+  if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16) return fail(PKV_EDTYPE, std::string(fn) + ": cache and q must be BF16");
+  if (c.block_size != 16) return fail(PKV_EINVAL, std::string(fn) + ": block_size must be 16");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
+    return fail(PKV_EINVAL, std::string(fn) + ": bad size");
+  if (num_q_heads % c.num_kv_heads != 0)
+    return fail(PKV_EINVAL, std::string(fn) + ": num_q_heads must be a multiple of num_kv_heads");
+  const int group = num_q_heads / c.num_kv_heads;
+  if (!(group == 1 || group == 2 || (group % 4 == 0 && group <= 64)))
+    return fail(PKV_EINVAL, std::string(fn) + ": Hq/Hkv must be 1, 2 or a multiple of 4 up to 64");
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!q || !q_start || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, std::string(fn) + ": q and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, std::string(fn) + ": scale is not finite");
+  if (check_mode()) {
+    std::vector<int32_t> qs, lens, bt;
+    if (int st = copy_to_host(qs, q_start, (size_t)num_seqs + 1, s)) return st;
+    if (int st = copy_to_host(lens, seq_lens, (size_t)num_seqs, s)) return st;
+    if (int st = copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, s)) return st;
+    if (qs[0] != 0) return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: q_start[0] != 0");
+    for (int i = 0; i < num_seqs; ++i) {
+      const int cq = qs[i + 1] - qs[i];
+      if (cq < 0 || cq > max_q_len || lens[i] < cq || (int64_t)lens[i] > (int64_t)max_blocks * 16)
+        return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: bad q_start / seq_lens for sequence " + std::to_string(i));
+      if (int st = check_tables(bt, max_blocks, i, lens[i], c.num_blocks, fn)) return st;
+    }
+  }
+  p->cache = c;
+  p->q = q;
+  p->num_seqs = num_seqs;
+  p->num_q_heads = num_q_heads;
+  p->max_blocks = max_blocks;
+  p->max_q_len = max_q_len;
+  p->q_start = q_start;
+  p->block_tables = block_tables;
+  p->seq_lens = seq_lens;
+  p->scale = scale;
+  p->out = out;
+  return PKV_OK;
 }
 
 extern "C" {
@@ -382,48 +446,56 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
   clear_error();
   CacheView c;
   if (int st = validate_cache(cache, "pkv_attn_prefill_chunk", &c)) return st;
-  if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16)
-    return fail(PKV_EDTYPE, "pkv_attn_prefill_chunk: cache and q must be BF16");
-  if (c.block_size != 16) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: block_size must be 16");
-  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
-    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: bad size");
-  if (num_q_heads % c.num_kv_heads != 0)
-    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: num_q_heads must be a multiple of num_kv_heads");
-  const int group = num_q_heads / c.num_kv_heads;
-  if (!(group == 1 || group == 2 || (group % 4 == 0 && group <= 64)))
-    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: Hq/Hkv must be 1, 2 or a multiple of 4 up to 64");
-  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
-  if (!q || !q_start || !block_tables || !seq_lens || !out)
-    return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: NULL pointer");
-  if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: q and out must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: scale is not finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (check_mode()) {
-    std::vector<int32_t> qs, lens, bt;
-    if (int st = copy_to_host(qs, q_start, (size_t)num_seqs + 1, s)) return st;
-    if (int st = copy_to_host(lens, seq_lens, (size_t)num_seqs, s)) return st;
-    if (int st = copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, s)) return st;
-    if (qs[0] != 0) return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: PKV_CHECK: q_start[0] != 0");
-    for (int i = 0; i < num_seqs; ++i) {
-      const int cq = qs[i + 1] - qs[i];
-      if (cq < 0 || cq > max_q_len || lens[i] < cq || (int64_t)lens[i] > (int64_t)max_blocks * 16)
-        return fail(PKV_EINVAL, "pkv_attn_prefill_chunk: PKV_CHECK: bad q_start / seq_lens for sequence " + std::to_string(i));
-      if (int st = check_tables(bt, max_blocks, i, lens[i], c.num_blocks, "pkv_attn_prefill_chunk")) return st;
-    }
-  }
   PrefillParams p;
-  p.cache = c;
-  p.q = q;
-  p.num_seqs = num_seqs;
-  p.num_q_heads = num_q_heads;
-  p.max_blocks = max_blocks;
-  p.max_q_len = max_q_len;
-  p.q_start = q_start;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  p.scale = scale;
-  p.out = out;
+  if (int st = prefill_prepare("pkv_attn_prefill_chunk", c, q, q_dtype, num_seqs, num_q_heads, q_start, block_tables,
+                               max_blocks, seq_lens, max_q_len, scale, out, s, &p))
+    return st;
+  if (p.num_seqs == 0) return PKV_OK;
   return hip_status(launch_prefill(p, s), "pkv_attn_prefill_chunk");
+}
+
+PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, float scale,
+                                const pkv_chunk_batch* chunks, const pkv_decode_batch* decodes,
+                                pkv_stream stream) {
+  const char* fn = "pkv_attn_mixed_step";
+  clear_error();
+  CacheView c;
+  if (int st = validate_cache(cache, fn, &c)) return st;
+  if (!chunks || !decodes) return fail(PKV_EINVAL, std::string(fn) + ": chunks / decodes is NULL");
+  if (c.dtype != PKV_BF16) return fail(PKV_EDTYPE, std::string(fn) + ": the cache must be BF16");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PrefillParams pp;
+  if (int st = prefill_prepare(fn, c, chunks->q, PKV_BF16, chunks->num_seqs, num_q_heads, chunks->q_start,
+                               chunks->block_tables, chunks->max_blocks, chunks->seq_lens, chunks->max_q_len, scale,
+                               chunks->out, s, &pp))
+    return st;
+  if (pp.num_seqs > 0) {
+    if (!chunks->k_new || !chunks->v_new) return fail(PKV_EINVAL, std::string(fn) + ": chunk k_new / v_new is NULL");
+    if (!aligned16(chunks->k_new) || !aligned16(chunks->v_new))
+      return fail(PKV_EINVAL, std::string(fn) + ": chunk k_new / v_new must be 16-byte aligned");
+  }
+  const NewTokens app{decodes->k_new, decodes->v_new, PKV_BF16, nullptr, nullptr};
+  DecodeParams dp;
+  if (int st = decode_prepare(fn, c, &app, decodes->q, PKV_BF16, decodes->batch, num_q_heads, decodes->block_tables,
+                              decodes->max_blocks, decodes->seq_lens, decodes->max_seq_len, scale,
+                              decodes->partition_tokens, decodes->out, decodes->workspace, decodes->workspace_bytes,
+                              kDecodeMatrix, s, &dp))
+    return st;
+  if (pp.num_seqs > 0) {   // the chunks' tokens: extra workgroups of the decode launch
+    dp.x_k = chunks->k_new;
+    dp.x_v = chunks->v_new;
+    dp.x_cu = chunks->q_start;
+    dp.x_lens = chunks->seq_lens;
+    dp.x_tables = chunks->block_tables;
+    dp.x_max_blocks = chunks->max_blocks;
+    dp.x_seqs = chunks->num_seqs;
+    dp.x_max_q = chunks->max_q_len;
+    dp.new_dtype = PKV_BF16;
+  }
+  if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
+  if (pp.num_seqs == 0) return PKV_OK;
+  return hip_status(launch_prefill(pp, s), fn);
 }
 
 PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const int32_t* dst, int32_t n,

@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 29
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
@@ -165,6 +165,29 @@ def test_block_size_rules(lib, monkeypatch):
         assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
                                           None, 0, None) == pkv.PKV_EINVAL
         assert "block_size" in lib.pkv_last_error().decode()
+
+
+def test_mixed_step_validation(lib):
+    ref, _ = _fake_cache()
+    ch = pkv._ChunkBatch(0, None, None, None, None, None, 1, None, 0, None)
+    de = pkv._DecodeBatch(0, None, None, None, None, 1, None, 1, 0, None, None, 0)
+    call = lambda r, c, d, hq=32: lib.pkv_attn_mixed_step(r, hq, 0.1, c, d, None)  # noqa: E731
+    assert call(ref, ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK        # nothing to do, nothing launched
+    assert call(ref, None, ctypes.byref(de)) == pkv.PKV_EINVAL
+    assert call(_fake_cache(dtype=pkv.PKV_FP8_E4M3)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EDTYPE
+    assert call(_fake_cache(bs=32)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EINVAL   # prefill: 16 only
+    assert call(ref, ctypes.byref(ch), ctypes.byref(de), hq=24) == pkv.PKV_EINVAL             # group 3
+    # a chunk without its new K/V is refused before any launch
+    ch2 = pkv._ChunkBatch(1, 0x50000, 0x1, None, None, 0x2, 4, 0x3, 16, 0x80000)
+    assert call(ref, ctypes.byref(ch2), ctypes.byref(de)) == pkv.PKV_EINVAL
+    ch3 = pkv._ChunkBatch(1, 0x50000, 0x1, 0x60008, 0x70000, 0x2, 4, 0x3, 16, 0x80000)
+    assert call(ref, ctypes.byref(ch3), ctypes.byref(de)) == pkv.PKV_EINVAL     # misaligned k_new
+    # decodes: the decode rules (workspace for split-KV partitions)
+    de2 = pkv._DecodeBatch(2, 0x50000, 0x60000, 0x70000, 0x1, 4, 0x2, 64, 16, 0x80000, None, 0)
+    assert call(ref, ctypes.byref(ch), ctypes.byref(de2)) == pkv.PKV_EWORKSPACE
+    de3 = pkv._DecodeBatch(2, 0x50000, None, 0x70000, 0x1, 4, 0x2, 64, 0, 0x80000, None, 0)
+    assert call(ref, ctypes.byref(ch), ctypes.byref(de3)) == pkv.PKV_EINVAL     # k_new NULL
+    assert "pkv_attn_mixed_step" in lib.pkv_last_error().decode()
 
 
 def test_append_and_prefill_validation(lib):

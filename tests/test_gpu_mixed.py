@@ -1,0 +1,155 @@
+"""GPU: one mixed continuous-batching step (pkv_attn_mixed_step) against the
+separate calls — pkv_kv_append_paged for every new token, then
+pkv_attn_prefill_chunk and pkv_attn_decode — with the pool bytes and both
+outputs bit-identical, and against the oracle within 2e-3. The new tokens'
+slots hold NaN before the step."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_430_amd as pkv
+from oracle import attention
+
+from gpu_helpers import device, new_pools
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(shape, gen, dev):
+    return torch.randn(*shape, generator=gen, device=dev).to(torch.bfloat16)
+
+
+def _f64(t):
+    return t.float().cpu().double().numpy()
+
+
+def _case(dev, chunks, dec_ctx, hq, hkv, dh, seed):
+    """chunks: (prefix P, chunk C) per prefill sequence; dec_ctx: cached tokens
+    of each decode sequence before its new one. Prefixes and contexts are in
+    the pool; the step's tokens are not."""
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    lens = [p + c for p, c in chunks] + [t + 1 for t in dec_ctx]
+    nblk = [-(-t // 16) for t in lens]
+    max_blocks = max(nblk)
+    num_blocks = sum(nblk) + 7
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    pos = 0
+    for i, n in enumerate(nblk):
+        bt[i, :n] = perm[pos:pos + n]
+        pos += n
+    kp, vp = new_pools(num_blocks, hkv, dh, "bf16", dev)
+    cache = pkv.Cache(kp, vp)
+    ks = [_bf16((t, hkv, dh), gen, dev) for t in lens]
+    vs = [_bf16((t, hkv, dh), gen, dev) for t in lens]
+    first = [p for p, _ in chunks] + list(dec_ctx)          # first position appended by the step
+    for i in range(len(lens)):
+        if first[i] > 0:
+            s = pkv.pkv_slot_mapping(bt[i], 16, 0, first[i])
+            pkv.pkv_kv_append(cache, ks[i][:first[i]].contiguous(), vs[i][:first[i]].contiguous(),
+                              torch.from_numpy(s).to(dev))
+    n_ch = len(chunks)
+    qc = _bf16((sum(c for _, c in chunks), hq, dh), gen, dev)
+    qd = _bf16((len(dec_ctx), hq, dh), gen, dev)
+    new_k = torch.cat([ks[i][first[i]:] for i in range(len(lens))]).contiguous()
+    new_v = torch.cat([vs[i][first[i]:] for i in range(len(lens))]).contiguous()
+    n_new = [lens[i] - first[i] for i in range(len(lens))]
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    return dict(cache=cache, ks=ks, vs=vs, lens=lens, n_ch=n_ch, qc=qc, qd=qd, new_k=new_k, new_v=new_v,
+                cu=t(cu), first=t(np.array(first, dtype=np.int32)), max_new=max(n_new), bt=bt, t=t,
+                q_start=t(cu[:n_ch + 1]), chunk_tables=t(bt[:n_ch]), dec_tables=t(bt[n_ch:]),
+                chunk_lens=t(np.array(lens[:n_ch], dtype=np.int32)),
+                dec_lens=t(np.array(lens[n_ch:], dtype=np.int32)),
+                max_q=max([c for _, c in chunks] or [0]), msl=max(lens[n_ch:] or [1]),
+                scale=1.0 / np.sqrt(dh), n_chunk_rows=int(cu[n_ch]))
+
+
+def _clone(cache):
+    return pkv.Cache(cache.k.clone(), cache.v.clone())
+
+
+def _separate(c, cache, pt):
+    t = c["t"]
+    pkv.pkv_kv_append_paged(cache, c["new_k"], c["new_v"], t(c["bt"]), c["cu"], c["first"], c["max_new"])
+    out_p = out_d = None
+    if c["n_ch"]:
+        out_p = pkv.pkv_attn_prefill_chunk(cache, c["qc"], c["q_start"], c["chunk_tables"], c["chunk_lens"],
+                                           c["max_q"], c["scale"])
+    if len(c["lens"]) > c["n_ch"]:
+        out_d = pkv.pkv_attn_decode(cache, c["qd"], c["dec_tables"], c["dec_lens"], c["msl"], c["scale"],
+                                    partition_tokens=pt)
+    return out_p, out_d
+
+
+def _mixed(c, cache, pt):
+    r = c["n_chunk_rows"]
+    return pkv.pkv_attn_mixed_step(cache, c["scale"], c["qc"], c["new_k"][:r], c["new_v"][:r], c["q_start"],
+                                   c["chunk_tables"], c["chunk_lens"], c["max_q"], c["qd"], c["new_k"][r:],
+                                   c["new_v"][r:], c["dec_tables"], c["dec_lens"], c["msl"], partition_tokens=pt)
+
+
+def _oracle_check(c, out_p, out_d):
+    n_ch, scale = c["n_ch"], c["scale"]
+    qs = c["q_start"].cpu().numpy()
+    if n_ch:
+        got = out_p.cpu().double().numpy()
+        qc = _f64(c["qc"])
+        for i in range(n_ch):
+            ref = attention.prefill_chunk(qc[qs[i]:qs[i + 1]], np.transpose(_f64(c["ks"][i]), (1, 0, 2)),
+                                          np.transpose(_f64(c["vs"][i]), (1, 0, 2)), scale)
+            assert np.abs(got[qs[i]:qs[i + 1]] - ref).max() <= 2e-3, f"chunk {i}"
+    got = out_d.cpu().double().numpy() if out_d is not None else None
+    qd = _f64(c["qd"])
+    for j in range(len(c["lens"]) - n_ch):
+        i = n_ch + j
+        ref = attention.decode(qd[j:j + 1], [np.transpose(_f64(c["ks"][i]), (1, 0, 2))],
+                               [np.transpose(_f64(c["vs"][i]), (1, 0, 2))], scale)[0]
+        assert np.abs(got[j] - ref).max() <= 2e-3, f"decode {j}"
+
+
+@pytest.mark.parametrize("hq,hkv,dh,pt", [(32, 8, 128, 0), (32, 8, 128, 64), (16, 2, 64, 0), (8, 8, 128, 32),
+                                          (32, 1, 64, 48)])
+def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt):
+    dev = device()
+    chunks = [(0, 1), (5, 17), (100, 64), (1000, 130), (31, 33)]
+    dec_ctx = [0, 1, 15, 16, 200, 1023, 77]
+    c = _case(dev, chunks, dec_ctx, hq, hkv, dh, seed=hq + 3 * hkv + dh + pt)
+    ref = _clone(c["cache"])
+    mix = _clone(c["cache"])
+    rp, rd = _separate(c, ref, pt)
+    mp, md = _mixed(c, mix, pt)
+    torch.cuda.synchronize()
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
+    assert torch.equal(mp, rp)
+    assert torch.equal(md, rd)
+    _oracle_check(c, mp, md)
+
+
+def test_mixed_step_chunks_only_and_decodes_only():
+    dev = device()
+    # chunks only: the decode launch carries just the appending workgroups
+    c = _case(dev, [(40, 100), (0, 16)], [], 32, 8, 128, seed=5)
+    ref, mix = _clone(c["cache"]), _clone(c["cache"])
+    rp, _ = _separate(c, ref, 0)
+    mp, md = _mixed(c, mix, 0)
+    torch.cuda.synchronize()
+    assert md.numel() == 0
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
+    assert torch.equal(mp, rp)
+    _oracle_check(c, mp, None)
+    # decodes only
+    c = _case(dev, [], [3, 300, 4095], 32, 8, 128, seed=6)
+    ref, mix = _clone(c["cache"]), _clone(c["cache"])
+    _, rd = _separate(c, ref, 0)
+    mp, md = _mixed(c, mix, 0)
+    torch.cuda.synchronize()
+    assert mp.numel() == 0
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
+    assert torch.equal(md, rd)
+    _oracle_check(c, None, md)
