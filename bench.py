@@ -65,7 +65,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="cfg2-all4096", choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefix-index", "swap"])
+    p.add_argument("--workload", default="cfg2-all4096",
+                   choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefill-chunk", "prefix-index", "swap"])
+    p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
+    p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64],
                    help="tokens per pool block for the cfg2/cfg5 decode workloads")
@@ -607,6 +610,81 @@ def cpu_baseline_prefill(m, p0, flops):
 
 
 # ---------------------------------------------------------------------------
+# one prefill chunk alone (cfg4's head layout, any prefix and chunk length)
+# ---------------------------------------------------------------------------
+
+def run_prefill_chunk(args, dev):
+    """One sequence: a causal chunk of --chunk queries over --prefix cached
+    tokens plus the chunk's own (Hq=32, Hkv=8, Dh=128, bf16 N(0,1), 16-token
+    blocks at a seeded random permutation). A step is one
+    pkv_attn_prefill_chunk call; the kernel is the library's choice unless
+    PKV_PREFILL_KERNEL names one."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    hq, hkv, dh = 32, 8, 128
+    P, C = args.prefix, args.chunk
+    T = P + C
+    nb = -(-T // 16)
+    rng = np.random.default_rng(4306)
+    gen = torch.Generator(device=dev).manual_seed(4306)
+    kp = torch.randn(nb + 8, hkv, 16, dh, generator=gen, device=dev).to(torch.bfloat16)
+    vp = torch.randn(nb + 8, hkv, 16, dh, generator=gen, device=dev).to(torch.bfloat16)
+    cache = pkv.Cache(kp, vp)
+    table = torch.from_numpy(rng.permutation(nb + 8)[:nb].astype(np.int32)[None]).to(dev)
+    q = torch.randn(C, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
+    q_start = torch.tensor([0, C], dtype=torch.int32, device=dev)
+    lens = torch.tensor([T], dtype=torch.int32, device=dev)
+    out = torch.empty(C, hq, dh, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(dh)
+    stream = torch.cuda.current_stream(dev)
+    lib = pkv.load()
+
+    def step():
+        pkv._check(lib.pkv_attn_prefill_chunk(cache.ref(), q.data_ptr(), pkv.PKV_BF16, 1, hq, q_start.data_ptr(),
+                                              table.data_ptr(), nb, lens.data_ptr(), C, scale, out.data_ptr(), None,
+                                              0, stream.cuda_stream))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    timer = Timer(stream, args.steps)
+    for _ in range(args.steps):
+        timer.start()
+        step()
+        timer.stop()
+    torch.cuda.synchronize()
+    call = timer.ms()
+    avg = sum(call) / len(call)
+    flops = prefill_flops(P, C, hq, dh)
+    env = os.environ.get("PKV_PREFILL_KERNEL")
+    kernel = env if env in ("tiles", "columns") else ("columns" if C * hq < 256 * 64 and T <= 8192 else "tiles")
+    tf = flops / (avg * 1e-3) / 1e12
+    line = {
+        "metric": f"prefill chunk TFLOP/s (bf16 MFMA), C={C} on P={P}",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill-chunk", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
+                   "prefix_tokens": P, "chunk": C,
+                   "kernel": "prefill_kernel" if kernel == "tiles" else "decode_mfma_kernel (prefill columns)"},
+        "call_us": stats_us(call),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_launch": flops},
+    }
+    return line
+
+
+# ---------------------------------------------------------------------------
 # counter summaries
 # ---------------------------------------------------------------------------
 
@@ -825,6 +903,8 @@ def main():
         line = run_swap(args, dev)
     elif args.workload == "cfg4-mixed":
         line = run_cfg4(args, dev)
+    elif args.workload == "prefill-chunk":
+        line = run_prefill_chunk(args, dev)
     else:
         line = run_decode(args, dev)
     print(json.dumps(line), flush=True)

@@ -259,7 +259,15 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   max_q_len: host bound on C_s (sizes the grid)
  *   out:      device fp32, same shape as q
  * Cache dtype BF16, block_size 16; head_dim 64 or 128; Hq/Hkv 1, 2 or a
- * multiple of 4 up to 64. No workspace is needed (pass NULL, 0). */
+ * multiple of 4 up to 64. No workspace is needed (pass NULL, 0).
+ * Two kernels compute it: a tile kernel (64 query rows of one KV group per
+ * workgroup, key tiles shared through LDS), and the matrix-core decode kernel
+ * with (query head, query) pairs as its 16 columns and the keys split across
+ * its waves (tables of at most 8192 tokens). The call takes the column form
+ * when num_seqs · max_q_len · num_q_heads < 256 · 64 (too few rows to give
+ * every compute unit a tile kernel workgroup), the tile kernel otherwise;
+ * the environment variable PKV_PREFILL_KERNEL=tiles or =columns, read at
+ * every call, forces one where it applies. */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,

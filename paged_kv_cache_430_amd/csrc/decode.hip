@@ -105,6 +105,12 @@ struct KernelArgs {
   const int32_t* x_lens;
   const int32_t* x_tables;
   int x_max_blocks, x_seqs, x_wgs_per_seq, x_wgs;
+  // Chunked prefill on the matrix-core form: the 16 columns of a workgroup
+  // are (query head, query) pairs, 2^p_hg_shift heads × 16 / 2^p_hg_shift
+  // consecutive queries of one sequence; p_nqb query blocks per (sequence,
+  // KV head, head chunk); q_start as in the prefill call.
+  const int32_t* q_start;
+  int p_hg_shift, p_nqb;
 };
 
 struct MergeArgs {
@@ -593,17 +599,17 @@ struct MfmaGeometry {
   }
 };
 
-// n stored dwords (n = 1, 2 or 4) at a byte offset, non-temporal.
-template <int N>
+// n stored dwords (n = 1, 2 or 4) at a byte offset, with cache policy AUX.
+template <int N, int AUX = kCacheNonTemporal>
 __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&d)[N]) {
   if constexpr (N == 4) {
-    const uint4 x = buffer_load16_stream(r, off);
+    const uint4 x = buffer_load16_aux<AUX>(r, off);
     d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
   } else if constexpr (N == 2) {
-    const uint2 x = buffer_load8_stream(r, off);
+    const uint2 x = buffer_load8_aux<AUX>(r, off);
     d[0] = x.x; d[1] = x.y;
   } else {
-    d[0] = buffer_load4_stream(r, off);
+    d[0] = buffer_load4_aux<AUX>(r, off);
   }
 }
 
@@ -709,7 +715,7 @@ __device__ __forceinline__ void extra_append(const KernelArgs& a, int idx) {
                           per, a.block_size);
 }
 
-template <int KV, int DH, int NW, bool APPEND, bool EXTRA>
+template <int KV, int DH, int NW, bool APPEND, bool EXTRA, bool PREFILL = false>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   constexpr int kWaves = NW, kThreads = NW * kWave;
   constexpr int NH = kMfmaHeads;
@@ -733,13 +739,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     }
   }
   const uint32_t L = xcd_logical_index(flat, nflat);
-  const int chunk = L % a.num_chunks;
-  const int part = (L / a.num_chunks) % a.num_parts;
-  const int g = (L / a.num_chunks / a.num_parts) % a.hkv;
-  const int b = L / a.num_chunks / a.num_parts / a.hkv;
+  // decode: (sequence b, KV head g, head chunk, partition); prefill: (sequence
+  // b, KV head g, head chunk, query block qb), one partition over all keys
+  const int inner = PREFILL ? a.p_nqb : a.num_parts;
+  const int chunk = (L / (PREFILL ? a.p_nqb : 1)) % a.num_chunks;
+  const int part = PREFILL ? 0 : (L / a.num_chunks) % a.num_parts;
+  const int qblk = PREFILL ? L % a.p_nqb : 0;
+  const int g = (L / a.num_chunks / inner) % a.hkv;
+  const int b = L / a.num_chunks / inner / a.hkv;
   const int group = a.hq / a.hkv;
-  const int h0 = g * group + chunk * NH;
-  const int nh = min(NH, group - chunk * NH);                  // heads of this chunk
+  // prefill columns: head (col mod HG) of the chunk's HG heads, query qb·QB + col / HG
+  const int hg_shift = PREFILL ? a.p_hg_shift : 0;
+  const int h0 = PREFILL ? g * group + (chunk << hg_shift) : g * group + chunk * NH;
+  const int nh = PREFILL ? NH : min(NH, group - chunk * NH);   // columns of this workgroup
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -765,6 +777,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   // would also hold back every other scalar load issued before the first tile
   const int seq_len = (int)__builtin_amdgcn_raw_buffer_load_b32(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.seq_lens + b), 0, 4, kBufferRsrcWord3), 0, 0, 0);
+  int q_lo = 0, n_q = 0;   // prefill: the sequence's first query row and its query count C
+  if constexpr (PREFILL) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i qs = __builtin_amdgcn_raw_buffer_load_b64(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.q_start + b), 0, 8, kBufferRsrcWord3), 0, 0, 0);
+    q_lo = __builtin_amdgcn_readfirstlane(qs[0]);
+    n_q = __builtin_amdgcn_readfirstlane(qs[1]) - q_lo;
+  }
+  constexpr int kAux = PREFILL ? 0 : kCacheNonTemporal;   // prefill items share K/V through L2
 
 
   auto tile_rsrc = [&](const uint8_t* pool, int phys, int row0, int rows) {
@@ -784,9 +805,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     // K: whole rows per load (CPR lanes per row), restaged through LDS
 #pragma unroll
     for (int i = 0; i < G::NKI; ++i)
-      t.k[e][i] = buffer_load16_stream(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
+      t.k[e][i] = buffer_load16_aux<kAux>(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_dwords<VW>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+    for (int i = 0; i < 4; ++i) load_dwords<VW, kAux>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
   };
 
   // The wave's first block pair is requested from its table entries alone,
@@ -797,9 +818,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   for (int e = 0; e < 2; ++e)
     load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), unit_row0(2 * w + e), kBlockSize);
 
-  // q of head col as the B operand of each k-step (zeros past the chunk's heads)
+  // q of column col as the B operand of each k-step (zeros for an unused column)
+  const int qpb = NH >> hg_shift;                          // prefill: queries per query block
+  const int my_qi = qblk * qpb + (col >> hg_shift);        // prefill: this lane's column's query
   bf16x8_t qb[NDC];
-  {
+  if constexpr (PREFILL) {
+    const bool ok = my_qi < n_q;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((size_t)(q_lo + (ok ? my_qi : 0)) * a.hq + h0 + (col & ((1 << hg_shift) - 1))) * DH;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (ok) x = *reinterpret_cast<const uint4*>(qrow + G::k_elem(dc, kg));
+      qb[dc] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  } else {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.hq + h0 + (col < nh ? col : 0)) * DH;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
@@ -809,7 +842,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   }
 
   const int T = __builtin_amdgcn_readfirstlane(min(max(seq_len, 0), min(a.max_seq_len, a.max_blocks * bs)));
-  const int ntok = min(a.part_tokens, T - tok0);
+  // Keys the workgroup attends: decode, all T; prefill, up to its last
+  // query's position (query i of the chunk sits at T − C + i, causal and
+  // inclusive), each column masked at its own position.
+  int kend = T, my_pos = 0;
+  if constexpr (PREFILL) {
+    const int qlast = min(n_q, (qblk + 1) * qpb) - 1;
+    kend = __builtin_amdgcn_readfirstlane(qlast >= qblk * qpb ? max(0, T - n_q + qlast + 1) : 0);
+    my_pos = T - n_q + my_qi;
+  }
+  const int ntok = min(a.part_tokens, kend - tok0);
   const int nblk = ntok > 0 ? (ntok + kBlockSize - 1) / kBlockSize : 0;
   const int ntile = (nblk + 1) / 2;
   const int ntw = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;   // this wave's tiles
@@ -924,7 +966,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = 4 * kg + i < rows[e] ? st[e][i] * sc : -INFINITY;
+        bool keep = 4 * kg + i < rows[e];
+        if constexpr (PREFILL) keep = keep && block_index(j, e) * kBlockSize + 4 * kg + i <= my_pos;
+        const float v = keep ? st[e][i] * sc : -INFINITY;
         st[e][i] = v;
         mt = fmaxf(mt, v);
       }
@@ -1049,7 +1093,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       u = fmaf(wt, sh_u(ww, h, d), u);
       lt = fmaf(wt, sh_l[ww][h], lt);
     }
-    if (P == 1) {
+    if constexpr (PREFILL) {
+      const int qi = qblk * qpb + (h >> hg_shift);
+      if (qi < n_q)
+        a.out[((size_t)(q_lo + qi) * a.hq + h0 + (h & ((1 << hg_shift) - 1))) * DH + d] = lt > 0.0f ? u / lt : 0.0f;
+    } else if (P == 1) {
       a.out[((size_t)b * a.hq + h0 + h) * DH + d] = lt > 0.0f ? u * vscale / lt : 0.0f;
     } else {
       a.ws_u[(((size_t)b * a.hq + h0 + h) * P + part) * DH + d] = u * vscale;
@@ -1172,6 +1220,49 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const unsigned rows = (unsigned)((size_t)p.batch * p.num_q_heads);
   if (dh == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(rows), dim3(kMergeThreads), 0, s, m);
   else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(rows), dim3(kMergeThreads), 0, s, m);
+  return hipGetLastError();
+}
+
+int prefill_cols_heads(int group) {
+  int hg = 1;
+  while (hg < kMfmaHeads && group % (2 * hg) == 0) hg *= 2;
+  return hg;
+}
+
+hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s) {
+  if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
+  const int hkv = p.cache.num_kv_heads, group = p.num_q_heads / hkv;
+  const int hg = prefill_cols_heads(group);
+  if (p.max_blocks * kBlockSize > kPrefillColsMaxKeys || p.cache.block_size != kBlockSize || p.cache.dtype != kBF16)
+    return hipErrorInvalidValue;
+  KernelArgs a = {};
+  a.kc = static_cast<uint8_t*>(p.cache.k);
+  a.vc = static_cast<uint8_t*>(p.cache.v);
+  a.q = p.q;
+  a.block_tables = p.block_tables;
+  a.seq_lens = p.seq_lens;
+  a.out = p.out;
+  a.num_blocks = p.cache.num_blocks;
+  a.hkv = hkv;
+  a.hq = p.num_q_heads;
+  a.max_blocks = p.max_blocks;
+  a.max_seq_len = p.max_blocks * kBlockSize;
+  a.part_tokens = p.max_blocks * kBlockSize;
+  a.num_parts = 1;
+  a.num_chunks = group / hg;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.block_size = kBlockSize;
+  a.q_start = p.q_start;
+  a.p_hg_shift = __builtin_ctz((unsigned)hg);
+  a.p_nqb = (p.max_q_len + kMfmaHeads / hg - 1) / (kMfmaHeads / hg);
+  const size_t n = (size_t)p.num_seqs * hkv * a.num_chunks * a.p_nqb;
+  const dim3 block(kDecodeWaves * kWave);
+  if (p.cache.head_dim == 64)
+    hipLaunchKernelGGL((decode_mfma_kernel<kBF16, 64, kDecodeWaves, false, false, true>), dim3((unsigned)n), block, 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<kBF16, 128, kDecodeWaves, false, false, true>), dim3((unsigned)n), block,
+                       0, s, a);
   return hipGetLastError();
 }
 

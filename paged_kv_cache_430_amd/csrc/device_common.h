@@ -125,6 +125,27 @@ __device__ __forceinline__ uint32_t buffer_load4_stream(__amdgpu_buffer_rsrc_t r
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, kCacheNonTemporal);
 }
 
+// 16-, 8- or 4-byte raw buffer load with cache-policy operand AUX (0, or
+// kCacheNonTemporal for data read exactly once).
+template <int AUX>
+__device__ __forceinline__ uint4 buffer_load16_aux(__amdgpu_buffer_rsrc_t r, int offset) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, AUX);
+  return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+}
+
+template <int AUX>
+__device__ __forceinline__ uint2 buffer_load8_aux(__amdgpu_buffer_rsrc_t r, int offset) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i x = __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, AUX);
+  return make_uint2((uint32_t)x[0], (uint32_t)x[1]);
+}
+
+template <int AUX>
+__device__ __forceinline__ uint32_t buffer_load4_aux(__amdgpu_buffer_rsrc_t r, int offset) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, AUX);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Hardware hands consecutive workgroup ids to the XCDs round-robin. This

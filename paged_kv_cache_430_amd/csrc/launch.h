@@ -107,4 +107,12 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 
+// The same chunked prefill on the matrix-core decode kernel: each workgroup
+// takes 16 (query head, query) columns of one KV group — prefill_cols_heads
+// heads × the rest in consecutive queries — over all the keys they see, split
+// across its waves. Tables of at most kPrefillColsMaxKeys tokens.
+constexpr int kPrefillColsMaxKeys = 8192;
+int prefill_cols_heads(int group);
+hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s);
+
 }  // namespace pkv

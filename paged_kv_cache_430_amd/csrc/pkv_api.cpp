@@ -365,6 +365,24 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
   return hip_status(launch_decode(p, s), fn);
 }
 
+// The prefill kernel: the tile kernel (64 query rows of a KV group per
+// workgroup, one workgroup per compute unit), or the matrix-core decode kernel
+// with (head, query) columns (16 rows per workgroup, the keys split across
+// its waves; tables of at most kPrefillColsMaxKeys tokens). The tile kernel
+// is faster once the chunks give every compute unit its 64 rows; below that
+// (fewer than 256 · 64 query rows in the call) it leaves compute units idle
+// and the column form is used. PKV_PREFILL_KERNEL=tiles or =columns, read at
+// every call, overrides the choice where both apply.
+constexpr int64_t kPrefillTileRows = 256 * 64;
+static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
+  const bool cols_ok = (int64_t)p.max_blocks * 16 <= kPrefillColsMaxKeys;
+  const char* env = getenv("PKV_PREFILL_KERNEL");
+  bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
+  if (env && strcmp(env, "tiles") == 0) cols = false;
+  if (env && strcmp(env, "columns") == 0) cols = cols_ok;
+  return cols ? launch_prefill_cols(p, s) : launch_prefill(p, s);
+}
+
 // Checks a prefill call's arguments and fills *p; p->num_seqs == 0 means
 // nothing to launch.
 static int prefill_prepare(const char* fn, const CacheView& c, const void* q, int32_t q_dtype, int32_t num_seqs,
@@ -452,7 +470,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
                                max_blocks, seq_lens, max_q_len, scale, out, s, &p))
     return st;
   if (p.num_seqs == 0) return PKV_OK;
-  return hip_status(launch_prefill(p, s), "pkv_attn_prefill_chunk");
+  return hip_status(run_prefill(p, s), "pkv_attn_prefill_chunk");
 }
 
 PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, float scale,
@@ -495,7 +513,7 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
   if (pp.num_seqs == 0) return PKV_OK;
-  return hip_status(launch_prefill(pp, s), fn);
+  return hip_status(run_prefill(pp, s), fn);
 }
 
 PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src, const int32_t* dst, int32_t n,

@@ -112,7 +112,9 @@ def _oracle_check(c, out_p, out_d):
 
 @pytest.mark.parametrize("hq,hkv,dh,pt", [(32, 8, 128, 0), (32, 8, 128, 64), (16, 2, 64, 0), (8, 8, 128, 32),
                                           (32, 1, 64, 48)])
-def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt):
+@pytest.mark.parametrize("prefill_kernel", ["tiles", "columns"])
+def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, monkeypatch):
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
     dev = device()
     chunks = [(0, 1), (5, 17), (100, 64), (1000, 130), (31, 33)]
     dec_ctx = [0, 1, 15, 16, 200, 1023, 77]

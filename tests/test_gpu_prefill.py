@@ -13,6 +13,16 @@ from gpu_helpers import device, new_pools
 
 pytestmark = pytest.mark.gpu
 
+PREFILL_KERNELS = ["tiles", "columns"]
+
+
+@pytest.fixture(params=PREFILL_KERNELS)
+def prefill_kernel(request, monkeypatch):
+    """Both prefill kernels: the tile kernel and the matrix-core decode
+    kernel with (head, query) columns (PKV_PREFILL_KERNEL)."""
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", request.param)
+    return request.param
+
 
 def _bf16(shape, gen, dev):
     return torch.randn(*shape, generator=gen, device=dev).to(torch.bfloat16)
@@ -65,20 +75,20 @@ def _prefill_case(dev, seqs, hq, hkv, dh, seed):
 
 
 @pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (8, 8, 128), (16, 8, 64), (32, 4, 128), (4, 1, 64)])
-def test_ragged_chunks_one_call(hq, hkv, dh):
+def test_ragged_chunks_one_call(hq, hkv, dh, prefill_kernel):
     dev = device()
     seqs = [(0, 1), (0, 17), (5, 16), (100, 64), (33, 100), (2048, 3), (0, 130)]
     err, rel = _prefill_case(dev, seqs, hq, hkv, dh, seed=hq * 7 + dh)
     assert err <= 2e-3, f"max-abs {err:.3e}"
 
 
-def test_cfg4_chunk_alone_full_size():
+def test_cfg4_chunk_alone_full_size(prefill_kernel):
     dev = device()
     err, rel = _prefill_case(dev, [(2048, 512)], 32, 8, 128, seed=4304)
     assert err <= 2e-3 and rel < 5e-2
 
 
-def test_cfg4_mixed_step_with_shared_prefix():
+def test_cfg4_mixed_step_with_shared_prefix(prefill_kernel):
     """16 sequences share 1024 prefix tokens (64 full blocks, refcount 16), each
     owns 1024 more; S0 appends and attends a 512-token chunk; 64 other
     sequences append one token and decode. Blocks come from the library's
