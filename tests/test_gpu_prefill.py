@@ -82,6 +82,14 @@ def test_ragged_chunks_one_call(hq, hkv, dh, prefill_kernel):
     assert err <= 2e-3, f"max-abs {err:.3e}"
 
 
+def test_long_table_and_small_chunk(prefill_kernel):
+    """A small chunk on a table longer than the column form takes (8192
+    tokens): the library runs the tile kernel whatever PKV_PREFILL_KERNEL says."""
+    dev = device()
+    err, rel = _prefill_case(dev, [(9000, 20), (8170, 30)], 32, 8, 128, seed=77)
+    assert err <= 2e-3, f"max-abs {err:.3e}"
+
+
 def test_cfg4_chunk_alone_full_size(prefill_kernel):
     dev = device()
     err, rel = _prefill_case(dev, [(2048, 512)], 32, 8, 128, seed=4304)
