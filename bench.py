@@ -19,7 +19,7 @@ carry no per-call events); `cpu_baseline` times the float64 CPU oracle on a
 sample of the same batch on this host.
 
 --workload selects other decode workloads (same kind of line) or
-`cfg4-mixed`: one mixed step of the shared-prefix workload — a causal
+`shared-prefix-mixed`: one mixed step of the shared-prefix workload — a causal
 512-token prefill chunk on a 2048-token cache plus 64 single-token decodes —
 whose line reports the prefill chunk against the bf16 MFMA peak and the
 decodes against HBM.
@@ -56,8 +56,18 @@ CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h",
                   "paged_kv_cache_430_amd/csrc/append_common.h"]
-DECODE_WORKLOADS = ["cfg2-all4096", "cfg2-uniform", "cfg5-mha", "cfg5-gqa", "cfg5-mqa", "cfg5-gqa-fp8",
-                    "cfg3-b1", "cfg3-b4"]
+# decode workloads: name → (generator, its arguments)
+DECODE_WORKLOADS = {
+    "gqa-b32-t4096": ("gqa_b32", "all4096"),        # the headline: B=32 Hq=32 Hkv=8 Dh=128 T=4096 bf16
+    "gqa-b32-ragged": ("gqa_b32", "uniform"),       # the same with lengths uniform in [1, 4096]
+    "mha-b8-t8192": ("head_layouts_t8192", "mha"),
+    "gqa-b8-t8192": ("head_layouts_t8192", "gqa"),
+    "mqa-b8-t8192": ("head_layouts_t8192", "mqa"),
+    "gqa-fp8-b8-t8192": ("head_layouts_t8192", "gqa-fp8"),
+    "long-b1-t32768": ("long_context", 1),          # 32 layers' caches, one table
+    "long-b4-t32768": ("long_context", 4),
+}
+MIXED_WORKLOAD = "shared-prefix-mixed"
 
 
 def parse():
@@ -65,17 +75,17 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="cfg2-all4096",
-                   choices=DECODE_WORKLOADS + ["cfg4-mixed", "prefill-chunk", "prefix-index", "swap"])
+    p.add_argument("--workload", default="gqa-b32-t4096",
+                   choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64],
-                   help="tokens per pool block for the cfg2/cfg5 decode workloads")
+                   help="tokens per pool block for the B=32 and T=8192 decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--unfused", action="store_true",
                    help="decode workloads: append in its own launch before the decode (default: one launch); "
-                        "cfg4-mixed: append, prefill and decode as three calls (default: pkv_attn_mixed_step)")
+                        "shared-prefix-mixed: append, prefill and decode as three calls (default: pkv_attn_mixed_step)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
                    help="after timing, copy a 256 MiB scratch cache with pkv_copy_blocks (counter calibration)")
@@ -195,14 +205,12 @@ def make_decode_setup(name, dev, block_size=16):
     import paged_kv_cache_430_amd as pkv
     import workloads
 
-    if name.startswith("cfg2"):
-        make = lambda copies: workloads.cfg2(name.split("-", 1)[1], device=dev, copies=copies,  # noqa: E731
-                                             block_size=block_size)
-    elif name.startswith("cfg5"):
-        make = lambda copies: workloads.cfg5(name.split("-", 1)[1], device=dev, copies=copies,  # noqa: E731
-                                             block_size=block_size)
-    else:
+    gen_name, arg = DECODE_WORKLOADS[name]
+    if gen_name == "long_context":
         make = None
+    else:
+        gen = getattr(workloads, gen_name)
+        make = lambda copies: gen(arg, device=dev, copies=copies, block_size=block_size)  # noqa: E731
     if make is not None:
         probe = make(1)
         elt = 1 if probe.cache_dtype == "fp8" else 2
@@ -213,8 +221,7 @@ def make_decode_setup(name, dev, block_size=16):
     else:
         if block_size != 16:
             raise SystemExit("bench.py: the long-context workloads use 16-token blocks")
-        b = int(name.split("-b")[1])
-        ws = workloads.cfg3(batch=b, device=dev, layers=32)
+        ws = workloads.long_context(batch=arg, device=dev, layers=32)
         copies = 1
     layers = []
     for w in ws:
@@ -327,7 +334,7 @@ def run_decode(args, dev):
     achieved = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     partition = pt or pkv.pkv_attn_decode_auto_partition(cache_code, B, hq, hkv, T)
     line = {
-        "metric": (METRIC if args.workload == "cfg2-all4096" and w0.block_size == 16 else
+        "metric": (METRIC if args.workload == "gqa-b32-t4096" and w0.block_size == 16 else
                    f"decode-attn KV HBM GB/s ({args.workload}, {w0.block_size}-token blocks)"),
         "value": round(value, 2),
         "unit": "GB/s",
@@ -410,10 +417,10 @@ def _blas_threads():
 
 
 # ---------------------------------------------------------------------------
-# cfg4: mixed chunked prefill + decode with a shared prefix
+# mixed chunked prefill + decode with a shared prefix
 # ---------------------------------------------------------------------------
 
-def make_cfg4_setup(dev):
+def make_mixed_setup(dev):
     """Blocks come from the library's allocator with the workload's seeded free
     order: 16 sequences share the prefix blocks (refcount 16) and own their
     private blocks; S0 reserves its 512-token chunk; 64 decode sequences hold
@@ -424,7 +431,7 @@ def make_cfg4_setup(dev):
     import paged_kv_cache_430_amd as pkv
     import workloads
 
-    m = workloads.cfg4(device=dev)
+    m = workloads.shared_prefix_mixed(device=dev)
     bs, hkv, dh = 16, m.hkv, m.head_dim
     alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
     kp = torch.full((m.num_blocks, hkv, bs, dh), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -473,13 +480,13 @@ def make_cfg4_setup(dev):
                 q_start=torch.tensor([0, m.chunk], dtype=torch.int32, device=dev))
 
 
-def run_cfg4(args, dev):
+def run_mixed(args, dev):
     import numpy as np
     import torch
 
     import paged_kv_cache_430_amd as pkv
 
-    S = make_cfg4_setup(dev)
+    S = make_mixed_setup(dev)
     m = S["m"]
     hq, hkv, dh = m.hq, m.hkv, m.head_dim
     n_dec = len(m.decode_ctx)
@@ -555,7 +562,7 @@ def run_cfg4(args, dev):
     d_bytes = decode_bytes(m.decode_ctx + 1, hq, hkv, dh, 2, 2, False)
     p_tflops = flops / (p_avg * 1e-3) / 1e12
     line = {
-        "metric": "cfg4 mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + 64 decodes",
+        "metric": "mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + 64 decodes, shared prefix",
         "value": round(p_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -567,7 +574,7 @@ def run_cfg4(args, dev):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "cfg4-mixed", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
+        "config": {"workload": MIXED_WORKLOAD, "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
                    "prefix_tokens": S["p0"], "chunk": m.chunk, "shared_prefix_tokens": m.shared,
                    "sharers": m.n_share, "decodes": n_dec,
                    "decode_ctx_mean": float(np.mean(m.decode_ctx)) + 1.0,
@@ -610,7 +617,7 @@ def cpu_baseline_prefill(m, p0, flops):
 
 
 # ---------------------------------------------------------------------------
-# one prefill chunk alone (cfg4's head layout, any prefix and chunk length)
+# one prefill chunk alone (the mixed step's head layout, any prefix and chunk length)
 # ---------------------------------------------------------------------------
 
 def run_prefill_chunk(args, dev):
@@ -828,7 +835,7 @@ def run_prefix_index(args):
 # ---------------------------------------------------------------------------
 
 def run_swap(args, dev):
-    """4096 scattered blocks of a cfg2-shaped pool (Hkv=8, Dh=128, bf16: 64 KiB
+    """4096 scattered blocks of a pool shaped like the headline's (Hkv=8, Dh=128, bf16: 64 KiB
     of K+V per block, 256 MiB per call) out to pinned host memory and back in.
     `value` is the swap-out rate; the line also carries the swap-in rate.
     Both directions are bound by the host link, not by HBM."""
@@ -883,7 +890,7 @@ def main():
         summarize_counters(args.counters[0], args.counters[1], args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(decode shards by sequence or KV head with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
@@ -901,8 +908,8 @@ def main():
     pkv.load()
     if args.workload == "swap":
         line = run_swap(args, dev)
-    elif args.workload == "cfg4-mixed":
-        line = run_cfg4(args, dev)
+    elif args.workload == MIXED_WORKLOAD:
+        line = run_mixed(args, dev)
     elif args.workload == "prefill-chunk":
         line = run_prefill_chunk(args, dev)
     else:

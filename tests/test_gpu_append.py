@@ -23,9 +23,9 @@ def _bits(t):
     return t.cpu().numpy()
 
 
-def test_cfg1_append_pool_bytes_and_36th_token():
+def test_single_seq_append_pool_bytes_and_36th_token():
     dev = device()
-    w = workloads.cfg1(device=dev)
+    w = workloads.single_seq_f32(device=dev)
     table = list(w.block_tables[0, 0])
     kp, vp = new_pools(8, 1, 64, "f32", dev)
     cache = pkv.Cache(kp, vp)

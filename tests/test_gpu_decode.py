@@ -66,24 +66,24 @@ def assert_close(got, ref, tol, what):
         assert err <= tol, f"{what}: sequence {b} max-abs error {err:.3e} > {tol}"
 
 
-def test_cfg1_fp32_before_and_after_append():
+def test_single_seq_fp32_before_and_after_append():
     dev = device()
-    w = workloads.cfg1(device=dev)
+    w = workloads.single_seq_f32(device=dev)
     w35 = workloads.DecodeInputs(**{f: getattr(w, f) for f in w.__dataclass_fields__})
     w35.seq_lens = np.array([35], dtype=np.int32)
     w35.cu_seqlens = np.array([0, 35], dtype=np.int64)
     w35.k, w35.v = w.k[:35], w.v[:35]
     cache = build_cache(w35, dev)
     got35 = run_decode(w35, cache, dev)
-    assert_close({0: got35[0]}, oracle_decode(w35), 1e-5, "cfg1 T=35")
+    assert_close({0: got35[0]}, oracle_decode(w35), 1e-5, "single sequence T=35")
     # append the 36th token through the slot mapping, then attend over 36
     s = pkv.pkv_slot_mapping(w.block_tables[0, 0], 16, 35, 1)
     pkv.pkv_kv_append(cache, w.k[35:].contiguous(), w.v[35:].contiguous(), torch.from_numpy(s).to(dev))
     got36 = run_decode(w, cache, dev)
-    assert_close({0: got36[0]}, oracle_decode(w), 1e-5, "cfg1 T=36")
+    assert_close({0: got36[0]}, oracle_decode(w), 1e-5, "single sequence T=36")
     # split into 16-token partitions: the in-kernel merge must agree too
     got_split = run_decode(w, cache, dev, partition_tokens=16)
-    assert_close({0: got_split[0]}, oracle_decode(w), 1e-5, "cfg1 T=36 split 16")
+    assert_close({0: got_split[0]}, oracle_decode(w), 1e-5, "single sequence T=36 split 16")
 
 
 @pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [
@@ -146,58 +146,58 @@ def test_empty_sequence_and_clamped_length():
     assert out.shape == (0, 8, 128)
 
 
-def test_cfg2_uniform_full_size():
+def test_gqa_b32_ragged_full_size():
     dev = device()
-    w = workloads.cfg2("uniform", device=dev)
+    w = workloads.gqa_b32("uniform", device=dev)
     cache = build_cache(w, dev)
     ref = oracle_decode(w)
     for kern in kernels_for("bf16"):
         got = run_decode(w, cache, dev, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} cfg2 uniform")
+        assert_close(got, ref, 2e-3, f"{kern} B=32 ragged")
 
 
-def test_cfg2_all4096_full_size_each_copy():
+def test_gqa_b32_t4096_full_size_each_copy():
     """The metric configuration, every table copy the benchmark rotates through."""
     dev = device()
-    w = workloads.cfg2("all4096", device=dev, copies=2)
+    w = workloads.gqa_b32("all4096", device=dev, copies=2)
     cache = build_cache(w, dev)
     ref = oracle_decode(w)
     scale_ref = max(float(np.abs(r).max()) for r in ref.values())
     for kern in kernels_for("bf16"):
         for c in range(w.copies):
             got = run_decode(w, cache, dev, copy=c, kernel=kern)
-            assert_close(got, ref, 2e-3, f"{kern} cfg2 all4096 copy {c}")
+            assert_close(got, ref, 2e-3, f"{kern} B=32 T=4096 copy {c}")
             rel = max(float(np.abs(got[b] - ref[b]).max()) for b in ref) / scale_ref
             assert rel < 2e-2
 
 
 @pytest.mark.parametrize("kind", ["mha", "gqa", "mqa", "gqa-fp8"])
-def test_cfg5_head_layouts_full_size(kind):
+def test_head_layouts_t8192_full_size(kind):
     dev = device()
-    w = workloads.cfg5(kind, device=dev)
+    w = workloads.head_layouts_t8192(kind, device=dev)
     cache = build_cache(w, dev)
     ref = oracle_decode(w)
     for kern in kernels_for("bf16"):
         got = run_decode(w, cache, dev, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} cfg5 {kind}")
+        assert_close(got, ref, 2e-3, f"{kern} T=8192 {kind}")
 
 
-def test_cfg3_long_context_b1_layers_and_b4():
+def test_long_context_b1_layers_and_b4():
     dev = device()
-    layers = workloads.cfg3(batch=1, device=dev, layers=3)
+    layers = workloads.long_context(batch=1, device=dev, layers=3)
     for li, w in enumerate(layers):
         cache = build_cache(w, dev)
         ref = oracle_decode(w)
         for kern in kernels_for("bf16"):
             got = run_decode(w, cache, dev, partition_tokens=512, kernel=kern)
-            assert_close(got, ref, 2e-3, f"{kern} cfg3 B=1 layer {li}")
+            assert_close(got, ref, 2e-3, f"{kern} T=32768 B=1 layer {li}")
         del cache
-    w4 = workloads.cfg3(batch=4, device=dev, layers=1)[0]
+    w4 = workloads.long_context(batch=4, device=dev, layers=1)[0]
     cache = build_cache(w4, dev)
     ref = oracle_decode(w4)
     for kern in kernels_for("bf16"):
         got = run_decode(w4, cache, dev, partition_tokens=512, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} cfg3 B=4")
+        assert_close(got, ref, 2e-3, f"{kern} T=32768 B=4")
 
 
 @pytest.mark.parametrize("cache_dtype,kern", [("f32", "vector"), ("bf16", "vector"), ("bf16", "matrix")])

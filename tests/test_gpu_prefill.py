@@ -90,19 +90,19 @@ def test_long_table_and_small_chunk(prefill_kernel):
     assert err <= 2e-3, f"max-abs {err:.3e}"
 
 
-def test_cfg4_chunk_alone_full_size(prefill_kernel):
+def test_512_chunk_on_2048_tokens_full_size(prefill_kernel):
     dev = device()
     err, rel = _prefill_case(dev, [(2048, 512)], 32, 8, 128, seed=4304)
     assert err <= 2e-3 and rel < 5e-2
 
 
-def test_cfg4_mixed_step_with_shared_prefix(prefill_kernel):
+def test_shared_prefix_mixed_step(prefill_kernel):
     """16 sequences share 1024 prefix tokens (64 full blocks, refcount 16), each
     owns 1024 more; S0 appends and attends a 512-token chunk; 64 other
     sequences append one token and decode. Blocks come from the library's
     allocator with a seeded free order."""
     dev = device()
-    m = workloads.cfg4(device=dev)
+    m = workloads.shared_prefix_mixed(device=dev)
     bs, hkv, hq, dh = 16, m.hkv, m.hq, m.head_dim
     alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
     kp, vp = new_pools(m.num_blocks, hkv, dh, "bf16", dev)

@@ -26,7 +26,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-SEEDS = {"cfg1": 4301, "cfg2": 4302, "cfg3": 4303, "cfg4": 4304, "cfg5": 4305}
+SEEDS = {"single_seq_f32": 4301, "gqa_b32": 4302, "long_context": 4303, "shared_prefix_mixed": 4304,
+         "head_layouts_t8192": 4305}
 BLOCK_SIZE = 16
 
 
@@ -130,10 +131,10 @@ def decode_inputs(name, seed, seq_lens, hq, hkv, head_dim, cache_dtype, device,
 
 # ---- named workloads -------------------------------------------------------
 
-def cfg1(device="cpu"):
+def single_seq_f32(device="cpu"):
     """Single sequence, fp32: B=1, Hq=4, Hkv=1, Dh=64, 35 cached tokens + the
     36th appended; 3 blocks at random ids from a pool of 8."""
-    seed = SEEDS["cfg1"]
+    seed = SEEDS["single_seq_f32"]
     rng = np.random.default_rng(seed)
     ids = rng.choice(8, 3, replace=False).astype(np.int32)
     gen = _gen(seed, device)
@@ -142,15 +143,15 @@ def cfg1(device="cpu"):
     v = _randn((36, 1, 64), gen, device, "f32")
     tables = np.full((1, 1, 3), -1, dtype=np.int32)
     tables[0, 0, :] = ids
-    return DecodeInputs("cfg1", seed, 1, 4, 1, 64, BLOCK_SIZE, "f32",
+    return DecodeInputs("single-seq-f32-t35", seed, 1, 4, 1, 64, BLOCK_SIZE, "f32",
                         np.array([36], dtype=np.int32), np.array([0, 36], dtype=np.int64),
                         tables, 8, q, k, v, scale=1.0 / 8.0)
 
 
-def cfg2(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096, block_size=BLOCK_SIZE):
+def gqa_b32(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096, block_size=BLOCK_SIZE):
     """GQA decode, bf16: B=32, Hq=32, Hkv=8, Dh=128; lengths all 4096 or
     uniform in [1, 4096]."""
-    seed = SEEDS["cfg2"]
+    seed = SEEDS["gqa_b32"]
     rng = np.random.default_rng(seed)
     if variant == "all4096":
         lens = np.full(batch, max_len, dtype=np.int32)
@@ -158,18 +159,19 @@ def cfg2(variant="all4096", device="cpu", copies=1, batch=32, max_len=4096, bloc
         lens = rng.integers(1, max_len + 1, batch).astype(np.int32)
     else:
         raise ValueError(variant)
-    return decode_inputs(f"cfg2-{variant}", seed, lens, 32, 8, 128, "bf16", device,
+    name = {"all4096": f"gqa-b{batch}-t{max_len}", "uniform": f"gqa-b{batch}-ragged"}[variant]
+    return decode_inputs(name, seed, lens, 32, 8, 128, "bf16", device,
                          block_size=block_size, copies=copies, rng=rng)
 
 
-def cfg3(batch=1, device="cpu", tokens=32768, layers=32):
+def long_context(batch=1, device="cpu", tokens=32768, layers=32):
     """Long context, bf16: B ∈ {1, 4}, T=32768, Hq=32, Hkv=8, Dh=128, one
     table per sequence shared by `layers` independent caches (one pool per
     layer, each drawn from its own stream)."""
-    seed = SEEDS["cfg3"]
+    seed = SEEDS["long_context"]
     rng = np.random.default_rng(seed)
     lens = np.full(batch, tokens, dtype=np.int32)
-    base = decode_inputs(f"cfg3-B{batch}", seed, lens, 32, 8, 128, "bf16", device, rng=rng)
+    base = decode_inputs(f"long-b{batch}-t{tokens}", seed, lens, 32, 8, 128, "bf16", device, rng=rng)
     out = [base]
     for layer in range(1, layers):
         gen = _gen(seed * 1000 + layer, device)
@@ -181,15 +183,15 @@ def cfg3(batch=1, device="cpu", tokens=32768, layers=32):
     return out
 
 
-def cfg5(kind, device="cpu", batch=8, tokens=8192, copies=1, block_size=BLOCK_SIZE):
+def head_layouts_t8192(kind, device="cpu", batch=8, tokens=8192, copies=1, block_size=BLOCK_SIZE):
     """Head-layout / KV-dtype sweep at T=8192, B=8, Dh=128: "mha" 32/32,
     "gqa" 32/8, "mqa" 32/1 in bf16, "gqa-fp8" 32/8 with e4m3 storage."""
-    seed = SEEDS["cfg5"]
+    seed = SEEDS["head_layouts_t8192"]
     hkv, dt = {"mha": (32, "bf16"), "gqa": (8, "bf16"), "mqa": (1, "bf16"),
                "gqa-fp8": (8, "fp8")}[kind]
     rng = np.random.default_rng(seed)
     lens = np.full(batch, tokens, dtype=np.int32)
-    return decode_inputs(f"cfg5-{kind}", seed, lens, 32, hkv, 128, dt, device,
+    return decode_inputs(f"{kind}-b{batch}-t{tokens}", seed, lens, 32, hkv, 128, dt, device,
                          block_size=block_size, copies=copies, rng=rng)
 
 
@@ -220,10 +222,10 @@ class MixedInputs:
     scale: float = 1.0
 
 
-def cfg4(device="cpu", n_share=16, shared=1024, private=1024, chunk=512, n_decode=64,
+def shared_prefix_mixed(device="cpu", n_share=16, shared=1024, private=1024, chunk=512, n_decode=64,
          ctx_lo=256, ctx_hi=2048, hq=32, hkv=8, head_dim=128):
     """Mixed chunked prefill + decode with a shared prefix (bf16)."""
-    seed = SEEDS["cfg4"]
+    seed = SEEDS["shared_prefix_mixed"]
     bs = BLOCK_SIZE
     rng = np.random.default_rng(seed)
     ctx = rng.integers(ctx_lo, ctx_hi + 1, n_decode).astype(np.int32)
