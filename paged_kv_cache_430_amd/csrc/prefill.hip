@@ -13,6 +13,9 @@
 // of 64/GW queries), three streams of four waves: stream s takes key tiles
 // s, s+3, s+6, … (three waves per SIMD, so each hides the others' latencies),
 // and the streams' online-softmax states are merged into stream 0 at the end.
+// When the query tiles alone give two or more workgroups per CU, each
+// workgroup is one stream of four waves over all its keys instead, three
+// workgroups to a CU, so their barriers do not hold one another back.
 // Within a stream, wave w takes head w % GW and 16 queries. Keys go in tiles
 // of 64 = four blocks; wave w of a stream gathers block w of its tiles:
 //   * K and V of the block come in through raw buffer loads whose record limit
@@ -39,9 +42,11 @@ namespace pkv {
 
 namespace {
 
-constexpr int kStreams = 3;                      // key streams: tiles s, s + 3, … (3 measured best)
 constexpr int kStreamWaves = 4;                  // waves of one stream
-constexpr int kThreads = kStreams * kStreamWaves * kWave;
+// Workgroups of four waves (one stream) run three to a CU once the query
+// tiles alone give at least this many (2 per CU); below it, one 12-wave
+// workgroup per CU splits each query tile's keys over three streams.
+constexpr int kOneStreamTiles = 2 * 256;
 constexpr int kKeys = 64;                        // keys per tile
 constexpr int kTileBlocks = kKeys / kBlockSize;  // blocks per tile, one per wave of a stream
 static_assert(kTileBlocks == kStreamWaves, "one block of each key tile per wave");
@@ -58,8 +63,12 @@ struct Args {
   float scale_log2;
 };
 
-template <int DH, int GW>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
+// NS key streams of four waves share a workgroup: NS = 3, one workgroup per
+// CU with its streams merged through LDS at the end; NS = 1, four-wave
+// workgroups, three per CU, each on its own barrier schedule.
+template <int DH, int GW, int NS>
+__global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args a) {
+  constexpr int kStreams = NS;
   constexpr int QT = 64 / GW;              // queries per workgroup
   constexpr int KROW = DH + 16;            // padded K row in LDS (elements; +16 measured fewest conflicts)
   constexpr int NDC = DH / 32;             // 32-wide k-steps for Q·Kᵀ
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   {
     float* xch = reinterpret_cast<float*>(&k_lds_all[0][0]);
     constexpr int NX = 2 + 4 * NDT;                        // floats per lane
-    static_assert(kStreamWaves * kWave * NX * 4 <= (int)sizeof(k_lds_all), "merge area");
+    static_assert(NS == 1 || kStreamWaves * kWave * NX * 4 <= (int)sizeof(k_lds_all), "merge area");
     float* mine = xch + ((size_t)w * kWave + lane) * NX;
 #pragma unroll
     for (int r = 1; r < kStreams; ++r) {
@@ -336,16 +345,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   }
 }
 
-template <int DH>
-hipError_t launch_gw(const PrefillParams& p, Args a, int gw, hipStream_t s) {
-  const size_t n = (size_t)p.num_seqs * a.hkv * a.num_chunks * a.num_qtiles;
-  const dim3 grid((unsigned)n), block(kThreads);
+template <int DH, int NS>
+hipError_t launch_gw(Args a, size_t n, int gw, hipStream_t s) {
+  const dim3 grid((unsigned)n), block(NS * kStreamWaves * kWave);
   switch (gw) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<DH, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<DH, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((prefill_kernel<DH, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<DH, 1, NS>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<DH, 2, NS>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((prefill_kernel<DH, 4, NS>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_dh(const PrefillParams& p, Args a, int gw, hipStream_t s) {
+  const size_t n = (size_t)p.num_seqs * a.hkv * a.num_chunks * a.num_qtiles;
+  return n >= (size_t)kOneStreamTiles ? launch_gw<DH, 1>(a, n, gw, s) : launch_gw<DH, 3>(a, n, gw, s);
 }
 
 }  // namespace
@@ -369,7 +383,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   a.num_chunks = group / gw;
   a.num_qtiles = (p.max_q_len + (64 / gw) - 1) / (64 / gw);
   a.scale_log2 = p.scale * 1.4426950408889634f;
-  return p.cache.head_dim == 64 ? launch_gw<64>(p, a, gw, s) : launch_gw<128>(p, a, gw, s);
+  return p.cache.head_dim == 64 ? launch_dh<64>(p, a, gw, s) : launch_dh<128>(p, a, gw, s);
 }
 
 }  // namespace pkv

@@ -82,6 +82,16 @@ def test_ragged_chunks_one_call(hq, hkv, dh, prefill_kernel):
     assert err <= 2e-3, f"max-abs {err:.3e}"
 
 
+@pytest.mark.parametrize("seqs", [[(0, 2048)], [(100, 64), (0, 1), (3000, 700), (5, 1500)]])
+def test_tile_kernel_four_wave_workgroups(seqs, monkeypatch):
+    """Enough query tiles (512 or more) for the tile kernel's four-wave
+    workgroups, three per CU."""
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
+    dev = device()
+    err, rel = _prefill_case(dev, seqs, 32, 8, 128, seed=11 + len(seqs))
+    assert err <= 2e-3, f"max-abs {err:.3e}"
+
+
 def test_long_table_and_small_chunk(prefill_kernel):
     """A small chunk on a table longer than the column form takes (8192
     tokens): the library runs the tile kernel whatever PKV_PREFILL_KERNEL says."""
