@@ -573,6 +573,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
 // The online softmax per head is the one above (log2 domain, lazy rescale,
 // wave-uniform decision); the waves merge through LDS and write the output
 // or the same partials for the reduce kernel.
+// "Blocks" here are 16-row units: a pool block of 32 or 64 tokens holds two
+// or four of them. The same kernel also runs (template flags) the decode
+// step's append (APPEND: each sequence's new token is written to its slot
+// and attended from the input), a mixed step's extra appends (EXTRA: the
+// grid's last workgroups store prefill-chunk tokens) and the chunked prefill
+// for small chunks (PREFILL: the 16 columns are (query head, query) pairs,
+// each masked causally at its own position).
 constexpr int kMfmaHeads = 16;   // query heads per workgroup (the MFMA N dimension)
 
 template <int KV, int DH>
