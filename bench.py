@@ -41,6 +41,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -95,10 +96,15 @@ def parse():
 
 
 def source_hash(paths):
+    """Hash of the decode sources' code: comments and blank space are left
+    out, so that only a change to what compiles marks the counters stale."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                    # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
