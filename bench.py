@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: paged decode attention on one MI355X.
 
-Default workload (the headline metric): GQA paged decode, B=32 sequences,
-Hq=32, Hkv=8, Dh=128, every sequence 4096 tokens, bf16 cache, block size 16.
-One step is the whole decode hot path for the batch:
-  1. slot mapping and KV append of the 32 new tokens (position 4095) through
-     the block tables, in one launch (pkv_kv_append_paged),
-  2. split-KV paged decode attention over all 4096 tokens.
+Default workload (the headline metric, `gqa-b32-t4096`): GQA paged decode,
+B=32 sequences, Hq=32, Hkv=8, Dh=128, every sequence 4096 tokens, bf16
+cache, block size 16. One step is the whole decode hot path for the batch —
+slot mapping and KV append of the 32 new tokens (position 4095) through the
+block tables, and split-KV paged decode attention over all 4096 tokens — in
+one launch (pkv_attn_decode_append); `--unfused` runs the append as its own
+launch (pkv_kv_append_paged) before pkv_attn_decode.
 Inputs are resident in HBM before timing. Copies of the pool behind separate
 block-table sets (at least 2 GiB in total) are used in rotation so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
@@ -18,11 +19,13 @@ stream it runs on in a second pass over the same steps (so the K timed steps
 carry no per-call events); `cpu_baseline` times the float64 CPU oracle on a
 sample of the same batch on this host.
 
---workload selects other decode workloads (same kind of line) or
+--workload selects other decode workloads (same kind of line);
 `shared-prefix-mixed`: one mixed step of the shared-prefix workload — a causal
-512-token prefill chunk on a 2048-token cache plus 64 single-token decodes —
-whose line reports the prefill chunk against the bf16 MFMA peak and the
-decodes against HBM.
+512-token prefill chunk on a 2048-token cache plus 64 single-token decodes,
+run as pkv_attn_mixed_step — whose line reports the prefill chunk against the
+bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
+(--chunk queries on --prefix tokens); `swap`: blocks to pinned host memory
+and back; `prefix-index`: the host prefix-cache index.
 
 Counter summaries: `--calib-copy` adds, after the timed steps, one
 pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
