@@ -27,7 +27,7 @@ Modules:
   paging     — block counts, position → (block, offset) → slot, pool scatter/gather
   fp8        — OCP e4m3fn decode and round-to-nearest-even saturating encode
   allocator  — a pure-Python model of the ref-counted block allocator
-  sizing     — KV-cache byte arithmetic
+  sizing     — KV-cache byte arithmetic; K/V positions built per generation step
   prefix     — full-block prefix reuse with a chained block hash
 
 Every function is pinned by a CPU test against values the pages print, closed

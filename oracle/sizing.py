@@ -27,3 +27,29 @@ def kv_bytes_varlen(layers, seq_lens, kv_heads, head_dim, bytes_per_element):
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_element):
     return kv_bytes(layers, 1, 1, kv_heads, head_dim, bytes_per_element)
+
+
+# ---- positions whose K/V are built during generation ------------------------
+# Page "03. KV Cache：用显存换计算", section on how much is recomputed without a
+# cache: without a cache every step feeds the whole history through the model
+# again, so step k builds K/V for the prompt plus the k − 1 tokens generated so
+# far; with a cache the first step (prefill) builds the prompt's K/V and every
+# later step builds only the one new position. Its table of three rounds counts
+# 4, then 1, then 1 new positions with the cache.
+
+def positions_built_per_step(prompt_tokens, generated_tokens, cached):
+    """K/V positions built at each of the generated_tokens steps."""
+    steps = []
+    have = 0                      # positions whose K/V survive from earlier steps
+    for k in range(generated_tokens):
+        seen = prompt_tokens + k  # history the step-k forward pass attends over
+        if cached:
+            steps.append(seen - have)
+            have = seen
+        else:
+            steps.append(seen)
+    return steps
+
+
+def positions_built(prompt_tokens, generated_tokens, cached):
+    return sum(positions_built_per_step(prompt_tokens, generated_tokens, cached))

@@ -168,3 +168,45 @@ def test_prefix_index_stops_at_first_miss_and_counts_hits():
     # the same block of tokens after a different parent is a different key
     idx.insert(list("ZZZZEFGH"), [20, 21])
     assert idx.match(list("ABCDEFGH")) == [10, 11]
+
+
+# ---- positions whose K/V are built during generation -------------------------
+
+def _brute_force_positions(prompt, generated, cached):
+    """Simulate the steps with a set standing in for the cache: a step's
+    forward pass covers positions 0 … prompt + k − 1; each one whose K/V is not
+    held is built (and, with a cache, kept)."""
+    held, built = set(), []
+    for k in range(generated):
+        n = 0
+        for pos in range(prompt + k):
+            if pos not in held:
+                n += 1
+                if cached:
+                    held.add(pos)
+        built.append(n)
+    return built
+
+
+def test_positions_built_page_values(golden):
+    g = golden("positions_built.json")
+    r = g["long_request"]
+    without = sizing.positions_built_per_step(r["prompt"], r["generated"], cached=False)
+    assert without[0] == r["first_step"] and without[1] == r["second_step_without_cache"]
+    assert without[-1] == r["last_step_without_cache"]
+    assert sum(without) == r["without_cache"]
+    assert sizing.positions_built(r["prompt"], r["generated"], cached=True) == r["with_cache"]
+    ratio = r["without_cache"] / r["with_cache"]
+    assert abs(ratio - r["ratio_printed_about"]) < 0.02 * r["ratio_printed_about"]   # 171.5
+    t = g["three_rounds"]
+    per = sizing.positions_built_per_step(t["prompt"], t["generated"], cached=True)
+    assert per == t["with_cache_per_round"] and sum(per) == t["with_cache_total"]
+
+
+@pytest.mark.parametrize("prompt,generated", [(1, 1), (1, 5), (4, 3), (7, 9), (30, 12)])
+def test_positions_built_brute_force(prompt, generated):
+    for cached in (False, True):
+        assert sizing.positions_built_per_step(prompt, generated, cached) == \
+            _brute_force_positions(prompt, generated, cached)
+    # quadratic against linear growth: the gap widens with the output length
+    assert sizing.positions_built(prompt, generated, False) >= sizing.positions_built(prompt, generated, True)
