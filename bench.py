@@ -87,6 +87,8 @@ def parse():
     p.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64],
                    help="tokens per pool block for the B=32 and T=8192 decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sharers-decode", action="store_true",
+                   help="shared-prefix-mixed: the 15 idle sharers (2048 tokens each) decode one token too")
     p.add_argument("--unfused", action="store_true",
                    help="decode workloads: append in its own launch before the decode (default: one launch); "
                         "shared-prefix-mixed: append, prefill and decode as three calls (default: pkv_attn_mixed_step)")
@@ -429,18 +431,20 @@ def _blas_threads():
 # mixed chunked prefill + decode with a shared prefix
 # ---------------------------------------------------------------------------
 
-def make_mixed_setup(dev):
+def make_mixed_setup(dev, sharers_decode=False):
     """Blocks come from the library's allocator with the workload's seeded free
     order: 16 sequences share the prefix blocks (refcount 16) and own their
     private blocks; S0 reserves its 512-token chunk; 64 decode sequences hold
-    their context plus the step's token."""
+    their context plus the step's token. With sharers_decode the other 15
+    sharers also decode: each reserves a private block for its token at
+    position 2048 and joins the decode batch after the 64."""
     import numpy as np
     import torch
 
     import paged_kv_cache_430_amd as pkv
     import workloads
 
-    m = workloads.shared_prefix_mixed(device=dev)
+    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=sharers_decode)
     bs, hkv, dh = 16, m.hkv, m.head_dim
     alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
     kp = torch.full((m.num_blocks, hkv, bs, dh), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -472,19 +476,31 @@ def make_mixed_setup(dev):
         alloc.reserve_append(dtabs[j], 0, ctx + 1)
         k, v = m.decode_kv[j]
         append(dtabs[j], 0, k[:ctx], v[:ctx])
+    dec_ctx = m.decode_ctx.astype(np.int32)
+    dec_q = m.decode_q
+    dec_new_k = [kv[0][-1:] for kv in m.decode_kv]
+    dec_new_v = [kv[1][-1:] for kv in m.decode_kv]
+    if sharers_decode:
+        for i in range(1, m.n_share):
+            alloc.reserve_append(tables[i], p0, 1)      # a new private block (2048 is block-aligned)
+        dtabs = np.concatenate([dtabs, np.stack(tables[1:])])
+        dec_ctx = np.concatenate([dec_ctx, np.full(m.n_share - 1, p0, dtype=np.int32)])
+        dec_q = torch.cat([dec_q, m.sharer_q]).contiguous()
+        dec_new_k.append(m.sharer_new_kv[0])
+        dec_new_v.append(m.sharer_new_kv[1])
     # the step's appends: the chunk's 512 tokens (S0) and one token per decode sequence
-    new_k = torch.cat([m.chunk_kv[0]] + [kv[0][-1:] for kv in m.decode_kv]).contiguous()
-    new_v = torch.cat([m.chunk_kv[1]] + [kv[1][-1:] for kv in m.decode_kv]).contiguous()
+    new_k = torch.cat([m.chunk_kv[0]] + dec_new_k).contiguous()
+    new_v = torch.cat([m.chunk_kv[1]] + dec_new_v).contiguous()
     all_tables = torch.from_numpy(np.concatenate([t0[None], dtabs])).to(dev)
-    n_dec = len(m.decode_ctx)
+    n_dec = len(dec_ctx)
     cu_new = torch.tensor([0, m.chunk] + list(range(m.chunk + 1, m.chunk + n_dec + 1)), dtype=torch.int32,
                           device=dev)
-    first_pos = torch.tensor([p0] + [int(c) for c in m.decode_ctx], dtype=torch.int32, device=dev)
+    first_pos = torch.tensor([p0] + [int(c) for c in dec_ctx], dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     return dict(m=m, cache=cache, p0=p0, max_blocks=max_blocks, all_tables=all_tables,
-                new_k=new_k, new_v=new_v, cu_new=cu_new, first_pos=first_pos,
+                new_k=new_k, new_v=new_v, cu_new=cu_new, first_pos=first_pos, dec_q=dec_q, dec_ctx=dec_ctx,
                 dec_tables=all_tables[1:].contiguous(), chunk_table=all_tables[:1].contiguous(),
-                dec_lens=torch.from_numpy((m.decode_ctx + 1).astype(np.int32)).to(dev),
+                dec_lens=torch.from_numpy((dec_ctx + 1).astype(np.int32)).to(dev),
                 chunk_lens=torch.tensor([p0 + m.chunk], dtype=torch.int32, device=dev),
                 q_start=torch.tensor([0, m.chunk], dtype=torch.int32, device=dev))
 
@@ -495,10 +511,10 @@ def run_mixed(args, dev):
 
     import paged_kv_cache_430_amd as pkv
 
-    S = make_mixed_setup(dev)
+    S = make_mixed_setup(dev, args.sharers_decode)
     m = S["m"]
     hq, hkv, dh = m.hq, m.hkv, m.head_dim
-    n_dec = len(m.decode_ctx)
+    n_dec = len(S["dec_ctx"])
     n_new = m.chunk + n_dec
     stream = torch.cuda.current_stream(dev)
     lib = pkv.load()
@@ -519,7 +535,7 @@ def run_mixed(args, dev):
     chunk_b = pkv._ChunkBatch(1, m.chunk_q.data_ptr(), S["q_start"].data_ptr(), k_ch.data_ptr(), v_ch.data_ptr(),
                               S["chunk_table"].data_ptr(), S["max_blocks"], S["chunk_lens"].data_ptr(), m.chunk,
                               out_p.data_ptr())
-    dec_b = pkv._DecodeBatch(n_dec, m.decode_q.data_ptr(), k_dec.data_ptr(), v_dec.data_ptr(),
+    dec_b = pkv._DecodeBatch(n_dec, S["dec_q"].data_ptr(), k_dec.data_ptr(), v_dec.data_ptr(),
                              S["dec_tables"].data_ptr(), S["max_blocks"], S["dec_lens"].data_ptr(), msl,
                              args.partition, out_d.data_ptr(), wsp, wsb)
 
@@ -540,7 +556,7 @@ def run_mixed(args, dev):
         if tp is not None:
             tp.stop()
             td.start()
-        pkv._check(lib.pkv_attn_decode(S["cache"].ref(), m.decode_q.data_ptr(), pkv.PKV_BF16, n_dec, hq,
+        pkv._check(lib.pkv_attn_decode(S["cache"].ref(), S["dec_q"].data_ptr(), pkv.PKV_BF16, n_dec, hq,
                                        S["dec_tables"].data_ptr(), S["max_blocks"], S["dec_lens"].data_ptr(), msl,
                                        m.scale, args.partition, out_d.data_ptr(), wsp, wsb, sh))
         if td is not None:
@@ -568,10 +584,10 @@ def run_mixed(args, dev):
     if args.calib_copy:
         calib_copy(dev)
     flops = prefill_flops(S["p0"], m.chunk, hq, dh)
-    d_bytes = decode_bytes(m.decode_ctx + 1, hq, hkv, dh, 2, 2, False)
+    d_bytes = decode_bytes(S["dec_ctx"] + 1, hq, hkv, dh, 2, 2, False)
     p_tflops = flops / (p_avg * 1e-3) / 1e12
     line = {
-        "metric": "mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + 64 decodes, shared prefix",
+        "metric": f"mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + {n_dec} decodes, shared prefix",
         "value": round(p_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -586,7 +602,8 @@ def run_mixed(args, dev):
         "config": {"workload": MIXED_WORKLOAD, "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
                    "prefix_tokens": S["p0"], "chunk": m.chunk, "shared_prefix_tokens": m.shared,
                    "sharers": m.n_share, "decodes": n_dec,
-                   "decode_ctx_mean": float(np.mean(m.decode_ctx)) + 1.0,
+                   "sharers_decoding": m.n_share - 1 if args.sharers_decode else 0,
+                   "decode_ctx_mean": float(np.mean(S["dec_ctx"])) + 1.0,
                    "step": ("append launch + prefill + decode" if args.unfused else
                             "pkv_attn_mixed_step: decode launch that also appends the chunk, then the prefill")},
         "prefill_us": stats_us(p_ms),

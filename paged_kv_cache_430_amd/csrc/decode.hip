@@ -50,6 +50,7 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 
+
 // Register layouts of one (block, head) tile of 16 token rows, RB bytes each.
 // K: a row is read by LPK lanes (4, 8 or 16); lane (tk = lane / LPK,
 //    jk = lane % LPK) holds rows tk + TPK·i (i < NTK) and, of each, the 16-byte
@@ -119,6 +120,18 @@ struct MergeArgs {
   float* out;
   int num_parts;
 };
+
+// Workgroups that stay together on one XCD: the head chunks and partitions
+// of up to four KV heads of one sequence (four when Hkv allows, else two or
+// one). Keeping a sequence's neighbouring heads together keeps its pool
+// blocks' adjacent head tiles on one XCD, and spreading the groups keeps a
+// run of long sequences in a batch off any single XCD. (Measured: whole
+// sequences per XCD left a batch whose last 15 sequences were its longest
+// 16% slower; single KV heads per XCD cost 1-2% on equal lengths.)
+__device__ __forceinline__ uint32_t decode_xcd_group(const KernelArgs& a) {
+  const int hg = a.hkv % 4 == 0 ? 4 : a.hkv % 2 == 0 ? 2 : 1;
+  return (uint32_t)(a.num_chunks * a.num_parts * hg);
+}
 
 // Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane
 // of a group receives the same bits (each step adds a commutative pair).
@@ -221,7 +234,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(KernelArgs a) 
   __shared__ __attribute__((aligned(16))) float sh_p[kWaves][kBlockSize][HC];   // K lanes → V lanes
 
   // ---- which (b, g, chunk, partition) ----------------------------------------
-  const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
+  const uint32_t L = grouped_xcd_index(flat_block_id(), flat_grid_size(), decode_xcd_group(a));
   const int chunk = L % a.num_chunks;
   const int part = (L / a.num_chunks) % a.num_parts;
   const int g = (L / a.num_chunks / a.num_parts) % a.hkv;
@@ -745,7 +758,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
       return;
     }
   }
-  const uint32_t L = xcd_logical_index(flat, nflat);
+  // prefill query blocks of one (sequence, KV head) share K/V: contiguous per XCD
+  const uint32_t L = PREFILL ? xcd_logical_index(flat, nflat) : grouped_xcd_index(flat, nflat, decode_xcd_group(a));
   // decode: (sequence b, KV head g, head chunk, partition); prefill: (sequence
   // b, KV head g, head chunk, query block qb), one partition over all keys
   const int inner = PREFILL ? a.p_nqb : a.num_parts;

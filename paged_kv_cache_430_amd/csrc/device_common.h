@@ -157,6 +157,19 @@ __device__ __forceinline__ uint32_t xcd_logical_index(uint32_t id, uint32_t n) {
   return (id % kNumXcd) * (n / kNumXcd) + id / kNumXcd;
 }
 
+// The same idea at a coarser grain, for work whose neighbours in a batch may
+// differ in size: consecutive logical indices come in groups of c that share
+// data (say, the workgroups of a few KV heads of one sequence); each group
+// stays on one XCD, and the groups are dealt to the XCDs in turn, so a run of
+// large groups in the batch spreads over all eight. Ids past the last whole
+// round of 8·c groups keep the hardware order. A bijection on [0, n).
+__device__ __forceinline__ uint32_t grouped_xcd_index(uint32_t id, uint32_t n, uint32_t c) {
+  const uint32_t full = n / (kNumXcd * c) * (kNumXcd * c);
+  if (id >= full) return id;
+  const uint32_t x = id % kNumXcd, s = id / kNumXcd;
+  return ((s / c) * kNumXcd + x) * c + s % c;
+}
+
 __device__ __forceinline__ uint32_t flat_block_id() {
   return blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
 }

@@ -155,3 +155,90 @@ def test_mixed_step_chunks_only_and_decodes_only():
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
     assert torch.equal(md, rd)
     _oracle_check(c, None, md)
+
+
+def test_shared_prefix_step_with_sharers_decoding():
+    """The shared-prefix workload with its idle sharers decoding too: S0 runs
+    its 512-token chunk on 2048 cached tokens; 64 separate sequences and the 15
+    other sharers (1024 shared + 1024 private tokens each) append one token and
+    decode, all in one pkv_attn_mixed_step. Blocks come from the library's
+    allocator: each sharer's token opens a private block (2048 is
+    block-aligned, so nothing is copied), and the prefix blocks keep their 16
+    references. Outputs against the oracle within 2e-3."""
+    import workloads
+
+    dev = device()
+    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=True)
+    bs, hkv, hq, dh = 16, m.hkv, m.hq, m.head_dim
+    alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
+    kp, vp = new_pools(m.num_blocks, hkv, dh, "bf16", dev)
+    cache = pkv.Cache(kp, vp)
+    max_blocks = (m.shared + m.private + m.chunk) // bs + 1
+
+    def append(table, first, k, v):
+        s = pkv.pkv_slot_mapping(table, bs, first, k.shape[0])
+        pkv.pkv_kv_append(cache, k.contiguous(), v.contiguous(), torch.from_numpy(s).to(dev))
+
+    prefix = np.full(max_blocks, -1, dtype=np.int32)
+    assert alloc.reserve_append(prefix, 0, m.shared) == []
+    append(prefix, 0, *m.prefix_kv)
+    n_pref = m.shared // bs
+    tables = []
+    for i in range(m.n_share):
+        t = prefix.copy()
+        if i > 0:
+            alloc.incref(prefix[:n_pref])
+        assert alloc.reserve_append(t, m.shared, m.private) == []
+        append(t, m.shared, *m.private_kv[i])
+        tables.append(t)
+    p0 = m.shared + m.private
+    t0 = tables[0]
+    assert alloc.reserve_append(t0, p0, m.chunk) == []
+    n_dec = len(m.decode_ctx)
+    dtabs = np.full((n_dec + m.n_share - 1, max_blocks), -1, dtype=np.int32)
+    for j, ctx in enumerate(m.decode_ctx):
+        ctx = int(ctx)
+        alloc.reserve_append(dtabs[j], 0, ctx + 1)
+        k, v = m.decode_kv[j]
+        append(dtabs[j], 0, k[:ctx], v[:ctx])
+    free_before = alloc.num_free()
+    for i in range(1, m.n_share):
+        assert alloc.reserve_append(tables[i], p0, 1) == []      # a new private block, no copy
+        dtabs[n_dec + i - 1] = tables[i]
+    assert alloc.num_free() == free_before - (m.n_share - 1)
+    assert all(alloc.refcount(int(b)) == m.n_share for b in prefix[:n_pref])
+    assert all(alloc.refcount(int(tables[i][p0 // bs])) == 1 for i in range(1, m.n_share))
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    dec_ctx = np.concatenate([m.decode_ctx, np.full(m.n_share - 1, p0)]).astype(np.int32)
+    dec_q = torch.cat([m.decode_q, m.sharer_q]).contiguous()
+    dec_k = torch.cat([m.decode_kv[j][0][-1:] for j in range(n_dec)] + [m.sharer_new_kv[0]]).contiguous()
+    dec_v = torch.cat([m.decode_kv[j][1][-1:] for j in range(n_dec)] + [m.sharer_new_kv[1]]).contiguous()
+    out_p, out_d = pkv.pkv_attn_mixed_step(
+        cache, m.scale, m.chunk_q, m.chunk_kv[0].contiguous(), m.chunk_kv[1].contiguous(),
+        torch.tensor([0, m.chunk], dtype=torch.int32, device=dev), t(t0[None]),
+        torch.tensor([p0 + m.chunk], dtype=torch.int32, device=dev), m.chunk,
+        dec_q, dec_k, dec_v, t(dtabs), t(dec_ctx + 1), max_blocks * bs)
+    torch.cuda.synchronize()
+
+    k0 = np.concatenate([_f64(m.prefix_kv[0]), _f64(m.private_kv[0][0]), _f64(m.chunk_kv[0])])
+    v0 = np.concatenate([_f64(m.prefix_kv[1]), _f64(m.private_kv[0][1]), _f64(m.chunk_kv[1])])
+    ref_p = attention.prefill_chunk(_f64(m.chunk_q), k0.transpose(1, 0, 2), v0.transpose(1, 0, 2), m.scale)
+    assert np.abs(out_p.cpu().double().numpy() - ref_p).max() <= 2e-3
+    qd = _f64(dec_q)
+    gd = out_d.cpu().double().numpy()
+    for j in range(n_dec):
+        k, v = m.decode_kv[j]
+        ref = attention.decode(qd[j:j + 1], [_f64(k).transpose(1, 0, 2)], [_f64(v).transpose(1, 0, 2)], m.scale)[0]
+        assert np.abs(gd[j] - ref).max() <= 2e-3, j
+    for i in range(1, m.n_share):
+        j = n_dec + i - 1
+        k = np.concatenate([_f64(m.prefix_kv[0]), _f64(m.private_kv[i][0]), _f64(m.sharer_new_kv[0][i - 1:i])])
+        v = np.concatenate([_f64(m.prefix_kv[1]), _f64(m.private_kv[i][1]), _f64(m.sharer_new_kv[1][i - 1:i])])
+        ref = attention.decode(qd[j:j + 1], [k.transpose(1, 0, 2)], [v.transpose(1, 0, 2)], m.scale)[0]
+        assert np.abs(gd[j] - ref).max() <= 2e-3, i
+    # the prefix blocks are unchanged by every append of the step
+    gk, gv = pkv.pkv_debug_gather(cache, t(prefix[:n_pref]), m.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(gk.cpu(), m.prefix_kv[0].cpu().permute(1, 0, 2))
+    assert torch.equal(gv.cpu(), m.prefix_kv[1].cpu().permute(1, 0, 2))

@@ -220,11 +220,17 @@ class MixedInputs:
     decode_kv: List[List[torch.Tensor]] = field(default_factory=list)   # per seq [k, v] [ctx+1, Hkv, Dh]
     decode_q: Optional[torch.Tensor] = None                             # [n_decode, Hq, Dh]
     scale: float = 1.0
+    # sharers_decode variant: sequences 1 … n_share−1 also decode one token
+    # (position shared + private), drawn after everything above
+    sharer_new_kv: Optional[List[torch.Tensor]] = None                  # k, v [n_share−1, Hkv, Dh]
+    sharer_q: Optional[torch.Tensor] = None                             # [n_share−1, Hq, Dh]
 
 
 def shared_prefix_mixed(device="cpu", n_share=16, shared=1024, private=1024, chunk=512, n_decode=64,
-         ctx_lo=256, ctx_hi=2048, hq=32, hkv=8, head_dim=128):
-    """Mixed chunked prefill + decode with a shared prefix (bf16)."""
+         ctx_lo=256, ctx_hi=2048, hq=32, hkv=8, head_dim=128, sharers_decode=False):
+    """Mixed chunked prefill + decode with a shared prefix (bf16). With
+    sharers_decode the n_share − 1 sequences that share S0's prefix decode one
+    token each as well (their draws come last, so the rest is unchanged)."""
     seed = SEEDS["shared_prefix_mixed"]
     bs = BLOCK_SIZE
     rng = np.random.default_rng(seed)
@@ -242,4 +248,7 @@ def shared_prefix_mixed(device="cpu", n_share=16, shared=1024, private=1024, chu
     m.decode_kv = [[r(int(t) + 1, hkv), r(int(t) + 1, hkv)] for t in ctx]
     m.decode_q = _randn((n_decode, hq, head_dim), gen, device, "bf16")
     m.scale = float(1.0 / np.sqrt(head_dim))
+    if sharers_decode:
+        m.sharer_new_kv = [r(n_share - 1, hkv), r(n_share - 1, hkv)]
+        m.sharer_q = _randn((n_share - 1, hq, head_dim), gen, device, "bf16")
     return m
