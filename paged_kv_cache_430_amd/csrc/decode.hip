@@ -124,10 +124,11 @@ struct MergeArgs {
 // Workgroups that stay together on one XCD: the head chunks and partitions
 // of up to four KV heads of one sequence (four when Hkv allows, else two or
 // one). Keeping a sequence's neighbouring heads together keeps its pool
-// blocks' adjacent head tiles on one XCD, and spreading the groups keeps a
-// run of long sequences in a batch off any single XCD. (Measured: whole
-// sequences per XCD left a batch whose last 15 sequences were its longest
-// 16% slower; single KV heads per XCD cost 1-2% on equal lengths.)
+// blocks' adjacent head tiles on one XCD, and dealing the groups out in turn
+// keeps a run of long sequences in a batch off any single XCD. (Measured: a
+// contiguous range of sequences per XCD made a batch whose last 15 sequences
+// were its longest 20% slower; single KV heads per XCD cost 1-2% on equal
+// lengths.)
 __device__ __forceinline__ uint32_t decode_xcd_group(const KernelArgs& a) {
   const int hg = a.hkv % 4 == 0 ? 4 : a.hkv % 2 == 0 ? 2 : 1;
   return (uint32_t)(a.num_chunks * a.num_parts * hg);
