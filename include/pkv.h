@@ -48,7 +48,9 @@ extern "C" {
 
 typedef enum pkv_status {
   PKV_OK = 0,
-  PKV_EINVAL = -1,      /* bad shape, size, pointer or id                      */
+  PKV_EINVAL = -1,      /* bad shape, size, pointer or id; also an attention  */
+                        /* call whose launch would need more than 2^31 - 1    */
+                        /* workgroups                                          */
   PKV_ENOBLOCKS = -2,   /* allocator: not enough free blocks (state unchanged) */
   PKV_EDTYPE = -3,      /* unsupported dtype combination                       */
   PKV_EREF = -4,        /* allocator: reference count misuse                   */

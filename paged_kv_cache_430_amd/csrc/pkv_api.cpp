@@ -26,6 +26,7 @@ namespace {
 
 // a wave reads its share of a partition's table entries one per lane
 constexpr int32_t kMaxPartition = 64 * 16 * kDecodeWaves;
+constexpr int64_t kMaxWorkgroups = INT32_MAX;   // one launch grid dimension
 // MI355X compute units: the automatic partition size aims at one decode
 // workgroup (8 waves, a whole CU at the kernel's register use) per CU
 constexpr int32_t kComputeUnits = 256;
@@ -305,6 +306,13 @@ static int decode_prepare(const char* fn, const CacheView& c, const NewTokens* a
     return fail(PKV_EINVAL, std::string(fn) + ": block sizes other than 16 need the matrix-core decode (bf16 or fp8 cache)");
   const int32_t pt = effective_partition(batch, num_q_heads, c.num_kv_heads, max_seq_len, partition_tokens, kernel);
   const int32_t parts = max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
+  {   // the split kernel's workgroups and the reduce kernel's rows must fit a launch grid
+    const int group = num_q_heads / c.num_kv_heads;
+    const int hpw = decode_heads_per_wg(group, kernel);
+    const int64_t wgs = (int64_t)batch * c.num_kv_heads * ((group + hpw - 1) / hpw) * parts;
+    if (wgs > kMaxWorkgroups || (int64_t)batch * num_q_heads > kMaxWorkgroups)
+      return fail(PKV_EINVAL, std::string(fn) + ": batch x heads x partitions needs more than 2^31 - 1 workgroups");
+  }
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) + " bytes");
@@ -400,6 +408,10 @@ static int prefill_prepare(const char* fn, const CacheView& c, const void* q, in
   if (!(group == 1 || group == 2 || (group % 4 == 0 && group <= 64)))
     return fail(PKV_EINVAL, std::string(fn) + ": Hq/Hkv must be 1, 2 or a multiple of 4 up to 64");
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  // either kernel takes at least 16 (query head, query) rows per workgroup,
+  // plus at most one partial query block per head group
+  if ((int64_t)num_seqs * num_q_heads * (max_q_len / 16 + 1) > kMaxWorkgroups)
+    return fail(PKV_EINVAL, std::string(fn) + ": sequences x heads x queries need more than 2^31 - 1 workgroups");
   if (!q || !q_start || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, std::string(fn) + ": q and out must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, std::string(fn) + ": scale is not finite");
@@ -501,6 +513,12 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
                               kDecodeMatrix, s, &dp))
     return st;
   if (pp.num_seqs > 0) {   // the chunks' tokens: extra workgroups of the decode launch
+    const int group = num_q_heads / c.num_kv_heads;
+    const int hpw = decode_heads_per_wg(group, kDecodeMatrix);
+    const int64_t dec_wgs = (int64_t)dp.batch * c.num_kv_heads * ((group + hpw - 1) / hpw) * dp.num_parts;
+    const int64_t x_wgs = (int64_t)chunks->num_seqs * ((chunks->max_q_len + 15) / 16) + 8;
+    if (dec_wgs + x_wgs > kMaxWorkgroups)
+      return fail(PKV_EINVAL, std::string(fn) + ": the decode launch with its appending workgroups exceeds 2^31 - 1");
     dp.x_k = chunks->k_new;
     dp.x_v = chunks->v_new;
     dp.x_cu = chunks->q_start;

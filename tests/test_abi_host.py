@@ -109,6 +109,10 @@ def test_decode_argument_validation(lib):
     assert call(pt=16, ws=0x90008, wsb=need) == pkv.PKV_EINVAL   # misaligned workspace
     assert call(b=0) == pkv.PKV_OK                           # nothing to do, nothing launched
     assert lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2, 32, 8, 128, 64, 64) == 0
+    # a grid past 2^31 - 1 workgroups is refused (batch x KV heads x partitions)
+    huge = lib.pkv_attn_decode_workspace_bytes(pkv.PKV_BF16, 2 ** 26, 32, 8, 128, 64, 16)
+    assert call(b=2 ** 26, pt=16, ws=0x90000, wsb=huge) == pkv.PKV_EINVAL
+    assert "2^31" in lib.pkv_last_error().decode()
 
 
 def test_auto_partition_rule(lib, monkeypatch):
@@ -201,6 +205,9 @@ def test_append_and_prefill_validation(lib):
                                       None, 0, None) == pkv.PKV_EDTYPE
     assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 24, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
                                       None, 0, None) == pkv.PKV_EINVAL     # group 3
+    assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 2 ** 20, 32, 0x1, 0x2, 4, 0x3, 1024, 0.1, 0x80000,
+                                      None, 0, None) == pkv.PKV_EINVAL     # grid past 2^31 - 1
+    assert "2^31" in lib.pkv_last_error().decode()
     # fused slot mapping + append: same dtype rules, pointer and size checks
     ap = lib.pkv_kv_append_paged
     assert ap(ref, 0x50000, 0x60000, pkv.PKV_F32, 2, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EDTYPE
