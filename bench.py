@@ -25,7 +25,8 @@ sample of the same batch on this host.
 run as pkv_attn_mixed_step — whose line reports the prefill chunk against the
 bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
 (--chunk queries on --prefix tokens); `swap`: blocks to pinned host memory
-and back; `prefix-index`: the host prefix-cache index.
+and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
+streaming-read rate for the decode's 4 KiB tiles, in order and scattered.
 
 Counter summaries: `--calib-copy` adds, after the timed steps, one
 pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
@@ -80,7 +81,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa-b32-t4096",
-                   choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap"])
+                   choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap",
+                            "read-ceiling"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
@@ -910,6 +912,61 @@ def run_swap(args, dev):
     }
 
 
+# ---------------------------------------------------------------------------
+# the box's read-bandwidth ceiling for the decode's access pattern
+# ---------------------------------------------------------------------------
+
+def run_read_ceiling(args, dev):
+    """pkv_debug_stream_read over a 2 GiB buffer of 4 KiB tiles (the decode's
+    (block, head) tile at bf16, Dh=128, 16-token blocks), with the decode's
+    non-temporal buffer loads and no arithmetic: tiles in order, and tiles in a
+    seeded random order (a paged pool read through its tables), each with one
+    8-wave workgroup per CU (the decode's shape) and with four per CU. `value`
+    is the scattered order at one workgroup per CU."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    n_tiles = MALL_BYTES // 4096
+    buf = torch.empty(n_tiles * 1024, dtype=torch.int32, device=dev)
+    buf.random_(generator=torch.Generator(device=dev).manual_seed(4307))
+    rng = np.random.default_rng(4307)
+    orders = {"in order": torch.arange(n_tiles, dtype=torch.int32, device=dev),
+              "random order": torch.from_numpy(rng.permutation(n_tiles).astype(np.int32)).to(dev)}
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, ids in orders.items():
+        for nwg in (256, 1024):
+            sink = torch.empty(nwg, dtype=torch.int32, device=dev)
+            for _ in range(args.warmup):
+                pkv.pkv_debug_stream_read(buf, ids, nwg, sink)
+            timer = Timer(stream, args.steps)
+            for _ in range(args.steps):
+                timer.start()
+                pkv.pkv_debug_stream_read(buf, ids, nwg, sink)
+                timer.stop()
+            torch.cuda.synchronize()
+            ms = timer.ms()
+            avg = sum(ms) / len(ms)
+            res[f"{name}, {nwg} workgroups"] = {"GB/s": round(n_tiles * 4096 / (avg * 1e-3) / 1e9, 1),
+                                                "call_us": stats_us(ms)}
+    key = "random order, 256 workgroups"
+    gbs = res[key]["GB/s"]
+    return {
+        "metric": "HBM streaming-read ceiling: 2 GiB of 4 KiB tiles in random order, GB/s",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res[key]["call_us"]["mean"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "read-ceiling", "bytes_per_call": n_tiles * 4096, "tile_bytes": 4096,
+                   "waves_per_workgroup": 8},
+        "results": res,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "stream_read_kernel",
+                     "bytes_per_launch": n_tiles * 4096},
+    }
+
+
 def main():
     args = parse()
     if args.counters:
@@ -938,6 +995,8 @@ def main():
         line = run_mixed(args, dev)
     elif args.workload == "prefill-chunk":
         line = run_prefill_chunk(args, dev)
+    elif args.workload == "read-ceiling":
+        line = run_read_ceiling(args, dev)
     else:
         line = run_decode(args, dev)
     print(json.dumps(line), flush=True)

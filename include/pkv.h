@@ -359,6 +359,21 @@ PKV_API int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, 
 PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_bytes, const int32_t* ids, int32_t n,
                         pkv_stream stream);
 
+/* Measurement aid (not on the attention path): the HBM read rate for the
+ * access pattern of paged decode, which streams 4 KiB (block, head) tiles
+ * found through a block table ([P2] Q028; [P3] 6.5). Reads tiles of 4096
+ * bytes from buf in the order tile_ids gives, with the decode kernels'
+ * non-temporal buffer loads, in num_workgroups workgroups of 8 waves:
+ * workgroup i reads ids [i*n_tiles/num_workgroups, (i+1)*n_tiles/num_workgroups)
+ * and writes the XOR of every dword it read to sink[i].
+ *   buf: device, buf_tiles * 4096 bytes, 16-byte aligned; ids outside
+ *        [0, buf_tiles) are skipped.
+ *   tile_ids: device int32 [n_tiles]; sink: device uint32 [num_workgroups].
+ * PKV_EINVAL for negative sizes, NULL pointers or a misaligned buf.
+ * Asynchronous on the stream. */
+PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int32_t* tile_ids, int32_t n_tiles,
+                                  int32_t num_workgroups, uint32_t* sink, pkv_stream stream);
+
 /* Test aid: read one sequence back through its table into the semantic
  * layout [num_kv_heads, seq_len, head_dim] of the stored dtype ([P2] Q025:
  * K and V each [B, H_kv, T, Dh]; Q028: paging changes placement, not order).

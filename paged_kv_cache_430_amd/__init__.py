@@ -20,6 +20,7 @@ __all__ = [
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
     "pkv_attn_decode_append",
     "pkv_attn_prefill_chunk", "pkv_attn_mixed_step", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
+    "pkv_debug_stream_read",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]
 
@@ -83,6 +84,7 @@ _SIGS = {
                                            ctypes.POINTER(_ChunkBatch), ctypes.POINTER(_DecodeBatch), _VP]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP]),
     "pkv_debug_gather": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, _VP, _VP]),
+    "pkv_debug_stream_read": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, _I32, _I32, _VP, _VP]),
     "pkv_swap_out": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "pkv_swap_in": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, ctypes.c_size_t, _VP, _I32, _VP]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _VP, ctypes.POINTER(_VP)]),
@@ -319,6 +321,19 @@ def pkv_swap_in(cache, host, ids, stream=None):
     """host (pinned, as written by pkv_swap_out) → blocks ids (device int32)."""
     _check(load().pkv_swap_in(cache.ref(), _ptr(host), host.numel() * host.element_size(), _ptr(ids), ids.numel(),
                               _stream(stream, cache.device)))
+
+
+def pkv_debug_stream_read(buf, tile_ids, num_workgroups, sink=None, stream=None):
+    """Read the 4 KiB tiles of `buf` (a 16-byte aligned device tensor) listed in
+    `tile_ids` (device int32) in that order; returns the per-workgroup XOR of
+    what was read (device uint32 [num_workgroups])."""
+    dev = buf.device
+    if sink is None:
+        sink = torch.empty(num_workgroups, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().pkv_debug_stream_read(_ptr(buf), nbytes // 4096, _ptr(tile_ids), tile_ids.numel(), num_workgroups,
+                                        _ptr(sink), _stream(stream, dev)))
+    return sink
 
 
 def pkv_debug_gather(cache, block_table, seq_len, stream=None):

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
-SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp", "kv_append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp", "kv_append.hip", "decode.hip", "prefill.hip",
+           "read_probe.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

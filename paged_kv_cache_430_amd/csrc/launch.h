@@ -92,6 +92,8 @@ constexpr int kDecodeMatrix = 1;
 
 // Heads of one KV group handled by one decode workgroup of the given kernel.
 int decode_heads_per_wg(int group, int kernel);
+hipError_t launch_stream_read(const void* buf, int64_t buf_tiles, const int32_t* ids, int n_tiles, int num_wgs,
+                              uint32_t* sink, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 struct PrefillParams {

@@ -602,4 +602,17 @@ PKV_API int pkv_debug_gather(const pkv_cache* cache, const int32_t* block_table,
                     "pkv_debug_gather");
 }
 
+PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int32_t* tile_ids, int32_t n_tiles,
+                                  int32_t num_workgroups, uint32_t* sink, pkv_stream stream) {
+  clear_error();
+  const char* fn = "pkv_debug_stream_read";
+  if (buf_tiles < 0 || n_tiles < 0 || num_workgroups <= 0 || num_workgroups > kMaxWorkgroups)
+    return fail(PKV_EINVAL, std::string(fn) + ": bad size");
+  if (n_tiles == 0) return PKV_OK;
+  if (!buf || !tile_ids || !sink) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!aligned16(buf)) return fail(PKV_EINVAL, std::string(fn) + ": buf must be 16-byte aligned");
+  return hip_status(launch_stream_read(buf, buf_tiles, tile_ids, n_tiles, num_workgroups, sink,
+                                       static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

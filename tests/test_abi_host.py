@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
