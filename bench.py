@@ -416,7 +416,7 @@ def cpu_baseline_decode(w, target_s, d_bytes):
         seqs += 1
         b = (b + 1) % w.batch
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle", "host": _host_libs(),
             "sample": f"{seqs} sequences of the batch (float64 numpy, materialised softmax over contiguous K/V), "
                       f"{el:.1f} s of oracle compute; GB/s on the same algorithmic bytes"}
 
@@ -427,6 +427,21 @@ def _blas_threads():
         return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         return 1
+
+
+def _host_libs():
+    """numpy's version and the BLAS it calls (library, version, threads)."""
+    import numpy as np
+    libs = {"numpy": np.__version__}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            libs["blas"] = {"library": blas[0].get("internal_api"), "version": blas[0].get("version"),
+                            "threads": blas[0].get("num_threads")}
+    except Exception:  # noqa: BLE001
+        pass
+    return libs
 
 
 # ---------------------------------------------------------------------------
@@ -639,7 +654,7 @@ def cpu_baseline_prefill(m, p0, flops):
     oracle.attention.prefill_chunk(q, k, v, m.scale)
     el = time.perf_counter() - t0
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
-            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle", "host": _host_libs(),
             "sample": f"the whole 512-query chunk on {p0 + m.chunk} cached tokens, once "
                       f"(float64 numpy, materialised causal softmax), {el:.2f} s"}
 
@@ -853,7 +868,7 @@ def run_prefix_index(args):
             reps += 1
         el_o = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(lookups * reps / el_o, 1), "unit": "blocks/s", "cores": 1,
-                                "kind": "oracle", "sample": f"{reps} passes over the 512 prompts (Python dict of "
+                                "kind": "oracle", "host": _host_libs(), "sample": f"{reps} passes over the 512 prompts (Python dict of "
                                                             f"nested-tuple keys), {el_o:.2f} s"}
     return line
 
