@@ -86,7 +86,7 @@ def parse():
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
-    p.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64],
+    p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
                    help="tokens per pool block for the B=32 and T=8192 decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sharers-decode", action="store_true",

@@ -67,8 +67,8 @@ typedef enum pkv_dtype {
 typedef void* pkv_stream;   /* a hipStream_t */
 
 /* One layer's paged cache. Borrowed: the library keeps no pointer past a call.
- * Supported: block_size 16, 32 or 64; head_dim 64 or 128; dtype F32, BF16 or
- * FP8_E4M3. Every call takes 16-, 32- and 64-token blocks except the F32
+ * Supported: block_size 8, 16, 32 or 64; head_dim 64 or 128; dtype F32, BF16 or
+ * FP8_E4M3. Every call takes 8-, 16-, 32- and 64-token blocks except the F32
  * decode (its vector-ALU kernel) and pkv_attn_prefill, which take 16. [P2]
  * Q028 leaves the block size to the implementation and, in its follow-up on
  * smaller blocks, names the trade: a larger block wastes more tail slots

@@ -94,7 +94,7 @@ struct KernelArgs {
   const float* k_inv;
   const float* v_inv;
   int new_dtype;
-  int block_size;    // pool block: 16, 32 or 64 tokens (the matrix-core form; 16 for the vector form)
+  int block_size;    // pool block: 8, 16, 32 or 64 tokens (the matrix-core form; 16 for the vector form)
   // Further appends done by the last x_wgs workgroups of the matrix-core
   // form, kExtraTokens tokens each (a mixed step's prefill chunks): sequence
   // s's rows x_cu[s] … x_cu[s+1]−1 of x_k / x_v (new_dtype) are its last
@@ -736,7 +736,7 @@ __device__ __forceinline__ void extra_append(const KernelArgs& a, int idx) {
                           per, a.block_size);
 }
 
-template <int KV, int DH, int NW, bool APPEND, bool EXTRA, bool PREFILL = false>
+template <int KV, int DH, int NW, bool APPEND, bool EXTRA, bool PREFILL = false, bool SPLIT8 = false>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   constexpr int kWaves = NW, kThreads = NW * kWave;
   constexpr int NH = kMfmaHeads;
@@ -782,19 +782,27 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   const int tok0 = part * a.part_tokens;
   // The kernel works in 16-row units ("blocks" below); a pool block of
   // bs = 16, 32 or 64 tokens holds bs/16 of them, unit u at rows
-  // (u mod bs/16)·16 … of table entry u / (bs/16).
+  // (u mod bs/16)·16 … of table entry u / (bs/16). With 8-token blocks
+  // (SPLIT8) unit u is the 8 rows of entry 2u followed by the 8 rows of
+  // entry 2u + 1: lanes 0-31 (key groups 0, 1) hold keys of the first, lanes
+  // 32-63 keys of the second, and every load that would span both is issued
+  // once per half-wave, each half with its own block's buffer resource.
   const int bs = a.block_size;
-  const int unit_shift = __builtin_amdgcn_readfirstlane(__builtin_ctz((unsigned)bs / kBlockSize));   // log2(bs/16)
+  const int unit_shift =
+      SPLIT8 ? 0 : __builtin_amdgcn_readfirstlane(__builtin_ctz((unsigned)bs / kBlockSize));   // log2(bs/16)
   const int unit_mask = (1 << unit_shift) - 1;
   const size_t head_stride = (size_t)bs * G::RB;              // bytes of one (pool block, head)
   // Table entries, loaded beside the length: wave w takes unit pairs
   // (tiles) w, w + kWaves, …; lane j holds unit 2·(w + kWaves·(j/2)) + j%2.
   const int lb0 = tok0 / kBlockSize;                         // the partition's first unit
-  const int cap = min(a.part_tokens / kBlockSize, (a.max_blocks << unit_shift) - lb0);
+  const int units_in_table = SPLIT8 ? (a.max_blocks + 1) / 2 : a.max_blocks << unit_shift;
+  const int cap = min(a.part_tokens / kBlockSize, units_in_table - lb0);
   const int jb = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
-  const int phys_all = jb < cap ? bt[(lb0 + jb) >> unit_shift] : -1;
-  auto unit_row0 = [&](int idx) { return ((lb0 + idx) & unit_mask) * kBlockSize; };   // first pool row of unit idx
+  const int phys_all = jb < cap ? bt[SPLIT8 ? 2 * (lb0 + jb) : (lb0 + jb) >> unit_shift] : -1;
+  // SPLIT8: the unit's second block (entry 2u + 1, which may lie past the table)
+  const int phys_all2 = SPLIT8 && jb < cap && 2 * (lb0 + jb) + 1 < a.max_blocks ? bt[2 * (lb0 + jb) + 1] : -1;
+  auto unit_row0 = [&](int idx) { return SPLIT8 ? 0 : ((lb0 + idx) & unit_mask) * kBlockSize; };   // first pool row
   // the length through a vector-memory load: the scalar-cache wait for it
   // would also hold back every other scalar load issued before the first tile
   const int seq_len = (int)__builtin_amdgcn_raw_buffer_load_b32(
@@ -820,16 +828,39 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     uint4 k[2][G::NKI];       // [block][whole-row load]
     uint32_t v[2][4][VW];     // [block][key of the lane's quad]
   };
-  // unit e of a tile: `rows` rows from row0 of table entry phys
-  auto load_blocks = [&](Tile& t, int e, int phys, int row0, int rows) {
-    const auto rk = tile_rsrc(a.kc, phys, row0, rows);
-    const auto rv = tile_rsrc(a.vc, phys, row0, rows);
-    // K: whole rows per load (CPR lanes per row), restaged through LDS
+  // unit e of a tile: `rows` rows from row0 of table entry phys (SPLIT8: the
+  // first 8 of them from entry phys, the rest from entry phys2)
+  auto load_blocks = [&](Tile& t, int e, int phys, int phys2, int row0, int rows) {
+    if constexpr (SPLIT8) {
+      const auto rk0 = tile_rsrc(a.kc, phys, 0, min(rows, 8)), rk1 = tile_rsrc(a.kc, phys2, 0, max(rows - 8, 0));
+      const auto rv0 = tile_rsrc(a.vc, phys, 0, min(rows, 8)), rv1 = tile_rsrc(a.vc, phys2, 0, max(rows - 8, 0));
+      // K: a load of RPI ≤ 8 whole rows lies in one block; 16 rows (fp8, Dh=64) split by half-wave
 #pragma unroll
-    for (int i = 0; i < G::NKI; ++i)
-      t.k[e][i] = buffer_load16_aux<kAux>(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
+      for (int i = 0; i < G::NKI; ++i) {
+        const int row = i * G::RPI + lane / G::CPR, cb = (lane % G::CPR) * 16;
+        if constexpr (G::RPI <= 8) {
+          t.k[e][i] = buffer_load16_aux<kAux>(i * G::RPI < 8 ? rk0 : rk1, (row % 8) * G::RB + cb);
+        } else {
+          if (row < 8) t.k[e][i] = buffer_load16_aux<kAux>(rk0, row * G::RB + cb);
+          else t.k[e][i] = buffer_load16_aux<kAux>(rk1, (row - 8) * G::RB + cb);
+        }
+      }
+      // V: key group kg holds rows 4kg … 4kg+3, so lanes 0-31 read the first block, 32-63 the second
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_dwords<VW, kAux>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+      for (int i = 0; i < 4; ++i) {
+        if (kg < 2) load_dwords<VW, kAux>(rv0, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+        else load_dwords<VW, kAux>(rv1, (4 * kg - 8 + i) * G::RB + col * VW * 4, t.v[e][i]);
+      }
+    } else {
+      const auto rk = tile_rsrc(a.kc, phys, row0, rows);
+      const auto rv = tile_rsrc(a.vc, phys, row0, rows);
+      // K: whole rows per load (CPR lanes per row), restaged through LDS
+#pragma unroll
+      for (int i = 0; i < G::NKI; ++i)
+        t.k[e][i] = buffer_load16_aux<kAux>(rk, (i * G::RPI + lane / G::CPR) * G::RB + (lane % G::CPR) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_dwords<VW, kAux>(rv, (4 * kg + i) * G::RB + col * VW * 4, t.v[e][i]);
+    }
   };
 
   // The wave's first block pair is requested from its table entries alone,
@@ -838,7 +869,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   Tile first;
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), unit_row0(2 * w + e), kBlockSize);
+    load_blocks(first, e, __builtin_amdgcn_readlane(phys_all, e), SPLIT8 ? __builtin_amdgcn_readlane(phys_all2, e) : -1,
+                unit_row0(2 * w + e), kBlockSize);
 
   // q of column col as the B operand of each k-step (zeros for an unused column)
   const int qpb = NH >> hg_shift;                          // prefill: queries per query block
@@ -878,6 +910,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   const int ntile = (nblk + 1) / 2;
   const int ntw = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;   // this wave's tiles
   const int my_phys = (lane >> 1) < ntw ? phys_all : -1;
+  const int my_phys2 = SPLIT8 && (lane >> 1) < ntw ? phys_all2 : -1;
   float sc = a.scale_log2;
   if constexpr (KV == kFP8) sc *= a.k_scale[g];
 
@@ -917,11 +950,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   auto rows_of = [&](int idx) { return min(kBlockSize, max(0, ntok - idx * kBlockSize)); };
   // block e (0, 1) of the wave's j-th tile
   auto block_phys = [&](int j, int e) { return j < ntw ? __builtin_amdgcn_readlane(my_phys, 2 * j + e) : -1; };
+  auto block_phys2 = [&](int j, int e) {   // SPLIT8: the unit's second block
+    return SPLIT8 && j < ntw ? __builtin_amdgcn_readlane(my_phys2, 2 * j + e) : -1;
+  };
   auto block_index = [&](int j, int e) { return 2 * (w + kWaves * j) + e; };
   auto load_tile = [&](int j, Tile& t) {
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      load_blocks(t, e, block_phys(j, e), unit_row0(block_index(j, e)), rows_of(block_index(j, e)));
+      load_blocks(t, e, block_phys(j, e), block_phys2(j, e), unit_row0(block_index(j, e)), rows_of(block_index(j, e)));
   };
 
   float m_run = -INFINITY, l_run = 0.0f;     // head col; l is this lane's share
@@ -930,11 +966,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto use_tile = [&](int j, const Tile& t) {
-    int rows[2];
+    // rmask[e] bit r: row r of unit e is a key to attend (inside the sequence,
+    // in a block of the pool)
+    uint32_t rmask[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int phys = block_phys(j, e);
-      rows[e] = (unsigned)phys < (unsigned)a.num_blocks ? rows_of(block_index(j, e)) : 0;
+      const int r = rows_of(block_index(j, e));
+      if constexpr (SPLIT8) {
+        const int r0 = (unsigned)block_phys(j, e) < (unsigned)a.num_blocks ? min(r, 8) : 0;
+        const int r1 = (unsigned)block_phys2(j, e) < (unsigned)a.num_blocks ? max(r - 8, 0) : 0;
+        rmask[e] = ((1u << r0) - 1u) | (((1u << r1) - 1u) << 8);
+      } else {
+        rmask[e] = (unsigned)block_phys(j, e) < (unsigned)a.num_blocks ? (1u << r) - 1u : 0u;
+      }
     }
     // K rows to the wave's LDS stage, then back as the A operand (row col)
     uint8_t* stage = sh_region[w];
@@ -988,7 +1032,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bool keep = 4 * kg + i < rows[e];
+        bool keep = (rmask[e] >> (4 * kg + i)) & 1u;
         if constexpr (PREFILL) keep = keep && block_index(j, e) * kBlockSize + 4 * kg + i <= my_pos;
         const float v = keep ? st[e][i] * sc : -INFINITY;
         st[e][i] = v;
@@ -1037,7 +1081,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int q2 = 0; q2 < NP; ++q2) vp[e][i][q2] = 4 * kg + i < rows[e] ? vp[e][i][q2] : 0u;
+          for (int q2 = 0; q2 < NP; ++q2) vp[e][i][q2] = (rmask[e] >> (4 * kg + i)) & 1u ? vp[e][i][q2] : 0u;
     }
     if constexpr (APPEND) {   // the new token's V slice from v_new
       uint32_t vn[NP];
@@ -1157,6 +1201,15 @@ hipError_t launch_mfma(const DecodeParams& p, const KernelArgs& a, hipStream_t s
       return hipGetLastError();
     }
     return hipErrorInvalidValue;   // the mixed step takes bf16 caches only
+  }
+  if (a.block_size == 8) {   // 16-row units over pairs of 8-token blocks
+    if (a.k_new)
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, false, false, true>), dim3((unsigned)n), block,
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, false, false, false, true>), dim3((unsigned)n),
+                         block, 0, s, a);
+    return hipGetLastError();
   }
   if (a.k_new)
     hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, false>), dim3((unsigned)n), block, 0, s, a);

@@ -14,7 +14,7 @@ inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
 
 struct CacheView {
   int num_blocks, num_kv_heads, head_dim, dtype;
-  int block_size;   // tokens per block: 16, 32 or 64
+  int block_size;   // tokens per block: 8, 16, 32 or 64
   void* k;
   void* v;
   const float* k_scale;

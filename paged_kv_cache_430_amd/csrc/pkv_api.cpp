@@ -48,8 +48,8 @@ int hip_status(hipError_t e, const char* what) {
 int validate_cache(const pkv_cache* c, const char* fn, CacheView* view) {
   const std::string f(fn);
   if (!c) return fail(PKV_EINVAL, f + ": cache is NULL");
-  if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
-    return fail(PKV_EINVAL, f + ": block_size must be 16, 32 or 64");
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PKV_EINVAL, f + ": block_size must be 8, 16, 32 or 64");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(PKV_EINVAL, f + ": head_dim must be 64 or 128");
   if (c->num_kv_heads <= 0) return fail(PKV_EINVAL, f + ": num_kv_heads must be positive");
   if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX / c->block_size)
@@ -180,8 +180,8 @@ PKV_API int pkv_slot_mapping_device(const int32_t* block_tables, int32_t max_blo
                                     const int32_t* first_pos, int32_t n_tokens, int32_t* out_slots,
                                     pkv_stream stream) {
   clear_error();
-  if (block_size != 16 && block_size != 32 && block_size != 64)
-    return fail(PKV_EINVAL, "pkv_slot_mapping_device: block_size must be 16, 32 or 64");
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PKV_EINVAL, "pkv_slot_mapping_device: block_size must be 8, 16, 32 or 64");
   if (num_seqs < 0 || n_tokens < 0 || max_blocks < 0) return fail(PKV_EINVAL, "pkv_slot_mapping_device: negative size");
   if (num_seqs > 0 && n_tokens > 0 && (!block_tables || !cu_new || !first_pos || !out_slots))
     return fail(PKV_EINVAL, "pkv_slot_mapping_device: NULL pointer");

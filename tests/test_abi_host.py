@@ -74,7 +74,7 @@ def _fake_cache(dtype=pkv.PKV_BF16, dh=128, bs=16, hkv=8):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("block_size", 8, pkv.PKV_EINVAL), ("head_dim", 96, pkv.PKV_EINVAL), ("num_kv_heads", 0, pkv.PKV_EINVAL),
+    ("block_size", 4, pkv.PKV_EINVAL), ("head_dim", 96, pkv.PKV_EINVAL), ("num_kv_heads", 0, pkv.PKV_EINVAL),
     ("num_blocks", 0, pkv.PKV_EINVAL), ("dtype", 7, pkv.PKV_EDTYPE), ("k_cache", 0x10008, pkv.PKV_EINVAL),
 ])
 def test_decode_rejects_bad_cache(lib, field, value, status):
@@ -151,13 +151,13 @@ def test_auto_partition_rule(lib, monkeypatch):
 
 
 def test_block_size_rules(lib, monkeypatch):
-    """16-, 32- and 64-token blocks; the F32 (vector) decode and the prefill take 16 only."""
+    """8-, 16-, 32- and 64-token blocks; the F32 (vector) decode and the prefill take 16 only."""
     def decode(ref, b=1, msl=64, dtype=pkv.PKV_BF16):
         return lib.pkv_attn_decode(ref, 0x50000, dtype, b, 8, 0x60000, 4, 0x70000, msl, 0.1, 0, 0x80000,
                                    None, 0, None)
-    for bs in (8, 24, 48, 128):
+    for bs in (4, 24, 48, 128):
         assert decode(_fake_cache(bs=bs)[0], b=0) == pkv.PKV_EINVAL, bs
-    for bs in (32, 64):
+    for bs in (8, 32, 64):
         ref, _ = _fake_cache(bs=bs)
         assert decode(ref, b=0, msl=4 * bs) == pkv.PKV_OK
         assert decode(ref, b=0, msl=4 * bs + 1) == pkv.PKV_EINVAL          # beyond max_blocks · bs

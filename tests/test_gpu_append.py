@@ -207,10 +207,10 @@ def test_fused_append_matches_slot_mapping_then_append(cache_dtype, in_dtype, dh
     assert np.array_equal(_bits(kc), _bits(ka))
 
 
-@pytest.mark.parametrize("bs", [32, 64])
-def test_append_and_slots_at_larger_block_sizes(bs):
-    """Slot mapping (host and device), append and gather with 32- and 64-token
-    blocks, bit-exact against the oracle's scatter."""
+@pytest.mark.parametrize("bs", [8, 32, 64])
+def test_append_and_slots_at_other_block_sizes(bs):
+    """Slot mapping (host and device), append and gather with 8-, 32- and
+    64-token blocks, bit-exact against the oracle's scatter."""
     dev = device()
     rng = np.random.default_rng(40 + bs)
     nblocks, hkv, dh = 24, 2, 64

@@ -321,11 +321,13 @@ def test_decode_append_in_one_launch(cache_dtype, in_dtype, hq, hkv, dh, pt):
     assert torch.isfinite(out_ref).all()
 
 
-@pytest.mark.parametrize("bs", [32, 64])
-@pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [("bf16", 32, 8, 128), ("fp8", 16, 2, 64), ("bf16", 32, 1, 64)])
-def test_block_sizes_32_and_64(bs, cache_dtype, hq, hkv, dh):
-    """Pools of 32- and 64-token blocks (matrix-core decode): ragged lengths,
-    partitions that split a block, the fused append, NaN slots elsewhere."""
+@pytest.mark.parametrize("bs", [8, 32, 64])
+@pytest.mark.parametrize("cache_dtype,hq,hkv,dh", [("bf16", 32, 8, 128), ("fp8", 16, 2, 64), ("bf16", 32, 1, 64),
+                                                   ("fp8", 32, 8, 128)])
+def test_block_sizes_8_32_and_64(bs, cache_dtype, hq, hkv, dh):
+    """Pools of 8-, 32- and 64-token blocks (matrix-core decode): ragged
+    lengths, partitions that split a block, the fused append, NaN slots
+    elsewhere. At 8 tokens every 16-row unit spans two unrelated blocks."""
     from gpu_helpers import NAN_FP8
     dev = device()
     lens_ = [1, 15, 16, 31, 33, 64, 65, 500, 1031]

@@ -25,7 +25,7 @@ def _decode_case(seed):
     cache_dtype = ["bf16", "fp8", "f32"][seed % 3]
     hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
     dh = [64, 128][int(rng.integers(2))]
-    bs = 16 if cache_dtype == "f32" else [16, 32, 64][int(rng.integers(3))]
+    bs = 16 if cache_dtype == "f32" else [16, 32, 64, 8][int(rng.integers(4))]
     b = int(rng.integers(1, 9))
     lens_ = [int(x) for x in rng.integers(1, 2500, b)]
     pt = [0, 16, 48, 256, 1024][int(rng.integers(5))]

@@ -30,7 +30,7 @@ def _bytes(t):
 
 
 @pytest.mark.parametrize("dtype,hkv,dh,bs", [("bf16", 8, 128, 16), ("fp8", 8, 128, 16), ("f32", 2, 64, 16),
-                                             ("bf16", 2, 64, 32), ("fp8", 4, 128, 64)])
+                                             ("bf16", 2, 64, 32), ("fp8", 4, 128, 64), ("bf16", 4, 128, 8)])
 def test_swap_round_trip_is_bit_exact(dtype, hkv, dh, bs):
     dev = device()
     nb = 64
