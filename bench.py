@@ -677,11 +677,14 @@ def run_prefill_chunk(args, dev):
     hq, hkv, dh = 32, 8, 128
     P, C = args.prefix, args.chunk
     T = P + C
-    nb = -(-T // 16)
+    bsz = args.block_size
+    if bsz < 16:
+        raise SystemExit("prefill-chunk: the prefill takes 16-, 32- or 64-token blocks")
+    nb = -(-T // bsz)
     rng = np.random.default_rng(4306)
     gen = torch.Generator(device=dev).manual_seed(4306)
-    kp = torch.randn(nb + 8, hkv, 16, dh, generator=gen, device=dev).to(torch.bfloat16)
-    vp = torch.randn(nb + 8, hkv, 16, dh, generator=gen, device=dev).to(torch.bfloat16)
+    kp = torch.randn(nb + 8, hkv, bsz, dh, generator=gen, device=dev).to(torch.bfloat16)
+    vp = torch.randn(nb + 8, hkv, bsz, dh, generator=gen, device=dev).to(torch.bfloat16)
     cache = pkv.Cache(kp, vp)
     table = torch.from_numpy(rng.permutation(nb + 8)[:nb].astype(np.int32)[None]).to(dev)
     q = torch.randn(C, hq, dh, generator=gen, device=dev).to(torch.bfloat16)
@@ -717,14 +720,14 @@ def run_prefill_chunk(args, dev):
     avg = sum(call) / len(call)
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
-    kernel = env if env in ("tiles", "columns") else ("columns" if C * hq < 256 * 64 and T <= 8192 else "tiles")
+    kernel = env if env in ("tiles", "columns") else ("columns" if C * hq < 256 * 64 and nb * bsz <= 8192 else "tiles")
     tf = flops / (avg * 1e-3) / 1e12
     line = {
         "metric": f"prefill chunk TFLOP/s (bf16 MFMA), C={C} on P={P}",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill-chunk", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": 16,
+        "config": {"workload": "prefill-chunk", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": bsz,
                    "prefix_tokens": P, "chunk": C,
                    "kernel": "prefill_kernel" if kernel == "tiles" else "decode_mfma_kernel (prefill columns)"},
         "call_us": stats_us(call),

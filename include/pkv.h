@@ -69,7 +69,8 @@ typedef void* pkv_stream;   /* a hipStream_t */
 /* One layer's paged cache. Borrowed: the library keeps no pointer past a call.
  * Supported: block_size 8, 16, 32 or 64; head_dim 64 or 128; dtype F32, BF16 or
  * FP8_E4M3. Every call takes 8-, 16-, 32- and 64-token blocks except the F32
- * decode (its vector-ALU kernel) and pkv_attn_prefill, which take 16. [P2]
+ * decode (its vector-ALU kernel, 16 only), pkv_attn_prefill_chunk and
+ * pkv_attn_mixed_step (16, 32 or 64). [P2]
  * Q028 leaves the block size to the implementation and, in its follow-up on
  * smaller blocks, names the trade: a larger block wastes more tail slots
  * (blocks·bs − T) but needs fewer table entries and lookups.
@@ -260,7 +261,7 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   seq_lens: device int32 [num_seqs], T_s >= C_s
  *   max_q_len: host bound on C_s (sizes the grid)
  *   out:      device fp32, same shape as q
- * Cache dtype BF16, block_size 16; head_dim 64 or 128; Hq/Hkv 1, 2 or a
+ * Cache dtype BF16, block_size 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2 or a
  * multiple of 4 up to 64. No workspace is needed (pass NULL, 0).
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
  * workgroup, key tiles shared through LDS), and the matrix-core decode kernel
@@ -292,7 +293,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * pool bytes and both outputs are bit-identical to the separate calls'.
  *   chunks:  see pkv_chunk_batch; num_seqs may be 0
  *   decodes: see pkv_decode_batch; batch may be 0
- * BF16 cache and inputs, block_size 16, the matrix-core decode whatever
+ * BF16 cache and inputs, block_size 16, 32 or 64, the matrix-core decode whatever
  * PKV_DECODE_KERNEL says. A chunk's new positions must not lie in blocks the
  * decodes read (shared prefix blocks are full, so copy-on-write of a shared
  * tail keeps this). */

@@ -1308,7 +1308,8 @@ hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
   const int hkv = p.cache.num_kv_heads, group = p.num_q_heads / hkv;
   const int hg = prefill_cols_heads(group);
-  if (p.max_blocks * kBlockSize > kPrefillColsMaxKeys || p.cache.block_size != kBlockSize || p.cache.dtype != kBF16)
+  const int64_t keys = (int64_t)p.max_blocks * p.cache.block_size;
+  if (keys > kPrefillColsMaxKeys || p.cache.block_size < kBlockSize || p.cache.dtype != kBF16)
     return hipErrorInvalidValue;
   KernelArgs a = {};
   a.kc = static_cast<uint8_t*>(p.cache.k);
@@ -1321,12 +1322,12 @@ hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s) {
   a.hkv = hkv;
   a.hq = p.num_q_heads;
   a.max_blocks = p.max_blocks;
-  a.max_seq_len = p.max_blocks * kBlockSize;
-  a.part_tokens = p.max_blocks * kBlockSize;
+  a.max_seq_len = (int)keys;
+  a.part_tokens = (int)keys;
   a.num_parts = 1;
   a.num_chunks = group / hg;
   a.scale_log2 = p.scale * 1.4426950408889634f;
-  a.block_size = kBlockSize;
+  a.block_size = p.cache.block_size;
   a.q_start = p.q_start;
   a.p_hg_shift = __builtin_ctz((unsigned)hg);
   a.p_nqb = (p.max_q_len + kMfmaHeads / hg - 1) / (kMfmaHeads / hg);

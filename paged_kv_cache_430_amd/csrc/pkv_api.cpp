@@ -383,7 +383,7 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
 // every call, overrides the choice where both apply.
 constexpr int64_t kPrefillTileRows = 256 * 64;
 static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
-  const bool cols_ok = (int64_t)p.max_blocks * 16 <= kPrefillColsMaxKeys;
+  const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
   if (env && strcmp(env, "tiles") == 0) cols = false;
@@ -399,7 +399,7 @@ static int prefill_prepare(const char* fn, const CacheView& c, const void* q, in
                            hipStream_t s, PrefillParams* p) {
   p->num_seqs = 0;
   if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16) return fail(PKV_EDTYPE, std::string(fn) + ": cache and q must be BF16");
-  if (c.block_size != 16) return fail(PKV_EINVAL, std::string(fn) + ": block_size must be 16");
+  if (c.block_size < 16) return fail(PKV_EINVAL, std::string(fn) + ": block_size must be 16, 32 or 64");
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
     return fail(PKV_EINVAL, std::string(fn) + ": bad size");
   if (num_q_heads % c.num_kv_heads != 0)
@@ -423,9 +423,9 @@ static int prefill_prepare(const char* fn, const CacheView& c, const void* q, in
     if (qs[0] != 0) return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: q_start[0] != 0");
     for (int i = 0; i < num_seqs; ++i) {
       const int cq = qs[i + 1] - qs[i];
-      if (cq < 0 || cq > max_q_len || lens[i] < cq || (int64_t)lens[i] > (int64_t)max_blocks * 16)
+      if (cq < 0 || cq > max_q_len || lens[i] < cq || (int64_t)lens[i] > (int64_t)max_blocks * c.block_size)
         return fail(PKV_EINVAL, std::string(fn) + ": PKV_CHECK: bad q_start / seq_lens for sequence " + std::to_string(i));
-      if (int st = check_tables(bt, max_blocks, i, lens[i], c.num_blocks, fn)) return st;
+      if (int st = check_tables(bt, max_blocks, i, lens[i], c.num_blocks, fn, c.block_size)) return st;
     }
   }
   p->cache = c;

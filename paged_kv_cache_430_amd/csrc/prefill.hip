@@ -60,6 +60,7 @@ struct Args {
   const int32_t* seq_lens;
   float* out;
   int num_blocks, hkv, hq, max_blocks, num_qtiles, num_chunks;
+  int unit_shift;   // log2(block_size / 16): a pool block holds 1, 2 or 4 16-row units
   float scale_log2;
 };
 
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
   uint16_t* v_lds = v_lds_all[stream];
   const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
   const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;   // queries of this sequence
-  const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], a.max_blocks * kBlockSize));
+  const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], (a.max_blocks << a.unit_shift) * kBlockSize));
   if (qtile * QT >= C || T <= 0) return;
   const int base_pos = T - C;                             // position of query 0
   const int group = a.hq / a.hkv;
@@ -118,7 +119,9 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
   const int kend = min(T, base_pos + wg_last_q + 1);
   const int ntiles = (kend + kKeys - 1) / kKeys;
   const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
-  const size_t head_stride = (size_t)kBlockSize * RB;    // bytes of one (block, head)
+  // 16-row unit u is rows (u mod 2^shift)·16 … of pool block entry u >> shift
+  const int unit_mask = (1 << a.unit_shift) - 1;
+  const size_t head_stride = ((size_t)kBlockSize * RB) << a.unit_shift;   // bytes of one (pool block, head)
 
   // Qᵀ operand: lane holds Q[my_q][dc*32 + kg*8 .. +7]
   bf16x8_t qreg[NDC];
@@ -145,12 +148,13 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
   };
   auto table_entry = [&](int kt) -> int {
     const int lb = kt * kTileBlocks + w;
-    return lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb]) : -1;
+    return lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb >> a.unit_shift]) : -1;
   };
   auto fetch = [&](int kt, int phys, Stage& st) {
     const int rows = min(kBlockSize, max(0, kend - (kt * kTileBlocks + w) * kBlockSize));
     const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
-    const size_t off = ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride;
+    const int unit_row0 = ((kt * kTileBlocks + w) & unit_mask) * kBlockSize;
+    const size_t off = ((size_t)(ok ? phys : 0) * a.hkv + g) * head_stride + (size_t)unit_row0 * RB;
     const int records = __builtin_amdgcn_readfirstlane(ok ? rows * RB : 0);
     const auto rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.kc + off), 0, records, kBufferRsrcWord3);
@@ -382,6 +386,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   a.max_blocks = p.max_blocks;
   a.num_chunks = group / gw;
   a.num_qtiles = (p.max_q_len + (64 / gw) - 1) / (64 / gw);
+  a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   return p.cache.head_dim == 64 ? launch_dh<64>(p, a, gw, s) : launch_dh<128>(p, a, gw, s);
 }

@@ -151,7 +151,7 @@ def test_auto_partition_rule(lib, monkeypatch):
 
 
 def test_block_size_rules(lib, monkeypatch):
-    """8-, 16-, 32- and 64-token blocks; the F32 (vector) decode and the prefill take 16 only."""
+    """8-, 16-, 32- and 64-token blocks; the F32 (vector) decode takes 16 only, the prefill 16, 32 or 64."""
     def decode(ref, b=1, msl=64, dtype=pkv.PKV_BF16):
         return lib.pkv_attn_decode(ref, 0x50000, dtype, b, 8, 0x60000, 4, 0x70000, msl, 0.1, 0, 0x80000,
                                    None, 0, None)
@@ -166,9 +166,13 @@ def test_block_size_rules(lib, monkeypatch):
         monkeypatch.setenv("PKV_DECODE_KERNEL", "vector")
         assert decode(ref) == pkv.PKV_EINVAL
         monkeypatch.delenv("PKV_DECODE_KERNEL")
-        assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                          None, 0, None) == pkv.PKV_EINVAL
-        assert "block_size" in lib.pkv_last_error().decode()
+        if bs == 8:   # the prefill and the mixed step take 16, 32 or 64
+            assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
+                                              None, 0, None) == pkv.PKV_EINVAL
+            assert "block_size" in lib.pkv_last_error().decode()
+        else:         # accepted: nothing to launch with no sequences
+            assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 0, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
+                                              None, 0, None) == pkv.PKV_OK
 
 
 def test_mixed_step_validation(lib):
@@ -179,7 +183,8 @@ def test_mixed_step_validation(lib):
     assert call(ref, ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK        # nothing to do, nothing launched
     assert call(ref, None, ctypes.byref(de)) == pkv.PKV_EINVAL
     assert call(_fake_cache(dtype=pkv.PKV_FP8_E4M3)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EDTYPE
-    assert call(_fake_cache(bs=32)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EINVAL   # prefill: 16 only
+    assert call(_fake_cache(bs=8)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EINVAL    # prefill: 16, 32, 64
+    assert call(_fake_cache(bs=32)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK       # nothing to launch
     assert call(ref, ctypes.byref(ch), ctypes.byref(de), hq=24) == pkv.PKV_EINVAL             # group 3
     # a chunk without its new K/V is refused before any launch
     ch2 = pkv._ChunkBatch(1, 0x50000, 0x1, None, None, 0x2, 4, 0x3, 16, 0x80000)

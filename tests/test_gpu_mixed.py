@@ -24,14 +24,14 @@ def _f64(t):
     return t.float().cpu().double().numpy()
 
 
-def _case(dev, chunks, dec_ctx, hq, hkv, dh, seed):
+def _case(dev, chunks, dec_ctx, hq, hkv, dh, seed, bs=16):
     """chunks: (prefix P, chunk C) per prefill sequence; dec_ctx: cached tokens
     of each decode sequence before its new one. Prefixes and contexts are in
     the pool; the step's tokens are not."""
     gen = torch.Generator(device=dev).manual_seed(seed)
     rng = np.random.default_rng(seed)
     lens = [p + c for p, c in chunks] + [t + 1 for t in dec_ctx]
-    nblk = [-(-t // 16) for t in lens]
+    nblk = [-(-t // bs) for t in lens]
     max_blocks = max(nblk)
     num_blocks = sum(nblk) + 7
     perm = rng.permutation(num_blocks).astype(np.int32)
@@ -40,14 +40,14 @@ def _case(dev, chunks, dec_ctx, hq, hkv, dh, seed):
     for i, n in enumerate(nblk):
         bt[i, :n] = perm[pos:pos + n]
         pos += n
-    kp, vp = new_pools(num_blocks, hkv, dh, "bf16", dev)
+    kp, vp = new_pools(num_blocks, hkv, dh, "bf16", dev, block_size=bs)
     cache = pkv.Cache(kp, vp)
     ks = [_bf16((t, hkv, dh), gen, dev) for t in lens]
     vs = [_bf16((t, hkv, dh), gen, dev) for t in lens]
     first = [p for p, _ in chunks] + list(dec_ctx)          # first position appended by the step
     for i in range(len(lens)):
         if first[i] > 0:
-            s = pkv.pkv_slot_mapping(bt[i], 16, 0, first[i])
+            s = pkv.pkv_slot_mapping(bt[i], bs, 0, first[i])
             pkv.pkv_kv_append(cache, ks[i][:first[i]].contiguous(), vs[i][:first[i]].contiguous(),
                               torch.from_numpy(s).to(dev))
     n_ch = len(chunks)
@@ -123,6 +123,26 @@ def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, monk
     mix = _clone(c["cache"])
     rp, rd = _separate(c, ref, pt)
     mp, md = _mixed(c, mix, pt)
+    torch.cuda.synchronize()
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
+    assert torch.equal(mp, rp)
+    assert torch.equal(md, rd)
+    _oracle_check(c, mp, md)
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("prefill_kernel", ["tiles", "columns"])
+def test_mixed_step_at_block_sizes_32_and_64(bs, prefill_kernel, monkeypatch):
+    """The mixed step on pools of 32- and 64-token blocks: chunk and decode
+    tokens land inside larger blocks; bit-identical to the separate calls."""
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
+    dev = device()
+    c = _case(dev, [(0, 1), (5, 17), (100, 64), (1000, 130), (31, 33)], [0, 1, 15, 16, 200, 1023, 77],
+              32, 8, 128, seed=90 + bs, bs=bs)
+    ref, mix = _clone(c["cache"]), _clone(c["cache"])
+    rp, rd = _separate(c, ref, 48)
+    mp, md = _mixed(c, mix, 48)
     torch.cuda.synchronize()
     assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))

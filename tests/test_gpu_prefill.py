@@ -32,25 +32,26 @@ def _f64(t):
     return t.float().cpu().double().numpy()
 
 
-def _prefill_case(dev, seqs, hq, hkv, dh, seed):
-    """seqs: list of (prefix P, chunk C). Returns (max-abs error, normalised error)."""
+def _prefill_case(dev, seqs, hq, hkv, dh, seed, bs=16):
+    """seqs: list of (prefix P, chunk C); bs: tokens per pool block. Returns
+    (max-abs error, normalised error)."""
     gen = torch.Generator(device=dev).manual_seed(seed)
     rng = np.random.default_rng(seed)
-    total_blocks = sum(-(-(p + c) // 16) for p, c in seqs)
+    total_blocks = sum(-(-(p + c) // bs) for p, c in seqs)
     perm = rng.permutation(total_blocks + 5).astype(np.int32)
-    max_blocks = max(-(-(p + c) // 16) for p, c in seqs)
+    max_blocks = max(-(-(p + c) // bs) for p, c in seqs)
     bt = np.full((len(seqs), max_blocks), -1, dtype=np.int32)
-    kp, vp = new_pools(total_blocks + 5, hkv, dh, "bf16", dev)
+    kp, vp = new_pools(total_blocks + 5, hkv, dh, "bf16", dev, block_size=bs)
     cache = pkv.Cache(kp, vp)
     pos = 0
     qs, ks, vs = [], [], []
     for i, (p, c) in enumerate(seqs):
-        nb = -(-(p + c) // 16)
+        nb = -(-(p + c) // bs)
         bt[i, :nb] = perm[pos:pos + nb]
         pos += nb
         k = _bf16((p + c, hkv, dh), gen, dev)
         v = _bf16((p + c, hkv, dh), gen, dev)
-        slots = pkv.pkv_slot_mapping(bt[i], 16, 0, p + c)
+        slots = pkv.pkv_slot_mapping(bt[i], bs, 0, p + c)
         pkv.pkv_kv_append(cache, k, v, torch.from_numpy(slots).to(dev))
         qs.append(_bf16((c, hq, dh), gen, dev))
         ks.append(k)
@@ -104,6 +105,19 @@ def test_512_chunk_on_2048_tokens_full_size(prefill_kernel):
     dev = device()
     err, rel = _prefill_case(dev, [(2048, 512)], 32, 8, 128, seed=4304)
     assert err <= 2e-3 and rel < 5e-2
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (16, 8, 64), (4, 1, 64)])
+def test_ragged_chunks_at_block_sizes_32_and_64(bs, hq, hkv, dh, prefill_kernel):
+    """Both prefill kernels on pools of 32- and 64-token blocks: a 16-row unit
+    is part of a pool block (rows (u mod bs/16)·16 of entry u / (bs/16)); chunks
+    and prefixes that start and end inside blocks."""
+    dev = device()
+    seqs = [(0, 1), (0, 17), (5, 16), (100, 64), (33, 100), (2048, 3), (0, 130), (40, 9)]
+    err, rel = _prefill_case(dev, seqs, hq, hkv, dh, seed=70 + bs + dh, bs=bs)
+    assert err <= 2e-3, f"max-abs {err:.3e}"
+    assert rel < 5e-2
 
 
 def test_shared_prefix_mixed_step(prefill_kernel):
