@@ -27,6 +27,7 @@ bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
 (--chunk queries on --prefix tokens); `swap`: blocks to pinned host memory
 and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
 streaming-read rate for the decode's 4 KiB tiles, in order and scattered.
+`append`: slot mapping and KV append in one launch, at the mixed step's size and in bulk.
 
 Counter summaries: `--calib-copy` adds, after the timed steps, one
 pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
@@ -82,7 +83,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa-b32-t4096",
                    choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap",
-                            "read-ceiling"])
+                            "read-ceiling", "append"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
@@ -985,6 +986,102 @@ def run_read_ceiling(args, dev):
     }
 
 
+# ---------------------------------------------------------------------------
+# slot mapping + KV append alone
+# ---------------------------------------------------------------------------
+
+def run_append(args, dev):
+    """pkv_kv_append_paged (slot mapping and append in one launch), bf16 pool,
+    Hkv=8, Dh=128, 16-token blocks at a seeded random permutation. Two shapes:
+    the shared-prefix mixed step's appends (a 512-token chunk on a 2048-token
+    cache plus 64 sequences appending one token: 576 tokens) and a bulk append
+    of 16 sequences x 2048 tokens (32768 tokens), whose rate is `value`.
+    Algorithmic bytes per token: K and V read from the input and written to
+    the pool (2 x Hkv x Dh x 2 bytes each way) plus one table entry and one
+    slot computation's inputs (8 bytes)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    hkv, dh, bs = 8, 128, 16
+    per_token = 2 * hkv * dh * 2 * 2 + 8
+    rng = np.random.default_rng(4308)
+    gen = torch.Generator(device=dev).manual_seed(4308)
+    stream = torch.cuda.current_stream(dev)
+
+    def setup(first, counts):
+        total_blocks = sum(-(-(f + c) // bs) for f, c in zip(first, counts))
+        perm = rng.permutation(total_blocks).astype(np.int32)
+        max_blocks = max(-(-(f + c) // bs) for f, c in zip(first, counts))
+        bt = np.full((len(first), max_blocks), -1, dtype=np.int32)
+        pos = 0
+        for i, (f, c) in enumerate(zip(first, counts)):
+            nb = -(-(f + c) // bs)
+            bt[i, :nb] = perm[pos:pos + nb]
+            pos += nb
+        kp = torch.zeros(total_blocks, hkv, bs, dh, dtype=torch.bfloat16, device=dev)
+        cache = pkv.Cache(kp, torch.zeros_like(kp))
+        n = sum(counts)
+        k = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=dev)
+        fp = torch.tensor(np.array(first, dtype=np.int32), device=dev)
+        return cache, k, v, torch.from_numpy(bt).to(dev), cu, fp, max(counts), bt, n
+
+    def timed(c):
+        cache, k, v, btd, cu, fp, mx, _, n = c
+        for _ in range(args.warmup):
+            pkv.pkv_kv_append_paged(cache, k, v, btd, cu, fp, mx)
+        timer = Timer(stream, args.steps)
+        for _ in range(args.steps):
+            timer.start()
+            pkv.pkv_kv_append_paged(cache, k, v, btd, cu, fp, mx)
+            timer.stop()
+        torch.cuda.synchronize()
+        return timer.ms()
+
+    step = setup([2048] + [int(t) for t in rng.integers(256, 2049, 64)], [512] + [1] * 64)
+    bulk = setup([0] * 16, [2048] * 16)
+    ms_step, ms_bulk = timed(step), timed(bulk)
+    avg_bulk = sum(ms_bulk) / len(ms_bulk)
+    gbs = bulk[-1] * per_token / (avg_bulk * 1e-3) / 1e9
+    line = {
+        "metric": "paged KV append (slot mapping + append, one launch), bulk 32768 tokens, GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(avg_bulk, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "append", "kv_heads": hkv, "head_dim": dh, "block_size": bs,
+                   "bulk_tokens": bulk[-1], "step_tokens": step[-1], "bytes_per_token": per_token},
+        "bulk_us": stats_us(ms_bulk),
+        "step_576_tokens_us": stats_us(ms_step),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "kv_append_paged_kernel",
+                     "bytes_per_launch": bulk[-1] * per_token},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        _, k, v, _, _, _, _, bt, _ = bulk
+        kh = k.float().cpu().numpy()
+        vh = v.float().cpu().numpy()
+        pool_k = np.zeros((int(bt.max()) + 1, hkv, bs, dh), dtype=np.float32)
+        pool_v = np.zeros_like(pool_k)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < bulk[-1]:
+            seq, off = divmod(done, 2048)
+            slots = oracle.paging.slot_mapping(bt[seq], off, 256, bs)
+            oracle.paging.append(pool_k, kh[done:done + 256], slots, bs)
+            oracle.paging.append(pool_v, vh[done:done + 256], slots, bs)
+            done += 256
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(done * per_token / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "host": _host_libs(),
+                                "sample": f"{done} of the bulk tokens through the oracle's slot mapping and "
+                                          f"append (Python loop per token), {el:.2f} s"}
+    return line
+
+
 def main():
     args = parse()
     if args.counters:
@@ -1015,6 +1112,8 @@ def main():
         line = run_prefill_chunk(args, dev)
     elif args.workload == "read-ceiling":
         line = run_read_ceiling(args, dev)
+    elif args.workload == "append":
+        line = run_append(args, dev)
     else:
         line = run_decode(args, dev)
     print(json.dumps(line), flush=True)
