@@ -28,6 +28,7 @@ bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
 and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
 streaming-read rate for the decode's 4 KiB tiles, in order and scattered.
 `append`: slot mapping and KV append in one launch, at the mixed step's size and in bulk.
+`allocator`: the host block allocator on the shared-prefix workload's bookkeeping.
 
 Counter summaries: `--calib-copy` adds, after the timed steps, one
 pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
@@ -83,7 +84,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa-b32-t4096",
                    choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap",
-                            "read-ceiling", "append"])
+                            "read-ceiling", "append", "allocator"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
@@ -1082,6 +1083,94 @@ def run_append(args, dev):
     return line
 
 
+# ---------------------------------------------------------------------------
+# the host block allocator
+# ---------------------------------------------------------------------------
+
+def run_allocator(args):
+    """Host workload for the block allocator: the shared-prefix workload's
+    block bookkeeping, built and torn down once per step. 16 sequences share
+    a 1024-token prefix (64 full blocks, one allocation then 15 increfs) and
+    grow 1024 private tokens each; sequence 0 reserves a 512-token chunk; 64
+    other sequences reserve their contexts (uniform in [257, 2049] tokens);
+    then every table is released (decref). Reported as allocator calls per
+    second through the Python binding (each call crosses ctypes); the
+    oracle's pure-Python model runs the same calls."""
+    import numpy as np
+
+    import paged_kv_cache_430_amd as pkv
+    from oracle import allocator as oalloc
+
+    bs, shared, private, chunk, n_share = 16, 1024, 1024, 512, 16
+    rng = np.random.default_rng(4304)
+    ctx = rng.integers(257, 2050, 64)
+    max_blocks = (shared + private + chunk) // bs + 1
+    num_blocks = shared // bs + n_share * private // bs + chunk // bs + int(sum(-(-int(t) // bs) for t in ctx)) + 64
+
+    def one_step(a, native):
+        calls = 0
+        def reserve(t, l, n):
+            nonlocal calls
+            calls += 1
+            if native:
+                a.reserve_append(t, l, n)
+                return t
+            st, t2, _ = a.reserve_append(t, l, n)
+            assert st == oalloc.OK
+            return t2
+        def table():
+            return np.full(max_blocks, -1, dtype=np.int32) if native else [-1] * max_blocks
+        prefix = reserve(table(), 0, shared)
+        tables = []
+        for i in range(n_share):
+            t = prefix.copy() if native else list(prefix)
+            if i > 0:
+                a.incref(t[:shared // bs])
+                calls += 1
+            tables.append(reserve(t, shared, private))
+        tables[0] = reserve(tables[0], shared + private, chunk)
+        for c in ctx:
+            tables.append(reserve(table(), 0, int(c)))
+        for t in tables:
+            a.decref(t[t >= 0] if native else [x for x in t if x >= 0])
+            calls += 1
+        return calls
+
+    nat = pkv.BlockAllocator(num_blocks, bs)
+    for _ in range(args.warmup):
+        one_step(nat, True)
+    t0 = time.perf_counter()
+    calls = 0
+    for _ in range(args.steps):
+        calls += one_step(nat, True)
+    el = time.perf_counter() - t0
+    assert nat.num_free() == num_blocks
+    line = {
+        "metric": "block allocator: shared-prefix set-up and release, allocator calls per second (host)",
+        "value": round(calls / el, 1), "unit": "calls/s", "n_gpus": 0, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "allocator", "block_size": bs, "num_blocks": num_blocks, "sharers": n_share,
+                   "shared_tokens": shared, "private_tokens": private, "chunk": chunk, "decodes": len(ctx),
+                   "calls_per_step": calls // args.steps},
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        model = oalloc.ModelAllocator(num_blocks, bs)
+        t0 = time.perf_counter()
+        reps, mcalls = 0, 0
+        while reps < args.steps and time.perf_counter() - t0 < args.cpu_seconds:
+            mcalls += one_step(model, False)
+            reps += 1
+        mel = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(mcalls / mel, 1), "unit": "calls/s", "cores": 1,
+                                "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "host": _host_libs(),
+                                "sample": f"{reps} of the same steps on the oracle's pure-Python allocator model, "
+                                          f"{mel:.2f} s"}
+    return line
+
+
 def main():
     args = parse()
     if args.counters:
@@ -1095,6 +1184,9 @@ def main():
 
     if args.workload == "prefix-index":   # host only
         print(json.dumps(run_prefix_index(args)), flush=True)
+        return
+    if args.workload == "allocator":      # host only
+        print(json.dumps(run_allocator(args)), flush=True)
         return
 
     import torch
