@@ -156,6 +156,23 @@ def test_gqa_b32_ragged_full_size():
         assert_close(got, ref, 2e-3, f"{kern} B=32 ragged")
 
 
+@pytest.mark.parametrize("hq,hkv,b", [(8, 2, 301), (32, 8, 97), (12, 6, 150)])
+def test_many_sequences_ragged_every_workgroup_order(hq, hkv, b):
+    """Hundreds of short ragged sequences: several rounds of workgroups, and
+    grids that are not a whole number of rounds of 8 XCD groups, so both the
+    grouped part of the workgroup order and its hardware-order tail run;
+    explicit partitions split some sequences."""
+    dev = device()
+    rng = np.random.default_rng(b + hkv)
+    lens_ = [int(x) for x in rng.integers(1, 300, b)]
+    w = workloads.decode_inputs("many", 31 + b, lens_, hq, hkv, 64, "bf16", dev)
+    cache = build_cache(w, dev)
+    ref = oracle_decode(w)
+    for pt in (0, 16, 112):
+        got = run_decode(w, cache, dev, partition_tokens=pt, kernel="matrix")
+        assert_close(got, ref, 2e-3, f"B={b} {hq}/{hkv} pt{pt}")
+
+
 def test_gqa_b32_t4096_full_size_each_copy():
     """The metric configuration, every table copy the benchmark rotates through."""
     dev = device()
