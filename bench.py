@@ -571,7 +571,7 @@ def run_mixed(args, dev):
         pkv._check(lib.pkv_attn_prefill_chunk(S["cache"].ref(), m.chunk_q.data_ptr(), pkv.PKV_BF16, 1, hq,
                                               S["q_start"].data_ptr(), S["chunk_table"].data_ptr(),
                                               S["max_blocks"], S["chunk_lens"].data_ptr(), m.chunk, m.scale,
-                                              out_p.data_ptr(), None, 0, sh))
+                                              out_p.data_ptr(), sh))
         if tp is not None:
             tp.stop()
             td.start()
@@ -699,8 +699,8 @@ def run_prefill_chunk(args, dev):
 
     def step():
         pkv._check(lib.pkv_attn_prefill_chunk(cache.ref(), q.data_ptr(), pkv.PKV_BF16, 1, hq, q_start.data_ptr(),
-                                              table.data_ptr(), nb, lens.data_ptr(), C, scale, out.data_ptr(), None,
-                                              0, stream.cuda_stream))
+                                              table.data_ptr(), nb, lens.data_ptr(), C, scale, out.data_ptr(),
+                                              stream.cuda_stream))
 
     for _ in range(args.warmup):
         step()

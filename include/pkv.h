@@ -262,7 +262,7 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   max_q_len: host bound on C_s (sizes the grid)
  *   out:      device fp32, same shape as q
  * Cache dtype BF16, block_size 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2 or a
- * multiple of 4 up to 64. No workspace is needed (pass NULL, 0).
+ * multiple of 4 up to 64. No workspace is needed.
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
  * workgroup, key tiles shared through LDS), and the matrix-core decode kernel
  * with (query head, query) pairs as its 16 columns and the keys split across
@@ -275,8 +275,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,
                                    const int32_t* seq_lens, int32_t max_q_len, float scale,
-                                   float* out, void* workspace, size_t workspace_bytes,
-                                   pkv_stream stream);
+                                   float* out, pkv_stream stream);
 
 /* ---------------------------------------------------------------------------
  * One continuous-batching step over a mixed batch — [P3] 6.6 (at an

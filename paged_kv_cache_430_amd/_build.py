@@ -2,11 +2,23 @@
 
 Every call recompiles all sources (each translation unit in parallel) and
 links `paged_kv_cache_430_amd/libpkv.so`. hipcc cross-compiles without a GPU.
+
+`python -m paged_kv_cache_430_amd._build --asan` builds a second library,
+`_build_asan/libpkv_asan.so`, whose host-only sources (argument validation,
+the allocator, the prefix index) are compiled by g++ with AddressSanitizer;
+the kernels are the same objects as in libpkv.so. Run the host tests on it
+with the sanitizer runtime preloaded (the interpreter itself is not
+instrumented):
+
+    LD_PRELOAD=$(g++ -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+    PKV_LIB=paged_kv_cache_430_amd/_build_asan/libpkv_asan.so \
+    python -m pytest tests -m "not gpu"
 """
 
 import os
 import shutil
 import subprocess
+import sys
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -16,6 +28,10 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp", "kv_append.hip", "decode.hip", "prefill.hip",
            "read_probe.hip"]
+HOST_SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp"]   # no device code
+ASAN_DIR = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libpkv_asan.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -63,5 +79,40 @@ def build(verbose=False):
     return LIB
 
 
+def _run(cmd, what):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{what} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+
+def build_asan(verbose=False):
+    """libpkv.so's kernels plus AddressSanitizer-instrumented host sources.
+
+    The host sources call the HIP runtime API only, so g++ compiles them
+    against the ROCm headers; the kernel objects come from build()."""
+    build(verbose=verbose)
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    gxx = shutil.which("g++")
+    if not gxx:
+        raise RuntimeError("g++ not found")
+    flags = ["-O1", "-g", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden", "-fno-omit-frame-pointer",
+             "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
+    san = "-fsanitize=address"
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(ASAN_DIR, src + ".o")
+        _run([gxx, *flags, san, "-c", os.path.join(CSRC, src), "-o", obj], f"g++ (asan) {src}")
+        objs.append(obj)
+    objs += [os.path.join(BUILD, src + ".o") for src in SOURCES if src not in HOST_SOURCES]
+    _run([gxx, "-shared", san, "-o", ASAN_LIB, *objs, "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"], "asan link")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--asan" in sys.argv[1:]:
+        build_asan(verbose=True)
+    else:
+        build(verbose=True)

@@ -12,12 +12,16 @@
 namespace pkv {
 
 // Slot of logical position pos through one sequence's table row; −1 when the
-// position's block is beyond max_blocks or its entry is negative.
+// position's block is beyond max_blocks, its entry is negative, or the slot
+// does not fit in int32 (a garbage entry must not wrap into the pool: the
+// product is formed in 64 bits, and any slot the pool can hold is below 2^31).
 __device__ __forceinline__ int slot_of(const int32_t* __restrict__ bt, int max_blocks, int pos, int bs) {
   const int lb = pos / bs;
   if (pos < 0 || lb >= max_blocks) return -1;
   const int phys = bt[lb];
-  return phys >= 0 ? phys * bs + pos % bs : -1;
+  if (phys < 0) return -1;
+  const int64_t slot = (int64_t)phys * bs + pos % bs;
+  return slot <= (int64_t)INT32_MAX ? (int)slot : -1;
 }
 
 // One token's K and V rows into its slot: threads of the workgroup stride

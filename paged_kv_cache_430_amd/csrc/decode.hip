@@ -1242,7 +1242,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (p.batch == 0 && p.x_seqs == 0) return hipSuccess;
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int hc = decode_heads_per_wg(group, p.kernel);
-  KernelArgs a;
+  KernelArgs a{};
   a.kc = static_cast<uint8_t*>(p.cache.k);
   a.vc = static_cast<uint8_t*>(p.cache.v);
   a.k_scale = p.cache.k_scale;

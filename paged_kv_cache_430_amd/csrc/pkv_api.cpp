@@ -469,10 +469,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,
                                    const int32_t* seq_lens, int32_t max_q_len, float scale,
-                                   float* out, void* workspace, size_t workspace_bytes,
-                                   pkv_stream stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                                   float* out, pkv_stream stream) {
   clear_error();
   CacheView c;
   if (int st = validate_cache(cache, "pkv_attn_prefill_chunk", &c)) return st;
@@ -506,7 +503,7 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
       return fail(PKV_EINVAL, std::string(fn) + ": chunk k_new / v_new must be 16-byte aligned");
   }
   const NewTokens app{decodes->k_new, decodes->v_new, PKV_BF16, nullptr, nullptr};
-  DecodeParams dp;
+  DecodeParams dp{};
   if (int st = decode_prepare(fn, c, &app, decodes->q, PKV_BF16, decodes->batch, num_q_heads, decodes->block_tables,
                               decodes->max_blocks, decodes->seq_lens, decodes->max_seq_len, scale,
                               decodes->partition_tokens, decodes->out, decodes->workspace, decodes->workspace_bytes,

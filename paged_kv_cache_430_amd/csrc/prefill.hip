@@ -150,6 +150,18 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
     const int lb = kt * kTileBlocks + w;
     return lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb >> a.unit_shift]) : -1;
   };
+  // bit b set: block b of key tile kt names a pool block (an id outside the
+  // pool, or −1, reads as zeros and its keys must be masked, not scored 0)
+  auto tile_valid = [&](int kt) -> int {
+    int mask = 0;
+#pragma unroll
+    for (int b = 0; b < kTileBlocks; ++b) {
+      const int lb = kt * kTileBlocks + b;
+      const int phys = lb * kBlockSize < kend ? __builtin_amdgcn_readfirstlane(bt[lb >> a.unit_shift]) : 0;
+      mask |= ((unsigned)phys < (unsigned)a.num_blocks) << b;
+    }
+    return mask;
+  };
   auto fetch = [&](int kt, int phys, Stage& st) {
     const int rows = min(kBlockSize, max(0, kend - (kt * kTileBlocks + w) * kBlockSize));
     const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
@@ -208,13 +220,15 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
       }
       st[t4] = acc;
     }
-    // inclusive causal mask, only where the tile reaches past the wave's first query
-    if (key0 + kKeys - 1 > wave_first_pos) {
+    // inclusive causal mask, only where the tile reaches past the wave's
+    // first query, and the keys of blocks outside the pool
+    const int valid = tile_valid(kt);
+    if (key0 + kKeys - 1 > wave_first_pos || valid != (1 << kTileBlocks) - 1) {
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (key0 + t4 * 16 + kg * 4 + i > my_pos) st[t4][i] = -INFINITY;
+          if (key0 + t4 * 16 + kg * 4 + i > my_pos || !((valid >> t4) & 1)) st[t4][i] = -INFINITY;
     }
     // online softmax: the lane's 16 scores all belong to query my_q
     float mt = fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3]));
@@ -322,8 +336,8 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
       __syncthreads();
       if (stream == 0) {
         const float m1 = mine[0];
-        const float mt = fmaxf(m_run, m1);                 // finite: stream 0 saw key 0
-        const float a0 = fast_exp2((m_run - mt) * a.scale_log2);
+        const float mt = fmaxf(m_run, m1);                 // −inf only if neither saw a valid key
+        const float a0 = m_run == -INFINITY ? 0.0f : fast_exp2((m_run - mt) * a.scale_log2);
         const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2((m1 - mt) * a.scale_log2);
         l_run = a0 * l_run + a1 * mine[1];
 #pragma unroll
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(NS * kStreamWaves * kWave) void prefill_kernel(Args
   // ---- finish: l over the four lanes of a query, o = u / l ----
   const float lt = pair_halves32(pair_rows16(l_run, AddOp()), AddOp());
   if (!q_valid) return;
-  const float inv = 1.0f / lt;
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;   // no valid key at all: zeros
   float* op = a.out + ((size_t)(q_lo + my_q) * a.hq + head) * DH + kg * 4;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {

@@ -76,3 +76,32 @@ def tables(w, dev, copy=0):
 
 def lens(w, dev):
     return torch.from_numpy(w.seq_lens.astype(np.int32)).to(dev)
+
+
+def parity(label, got, ref, tol, norm_tol=None):
+    """Assert max-abs(got − ref) <= tol over every listed sequence (and, with
+    norm_tol, max-abs / max|ref| <= norm_tol: at long contexts |o| is small,
+    so the absolute bound alone is loose). got, ref: dicts of arrays keyed by
+    sequence, or two arrays. Returns (max-abs, normalised error). When
+    PKV_PARITY_LOG names a file, one JSON line per call is appended to it."""
+    import json
+    import os
+    if not isinstance(ref, dict):
+        got, ref = {0: np.asarray(got)}, {0: np.asarray(ref)}
+    err, peak = 0.0, 0.0
+    for b, r in ref.items():
+        g = np.asarray(got[b])
+        assert np.isfinite(g).all(), f"{label}: non-finite output for sequence {b}"
+        e = float(np.abs(g - r).max()) if r.size else 0.0
+        assert e <= tol, f"{label}: sequence {b} max-abs error {e:.3e} > {tol}"
+        err = max(err, e)
+        peak = max(peak, float(np.abs(r).max()) if r.size else 0.0)
+    norm = err / peak if peak > 0 else 0.0
+    if norm_tol is not None:
+        assert norm <= norm_tol, f"{label}: max-abs / max|o| = {norm:.3e} > {norm_tol}"
+    path = os.environ.get("PKV_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": label, "max_abs": err, "max_abs_out": peak, "normalised": norm,
+                                "tol": tol, "norm_tol": norm_tol}) + "\n")
+    return err, norm

@@ -168,11 +168,11 @@ def test_block_size_rules(lib, monkeypatch):
         monkeypatch.delenv("PKV_DECODE_KERNEL")
         if bs == 8:   # the prefill and the mixed step take 16, 32 or 64
             assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                              None, 0, None) == pkv.PKV_EINVAL
+                                              None) == pkv.PKV_EINVAL
             assert "block_size" in lib.pkv_last_error().decode()
         else:         # accepted: nothing to launch with no sequences
             assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 0, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                              None, 0, None) == pkv.PKV_OK
+                                              None) == pkv.PKV_OK
 
 
 def test_mixed_step_validation(lib):
@@ -207,11 +207,11 @@ def test_append_and_prefill_validation(lib):
     ref8, _ = _fake_cache(dtype=pkv.PKV_FP8_E4M3)
     assert lib.pkv_kv_append(ref8, 0x50000, 0x60000, pkv.PKV_BF16, 4, 0x70000, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_attn_prefill_chunk(ref8, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                      None, 0, None) == pkv.PKV_EDTYPE
+                                      None) == pkv.PKV_EDTYPE
     assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 24, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                      None, 0, None) == pkv.PKV_EINVAL     # group 3
+                                      None) == pkv.PKV_EINVAL     # group 3
     assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 2 ** 20, 32, 0x1, 0x2, 4, 0x3, 1024, 0.1, 0x80000,
-                                      None, 0, None) == pkv.PKV_EINVAL     # grid past 2^31 - 1
+                                      None) == pkv.PKV_EINVAL     # grid past 2^31 - 1
     assert "2^31" in lib.pkv_last_error().decode()
     # fused slot mapping + append: same dtype rules, pointer and size checks
     ap = lib.pkv_kv_append_paged

@@ -16,11 +16,19 @@ import paged_kv_cache_430_amd as pkv
 import workloads
 from oracle import attention
 
-from gpu_helpers import build_cache, device, lens, oracle_seq, tables
+from gpu_helpers import build_cache, device, lens, oracle_seq, parity, tables
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-3}
+# Full-size configurations also bound the error relative to the largest
+# output magnitude: with N(0,1) inputs |o| falls to a few hundredths at
+# T = 4096–32768, where 2e-3 absolute alone would allow a few percent. The
+# kernels accumulate in fp32 from exact bf16/e4m3 operands, and the matrix
+# form carries probabilities to ~16 bits (2^-16 ≈ 1.5e-5 relative per term,
+# averaging down over many keys), so 1e-4 leaves a wide margin over what the
+# arithmetic allows and still catches any dropped or doubled term.
+NORM_TOL = 1e-4
 
 
 def kernels_for(cache_dtype):
@@ -153,7 +161,7 @@ def test_gqa_b32_ragged_full_size():
     ref = oracle_decode(w)
     for kern in kernels_for("bf16"):
         got = run_decode(w, cache, dev, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} B=32 ragged")
+        parity(f"decode {kern} gqa-b32-ragged", got, ref, 2e-3, NORM_TOL)
 
 
 @pytest.mark.parametrize("hq,hkv,b", [(8, 2, 301), (32, 8, 97), (12, 6, 150)])
@@ -179,13 +187,10 @@ def test_gqa_b32_t4096_full_size_each_copy():
     w = workloads.gqa_b32("all4096", device=dev, copies=2)
     cache = build_cache(w, dev)
     ref = oracle_decode(w)
-    scale_ref = max(float(np.abs(r).max()) for r in ref.values())
     for kern in kernels_for("bf16"):
         for c in range(w.copies):
             got = run_decode(w, cache, dev, copy=c, kernel=kern)
-            assert_close(got, ref, 2e-3, f"{kern} B=32 T=4096 copy {c}")
-            rel = max(float(np.abs(got[b] - ref[b]).max()) for b in ref) / scale_ref
-            assert rel < 2e-2
+            parity(f"decode {kern} gqa-b32-t4096 copy {c}", got, ref, 2e-3, NORM_TOL)
 
 
 @pytest.mark.parametrize("kind", ["mha", "gqa", "mqa", "gqa-fp8"])
@@ -196,7 +201,7 @@ def test_head_layouts_t8192_full_size(kind):
     ref = oracle_decode(w)
     for kern in kernels_for("bf16"):
         got = run_decode(w, cache, dev, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} T=8192 {kind}")
+        parity(f"decode {kern} {kind}-b8-t8192", got, ref, 2e-3, NORM_TOL)
 
 
 def test_long_context_b1_layers_and_b4():
@@ -207,14 +212,18 @@ def test_long_context_b1_layers_and_b4():
         ref = oracle_decode(w)
         for kern in kernels_for("bf16"):
             got = run_decode(w, cache, dev, partition_tokens=512, kernel=kern)
-            assert_close(got, ref, 2e-3, f"{kern} T=32768 B=1 layer {li}")
+            parity(f"decode {kern} long-b1-t32768 layer {li} pt512", got, ref, 2e-3, NORM_TOL)
+        got = run_decode(w, cache, dev, kernel="matrix")
+        parity(f"decode matrix long-b1-t32768 layer {li} auto", got, ref, 2e-3, NORM_TOL)
         del cache
     w4 = workloads.long_context(batch=4, device=dev, layers=1)[0]
     cache = build_cache(w4, dev)
     ref = oracle_decode(w4)
     for kern in kernels_for("bf16"):
         got = run_decode(w4, cache, dev, partition_tokens=512, kernel=kern)
-        assert_close(got, ref, 2e-3, f"{kern} T=32768 B=4")
+        parity(f"decode {kern} long-b4-t32768 pt512", got, ref, 2e-3, NORM_TOL)
+    got = run_decode(w4, cache, dev, kernel="matrix")
+    parity("decode matrix long-b4-t32768 auto", got, ref, 2e-3, NORM_TOL)
 
 
 @pytest.mark.parametrize("cache_dtype,kern", [("f32", "vector"), ("bf16", "vector"), ("bf16", "matrix")])
