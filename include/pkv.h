@@ -214,6 +214,28 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
                             float scale, int32_t partition_tokens, float* out,
                             void* workspace, size_t workspace_bytes, pkv_stream stream);
 
+/* pkv_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split-KV partials go to the
+ * library's own static device array of 8 MiB (8,388,608 bytes) per GPU,
+ * which each GPU the library runs on holds until the process ends; its
+ * device address is looked up on the first call on a device. The call
+ * allocates nothing and launches the same kernels with the same partition
+ * choice as pkv_attn_decode, so the output is identical. The caller passes
+ * inputs and outputs as for pkv_attn_decode.
+ * PKV_EWORKSPACE (nothing launched) if pkv_attn_decode_workspace_bytes for
+ * the same arguments exceeds 8 MiB (for example batch 4, 32 query heads,
+ * head_dim 128 and 64 partitions need 4.26 MB; pick larger partitions
+ * otherwise). Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (several streams, several threads) race and must be
+ * serialised by the caller. The array needs no clearing (its contents are
+ * written before they are read in every call). PKV_CHECK is not honoured
+ * here (its checking copies would allocate and synchronise). */
+PKV_API int pkv_attn_decode_noalloc(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
+                                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                    int32_t partition_tokens, float* out, pkv_stream stream);
+
 /* The decode step's append and attention in one launch (BF16 and FP8
  * caches): sequence b's new token k_new[b], v_new[b] ([batch, num_kv_heads,
  * head_dim] in in_dtype, 16-byte aligned; BF16 for a BF16 cache, BF16 or F32

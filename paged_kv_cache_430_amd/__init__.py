@@ -18,7 +18,7 @@ __all__ = [
     "PKVError", "Cache", "BlockAllocator", "PrefixIndex", "load",
     "pkv_version", "pkv_slot_mapping", "pkv_slot_mapping_device", "pkv_kv_append", "pkv_kv_append_paged",
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
-    "pkv_attn_decode_append",
+    "pkv_attn_decode_append", "pkv_attn_decode_noalloc",
     "pkv_attn_prefill_chunk", "pkv_attn_mixed_step", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
     "pkv_debug_stream_read",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
@@ -77,6 +77,8 @@ _SIGS = {
     "pkv_attn_decode_auto_partition": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_attn_decode": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32, _VP,
                                        _I32, ctypes.c_float, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
+    "pkv_attn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _I32, _I32, _VP, _I32,
+                                               _VP, _I32, ctypes.c_float, _I32, _VP, _VP]),
     "pkv_attn_decode_append": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _VP, _I32, _VP, _VP, _VP, _I32,
                                               _I32, _I32, _VP, _I32, _VP, _I32, ctypes.c_float, _I32, _VP, _VP,
                                               ctypes.c_size_t, _VP]),
@@ -252,6 +254,17 @@ def pkv_attn_decode(cache, q, block_tables, seq_lens, max_seq_len, scale, partit
     _check(load().pkv_attn_decode(cache.ref(), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
                                   block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
                                   partition_tokens, _ptr(out), _ptr(workspace), wbytes, _stream(stream, dev)))
+    return out
+
+
+def pkv_attn_decode_noalloc(cache, q, block_tables, seq_lens, max_seq_len, scale, out, partition_tokens=0,
+                            stream=None):
+    """pkv_attn_decode with the library's static split-KV scratch: no workspace,
+    and nothing allocated (out is the caller's [B, Hq, Dh] fp32 tensor)."""
+    b, hq, dh = q.shape
+    _check(load().pkv_attn_decode_noalloc(cache.ref(), _ptr(q), _dtype_code(q), b, hq, _ptr(block_tables),
+                                          block_tables.shape[1], _ptr(seq_lens), max_seq_len, float(scale),
+                                          partition_tokens, _ptr(out), _stream(stream, q.device)))
     return out
 
 

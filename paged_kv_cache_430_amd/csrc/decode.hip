@@ -40,6 +40,8 @@
 // Masked slots (past the sequence end) are selected out or read as zeros,
 // never multiplied by zero, and blocks whose id is outside the pool are
 // skipped: pool slots may hold NaN.
+#include <mutex>
+
 #include "append_common.h"
 #include "device_common.h"
 #include "launch.h"
@@ -1302,6 +1304,31 @@ int prefill_cols_heads(int group) {
   int hg = 1;
   while (hg < kMfmaHeads && group % (2 * hg) == 0) hg *= 2;
   return hg;
+}
+
+// Split-KV scratch of pkv_attn_decode_noalloc, for callers that cannot
+// allocate device memory. Each GPU that runs the library holds its own copy of
+// this array until the process ends. Host code never passes `scratch` itself
+// to a kernel (on the host the name stands for a host-side shadow, not a
+// device address): the device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current and kept per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+hipError_t decode_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s) {

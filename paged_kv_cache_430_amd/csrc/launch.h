@@ -96,6 +96,12 @@ hipError_t launch_stream_read(const void* buf, int64_t buf_tiles, const int32_t*
                               uint32_t* sink, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
+// The library's own split-KV scratch for pkv_attn_decode_noalloc: a static
+// device array of kDecodeStaticScratchBytes per GPU. *ptr receives its device
+// address on the current device (looked up on the first call per device).
+constexpr size_t kDecodeStaticScratchBytes = size_t(8) << 20;
+hipError_t decode_static_scratch(void** ptr);
+
 struct PrefillParams {
   CacheView cache;
   const void* q;

@@ -273,7 +273,7 @@ static int decode_prepare(const char* fn, const CacheView& c, const NewTokens* a
                           int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
                           const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
                           float* out, void* workspace, size_t workspace_bytes, int kernel, hipStream_t s,
-                          DecodeParams* p) {
+                          DecodeParams* p, bool static_scratch = false) {
   p->cache = c;
   p->batch = 0;
   p->num_q_heads = num_q_heads;
@@ -314,10 +314,19 @@ static int decode_prepare(const char* fn, const CacheView& c, const NewTokens* a
       return fail(PKV_EINVAL, std::string(fn) + ": batch x heads x partitions needs more than 2^31 - 1 workgroups");
   }
   const size_t need = decode_ws_bytes(batch, num_q_heads, c.head_dim, max_seq_len, pt);
+  if (static_scratch && need > 0) {   // the library's static array instead of a caller's workspace
+    if (need > kDecodeStaticScratchBytes)
+      return fail(PKV_EWORKSPACE, std::string(fn) + ": the split-KV partials need " + std::to_string(need) +
+                                      " bytes, more than the library's static scratch of " +
+                                      std::to_string(kDecodeStaticScratchBytes) +
+                                      " bytes; pass larger partitions or use pkv_attn_decode with a workspace");
+    if (hipError_t e = decode_static_scratch(&workspace)) return hip_status(e, fn);
+    workspace_bytes = kDecodeStaticScratchBytes;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) + " bytes");
   if (need > 0 && !aligned16(workspace)) return fail(PKV_EINVAL, std::string(fn) + ": workspace must be 16-byte aligned");
-  if (check_mode()) {
+  if (check_mode() && !static_scratch) {   // the no-allocation call skips the checking copies
     std::vector<int32_t> lens, bt;
     if (int st = copy_to_host(lens, seq_lens, (size_t)batch, s)) return st;
     if (int st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks, s)) return st;
@@ -354,7 +363,8 @@ static int decode_prepare(const char* fn, const CacheView& c, const NewTokens* a
 static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* app, const void* q, int32_t q_dtype,
                        int32_t batch, int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_tokens,
-                       float* out, void* workspace, size_t workspace_bytes, pkv_stream stream) {
+                       float* out, void* workspace, size_t workspace_bytes, pkv_stream stream,
+                       bool static_scratch = false) {
   clear_error();
   CacheView c;
   if (int st = validate_cache(cache, fn, &c)) return st;
@@ -362,7 +372,8 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeParams p;
   if (int st = decode_prepare(fn, c, app, q, q_dtype, batch, num_q_heads, block_tables, max_blocks, seq_lens,
-                              max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes, kernel, s, &p))
+                              max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes, kernel, s, &p,
+                              static_scratch))
     return st;
   if (p.batch == 0) return PKV_OK;
   if (app && kernel != kDecodeMatrix) {   // the vector form: an append launch first
@@ -451,6 +462,14 @@ PKV_API int pkv_attn_decode(const pkv_cache* cache, const void* q, int32_t q_dty
                             size_t workspace_bytes, pkv_stream stream) {
   return decode_impl("pkv_attn_decode", cache, nullptr, q, q_dtype, batch, num_q_heads, block_tables, max_blocks,
                      seq_lens, max_seq_len, scale, partition_tokens, out, workspace, workspace_bytes, stream);
+}
+
+PKV_API int pkv_attn_decode_noalloc(const pkv_cache* cache, const void* q, int32_t q_dtype, int32_t batch,
+                                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                    int32_t partition_tokens, float* out, pkv_stream stream) {
+  return decode_impl("pkv_attn_decode_noalloc", cache, nullptr, q, q_dtype, batch, num_q_heads, block_tables,
+                     max_blocks, seq_lens, max_seq_len, scale, partition_tokens, out, nullptr, 0, stream, true);
 }
 
 PKV_API int pkv_attn_decode_append(const pkv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,

@@ -28,11 +28,25 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 31
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
     assert set(names) <= set(pkv._SIGS), set(names) - set(pkv._SIGS)
+
+
+def test_noalloc_decode_refuses_partials_beyond_its_static_scratch(lib):
+    """pkv_attn_decode_noalloc checks its partials against the static 8 MiB on
+    the host, before touching any device: 32 sequences x 32 heads x 64
+    partitions x (128 + 2) floats = 34 MB is refused; a bad argument is still
+    EINVAL; an empty batch launches nothing."""
+    ref, _ = _fake_cache()
+    call = lambda b, msl, pt, hq=32: lib.pkv_attn_decode_noalloc(ref, 0x50000, pkv.PKV_BF16, b, hq, 0x1, 64, 0x2,  # noqa: E731
+                                                                 msl, 0.1, pt, 0x80000, None)
+    assert call(32, 1024, 16) == pkv.PKV_EWORKSPACE
+    assert "static scratch" in lib.pkv_last_error().decode()
+    assert call(32, 1024, 24) == pkv.PKV_EINVAL           # partition not a multiple of 16
+    assert call(0, 1024, 16) == pkv.PKV_OK
 
 
 def test_version_and_error_string(lib):
