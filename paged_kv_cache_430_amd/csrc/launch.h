@@ -114,6 +114,9 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// The key-stream tile kernel: 64 query rows per workgroup, two key streams,
+// each a wave per 32-row half (see prefill.hip).
+hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s);
 
 // The same chunked prefill on the matrix-core decode kernel: each workgroup
 // takes 16 (query head, query) columns of one KV group — prefill_cols_heads

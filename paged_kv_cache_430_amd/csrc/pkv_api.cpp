@@ -397,9 +397,10 @@ static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
   const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
-  if (env && strcmp(env, "tiles") == 0) cols = false;
+  if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0)) cols = false;
   if (env && strcmp(env, "columns") == 0) cols = cols_ok;
-  return cols ? launch_prefill_cols(p, s) : launch_prefill(p, s);
+  if (cols) return launch_prefill_cols(p, s);
+  return env && strcmp(env, "tiles16") == 0 ? launch_prefill(p, s) : launch_prefill_stream(p, s);
 }
 
 // Checks a prefill call's arguments and fills *p; p->num_seqs == 0 means
@@ -425,7 +426,8 @@ static int prefill_prepare(const char* fn, const CacheView& c, const void* q, in
     return fail(PKV_EINVAL, std::string(fn) + ": sequences x heads x queries need more than 2^31 - 1 workgroups");
   if (!q || !q_start || !block_tables || !seq_lens || !out) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, std::string(fn) + ": q and out must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, std::string(fn) + ": scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PKV_EINVAL, std::string(fn) + ": scale must be positive and finite");
   if (check_mode()) {
     std::vector<int32_t> qs, lens, bt;
     if (int st = copy_to_host(qs, q_start, (size_t)num_seqs + 1, s)) return st;

@@ -35,6 +35,8 @@
 //     shuffle of P is needed; P enters as a bf16 high part (truncated) plus the
 //     bf16 rounding of the remainder (two MFMAs), which keeps the
 //     probabilities to ~16 bits.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -403,6 +405,612 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   return p.cache.head_dim == 64 ? launch_dh<64>(p, a, gw, s) : launch_dh<128>(p, a, gw, s);
+}
+
+// ===========================================================================
+// Key-stream form (the tile kernel): a workgroup of four waves, one per SIMD,
+// owns 64 query rows (GW ≤ 4 heads of one KV group × 64/GW queries). Wave w
+// takes row half w % 2 (32 rows) of key stream w / 2: stream s scores the
+// 32-key tiles s, s+2, s+4, …, and the two waves of a stream share each tile
+// through LDS. Per tile:
+//   * K and V reach LDS through LDS-direct buffer loads (no registers): one
+//     1 KiB load writes 16 bytes per lane in lane order, so a lane's global
+//     address decides which chunk of which row lands where. Each wave of a
+//     stream loads one 16-row unit of the tile. Rows past the last key the
+//     workgroup sees, and blocks outside the pool, read as zeros (and their
+//     scores are masked). Four buffers per stream: tile j+3 is requested
+//     while tile j is scored, so a tile's loads have a whole iteration to land.
+//   * Sᵀ = K·Qᵀ on v_mfma_f32_32x32x16_bf16 (32 keys × the wave's 32 rows),
+//     K operands read 16 bytes per lane, chunks XOR-swizzled by row so the 16
+//     lanes of a read meet 16 different bank groups.
+//   * Oᵀ += Vᵀ·Pᵀ on the same instruction. The Vᵀ operand comes straight from
+//     the row-major V tile through the transposing read ds_read_b64_tr_b16
+//     (chunks swizzled for it); the Pᵀ operand is the Sᵀ accumulator's own
+//     register order, so P needs no shuffle. P enters as a bf16 high part
+//     (truncated) plus the bf16 rounding of the rest (two products), which
+//     keeps the probabilities to ~16 bits.
+//   * Online softmax per row in the log2 domain with a lazily moved base: the
+//     exponent base may trail the row's running maximum by up to 2^8, so l
+//     and O are rescaled (o = u / l is the same for any base) only when a
+//     tile raises some row's maximum by more than that — in practice on the
+//     first tiles only.
+//   * Iteration j: the scores of tile j become P(j) while the matrix cores run
+//     PV of tile j−1 and Sᵀ of tile j+1; then one barrier makes tile j+2
+//     visible to both waves of the stream and frees tile j−1's buffers.
+// The two streams' states are merged through LDS at the end.
+namespace {
+
+constexpr int kSWaves = 4;             // waves per workgroup, one per SIMD
+constexpr int kSRows = 64;             // query rows of a workgroup
+constexpr int kSTile = 32;             // keys per tile
+constexpr int kSBufs = 4;              // LDS tile buffers per key stream
+constexpr int kSBatch = 32;            // tiles whose table entries one VGPR holds (two per tile)
+constexpr float kSlack = 8.0f;         // log2 units the exponent base may trail a row's maximum
+// The steady iteration skips the row maximum: it exponentiates against the
+// row's current base and falls back to the full update only if some lane's
+// tile sum passes 2^64 (fp32 and bf16 keep their precision up to 2^127, so
+// any base within 64 of the maximum is exact to use).
+constexpr float kGuard = 18446744073709551616.0f;   // 2^64
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+struct SArgs {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint16_t* q;
+  const int32_t* q_start;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;
+  int num_blocks, hkv, hq, max_blocks, num_qtiles, num_chunks, gw;
+  int unit_shift;   // log2(block_size / 16): a pool block holds 1, 2 or 4 16-row units
+  float scale_log2;
+};
+
+// XOR swizzles of an LDS tile row's 16-byte chunks. K: the 16 lanes of an
+// Sᵀ operand read take rows 0..15 at one chunk → 16 positions of a 256-byte
+// bank window. V: a transposing read takes 4 consecutive rows × 4 chunks per
+// 32 lanes → again 16 positions.
+template <int DH>
+__device__ __forceinline__ int swz_k(int r) { return DH == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int DH>
+__device__ __forceinline__ int swz_v(int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// LDS-direct loads of one 16-row unit: load i moves 16 bytes per lane from
+// voffset[i] + 1024·i to LDS address lds + 1024·i + 16·lane (the instruction
+// offset moves both addresses). M0 carries the LDS address, set once per
+// unit; the compiler keeps nothing in M0 in this kernel (gfx9 LDS
+// instructions do not read it).
+__device__ __forceinline__ void lds_load_unit4(i32x4_t rsrc, const int* vo, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:3072 lds"
+      :
+      : "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(lds), "s"(rsrc)
+      : "memory");
+}
+__device__ __forceinline__ void lds_load_unit2(i32x4_t rsrc, const int* vo, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 lds"
+      :
+      : "v"(vo[0]), "v"(vo[1]), "s"(lds), "s"(rsrc)
+      : "memory");
+}
+// vmcnt ≤ N: every load but the last N has landed
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// The loads above are invisible to the compiler's wait counting: these waits
+// (ordered against every memory access) cover them.
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(lds_u8*)(p); }
+
+template <int DH>
+__global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArgs a) {
+  constexpr int RB = DH * 2;                  // bytes of one key row of one head
+  constexpr int TB = kSTile * RB;             // bytes of one K or V tile
+  constexpr int NDC = DH / 16;                // k-steps of Sᵀ
+  constexpr int NDT = DH / 32;                // 32-row dh tiles of Oᵀ
+  constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  constexpr int RPL = kWave / CPR;            // rows per 1 KiB load
+  constexpr int LPU = kBlockSize / RPL;       // loads per 16-row unit
+  // [stream][buffer] tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[2 * kSBufs * TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[2 * kSBufs * TB];
+
+  // workgroup → (sequence, KV head, head chunk, query tile); query tiles run
+  // longest first (a chunk's last tile sees the most keys)
+  const uint32_t L = xcd_logical_index(flat_block_id(), flat_grid_size());
+  const int qtile = a.num_qtiles - 1 - (int)(L % a.num_qtiles);
+  const int chunk = (L / a.num_qtiles) % a.num_chunks;
+  const int g = (L / a.num_qtiles / a.num_chunks) % a.hkv;
+  const int s = L / a.num_qtiles / a.num_chunks / a.hkv;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int half = w & 1, stream = w >> 1;
+  const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
+  const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;
+  const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], (a.max_blocks << a.unit_shift) * kBlockSize));
+  const int QW = kSRows / a.gw;                // queries of the workgroup
+  if (qtile * QW >= C || T <= 0) return;       // uniform over the workgroup
+  const int base_pos = T - C;                  // position of query 0
+  const int n = lane & 31, hg = lane >> 5;     // Sᵀ column (the lane's row) and lane half
+
+  // the lane's row: workgroup row half·32 + n
+  const int R = half * 32 + n;
+  const int qi = qtile * QW + R % QW;
+  const bool row_ok = qi < C;
+  const int row_q = q_lo + (row_ok ? qi : 0);
+  const int row_head = g * (a.hq / a.hkv) + chunk * a.gw + R / QW;
+  const int row_pos = row_ok ? base_pos + qi : T - 1;
+  const int first_pos = base_pos + qtile * QW;                     // smallest query position
+  const int kend = min(T, base_pos + min(C, qtile * QW + QW));      // keys the workgroup sees
+  const int ntiles = (kend + kSTile - 1) / kSTile;
+  const int NT = (ntiles + 1) / 2;             // iterations; stream 1's last tile may lie past kend
+
+  // Qᵀ operands: k-step dc, lane (n, hg): Q[row][16dc + 8hg .. +7]
+  bf16x8_t qop[NDC];
+  {
+    const uint16_t* qp = a.q + ((size_t)row_q * a.hq + row_head) * DH + 8 * hg;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      qop[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * dc));
+  }
+
+  uint8_t* const kst = lds_k + stream * kSBufs * TB;
+  uint8_t* const vst = lds_v + stream * kSBufs * TB;
+
+  // LDS-direct load i of the wave's 16-row unit: lane → row i·RPL + lane/CPR
+  // of the unit, LDS chunk position lane % CPR holding the row's chunk
+  // (position ^ swizzle)
+  int koff[LPU], voff[LPU];
+#pragma unroll
+  for (int i = 0; i < LPU; ++i) {
+    const int r = i * RPL + lane / CPR, p = lane % CPR;
+    koff[i] = r * RB + ((p ^ swz_k<DH>(r)) << 4) - 1024 * i;   // the load's instruction offset adds 1024·i
+    voff[i] = r * RB + ((p ^ swz_v<DH>(r)) << 4) - 1024 * i;
+  }
+  const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
+  const int unit_mask = (1 << a.unit_shift) - 1;
+  const size_t head_stride = ((size_t)kBlockSize * RB) << a.unit_shift;   // bytes of one (pool block, head)
+  const char* kbase = reinterpret_cast<const char*>(a.kc);
+  const char* vbase = reinterpret_cast<const char*>(a.vc);
+
+  // Table entries of the stream's tiles, one per lane: batch b holds units
+  // 2t and 2t+1 of tiles t = stream + 2·(32b + lane/2), as pool block ids or
+  // −1 (outside the pool, or past the keys the workgroup sees). Read back
+  // with a lane read, so no iteration waits on a scalar memory load.
+  auto table_batch = [&](int b) -> int {
+    const int jj = b * kSBatch + (lane >> 1);
+    const int u = 2 * (stream + 2 * jj) + (lane & 1);
+    const int e = u * kBlockSize < kend ? bt[u >> a.unit_shift] : -1;
+    return (unsigned)e < (unsigned)a.num_blocks ? e : -1;
+  };
+  int tb_cur = table_batch(0);                         // batch of the tile whose loads are issued next
+  int tb_nxt = NT > kSBatch ? table_batch(1) : -1;
+  auto unit_phys_in = [&](int tb, int j, int h) -> int {
+    return __builtin_amdgcn_readlane(tb, 2 * (j & (kSBatch - 1)) + h);
+  };
+  // the wave's unit (h = half) of K or V of tile j into buffer j % kSBufs
+  // (an id of −1, or a unit past kend, fills the buffer with zeros)
+  auto unit_loads = [&](bool is_v, int j, int ph) {
+    const int u = 2 * (stream + 2 * j) + half;
+    const int rows = ph < 0 ? 0 : max(0, min(kBlockSize, kend - u * kBlockSize));
+    const size_t off = ((size_t)(ph < 0 ? 0 : ph) * a.hkv + g) * head_stride + (size_t)((u & unit_mask) * kBlockSize) * RB;
+    const uint64_t addr = (uint64_t)((is_v ? vbase : kbase) + off);
+    i32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32) & 0xffff);
+    r[2] = __builtin_amdgcn_readfirstlane(rows * RB);
+    r[3] = kBufferRsrcWord3;
+    const uint32_t d = lds_addr((is_v ? vst : kst) + (j % kSBufs) * TB + half * (kBlockSize * RB));
+    if constexpr (LPU == 4) lds_load_unit4(r, is_v ? voff : koff, d);
+    else lds_load_unit2(r, is_v ? voff : koff, d);
+  };
+
+  // Vᵀ operand reads: lane (group G = lane/16, m = lane%16) of dh tile dt,
+  // key step ks, half hh addresses row 16ks + 8hh + 4(G/2) + m/4, columns
+  // 32dt + 16(G%2) + 4(m%4) … +3; as m/4 ≡ row (mod 4), the swizzle turns
+  // chunk 4dt + c into 4(dt ^ r) + c
+  const int vm = lane & 15, vG = lane >> 4;
+  const int vrow0 = 4 * (vG >> 1) + (vm >> 2);
+  const int vcc = 2 * (vG & 1) + ((vm & 3) >> 1);
+  int vaddr[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int r3 = DH == 128 ? (vm >> 2) : ((vrow0 >> 1) & 1);
+    vaddr[dt] = vrow0 * RB + ((4 * (dt ^ r3) + vcc) << 4) + (vm & 1) * 8;
+  }
+  // K operand reads: row n, chunk 2dc + hg
+  int kaddr[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) kaddr[dc] = n * RB + (((2 * dc + hg) ^ swz_k<DH>(n)) << 4);
+
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16_t{};
+  float m_run = -INFINITY;    // exponent base of the lane's row (log2 units)
+  float l_run = 0.0f;         // this lane's part of the row sum
+  const float c2 = a.scale_log2;
+
+  auto scores = [&](int j) -> f32x16_t {
+    const uint8_t* kb = kst + (j % kSBufs) * TB;
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + kaddr[dc]));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qop[dc], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  struct Pbits {
+    bf16x8_t hi[2], lo[2];    // key steps 0, 1 (keys 0-15 and 16-31 of the tile)
+  };
+  auto pv = [&](int j, const Pbits& P) {
+    const uint8_t* vb = vst + (j % kSBufs) * TB;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint8_t* p = vb + vaddr[dt] + ks * 16 * RB;
+        const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)p);
+        const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)(p + 8 * RB));
+        const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
+        const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, P.hi[ks], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, P.lo[ks], o[dt], 0, 0, 0);
+      }
+  };
+  // scores of tile j → P; *alpha: the row's rescale factor (1 if its base
+  // did not move); returns whether any row of the wave moved
+  // bf16 pairs (−1, 0) and (0, −1) for the exact remainder p − trunc_bf16(p)
+  // on v_dot2c_f32_bf16. Held in registers the compiler cannot see into: as
+  // a folded inline constant the pair (−1, 0) reaches the instruction as the
+  // fp32 pattern of −1.0, i.e. the pair (0, −1).
+  uint32_t kNegOne0, kNegOne1;
+  asm("s_mov_b32 %0, 0xbf80" : "=s"(kNegOne0));
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(kNegOne1));
+  auto softmax = [&](int j, f32x16_t st, int valid_units, Pbits& P, float* alpha) -> bool {
+    const int key0 = (stream + 2 * j) * kSTile;
+    if (key0 + kSTile - 1 > first_pos || valid_units != 3) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hg + (r & 3);
+        if (key > row_pos || !((valid_units >> (r >> 3)) & 1)) st[r] = -INFINITY;
+      }
+    }
+    float mx = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+    mx = pair_halves32(mx, MaxOp()) * c2;
+    const bool need = mx > m_run + kSlack;             // never while the row has seen nothing (−inf)
+    const float moved_by = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mx);
+    *alpha = need ? moved_by : 1.0f;
+    m_run = need ? mx : m_run;
+    l_run *= *alpha;
+    const float mb = m_run == -INFINITY ? 0.0f : m_run;
+    float ps = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(st[8 * ks + 2 * i], c2, -mb));
+        const float p1 = fast_exp2(fmaf(st[8 * ks + 2 * i + 1], c2, -mb));
+        ps += p0 + p1;
+        hw[i] = __builtin_amdgcn_perm(__float_as_uint(p1), __float_as_uint(p0), 0x07060302u);
+        const float r0 = dot2_bf16(hw[i], kNegOne0, p0);     // p0 − its truncated bf16, exactly
+        const float r1 = dot2_bf16(hw[i], kNegOne1, p1);
+        lw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)r0, (__bf16)r1});
+      }
+      P.hi[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      P.lo[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    }
+    l_run += ps;
+    // keep P's computation in this iteration's block (the compiler would sink
+    // it to the next PV, past the branches, away from the products it should
+    // overlap with)
+    asm volatile("" : : "v"(P.hi[0]), "v"(P.hi[1]), "v"(P.lo[0]), "v"(P.lo[1]));
+    return __builtin_amdgcn_ballot_w64(need) != 0;
+  };
+
+  // ---- prologue: tiles 0, 1, 2 requested; tiles 0 and 1 visible ----
+  // valid-unit bits of tiles j, j+1, j+2 (bit h: unit h names a pool block)
+  auto vbits = [&](int tb, int j) -> int {
+    return (unit_phys_in(tb, j, 0) >= 0) | ((unit_phys_in(tb, j, 1) >= 0) << 1);
+  };
+  int vu_cur = vbits(tb_cur, 0);
+  int vu_next = NT > 1 ? vbits(tb_cur, 1) : 0;
+  int vu_after = NT > 2 ? vbits(tb_cur, 2) : 0;
+  // Load protocol: tiles 0..2 here (ids past NT fill zeros); every iteration
+  // but the last requests K of tile j+3 during its products and V of tile
+  // j+3 after its barrier, and waits before the barrier for all but the
+  // newest unit of loads (K of j+3), i.e. for tile j+2.
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int ph = unit_phys_in(tb_cur, t, half);
+    unit_loads(false, t, t < NT ? ph : -1);
+    unit_loads(true, t, t < NT ? ph : -1);
+  }
+  wait_loads_but<2 * LPU>();           // tiles 0 and 1
+  __syncthreads();
+  f32x16_t s_cur = scores(0);
+  Pbits p_prev, p_cur;
+
+  // K of tile j+3 (its buffer held K of tile j−1, done since iteration j−2);
+  // also the tile's valid bits. No branch: past NT the loads fill zeros.
+  int ph_k3 = -1, vu_k3 = 0;
+  auto k_refill = [&](int j) {
+    const int t = j + 3;
+    const int ph = unit_phys_in(tb_cur, t, half);
+    ph_k3 = t < NT ? ph : -1;
+    vu_k3 = vbits(tb_cur, t) & (t < NT ? 3 : 0);
+    unit_loads(false, t, ph_k3);
+  };
+  // after iteration j's barrier: V of tile j+3 (V of tile j−1 is consumed),
+  // rotate the valid bits and, every 32 tiles, the table batch
+  auto v_refill = [&](int j) {
+    const int t = j + 3;
+    unit_loads(true, t, ph_k3);
+    vu_cur = vu_next;
+    vu_next = vu_after;
+    vu_after = vu_k3;
+    if (((t + 1) & (kSBatch - 1)) == 0 && t + 1 < NT) {   // tile t+1 starts the next batch
+      tb_cur = tb_nxt;
+      tb_nxt = NT > t + 1 + kSBatch ? table_batch((t + 1) / kSBatch + 1) : -1;
+    }
+  };
+  // Iteration j. The first has no PV, the last no Sᵀ of a next tile; in
+  // between the body is one basic block up to the rare rescale branch, so
+  // the scheduler can interleave P(j)'s vector work with the PV(j−1) and
+  // Sᵀ(j+1) products.
+  auto body = [&](auto first_tag, auto last_tag, int j) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
+    float alpha;
+    const bool moved = softmax(j, s_cur, vu_cur, p_cur, &alpha);
+    if constexpr (!FIRST) pv(j - 1, p_prev);
+    if constexpr (!LAST) s_cur = scores(j + 1);
+    if (moved) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;       // after PV(j−1): O is in the old base
+    }
+    p_prev = p_cur;
+    if constexpr (!LAST) {
+      k_refill(j);
+      // tile j+2 lands and becomes visible to both waves; tile j−1's buffers are free
+      wait_loads_but<LPU>();
+      wait_lds_reads();
+      __syncthreads();
+      v_refill(j);
+    }
+  };
+  // The steady iteration (neither first nor last), scheduled by hand: one
+  // wave per SIMD, so the matrix cores stay busy only if the wave itself
+  // issues P(j)'s vector work between the products and requests LDS operands
+  // well before they are used. Scheduling barriers fence each step so the
+  // compiler keeps this order.
+  auto vread = [&](const uint8_t* vb, int dt, int ks) -> bf16x8_t {
+    const uint8_t* p = vb + vaddr[dt] + ks * 16 * RB;
+    const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)p);
+    const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)(p + 8 * RB));
+    const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+  };
+  auto kread = [&](const uint8_t* kb, int dc) -> bf16x8_t {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + kaddr[dc]));
+  };
+  // Returns true when P(j) must be redone with the full update (a tile well
+  // above some row's base); the caller does it before the next iteration.
+  int vu_prev = 0;
+  auto body_steady = [&](int j) -> bool {
+    const uint8_t* vb = vst + ((j + 3) % kSBufs) * TB;      // V of tile j−1
+    const uint8_t* kb = kst + ((j + 1) % kSBufs) * TB;      // K of tile j+1
+    f32x16_t st = s_cur;
+    const int key0 = (stream + 2 * j) * kSTile;
+    if (key0 + kSTile - 1 > first_pos || vu_cur != 3) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hg + (r & 3);
+        if (key > row_pos || !((vu_cur >> (r >> 3)) & 1)) st[r] = -INFINITY;
+      }
+    }
+    // every row of the wave has a finite base here (checked by the caller)
+    const float mb = m_run;
+    bf16x8_t v0[NDT], v1[NDT], kk[NDC];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) v0[dt] = vread(vb, dt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // P(j), two probabilities per piece, one piece per three products
+    uint32_t hw[8], lw[8];
+    float ps = 0.0f;
+    auto piece = [&](int i) {
+      const float p0 = fast_exp2(fmaf(st[2 * i], c2, -mb));
+      const float p1 = fast_exp2(fmaf(st[2 * i + 1], c2, -mb));
+      ps += p0 + p1;
+      hw[i] = __builtin_amdgcn_perm(__float_as_uint(p1), __float_as_uint(p0), 0x07060302u);
+      const float r0 = dot2_bf16(hw[i], kNegOne0, p0);
+      const float r1 = dot2_bf16(hw[i], kNegOne1, p1);
+      lw[i] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)r0, (__bf16)r1});
+      // computed here, between these products (the compiler would otherwise
+      // sink it to the next iteration, its only use)
+      asm volatile("" : : "v"(hw[i]), "v"(lw[i]), "v"(ps));
+    };
+    // The 24 (Dh 128) or 12 (Dh 64) products: PV(j−1) key step 0 (high, then
+    // low parts, dh-tile chains alternating), then key step 1 alternating
+    // with the single-chain Sᵀ(j+1). Step k runs product k, then piece k/3
+    // when k % 3 == 0; LDS operands are read at least two products ahead.
+    constexpr int NSTEP = 6 * NDT;
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      if (k < NDT) {
+        o[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[k], p_prev.hi[0], o[k], 0, 0, 0);
+        v1[k] = vread(vb, k, 1);
+      } else if (k < 2 * NDT) {
+        const int dt = k - NDT;
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p_prev.lo[0], o[dt], 0, 0, 0);
+        kk[dt] = kread(kb, dt);
+      } else if (k < 4 * NDT) {
+        const int h = (k - 2 * NDT) >> 1;
+        if (((k - 2 * NDT) & 1) == 0) {
+          o[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[h], p_prev.hi[1], o[h], 0, 0, 0);
+          kk[NDT + h] = kread(kb, NDT + h);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[h], qop[h], acc, 0, 0, 0);
+        }
+      } else {
+        const int h = (k - 4 * NDT) >> 1;
+        if (((k - 4 * NDT) & 1) == 0)
+          o[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[h], p_prev.lo[1], o[h], 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[NDT + h], qop[NDT + h], acc, 0, 0, 0);
+      }
+      if (k % 3 == 0 && k / 3 < 8) piece(k / 3);
+      if (k == NDT + 1) k_refill(j);                 // K of tile j+3: its buffer is free
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = NSTEP / 3; i < 8; ++i) piece(i);    // Dh 64: fewer products than pieces
+    const bool redo = __builtin_amdgcn_ballot_w64(!(ps <= kGuard)) != 0;
+    if (!redo) {
+      l_run += ps;
+      p_prev.hi[0] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      p_prev.hi[1] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[4], hw[5], hw[6], hw[7]));
+      p_prev.lo[0] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      p_prev.lo[1] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[4], lw[5], lw[6], lw[7]));
+    }
+    s_cur = acc;
+    vu_prev = vu_cur;
+    // tile j+2 lands and becomes visible to both waves; tile j−1's buffers are free
+    wait_loads_but<LPU>();
+    wait_lds_reads();
+    __syncthreads();
+    v_refill(j);
+    return redo;
+  };
+  // P(jj) again with the full update: the scores are recomputed from K of
+  // tile jj, still in its buffer (so no register keeps them through an
+  // iteration), the base moves to the row maximum, and l and O (holding
+  // PV(jj−1)) are rescaled.
+  auto redo_p = [&](int jj) {
+    float alpha;
+    if (softmax(jj, scores(jj), vu_prev, p_prev, &alpha)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+  };
+  if (NT == 1) {
+    body(std::true_type{}, std::true_type{}, 0);
+  } else {
+    body(std::true_type{}, std::false_type{}, 0);
+    int j = 1;
+    // full updates until every row of the wave has a base (a row whose keys
+    // have all been masked so far has none)
+    for (; j < NT - 1 && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0; ++j)
+      body(std::false_type{}, std::false_type{}, j);
+    bool redo = false;
+    for (; j < NT - 1; ++j) {
+      if (redo) redo_p(j - 1);
+      redo = body_steady(j);
+    }
+    if (redo) redo_p(j - 1);
+    body(std::false_type{}, std::true_type{}, NT - 1);
+  }
+  pv(NT - 1, p_prev);
+
+  // ---- merge the two streams: each wave of a row half finishes half of its dh tiles ----
+  wait_lds_reads();
+  __syncthreads();             // every wave's last LDS reads are done before the buffers are reused
+  float* mo = reinterpret_cast<float*>(lds_k);    // [wave][dt][16][64] Oᵀ parts
+  float* ml = reinterpret_cast<float*>(lds_v);    // [wave][64][2] m, l
+  static_assert(kSWaves * NDT * 16 * kWave * 4 <= 2 * kSBufs * TB, "merge area");
+  const float l_row = pair_halves32(l_run, AddOp());
+  {
+    float* my = mo + (size_t)w * NDT * 16 * kWave;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) my[(dt * 16 + r) * kWave + lane] = o[dt][r];
+    ml[(w * kWave + lane) * 2 + 0] = m_run;
+    ml[(w * kWave + lane) * 2 + 1] = l_row;
+  }
+  __syncthreads();
+  const int other = w ^ 2;                        // the other stream's wave on the same rows
+  const float m_o = ml[(other * kWave + lane) * 2], l_o = ml[(other * kWave + lane) * 2 + 1];
+  const float mx = fmaxf(m_run, m_o);
+  const float f_me = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mx);
+  const float f_o = m_o == -INFINITY ? 0.0f : fast_exp2(m_o - mx);
+  const float lsum = f_me * l_row + f_o * l_o;
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;    // no valid key at all: zeros
+  const float* theirs = mo + (size_t)other * NDT * 16 * kWave;
+  if (row_ok) {
+    float* op = a.out + ((size_t)row_q * a.hq + row_head) * DH + 4 * hg;
+#pragma unroll
+    for (int k = 0; k < NDT / 2; ++k) {
+      const int dt = stream * (NDT / 2) + k;      // stream 0: the first dh tiles, stream 1: the rest
+      // static indices only (a runtime index would put o in scratch memory)
+      const f32x16_t mine = stream ? o[NDT / 2 + k] : o[k];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * q4 + t;
+          v[t] = (f_me * mine[r] + f_o * theirs[(dt * 16 + r) * kWave + lane]) * inv;
+        }
+        *reinterpret_cast<float4*>(op + 32 * dt + 8 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_stream_dh(const PrefillParams& p, hipStream_t s) {
+  const int group = p.num_q_heads / p.cache.num_kv_heads;
+  const int gw = group >= 4 ? 4 : group;
+  SArgs a;
+  a.kc = static_cast<const uint8_t*>(p.cache.k);
+  a.vc = static_cast<const uint8_t*>(p.cache.v);
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.q_start = p.q_start;
+  a.block_tables = p.block_tables;
+  a.seq_lens = p.seq_lens;
+  a.out = p.out;
+  a.num_blocks = p.cache.num_blocks;
+  a.hkv = p.cache.num_kv_heads;
+  a.hq = p.num_q_heads;
+  a.max_blocks = p.max_blocks;
+  a.gw = gw;
+  a.num_chunks = group / gw;
+  a.num_qtiles = (p.max_q_len + (kSRows / gw) - 1) / (kSRows / gw);
+  a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  const size_t n = (size_t)p.num_seqs * a.hkv * a.num_chunks * a.num_qtiles;
+  hipLaunchKernelGGL((prefill_stream_kernel<DH>), dim3((unsigned)n), dim3(kSWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s) {
+  if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
+  return p.cache.head_dim == 64 ? launch_stream_dh<64>(p, s) : launch_stream_dh<128>(p, s);
 }
 
 }  // namespace pkv

@@ -227,6 +227,9 @@ def test_append_and_prefill_validation(lib):
     assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 2 ** 20, 32, 0x1, 0x2, 4, 0x3, 1024, 0.1, 0x80000,
                                       None) == pkv.PKV_EINVAL     # grid past 2^31 - 1
     assert "2^31" in lib.pkv_last_error().decode()
+    for bad in (0.0, -0.1, float("nan"), float("inf")):     # the kernels take scale > 0
+        assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, bad, 0x80000,
+                                          None) == pkv.PKV_EINVAL, bad
     # fused slot mapping + append: same dtype rules, pointer and size checks
     ap = lib.pkv_kv_append_paged
     assert ap(ref, 0x50000, 0x60000, pkv.PKV_F32, 2, 0x1, 0x2, 1, 0x3, 4, None, None, None, None) == pkv.PKV_EDTYPE

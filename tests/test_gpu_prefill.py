@@ -13,13 +13,14 @@ from gpu_helpers import device, new_pools, parity
 
 pytestmark = pytest.mark.gpu
 
-PREFILL_KERNELS = ["tiles", "columns"]
+PREFILL_KERNELS = ["tiles", "tiles16", "columns"]
 
 
 @pytest.fixture(params=PREFILL_KERNELS)
 def prefill_kernel(request, monkeypatch):
-    """Both prefill kernels: the tile kernel and the matrix-core decode
-    kernel with (head, query) columns (PKV_PREFILL_KERNEL)."""
+    """Every prefill kernel (PKV_PREFILL_KERNEL): the key-stream tile kernel,
+    the 16-row tile kernel, and the matrix-core decode kernel with (head,
+    query) columns."""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", request.param)
     return request.param
 
@@ -32,10 +33,11 @@ def _f64(t):
     return t.float().cpu().double().numpy()
 
 
-def _prefill_case(dev, seqs, hq, hkv, dh, seed, bs=16, label=None, norm_tol=None):
+def _prefill_case(dev, seqs, hq, hkv, dh, seed, bs=16, label=None, norm_tol=None, shape_q=None):
     """seqs: list of (prefix P, chunk C); bs: tokens per pool block. Checks
     max-abs <= 2e-3 (and the normalised error against norm_tol) and returns
-    (max-abs error, normalised error)."""
+    (max-abs error, normalised error). shape_q(i, q, k), if given, rewrites
+    sequence i's queries (C, Hq, Dh) in place from its keys (P+C, Hkv, Dh)."""
     gen = torch.Generator(device=dev).manual_seed(seed)
     rng = np.random.default_rng(seed)
     total_blocks = sum(-(-(p + c) // bs) for p, c in seqs)
@@ -55,6 +57,8 @@ def _prefill_case(dev, seqs, hq, hkv, dh, seed, bs=16, label=None, norm_tol=None
         slots = pkv.pkv_slot_mapping(bt[i], bs, 0, p + c)
         pkv.pkv_kv_append(cache, k, v, torch.from_numpy(slots).to(dev))
         qs.append(_bf16((c, hq, dh), gen, dev))
+        if shape_q is not None:
+            shape_q(i, qs[-1], k)
         ks.append(k)
         vs.append(v)
     q = torch.cat(qs).contiguous()
@@ -270,3 +274,26 @@ def test_blocks_missing_from_the_table_contribute_nothing(bs, prefill_kernel):
     got = out.cpu().double().numpy()
     parity(f"prefill {prefill_kernel} missing blocks bs{bs}", {i: got[q_start[i]:q_start[i + 1]] for i in refs},
            refs, 2e-3)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_scores_far_above_the_running_base(sign, prefill_kernel):
+    """Queries equal to ±40× one key in a late tile: that key's score exceeds
+    every earlier one by hundreds of powers of two (the kernel keeps a running
+    base per row and must rescale, not overflow), or falls far below all
+    others (its weight underflows to zero). Rows are spread over the chunk and
+    over the query heads of each KV head."""
+    dev = device()
+    hq, hkv, dh = 32, 8, 128
+    group = hq // hkv
+
+    def shape_q(i, q, k):
+        rng = np.random.default_rng(77 + i)
+        c = q.shape[0]
+        p = k.shape[0] - c
+        for r in range(0, c, 29):
+            h = int(rng.integers(hq))
+            t = int(rng.integers(min(p + r, 100), p + r + 1))   # a key the row sees
+            q[r, h] = (sign * 40.0 * k[t, h // group].float()).to(torch.bfloat16)
+
+    _prefill_case(dev, [(2048, 512), (700, 300)], hq, hkv, dh, seed=41, shape_q=shape_q)
