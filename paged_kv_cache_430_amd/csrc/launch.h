@@ -114,7 +114,7 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
-// The key-stream tile kernel: 64 query rows per workgroup, two key streams,
+// The key-stream tile kernel: 64 query rows per workgroup, four key streams,
 // each a wave per 32-row half (see prefill.hip).
 hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s);
 

@@ -408,18 +408,21 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
 }
 
 // ===========================================================================
-// Key-stream form (the tile kernel): a workgroup of four waves, one per SIMD,
+// Key-stream form (the tile kernel): a workgroup of eight waves, two per SIMD,
 // owns 64 query rows (GW ≤ 4 heads of one KV group × 64/GW queries). Wave w
 // takes row half w % 2 (32 rows) of key stream w / 2: stream s scores the
-// 32-key tiles s, s+2, s+4, …, and the two waves of a stream share each tile
-// through LDS. Per tile:
+// 32-key tiles s, s+4, s+8, …, and the two waves of a stream share each tile
+// through LDS. Two waves per SIMD let one wave's vector work, waits and loads
+// run while the other's products occupy the matrix core. Per tile:
 //   * K and V reach LDS through LDS-direct buffer loads (no registers): one
 //     1 KiB load writes 16 bytes per lane in lane order, so a lane's global
 //     address decides which chunk of which row lands where. Each wave of a
 //     stream loads one 16-row unit of the tile. Rows past the last key the
 //     workgroup sees, and blocks outside the pool, read as zeros (and their
-//     scores are masked). Four buffers per stream: tile j+3 is requested
-//     while tile j is scored, so a tile's loads have a whole iteration to land.
+//     scores are masked). Unit addresses come from a per-lane table built
+//     once per 32 tiles; the loads of a tile are spread between the products
+//     of the iteration before the one that needs them. K and V have rings of
+//     their own (three and two slots at Dh 128: all of the CU's 160 KiB).
 //   * Sᵀ = K·Qᵀ on v_mfma_f32_32x32x16_bf16 (32 keys × the wave's 32 rows),
 //     K operands read 16 bytes per lane, chunks XOR-swizzled by row so the 16
 //     lanes of a read meet 16 different bank groups.
@@ -435,15 +438,15 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
 //     tile raises some row's maximum by more than that — in practice on the
 //     first tiles only.
 //   * Iteration j: the scores of tile j become P(j) while the matrix cores run
-//     PV of tile j−1 and Sᵀ of tile j+1; then one barrier makes tile j+2
-//     visible to both waves of the stream and frees tile j−1's buffers.
-// The two streams' states are merged through LDS at the end.
+//     PV of tile j−1 and Sᵀ of tile j+1; then one barrier makes the next
+//     tiles visible to both waves of each stream and frees the slots the
+//     next iteration's loads go to.
+// The four streams' states are merged through LDS at the end.
 namespace {
 
-constexpr int kSWaves = 4;             // waves per workgroup, one per SIMD
+constexpr int kStreams = 4;            // key streams of a workgroup (a wave per row half each)
 constexpr int kSRows = 64;             // query rows of a workgroup
 constexpr int kSTile = 32;             // keys per tile
-constexpr int kSBufs = 4;              // LDS tile buffers per key stream
 constexpr int kSBatch = 32;            // tiles whose table entries one VGPR holds (two per tile)
 constexpr float kSlack = 8.0f;         // log2 units the exponent base may trail a row's maximum
 // The steady iteration skips the row maximum: it exponentiates against the
@@ -506,6 +509,17 @@ __device__ __forceinline__ void lds_load_unit2(i32x4_t rsrc, const int* vo, uint
       : "v"(vo[0]), "v"(vo[1]), "s"(lds), "s"(rsrc)
       : "memory");
 }
+// one load of a unit: instruction offset 1024·I (sets M0 itself, so the
+// loads of a unit can be spread between other instructions)
+template <int I>
+__device__ __forceinline__ void lds_load_one(i32x4_t rsrc, int vo, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen offset:%3 lds"
+      :
+      : "v"(vo), "s"(lds), "s"(rsrc), "n"(1024 * I)
+      : "memory");
+}
 // vmcnt ≤ N: every load but the last N has landed
 template <int N>
 __device__ __forceinline__ void wait_loads_but() {
@@ -519,18 +533,40 @@ __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmc
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(lds_u8*)(p); }
 
-template <int DH>
-__global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArgs a) {
+// Ring depths of a key stream's LDS tiles. K of tile t stays in K slot t % RK
+// from its request until the end of the iteration that exponentiates tile t
+// (a redo of that tile reads it again); V of tile t stays in V slot t % RV
+// until PV(t) is done. With RK = RV + 1 the K and V of one pair of requests
+// are both first needed RK − 2 iterations after they are issued. The deepest
+// rings that fit 160 KiB of LDS, at most five K slots.
+template <int DH, int NS>
+struct StreamRings {
+  static constexpr int TB = kSTile * DH * 2;
+  static constexpr int fit = (160 * 1024 / (NS * TB) + 1) / 2;   // NS·(2RK − 1)·TB ≤ 160 KiB
+  static constexpr int RK = fit > 5 ? 5 : fit;
+  static constexpr int RV = RK - 1;
+  static_assert(RK >= 3, "one iteration of cover at least");
+};
+
+template <int DH, int NS>
+__global__ __launch_bounds__(2 * NS * kWave, 1) void prefill_stream_kernel(SArgs a) {
+  constexpr int NW = 2 * NS;                  // waves: (stream, row half)
   constexpr int RB = DH * 2;                  // bytes of one key row of one head
   constexpr int TB = kSTile * RB;             // bytes of one K or V tile
+  constexpr int RK = StreamRings<DH, NS>::RK, RV = StreamRings<DH, NS>::RV;
   constexpr int NDC = DH / 16;                // k-steps of Sᵀ
   constexpr int NDT = DH / 32;                // 32-row dh tiles of Oᵀ
   constexpr int CPR = RB / 16;                // 16-byte chunks per row
   constexpr int RPL = kWave / CPR;            // rows per 1 KiB load
   constexpr int LPU = kBlockSize / RPL;       // loads per 16-row unit
-  // [stream][buffer] tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[2 * kSBufs * TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[2 * kSBufs * TB];
+  constexpr int PAIR = 2 * LPU;               // loads of one (K, V) request pair
+  constexpr int KV_BYTES = NS * (RK + RV) * TB;
+  constexpr int MERGE_BYTES = NW * (NDT * 16 + 2) * kWave * 4;
+  constexpr int LDS_BYTES = KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of a CU");
+  static_assert((4 * NDT) % NS == 0, "output groups per stream");
+  // [stream][K slot] tiles, then [stream][V slot]; the merge reuses it
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
   // workgroup → (sequence, KV head, head chunk, query tile); query tiles run
   // longest first (a chunk's last tile sees the most keys)
@@ -560,7 +596,7 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
   const int first_pos = base_pos + qtile * QW;                     // smallest query position
   const int kend = min(T, base_pos + min(C, qtile * QW + QW));      // keys the workgroup sees
   const int ntiles = (kend + kSTile - 1) / kSTile;
-  const int NT = (ntiles + 1) / 2;             // iterations; stream 1's last tile may lie past kend
+  const int NT = (ntiles + NS - 1) / NS;       // iterations; a stream's last tile may lie past kend
 
   // Qᵀ operands: k-step dc, lane (n, hg): Q[row][16dc + 8hg .. +7]
   bf16x8_t qop[NDC];
@@ -571,55 +607,100 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
       qop[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * dc));
   }
 
-  uint8_t* const kst = lds_k + stream * kSBufs * TB;
-  uint8_t* const vst = lds_v + stream * kSBufs * TB;
+  uint8_t* const kst = lds + stream * RK * TB;
+  uint8_t* const vst = lds + NS * RK * TB + stream * RV * TB;
 
   // LDS-direct load i of the wave's 16-row unit: lane → row i·RPL + lane/CPR
   // of the unit, LDS chunk position lane % CPR holding the row's chunk
   // (position ^ swizzle)
-  int koff[LPU], voff[LPU];
-#pragma unroll
-  for (int i = 0; i < LPU; ++i) {
-    const int r = i * RPL + lane / CPR, p = lane % CPR;
-    koff[i] = r * RB + ((p ^ swz_k<DH>(r)) << 4) - 1024 * i;   // the load's instruction offset adds 1024·i
-    voff[i] = r * RB + ((p ^ swz_v<DH>(r)) << 4) - 1024 * i;
-  }
+  // (the load's instruction offset adds 1024·i; across loads the K swizzle
+  // changes by 4i in the chunk index, the V swizzle not at all)
+  const int koff0 = (lane / CPR) * RB + (((lane % CPR) ^ swz_k<DH>(lane / CPR)) << 4);
+  const int voff0 = (lane / CPR) * RB + (((lane % CPR) ^ swz_v<DH>(lane / CPR)) << 4);
+  static_assert(DH == 64 || DH == 128, "the swizzle steps above");
   const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
   const int unit_mask = (1 << a.unit_shift) - 1;
   const size_t head_stride = ((size_t)kBlockSize * RB) << a.unit_shift;   // bytes of one (pool block, head)
   const char* kbase = reinterpret_cast<const char*>(a.kc);
   const char* vbase = reinterpret_cast<const char*>(a.vc);
 
-  // Table entries of the stream's tiles, one per lane: batch b holds units
-  // 2t and 2t+1 of tiles t = stream + 2·(32b + lane/2), as pool block ids or
-  // −1 (outside the pool, or past the keys the workgroup sees). Read back
-  // with a lane read, so no iteration waits on a scalar memory load.
-  auto table_batch = [&](int b) -> int {
+  // Request table of the stream's tiles, one entry per lane: batch b holds
+  // units 2t and 2t+1 of tiles t = stream + NS·(32b + lane/2). An entry is
+  // the K address of its unit (low word; the next 16 address bits and the
+  // unit's bytes before the workgroup's last visible key in the other word).
+  // An id outside the pool, or a unit past that key, has 0 bytes: its loads
+  // fill zeros. Requests read entries back with lane reads, so no iteration
+  // waits on a memory load or spends scalar work on addresses.
+  auto batch_ids = [&](int b) -> int {
     const int jj = b * kSBatch + (lane >> 1);
-    const int u = 2 * (stream + 2 * jj) + (lane & 1);
+    const int u = 2 * (stream + NS * jj) + (lane & 1);
     const int e = u * kBlockSize < kend ? bt[u >> a.unit_shift] : -1;
     return (unsigned)e < (unsigned)a.num_blocks ? e : -1;
   };
-  int tb_cur = table_batch(0);                         // batch of the tile whose loads are issued next
-  int tb_nxt = NT > kSBatch ? table_batch(1) : -1;
-  auto unit_phys_in = [&](int tb, int j, int h) -> int {
-    return __builtin_amdgcn_readlane(tb, 2 * (j & (kSBatch - 1)) + h);
+  uint32_t tl, th;        // entries of the batch holding the next K request
+  uint64_t vmask;         // bit 2i+h: unit h of the batch's tile i holds keys
+  auto make_table = [&](int b, int e) {
+    const int jj = b * kSBatch + (lane >> 1);
+    const int u = 2 * (stream + NS * jj) + (lane & 1);
+    const int rows = e < 0 ? 0 : max(0, min(kBlockSize, kend - u * kBlockSize));
+    const uint64_t addr = (uint64_t)(kbase + ((size_t)(e < 0 ? 0 : e) * a.hkv + g) * head_stride +
+                                     (size_t)((u & unit_mask) * kBlockSize) * RB);
+    tl = (uint32_t)addr;
+    th = ((uint32_t)(addr >> 32) & 0xffffu) | ((uint32_t)(rows * RB) << 16);
+    vmask = __builtin_amdgcn_ballot_w64(rows > 0);
   };
-  // the wave's unit (h = half) of K or V of tile j into buffer j % kSBufs
-  // (an id of −1, or a unit past kend, fills the buffer with zeros)
-  auto unit_loads = [&](bool is_v, int j, int ph) {
-    const int u = 2 * (stream + 2 * j) + half;
-    const int rows = ph < 0 ? 0 : max(0, min(kBlockSize, kend - u * kBlockSize));
-    const size_t off = ((size_t)(ph < 0 ? 0 : ph) * a.hkv + g) * head_stride + (size_t)((u & unit_mask) * kBlockSize) * RB;
-    const uint64_t addr = (uint64_t)((is_v ? vbase : kbase) + off);
+  make_table(0, batch_ids(0));
+  int ids_nxt = NT > kSBatch ? batch_ids(1) : -1;     // ids of the batch after it
+  const uint64_t dv = (uint64_t)(vbase - kbase);      // V's unit lies this far from K's
+  // valid-unit bits of tile t (in the current batch)
+  auto vbits = [&](int t) -> int { return (int)(uint32_t)(vmask >> (2 * (t & (kSBatch - 1)))) & 3; };
+  struct Ent {
+    uint32_t lo, hi;
+  };
+  // the wave's entry of tile t; after a batch's last tile the next batch
+  // becomes current
+  auto take_entry = [&](int t) -> Ent {
+    const int ln = 2 * (t & (kSBatch - 1)) + half;
+    const Ent e{(uint32_t)__builtin_amdgcn_readlane((int)tl, ln), (uint32_t)__builtin_amdgcn_readlane((int)th, ln)};
+    if (((t + 1) & (kSBatch - 1)) == 0 && t + 1 < NT) {
+      const int b = (t + 1) / kSBatch;
+      make_table(b, ids_nxt);
+      ids_nxt = NT > (b + 1) * kSBatch ? batch_ids(b + 1) : -1;
+    }
+    return e;
+  };
+  // A request: the unit's buffer resource and the LDS address of its slot
+  // (K of tile t in K slot t % RK, V in V slot t % RV), then its LPU loads.
+  struct Req {
+    int lo, hi, bytes;    // buffer resource words 0-2
+    uint32_t d;
+  };
+  auto make_req = [&](Ent e, bool is_v, int t) -> Req {
+    uint64_t addr = ((uint64_t)(e.hi & 0xffffu) << 32) | e.lo;
+    if (is_v) addr += dv;
+    const uint8_t* slot = is_v ? vst + (t % RV) * TB : kst + (t % RK) * TB;
+    return Req{(int)(uint32_t)addr, (int)(uint32_t)(addr >> 32), (int)(e.hi >> 16),
+               lds_addr(slot + half * (kBlockSize * RB))};
+  };
+  // (the resource is assembled from scalar words here: a vector of them
+  // carried across iterations may be given vector registers)
+  auto issue_one = [&](bool is_v, const Req& q, int i) {
     i32x4_t r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32) & 0xffff);
-    r[2] = __builtin_amdgcn_readfirstlane(rows * RB);
+    r[0] = __builtin_amdgcn_readfirstlane(q.lo);
+    r[1] = __builtin_amdgcn_readfirstlane(q.hi);
+    r[2] = __builtin_amdgcn_readfirstlane(q.bytes);
     r[3] = kBufferRsrcWord3;
-    const uint32_t d = lds_addr((is_v ? vst : kst) + (j % kSBufs) * TB + half * (kBlockSize * RB));
-    if constexpr (LPU == 4) lds_load_unit4(r, is_v ? voff : koff, d);
-    else lds_load_unit2(r, is_v ? voff : koff, d);
+    const uint32_t d = __builtin_amdgcn_readfirstlane(q.d);
+    switch (i) {
+      case 0: lds_load_one<0>(r, is_v ? voff0 : koff0, d); break;
+      case 1: lds_load_one<1>(r, is_v ? voff0 : koff0 ^ 64, d); break;
+      case 2: lds_load_one<2>(r, is_v ? voff0 : koff0 ^ 128, d); break;
+      default: lds_load_one<3>(r, is_v ? voff0 : koff0 ^ 192, d); break;
+    }
+  };
+  auto issue_req = [&](bool is_v, const Req& q) {
+#pragma unroll
+    for (int i = 0; i < LPU; ++i) issue_one(is_v, q, i);
   };
 
   // Vᵀ operand reads: lane (group G = lane/16, m = lane%16) of dh tile dt,
@@ -647,13 +728,23 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
   float l_run = 0.0f;         // this lane's part of the row sum
   const float c2 = a.scale_log2;
 
+  auto vread = [&](const uint8_t* vb, int dt, int ks) -> bf16x8_t {
+    const uint8_t* p = vb + vaddr[dt] + ks * 16 * RB;
+    const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)p);
+    const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)(p + 8 * RB));
+    const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+  };
+  auto kread = [&](const uint8_t* kb, int dc) -> bf16x8_t {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + kaddr[dc]));
+  };
   auto scores = [&](int j) -> f32x16_t {
-    const uint8_t* kb = kst + (j % kSBufs) * TB;
+    const uint8_t* kb = kst + (j % RK) * TB;
     f32x16_t acc = f32x16_t{};
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + kaddr[dc]));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qop[dc], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, dc), qop[dc], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);     // operands read one product ahead at most (registers)
     }
     return acc;
   };
@@ -661,22 +752,17 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
     bf16x8_t hi[2], lo[2];    // key steps 0, 1 (keys 0-15 and 16-31 of the tile)
   };
   auto pv = [&](int j, const Pbits& P) {
-    const uint8_t* vb = vst + (j % kSBufs) * TB;
+    const uint8_t* vb = vst + (j % RV) * TB;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t* p = vb + vaddr[dt] + ks * 16 * RB;
-        const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)p);
-        const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)(p + 8 * RB));
-        const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
-        const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        const bf16x8_t vv = vread(vb, dt, ks);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, P.hi[ks], o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, P.lo[ks], o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
   };
-  // scores of tile j → P; *alpha: the row's rescale factor (1 if its base
-  // did not move); returns whether any row of the wave moved
   // bf16 pairs (−1, 0) and (0, −1) for the exact remainder p − trunc_bf16(p)
   // on v_dot2c_f32_bf16. Held in registers the compiler cannot see into: as
   // a folded inline constant the pair (−1, 0) reaches the instruction as the
@@ -684,8 +770,11 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
   uint32_t kNegOne0, kNegOne1;
   asm("s_mov_b32 %0, 0xbf80" : "=s"(kNegOne0));
   asm("s_mov_b32 %0, 0xbf800000" : "=s"(kNegOne1));
+  // The full update of tile j: mask, row maximum, base moved when the maximum
+  // passes it by more than kSlack (l rescaled here; *alpha is O's factor),
+  // P as high and low bf16 parts. Returns whether any row of the wave moved.
   auto softmax = [&](int j, f32x16_t st, int valid_units, Pbits& P, float* alpha) -> bool {
-    const int key0 = (stream + 2 * j) * kSTile;
+    const int key0 = (stream + NS * j) * kSTile;
     if (key0 + kSTile - 1 > first_pos || valid_units != 3) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -712,6 +801,7 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
         const float p0 = fast_exp2(fmaf(st[8 * ks + 2 * i], c2, -mb));
         const float p1 = fast_exp2(fmaf(st[8 * ks + 2 * i + 1], c2, -mb));
         ps += p0 + p1;
+        asm volatile("" : "+v"(ps));    // summed here, so p0 and p1 die with their remainders
         hw[i] = __builtin_amdgcn_perm(__float_as_uint(p1), __float_as_uint(p0), 0x07060302u);
         const float r0 = dot2_bf16(hw[i], kNegOne0, p0);     // p0 − its truncated bf16, exactly
         const float r1 = dot2_bf16(hw[i], kNegOne1, p1);
@@ -728,105 +818,95 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
     return __builtin_amdgcn_ballot_w64(need) != 0;
   };
 
-  // ---- prologue: tiles 0, 1, 2 requested; tiles 0 and 1 visible ----
-  // valid-unit bits of tiles j, j+1, j+2 (bit h: unit h names a pool block)
-  auto vbits = [&](int tb, int j) -> int {
-    return (unit_phys_in(tb, j, 0) >= 0) | ((unit_phys_in(tb, j, 1) >= 0) << 1);
-  };
-  int vu_cur = vbits(tb_cur, 0);
-  int vu_next = NT > 1 ? vbits(tb_cur, 1) : 0;
-  int vu_after = NT > 2 ? vbits(tb_cur, 2) : 0;
-  // Load protocol: tiles 0..2 here (ids past NT fill zeros); every iteration
-  // but the last requests K of tile j+3 during its products and V of tile
-  // j+3 after its barrier, and waits before the barrier for all but the
-  // newest unit of loads (K of j+3), i.e. for tile j+2.
+  // ---- Load protocol ----
+  // Iteration j exponentiates tile j (scores from iteration j−1), runs PV of
+  // tile j−1 and Sᵀ of tile j+1. Its end waits for request pair j (K of tile
+  // j+2, V of tile j); the barrier then frees K of tile j and V of tile j−1,
+  // and iteration j+1 issues pair j+RK−2 (K of tile j+RK, V of tile j+RK−2)
+  // into those slots, its loads spread between its products so the vector
+  // memory path moves them while the matrix cores work. Requests past NT fill
+  // zeros. vq: valid-unit bits of the tiles whose K is requested (bits 2i,
+  // 2i+1: tile j+i); ea, eb: entries of the next two V requests, which trail
+  // K by two tiles.
+  int vq = 0;
+  Ent ea, eb;
+  {
+    Ent e[RK];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int ph = unit_phys_in(tb_cur, t, half);
-    unit_loads(false, t, t < NT ? ph : -1);
-    unit_loads(true, t, t < NT ? ph : -1);
+    for (int t = 0; t < RK; ++t) {
+      vq |= vbits(t) << (2 * t);
+      e[t] = take_entry(t);
+      issue_req(false, make_req(e[t], false, t));
+      if (t >= 2) issue_req(true, make_req(e[t - 2], true, t - 2));   // pairs 0 … RK−3
+    }
+    ea = e[RK - 2];
+    eb = e[RK - 1];
   }
-  wait_loads_but<2 * LPU>();           // tiles 0 and 1
+  wait_loads_but<LPU + (RK - 2) * PAIR>();    // K of tile 0
   __syncthreads();
   f32x16_t s_cur = scores(0);
-  Pbits p_prev, p_cur;
+  wait_loads_but<(RK - 2) * PAIR>();          // K of tile 1
+  wait_lds_reads();
+  __syncthreads();
+  Pbits p_prev;
 
-  // K of tile j+3 (its buffer held K of tile j−1, done since iteration j−2);
-  // also the tile's valid bits. No branch: past NT the loads fill zeros.
-  int ph_k3 = -1, vu_k3 = 0;
-  auto k_refill = [&](int j) {
-    const int t = j + 3;
-    const int ph = unit_phys_in(tb_cur, t, half);
-    ph_k3 = t < NT ? ph : -1;
-    vu_k3 = vbits(tb_cur, t) & (t < NT ? 3 : 0);
-    unit_loads(false, t, ph_k3);
+  // the requests iteration j+1 issues (prepared during iteration j)
+  Req pend_k, pend_v;
+  auto prepare_next = [&](int j) {
+    pend_v = make_req(ea, true, j + RK - 2);
+    const int t = j + RK;
+    const int nb = vbits(t);
+    const Ent e = take_entry(t);
+    pend_k = make_req(e, false, t);
+    vq = (vq >> 2) | (nb << (2 * (RK - 1)));
+    ea = eb;
+    eb = e;
   };
-  // after iteration j's barrier: V of tile j+3 (V of tile j−1 is consumed),
-  // rotate the valid bits and, every 32 tiles, the table batch
-  auto v_refill = [&](int j) {
-    const int t = j + 3;
-    unit_loads(true, t, ph_k3);
-    vu_cur = vu_next;
-    vu_next = vu_after;
-    vu_after = vu_k3;
-    if (((t + 1) & (kSBatch - 1)) == 0 && t + 1 < NT) {   // tile t+1 starts the next batch
-      tb_cur = tb_nxt;
-      tb_nxt = NT > t + 1 + kSBatch ? table_batch((t + 1) / kSBatch + 1) : -1;
-    }
+  auto issue_pending = [&]() {
+    issue_req(true, pend_v);
+    issue_req(false, pend_k);
   };
-  // Iteration j. The first has no PV, the last no Sᵀ of a next tile; in
-  // between the body is one basic block up to the rare rescale branch, so
-  // the scheduler can interleave P(j)'s vector work with the PV(j−1) and
-  // Sᵀ(j+1) products.
+  auto end_of_iteration = [&]() {
+    wait_loads_but<(RK - 3) * PAIR>();        // pair j: K of tile j+2, V of tile j
+    wait_lds_reads();
+    __syncthreads();
+  };
+  // Iteration j with the full update. The first has no PV, the last no Sᵀ of
+  // a next tile.
   auto body = [&](auto first_tag, auto last_tag, int j) {
     constexpr bool FIRST = decltype(first_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
-    float alpha;
-    const bool moved = softmax(j, s_cur, vu_cur, p_cur, &alpha);
+    if constexpr (!FIRST) issue_pending();
+    // PV(j−1) first, so its P and this tile's scores die before new ones are
+    // made (these iterations are rare; the phases are fenced apart)
     if constexpr (!FIRST) pv(j - 1, p_prev);
-    if constexpr (!LAST) s_cur = scores(j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    float alpha;
+    const bool moved = softmax(j, s_cur, vq & 3, p_prev, &alpha);
     if (moved) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;       // after PV(j−1): O is in the old base
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;       // O holds PV(j−1), in the old base
     }
-    p_prev = p_cur;
-    if constexpr (!LAST) {
-      k_refill(j);
-      // tile j+2 lands and becomes visible to both waves; tile j−1's buffers are free
-      wait_loads_but<LPU>();
-      wait_lds_reads();
-      __syncthreads();
-      v_refill(j);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) s_cur = scores(j + 1);
+    if constexpr (!LAST) prepare_next(j);
+    end_of_iteration();
   };
-  // The steady iteration (neither first nor last), scheduled by hand: one
-  // wave per SIMD, so the matrix cores stay busy only if the wave itself
-  // issues P(j)'s vector work between the products and requests LDS operands
-  // well before they are used. Scheduling barriers fence each step so the
-  // compiler keeps this order.
-  auto vread = [&](const uint8_t* vb, int dt, int ks) -> bf16x8_t {
-    const uint8_t* p = vb + vaddr[dt] + ks * 16 * RB;
-    const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)p);
-    const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_u8*)(p + 8 * RB));
-    const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
-  };
-  auto kread = [&](const uint8_t* kb, int dc) -> bf16x8_t {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + kaddr[dc]));
-  };
-  // Returns true when P(j) must be redone with the full update (a tile well
-  // above some row's base); the caller does it before the next iteration.
-  int vu_prev = 0;
-  auto body_steady = [&](int j) -> bool {
-    const uint8_t* vb = vst + ((j + 3) % kSBufs) * TB;      // V of tile j−1
-    const uint8_t* kb = kst + ((j + 1) % kSBufs) * TB;      // K of tile j+1
+  // The steady iteration (neither first nor last), scheduled by hand: the
+  // wave issues P(j)'s vector work between the products and requests LDS
+  // operands well before they are used; scheduling barriers fence each step
+  // so the compiler keeps this order.
+  auto body_steady = [&](int j) {
+    const uint8_t* vb = vst + ((j - 1) % RV) * TB;          // V of tile j−1
+    const uint8_t* kb = kst + ((j + 1) % RK) * TB;          // K of tile j+1
     f32x16_t st = s_cur;
-    const int key0 = (stream + 2 * j) * kSTile;
-    if (key0 + kSTile - 1 > first_pos || vu_cur != 3) {
+    const int vu = vq & 3;
+    const int key0 = (stream + NS * j) * kSTile;
+    if (key0 + kSTile - 1 > first_pos || vu != 3) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * hg + (r & 3);
-        if (key > row_pos || !((vu_cur >> (r >> 3)) & 1)) st[r] = -INFINITY;
+        if (key > row_pos || !((vu >> (r >> 3)) & 1)) st[r] = -INFINITY;
       }
     }
     // every row of the wave has a finite base here (checked by the caller)
@@ -882,38 +962,31 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[NDT + h], qop[NDT + h], acc, 0, 0, 0);
       }
       if (k % 3 == 0 && k / 3 < 8) piece(k / 3);
-      if (k == NDT + 1) k_refill(j);                 // K of tile j+3: its buffer is free
+      if (k >= 1 && k <= LPU) issue_one(true, pend_v, k - 1);
+      if (k > LPU && k <= 2 * LPU) issue_one(false, pend_k, k - 1 - LPU);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = NSTEP / 3; i < 8; ++i) piece(i);    // Dh 64: fewer products than pieces
     const bool redo = __builtin_amdgcn_ballot_w64(!(ps <= kGuard)) != 0;
-    if (!redo) {
-      l_run += ps;
-      p_prev.hi[0] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      p_prev.hi[1] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[4], hw[5], hw[6], hw[7]));
-      p_prev.lo[0] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      p_prev.lo[1] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[4], lw[5], lw[6], lw[7]));
-    }
+    l_run += redo ? 0.0f : ps;
+    p_prev.hi[0] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    p_prev.hi[1] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[4], hw[5], hw[6], hw[7]));
+    p_prev.lo[0] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    p_prev.lo[1] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[4], lw[5], lw[6], lw[7]));
     s_cur = acc;
-    vu_prev = vu_cur;
-    // tile j+2 lands and becomes visible to both waves; tile j−1's buffers are free
-    wait_loads_but<LPU>();
-    wait_lds_reads();
-    __syncthreads();
-    v_refill(j);
-    return redo;
-  };
-  // P(jj) again with the full update: the scores are recomputed from K of
-  // tile jj, still in its buffer (so no register keeps them through an
-  // iteration), the base moves to the row maximum, and l and O (holding
-  // PV(jj−1)) are rescaled.
-  auto redo_p = [&](int jj) {
-    float alpha;
-    if (softmax(jj, scores(jj), vu_prev, p_prev, &alpha)) {
+    if (redo) {
+      // a tile well above some row's base: P(j) again with the full update,
+      // from scores recomputed out of K of tile j (still in its slot; O holds
+      // PV(j−1) by now, in the old base)
+      float alpha;
+      if (softmax(j, scores(j), vu, p_prev, &alpha)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      }
     }
+    prepare_next(j);
+    end_of_iteration();
   };
   if (NT == 1) {
     body(std::true_type{}, std::true_type{}, 0);
@@ -924,22 +997,18 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
     // have all been masked so far has none)
     for (; j < NT - 1 && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0; ++j)
       body(std::false_type{}, std::false_type{}, j);
-    bool redo = false;
-    for (; j < NT - 1; ++j) {
-      if (redo) redo_p(j - 1);
-      redo = body_steady(j);
-    }
-    if (redo) redo_p(j - 1);
+    for (; j < NT - 1; ++j) body_steady(j);
     body(std::false_type{}, std::true_type{}, NT - 1);
   }
   pv(NT - 1, p_prev);
 
-  // ---- merge the two streams: each wave of a row half finishes half of its dh tiles ----
+  // ---- merge the streams: each wave writes its Oᵀ, m and l; the waves of a
+  // row half then finish a quarter (NS = 4) or half (NS = 2) of its outputs ----
+  wait_all_loads();            // requests past the last tile still write their zeros
   wait_lds_reads();
-  __syncthreads();             // every wave's last LDS reads are done before the buffers are reused
-  float* mo = reinterpret_cast<float*>(lds_k);    // [wave][dt][16][64] Oᵀ parts
-  float* ml = reinterpret_cast<float*>(lds_v);    // [wave][64][2] m, l
-  static_assert(kSWaves * NDT * 16 * kWave * 4 <= 2 * kSBufs * TB, "merge area");
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(lds);                   // [wave][dt][16][64] Oᵀ parts
+  float* ml = mo + (size_t)NW * NDT * 16 * kWave;              // [wave][64][2] m, l
   const float l_row = pair_halves32(l_run, AddOp());
   {
     float* my = mo + (size_t)w * NDT * 16 * kWave;
@@ -951,31 +1020,33 @@ __global__ __launch_bounds__(kSWaves * kWave, 1) void prefill_stream_kernel(SArg
     ml[(w * kWave + lane) * 2 + 1] = l_row;
   }
   __syncthreads();
-  const int other = w ^ 2;                        // the other stream's wave on the same rows
-  const float m_o = ml[(other * kWave + lane) * 2], l_o = ml[(other * kWave + lane) * 2 + 1];
-  const float mx = fmaxf(m_run, m_o);
-  const float f_me = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mx);
-  const float f_o = m_o == -INFINITY ? 0.0f : fast_exp2(m_o - mx);
-  const float lsum = f_me * l_row + f_o * l_o;
+  float f[NS], mx = -INFINITY, lsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    f[k] = ml[((2 * k + half) * kWave + lane) * 2];
+    mx = fmaxf(mx, f[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const float lk = ml[((2 * k + half) * kWave + lane) * 2 + 1];
+    f[k] = f[k] == -INFINITY ? 0.0f : fast_exp2(f[k] - mx);
+    lsum += f[k] * lk;
+  }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;    // no valid key at all: zeros
-  const float* theirs = mo + (size_t)other * NDT * 16 * kWave;
   if (row_ok) {
     float* op = a.out + ((size_t)row_q * a.hq + row_head) * DH + 4 * hg;
+    constexpr int G = 4 * NDT / NS;                       // 4-value groups of this wave
 #pragma unroll
-    for (int k = 0; k < NDT / 2; ++k) {
-      const int dt = stream * (NDT / 2) + k;      // stream 0: the first dh tiles, stream 1: the rest
-      // static indices only (a runtime index would put o in scratch memory)
-      const f32x16_t mine = stream ? o[NDT / 2 + k] : o[k];
+    for (int gg = 0; gg < G; ++gg) {
+      const int gi = stream * G + gg, dt = gi >> 2, q4 = gi & 3;
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float v[4];
+      for (int k = 0; k < NS; ++k) {
+        const float* src = mo + (size_t)(2 * k + half) * NDT * 16 * kWave + (dt * 16 + 4 * q4) * kWave + lane;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * q4 + t;
-          v[t] = (f_me * mine[r] + f_o * theirs[(dt * 16 + r) * kWave + lane]) * inv;
-        }
-        *reinterpret_cast<float4*>(op + 32 * dt + 8 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int t = 0; t < 4; ++t) v[t] += f[k] * src[t * kWave];
       }
+      *reinterpret_cast<float4*>(op + 32 * dt + 8 * q4) = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     }
   }
 }
@@ -1002,7 +1073,7 @@ hipError_t launch_stream_dh(const PrefillParams& p, hipStream_t s) {
   a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   const size_t n = (size_t)p.num_seqs * a.hkv * a.num_chunks * a.num_qtiles;
-  hipLaunchKernelGGL((prefill_stream_kernel<DH>), dim3((unsigned)n), dim3(kSWaves * kWave), 0, s, a);
+  hipLaunchKernelGGL((prefill_stream_kernel<DH, kStreams>), dim3((unsigned)n), dim3(2 * kStreams * kWave), 0, s, a);
   return hipGetLastError();
 }
 
