@@ -26,7 +26,9 @@ run as pkv_attn_mixed_step — whose line reports the prefill chunk against the
 bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
 (--chunk queries on --prefix tokens); `swap`: blocks to pinned host memory
 and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
-streaming-read rate for the decode's 4 KiB tiles, in order and scattered.
+streaming-read rate for the decode's 4 KiB tiles, in order and scattered;
+`mfma-ceiling`: the bf16 matrix-core rate sustained with every CU running the
+prefill's steady-iteration products (the chip's clock drops under that load).
 `append`: slot mapping and KV append in one launch, at the mixed step's size and in bulk.
 `allocator`: the host block allocator on the shared-prefix workload's bookkeeping.
 
@@ -38,6 +40,15 @@ FETCH_CSV WRITE_CSV --workload W` (no GPU needed) scales each counter by what
 it read for the copy and writes profiles/<kernel>_<workload>_traffic.json
 (picked up by later runs as roofline.traffic while the decode sources are
 unchanged) plus a text summary.
+
+Trace summaries: `python bench.py --trace-summary KERNEL_STATS_CSV --workload W
+[--chunk C]` (no GPU needed) records the mean duration of the workload's main
+kernel from a `rocprofv3 --kernel-trace --stats` run of this bench as
+profiles/<kernel>_<workload>_trace.json; while the kernel's sources are
+unchanged, later runs report it as roofline.trace (achieved and frac from the
+kernel's own duration) beside the event-timed roofline, which includes the
+launch. The prefill line also reports roofline.pipelined: K back-to-back
+calls between two events.
 """
 
 import argparse
@@ -63,6 +74,7 @@ CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h",
                   "paged_kv_cache_430_amd/csrc/append_common.h"]
+PREFILL_SOURCES = ["paged_kv_cache_430_amd/csrc/prefill.hip", "paged_kv_cache_430_amd/csrc/device_common.h"]
 # decode workloads: name → (generator, its arguments)
 DECODE_WORKLOADS = {
     "gqa-b32-t4096": ("gqa_b32", "all4096"),        # the headline: B=32 Hq=32 Hkv=8 Dh=128 T=4096 bf16
@@ -84,7 +96,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa-b32-t4096",
                    choices=list(DECODE_WORKLOADS) + [MIXED_WORKLOAD, "prefill-chunk", "prefix-index", "swap",
-                            "read-ceiling", "append", "allocator"])
+                            "read-ceiling", "mfma-ceiling", "append", "allocator"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
@@ -101,6 +113,9 @@ def parse():
                    help="after timing, copy a 256 MiB scratch cache with pkv_copy_blocks (counter calibration)")
     p.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this bench; no GPU needed")
+    p.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                   help="record the kernel durations of a rocprofv3 --kernel-trace --stats run of this bench "
+                        "(--workload, --chunk as in that run) under profiles/; no GPU needed")
     return p.parse_args()
 
 
@@ -207,6 +222,53 @@ def load_traffic(kernel, workload):
     if tr.get("source_hash") != source_hash(DECODE_SOURCES):
         return None
     return tr.get("bytes_per_launch")
+
+
+def trace_key(workload, chunk):
+    return f"{workload}-c{chunk}" if workload == "prefill-chunk" else workload
+
+
+def load_trace(kernel, key, sources, flops_or_bytes, peak, unit):
+    """The kernel's mean duration from a committed rocprofv3 kernel-trace
+    summary of this workload (profiles/<kernel>_<key>_trace.json), if it was
+    taken on the current sources, as a roofline entry; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{key}_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("source_hash") != source_hash(sources):
+        return None
+    ns = tr["mean_ns"]
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    achieved = flops_or_bytes / (ns * 1e-9) / scale
+    return {"timing": "rocprofv3 kernel trace, mean over the run's dispatches", "mean_us": round(ns / 1e3, 3),
+            "achieved": round(achieved, 2), "frac": round(achieved / peak, 4),
+            "summary": os.path.relpath(path, ROOT)}
+
+
+def summarize_trace(stats_csv, workload, chunk):
+    """Mean duration of the workload's main kernel in a rocprofv3
+    --kernel-trace --stats kernel_stats.csv, recorded with the hash of the
+    sources that build it."""
+    if workload == "prefill-chunk":
+        key, kernel, sources = "prefill_stream_kernel", "prefill_stream", PREFILL_SOURCES
+    else:
+        key, kernel, sources = "decode_mfma_kernel", "decode_mfma", DECODE_SOURCES
+    with open(stats_csv) as f:
+        rows = [r for r in csv.DictReader(f) if key in r["Name"]]
+    if not rows:
+        raise SystemExit(f"no {key} in {stats_csv}")
+    r = rows[0]
+    out = {"workload": trace_key(workload, chunk), "kernel": r["Name"], "calls": int(r["Calls"]),
+           "mean_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+           "source_hash": source_hash(sources)}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"{kernel}_{trace_key(workload, chunk)}_trace.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -377,7 +439,11 @@ def run_decode(args, dev):
                      "kernel": decode_kernel_base(w0.cache_dtype) + "_kernel" +
                                ("" if args.unfused else " (append fused)") +
                                (" + decode_merge_kernel" if partition < T else ""),
-                     "bytes_per_launch": call_bytes},
+                     "bytes_per_launch": call_bytes,
+                     "timing": "HIP events around each decode call on its stream (launch included)",
+                     "trace": (load_trace("decode_mfma", args.workload, DECODE_SOURCES, call_bytes, PEAK_HBM_GBS,
+                                          "GB/s")
+                               if partition >= T and decode_kernel_base(w0.cache_dtype) == "decode_mfma" else None)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w0, args.cpu_seconds, d_bytes)
@@ -722,8 +788,12 @@ def run_prefill_chunk(args, dev):
     avg = sum(call) / len(call)
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
-    kernel = env if env in ("tiles", "columns") else ("columns" if C * hq < 256 * 64 and nb * bsz <= 8192 else "tiles")
+    kernel = env if env in ("tiles", "tiles16", "columns") else (
+        "columns" if C * hq < 256 * 64 and nb * bsz <= 8192 else "tiles")
+    names = {"tiles": "prefill_stream_kernel", "tiles16": "prefill_kernel",
+             "columns": "decode_mfma_kernel (prefill columns)"}
     tf = flops / (avg * 1e-3) / 1e12
+    pipelined = flops / (ms * 1e-3) / 1e12
     line = {
         "metric": f"prefill chunk TFLOP/s (bf16 MFMA), C={C} on P={P}",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -731,10 +801,15 @@ def run_prefill_chunk(args, dev):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "prefill-chunk", "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "block_size": bsz,
                    "prefix_tokens": P, "chunk": C,
-                   "kernel": "prefill_kernel" if kernel == "tiles" else "decode_mfma_kernel (prefill columns)"},
+                   "kernel": names[kernel]},
         "call_us": stats_us(call),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_launch": flops},
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_launch": flops,
+                     "timing": "HIP events around each call on its stream (launch included)",
+                     "pipelined": {"timing": "K back-to-back calls between two events", "achieved": round(pipelined, 2),
+                                   "frac": round(pipelined / PEAK_BF16_TFLOPS, 4)},
+                     "trace": (load_trace("prefill_stream", trace_key("prefill-chunk", C), PREFILL_SOURCES, flops,
+                                          PEAK_BF16_TFLOPS, "TFLOP/s") if kernel == "tiles" else None)},
     }
     return line
 
@@ -935,6 +1010,47 @@ def run_swap(args, dev):
 # ---------------------------------------------------------------------------
 # the box's read-bandwidth ceiling for the decode's access pattern
 # ---------------------------------------------------------------------------
+
+def run_mfma_ceiling(args, dev):
+    """pkv_debug_mfma_rate: the prefill steady iteration's 24 bf16 products
+    per wave, from one 8-wave workgroup per CU (two waves per SIMD, as the
+    prefill runs) on N(0,1) operands, timed with events over K launches."""
+    import torch
+
+    import paged_kv_cache_430_amd as pkv
+
+    gen = torch.Generator(device=dev).manual_seed(4307)
+    ops = torch.randn(1024, generator=gen, device=dev).to(torch.bfloat16)
+    nwg = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        pkv.pkv_debug_mfma_rate(ops, iters, nwg, sink)
+    torch.cuda.synchronize()
+    timer = Timer(stream, args.steps)
+    for _ in range(args.steps):
+        timer.start()
+        pkv.pkv_debug_mfma_rate(ops, iters, nwg, sink)
+        timer.stop()
+    torch.cuda.synchronize()
+    ms = timer.ms()
+    avg = sum(ms) / len(ms)
+    flops = nwg * 8 * iters * 24 * 2 * 32 * 32 * 16
+    tf = flops / (avg * 1e-3) / 1e12
+    return {
+        "metric": "sustained bf16 MFMA TFLOP/s, prefill steady-iteration products, every CU busy",
+        "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(avg, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mfma-ceiling", "workgroups": nwg, "waves_per_workgroup": 8, "iterations": iters,
+                   "mfma": "v_mfma_f32_32x32x16_bf16 x 24 per wave-iteration"},
+        "call_us": stats_us(ms),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "mfma_rate_kernel",
+                     "flops_per_launch": flops},
+    }
+
 
 def run_read_ceiling(args, dev):
     """pkv_debug_stream_read over a 2 GiB buffer of 4 KiB tiles (the decode's
@@ -1176,6 +1292,9 @@ def main():
     if args.counters:
         summarize_counters(args.counters[0], args.counters[1], args.workload)
         return
+    if args.trace_summary:
+        summarize_trace(args.trace_summary, args.workload, args.chunk)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(decode shards by sequence or KV head with no exchange; see the design notes).",
@@ -1204,6 +1323,8 @@ def main():
         line = run_prefill_chunk(args, dev)
     elif args.workload == "read-ceiling":
         line = run_read_ceiling(args, dev)
+    elif args.workload == "mfma-ceiling":
+        line = run_mfma_ceiling(args, dev)
     elif args.workload == "append":
         line = run_append(args, dev)
     else:

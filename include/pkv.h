@@ -396,6 +396,24 @@ PKV_API int pkv_swap_in(const pkv_cache* cache, const void* host, size_t host_by
 PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int32_t* tile_ids, int32_t n_tiles,
                                   int32_t num_workgroups, uint32_t* sink, pkv_stream stream);
 
+/* Measurement aid (not on the attention path): the bf16 matrix-core rate
+ * the GPU sustains with every compute unit busy, for the products of the
+ * chunked prefill's steady iteration ([P2] Q027, the FlashAttention section:
+ * QK^T and PV done tile by tile on chip). Each of num_workgroups workgroups
+ * of 8 waves issues, per wave and per iteration, the 24
+ * v_mfma_f32_32x32x16_bf16 of that iteration in the same order and on the
+ * same five accumulators (four PV, one QK^T), and nothing else.
+ *   operands: device bf16, at least 8*(64+19) = 664 values, 16-byte aligned;
+ *             lane l reads values [8(l+j), 8(l+j)+8) as operand j < 20.
+ *   sink: device float [num_workgroups * 512]; lane l of wave w of workgroup
+ *         g writes the sum of its accumulators' 80 values to
+ *         sink[512 g + 64 w + l] (with every operand 1.0: 6144 * iterations).
+ * Flops per call: num_workgroups * 8 * iterations * 24 * 2 * 32*32*16.
+ * PKV_EINVAL for a negative iteration count, num_workgroups outside
+ * [1, 2^31 - 1], NULL pointers or misaligned operands. Asynchronous. */
+PKV_API int pkv_debug_mfma_rate(const void* operands, int32_t iterations, int32_t num_workgroups, float* sink,
+                                pkv_stream stream);
+
 /* Test aid: read one sequence back through its table into the semantic
  * layout [num_kv_heads, seq_len, head_dim] of the stored dtype ([P2] Q025:
  * K and V each [B, H_kv, T, Dh]; Q028: paging changes placement, not order).

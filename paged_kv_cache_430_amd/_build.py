@@ -27,7 +27,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp", "kv_append.hip", "decode.hip", "prefill.hip",
-           "read_probe.hip"]
+           "read_probe.hip", "mfma_probe.hip"]
 HOST_SOURCES = ["pkv_api.cpp", "allocator.cpp", "prefix.cpp"]   # no device code
 ASAN_DIR = os.path.join(PKG, "_build_asan")
 ASAN_LIB = os.path.join(ASAN_DIR, "libpkv_asan.so")

@@ -92,6 +92,10 @@ constexpr int kDecodeMatrix = 1;
 
 // Heads of one KV group handled by one decode workgroup of the given kernel.
 int decode_heads_per_wg(int group, int kernel);
+// Matrix-core rate probe (mfma_probe.hip): operands holds kMfmaProbeOperands
+// bf16 values; sink num_wgs * 512 floats.
+constexpr int kMfmaProbeOperands = 8 * (64 + 19);
+hipError_t launch_mfma_rate(const void* operands, int iterations, int num_wgs, float* sink, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t buf_tiles, const int32_t* ids, int n_tiles, int num_wgs,
                               uint32_t* sink, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

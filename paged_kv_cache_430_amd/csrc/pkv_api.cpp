@@ -620,6 +620,18 @@ PKV_API int pkv_debug_gather(const pkv_cache* cache, const int32_t* block_table,
                     "pkv_debug_gather");
 }
 
+PKV_API int pkv_debug_mfma_rate(const void* operands, int32_t iterations, int32_t num_workgroups, float* sink,
+                                pkv_stream stream) {
+  clear_error();
+  const char* fn = "pkv_debug_mfma_rate";
+  if (iterations < 0 || num_workgroups <= 0 || num_workgroups > kMaxWorkgroups)
+    return fail(PKV_EINVAL, std::string(fn) + ": bad size");
+  if (!operands || !sink) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!aligned16(operands)) return fail(PKV_EINVAL, std::string(fn) + ": operands must be 16-byte aligned");
+  return hip_status(launch_mfma_rate(operands, iterations, num_workgroups, sink, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int32_t* tile_ids, int32_t n_tiles,
                                   int32_t num_workgroups, uint32_t* sink, pkv_stream stream) {
   clear_error();

@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 32
+    assert len(names) == 33
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
@@ -211,6 +211,20 @@ def test_mixed_step_validation(lib):
     de3 = pkv._DecodeBatch(2, 0x50000, None, 0x70000, 0x1, 4, 0x2, 64, 0, 0x80000, None, 0)
     assert call(ref, ctypes.byref(ch), ctypes.byref(de3)) == pkv.PKV_EINVAL     # k_new NULL
     assert "pkv_attn_mixed_step" in lib.pkv_last_error().decode()
+
+
+def test_probe_argument_validation(lib):
+    """The measurement probes check sizes and pointers before launching."""
+    rate = lib.pkv_debug_mfma_rate
+    assert rate(0x50000, -1, 4, 0x60000, None) == pkv.PKV_EINVAL          # negative iteration count
+    assert rate(0x50000, 8, 0, 0x60000, None) == pkv.PKV_EINVAL           # no workgroups
+    assert rate(None, 8, 4, 0x60000, None) == pkv.PKV_EINVAL
+    assert rate(0x50000, 8, 4, None, None) == pkv.PKV_EINVAL
+    assert rate(0x50008, 8, 4, 0x60000, None) == pkv.PKV_EINVAL           # misaligned operands
+    read = lib.pkv_debug_stream_read
+    assert read(0x50000, 4, 0x60000, 8, 0, 0x70000, None) == pkv.PKV_EINVAL
+    assert read(0x50008, 4, 0x60000, 8, 2, 0x70000, None) == pkv.PKV_EINVAL
+    assert read(0x50000, 4, 0x60000, 0, 2, 0x70000, None) == pkv.PKV_OK    # nothing to read
 
 
 def test_append_and_prefill_validation(lib):
