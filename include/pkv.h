@@ -310,8 +310,14 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * decode sequence appends its token and attends (as pkv_attn_decode_append).
  * Two launches on the stream instead of three: the decode kernel, whose
  * last workgroups write the chunks' tokens, then the prefill kernel (a third,
- * the split-KV reduce, when the decodes use more than one partition). The
- * pool bytes and both outputs are bit-identical to the separate calls'.
+ * the split-KV reduce, when the decodes use more than one partition). With
+ * the environment variable PKV_MIXED=one, and when the prefill takes the
+ * key-stream kernel, the appends, decodes and prefill run as one launch:
+ * the prefill workgroups, last in the grid, wait on a per-call counter until
+ * the appending workgroups, first in the grid, have published the chunks'
+ * tokens (a library-owned table of 1024 such counters per GPU, so at most
+ * 1024 of these calls may be in flight on one GPU). Either way the pool
+ * bytes and both outputs are bit-identical to the separate calls'.
  *   chunks:  see pkv_chunk_batch; num_seqs may be 0
  *   decodes: see pkv_decode_batch; batch may be 0
  * BF16 cache and inputs, block_size 16, 32 or 64, the matrix-core decode whatever

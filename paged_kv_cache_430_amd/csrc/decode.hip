@@ -40,11 +40,13 @@
 // Masked slots (past the sequence end) are selected out or read as zeros,
 // never multiplied by zero, and blocks whose id is outside the pool are
 // skipped: pool slots may hold NaN.
+#include <atomic>
 #include <mutex>
 
 #include "append_common.h"
 #include "device_common.h"
 #include "launch.h"
+#include "prefill_stream.h"
 
 namespace pkv {
 
@@ -738,22 +740,34 @@ __device__ __forceinline__ void extra_append(const KernelArgs& a, int idx) {
                           per, a.block_size);
 }
 
+// Each wave's LDS region first stages its K blocks (two padded 16-row
+// blocks), then, after its loop, holds its accumulators for the merge.
+template <int KV, int DH>
+constexpr int mfma_region_bytes() {
+  using G = MfmaGeometry<KV, DH>;
+  constexpr int kStage = 2 * kBlockSize * G::KRS;
+  constexpr int kSlab = 4 * 4 * kMfmaHeads + 1;   // floats per dt slab of the accumulators (see the merge)
+  return kStage > G::NDT * kSlab * 4 ? kStage : G::NDT * kSlab * 4;
+}
+// LDS of a workgroup of NW waves: the regions, then each wave's m and l per head
+template <int KV, int DH, int NW>
+constexpr int mfma_lds_bytes() { return NW * mfma_region_bytes<KV, DH>() + 2 * NW * kMfmaHeads * 4; }
+
+// The matrix-core decode's work for workgroup `flat` of `nflat` (ids in the
+// hardware's order), on NW waves and mfma_lds_bytes<KV, DH, NW>() bytes of
+// LDS at `lds` (16-byte aligned).
 template <int KV, int DH, int NW, bool APPEND, bool EXTRA, bool PREFILL = false, bool SPLIT8 = false>
-__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
+__device__ __forceinline__ void decode_mfma_body(const KernelArgs& a, uint8_t* lds, uint32_t flat, uint32_t nflat) {
   constexpr int kWaves = NW, kThreads = NW * kWave;
   constexpr int NH = kMfmaHeads;
   using G = MfmaGeometry<KV, DH>;
   constexpr int NDC = G::NDC, NDT = G::NDT, KW = G::KW, VW = G::VW;
-  // Each wave's LDS region first stages its K blocks (two padded 16-row
-  // blocks), then, after its loop, holds its accumulators for the merge.
-  constexpr int kStage = 2 * kBlockSize * G::KRS;
   constexpr int kSlab = 4 * 4 * NH + 1;        // floats per dt slab of the accumulators (see the merge)
-  constexpr int kRegion = kStage > NDT * kSlab * 4 ? kStage : NDT * kSlab * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t sh_region[kWaves][kRegion];
-  __shared__ float sh_m[kWaves][NH];
-  __shared__ float sh_l[kWaves][NH];
+  constexpr int kRegion = mfma_region_bytes<KV, DH>();
+  auto sh_region = reinterpret_cast<uint8_t(*)[kRegion]>(lds);
+  auto sh_m = reinterpret_cast<float(*)[NH]>(lds + kWaves * kRegion);
+  auto sh_l = reinterpret_cast<float(*)[NH]>(lds + kWaves * kRegion + kWaves * NH * 4);
 
-  uint32_t flat = flat_block_id(), nflat = flat_grid_size();
   if constexpr (EXTRA) {   // the last x_wgs workgroups only append; they fill the decode's ragged tail
     nflat -= a.x_wgs;
     if (flat >= nflat) {
@@ -1178,6 +1192,80 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
   }
 }
 
+
+template <int KV, int DH, int NW, bool APPEND, bool EXTRA, bool PREFILL = false, bool SPLIT8 = false>
+__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<KV, DH, NW>()];
+  decode_mfma_body<KV, DH, NW, APPEND, EXTRA, PREFILL, SPLIT8>(a, lds, flat_block_id(), flat_grid_size());
+}
+
+// ---------------------------------------------------------------------------
+// The mixed step in one launch ("06 KV Cache、Prefix Cache、PagedAttention 与
+// vLLM", 6.6: one continuous-batching step mixes decodes and prefill chunks).
+// Workgroups in the hardware's order: first the chunks' appends (kExtraTokens
+// tokens each), then the decodes (each appending its own token), then the
+// chunks' prefill query tiles. A prefill workgroup reads the chunk's keys
+// from the pool, so it first waits until every append workgroup has
+// published its stores: the appends count themselves into a slot of
+// kMixedSlots counters (release at agent scope, which writes the XCD's L2
+// back, once per workgroup), and the prefill's first lane polls the count,
+// then acquires at agent scope (which invalidates stale lines) once. The hardware dispatches a grid's
+// workgroups in order, so every append workgroup is resident or done before
+// a prefill workgroup waits, and appends wait on nothing: the wait ends. It
+// is bounded all the same (about a quarter second), so that a broken
+// invariant costs a wrong result, not a hung GPU. The last prefill workgroup
+// subtracts the counts back out, leaving the slot at zero for its next use.
+constexpr int kMixedSlots = 1024;      // calls in flight per GPU, at most
+constexpr int kMixedMaxSpins = 1 << 20;
+__device__ unsigned mixed_sync[kMixedSlots][2];   // [slot]: appends done, prefill workgroups done
+
+struct MixedLayout {
+  uint32_t n_app, n_dec, n_dec_pad, n_pf, slot;
+};
+
+template <int DH>
+constexpr int mixed_lds_bytes() {
+  constexpr int d = mfma_lds_bytes<kBF16, DH, kDecodeWaves>(), p = stream_lds_bytes<DH, kStreams>();
+  return d > p ? d : p;
+}
+
+template <int DH>
+__global__ __launch_bounds__(kDecodeWaves * kWave, 1) void mixed_step_kernel(KernelArgs a, SArgs pa, MixedLayout m) {
+  static_assert(kDecodeWaves == 2 * kStreams, "one workgroup size for both bodies");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[mixed_lds_bytes<DH>()];
+  unsigned* sync = mixed_sync[m.slot];
+  const uint32_t flat = flat_block_id();
+  if (flat < m.n_app) {
+    extra_append<kBF16, DH, kDecodeWaves * kWave>(a, (int)flat);
+    // every wave's stores reach the XCD's L2; then one release at agent
+    // scope writes the L2 back (a fence per wave would write it back 8 times)
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (flat < m.n_app + m.n_dec_pad) {
+    const uint32_t id = flat - m.n_app;
+    if (id < m.n_dec) decode_mfma_body<kBF16, DH, kDecodeWaves, true, false>(a, lds, id, m.n_dec);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    for (int spins = 0; spins < kMixedMaxSpins; ++spins) {
+      if (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= m.n_app) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // one invalidate, not one per poll
+  }
+  __syncthreads();
+  prefill_stream_body<DH, kStreams>(pa, lds, xcd_logical_index(flat - m.n_app - m.n_dec_pad, m.n_pf));
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == m.n_pf - 1) {
+    __hip_atomic_fetch_sub(&sync[0], m.n_app, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_sub(&sync[1], m.n_pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Lanes per K row: 4 keeps the score reduction to two DPP steps and one
 // exponential per lane and head; eight heads per workgroup take 8 so that
 // their q slices fit in fewer registers.
@@ -1240,8 +1328,9 @@ int decode_heads_per_wg(int group, int kernel) {
   return 1;
 }
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  if (p.batch == 0 && p.x_seqs == 0) return hipSuccess;
+namespace {
+
+KernelArgs make_kernel_args(const DecodeParams& p) {
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int hc = decode_heads_per_wg(group, p.kernel);
   KernelArgs a{};
@@ -1279,6 +1368,53 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   a.x_seqs = p.x_seqs;
   a.x_wgs_per_seq = (p.x_max_q + kExtraTokens - 1) / kExtraTokens;
   a.x_wgs = p.x_seqs > 0 && a.x_wgs_per_seq > 0 ? (p.x_seqs * a.x_wgs_per_seq + 7) / 8 * 8 : 0;
+  return a;
+}
+
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
+  MergeArgs m;
+  m.ws_ml = p.ws_ml;
+  m.ws_u = p.ws_u;
+  m.out = p.out;
+  m.num_parts = p.num_parts;
+  const unsigned rows = (unsigned)((size_t)p.batch * p.num_q_heads);
+  if (p.cache.head_dim == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(rows), dim3(kMergeThreads), 0, s, m);
+  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(rows), dim3(kMergeThreads), 0, s, m);
+  return hipGetLastError();
+}
+
+std::atomic<uint32_t> g_mixed_slot{0};
+
+template <int DH>
+hipError_t launch_mixed_dh(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s) {
+  const KernelArgs a = make_kernel_args(dp);
+  const SArgs pa = make_sargs(pp);
+  MixedLayout m;
+  m.n_app = (uint32_t)a.x_wgs;
+  m.n_dec = dp.batch > 0 ? (uint32_t)((size_t)dp.batch * dp.cache.num_kv_heads * a.num_chunks * dp.num_parts) : 0u;
+  m.n_dec_pad = (m.n_dec + 7) / 8 * 8;      // keeps the prefill's ids aligned to the XCD rotation
+  m.n_pf = (uint32_t)stream_workgroups(pp, pa);
+  m.slot = g_mixed_slot.fetch_add(1, std::memory_order_relaxed) % kMixedSlots;
+  const size_t n = (size_t)m.n_app + m.n_dec_pad + m.n_pf;
+  hipLaunchKernelGGL(mixed_step_kernel<DH>, dim3((unsigned)n), dim3(kDecodeWaves * kWave), 0, s, a, pa, m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || dp.batch == 0 || dp.num_parts <= 1) return e;
+  return launch_merge(dp, s);
+}
+
+}  // namespace
+
+hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s) {
+  if (dp.kernel != kDecodeMatrix || dp.cache.dtype != kBF16 || pp.num_seqs == 0 || pp.max_q_len == 0)
+    return hipErrorInvalidValue;
+  return dp.cache.head_dim == 64 ? launch_mixed_dh<64>(dp, pp, s) : launch_mixed_dh<128>(dp, pp, s);
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
+  if (p.batch == 0 && p.x_seqs == 0) return hipSuccess;
+  const int group = p.num_q_heads / p.cache.num_kv_heads;
+  const int hc = decode_heads_per_wg(group, p.kernel);
+  const KernelArgs a = make_kernel_args(p);
   if (a.x_wgs > 0 && p.kernel != kDecodeMatrix) return hipErrorInvalidValue;
   const int dt = p.cache.dtype, dh = p.cache.head_dim;
   hipError_t e;
@@ -1289,15 +1425,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   else if (dt == kBF16) e = dh == 64 ? launch_hc<kBF16, 64>(p, a, hc, s) : launch_hc<kBF16, 128>(p, a, hc, s);
   else e = dh == 64 ? launch_hc<kFP8, 64>(p, a, hc, s) : launch_hc<kFP8, 128>(p, a, hc, s);
   if (e != hipSuccess || p.batch == 0 || p.num_parts <= 1) return e;
-  MergeArgs m;
-  m.ws_ml = p.ws_ml;
-  m.ws_u = p.ws_u;
-  m.out = p.out;
-  m.num_parts = p.num_parts;
-  const unsigned rows = (unsigned)((size_t)p.batch * p.num_q_heads);
-  if (dh == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(rows), dim3(kMergeThreads), 0, s, m);
-  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(rows), dim3(kMergeThreads), 0, s, m);
-  return hipGetLastError();
+  return launch_merge(p, s);
 }
 
 int prefill_cols_heads(int group) {

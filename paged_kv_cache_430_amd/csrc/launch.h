@@ -118,6 +118,11 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// The mixed step in one launch: the chunks' appends, the decodes (each
+// appending its token) and the chunks' prefill (key-stream form) in one grid;
+// bf16 cache, matrix-core decode; the split-KV reduce follows when the decodes
+// are split (see decode.hip).
+hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s);
 // The key-stream tile kernel: 64 query rows per workgroup, four key streams,
 // each a wave per 32-row half (see prefill.hip).
 hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s);

@@ -393,14 +393,26 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
 // and the column form is used. PKV_PREFILL_KERNEL=tiles or =columns, read at
 // every call, overrides the choice where both apply.
 constexpr int64_t kPrefillTileRows = 256 * 64;
-static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
+// The prefill kernel a call runs: the decode kernel's (head, query) columns
+// for small chunks, else the key-stream tile kernel; PKV_PREFILL_KERNEL
+// (tiles, tiles16, columns) overrides.
+enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream };
+static PrefillKernel prefill_kernel_for(const PrefillParams& p) {
   const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
   if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0)) cols = false;
   if (env && strcmp(env, "columns") == 0) cols = cols_ok;
-  if (cols) return launch_prefill_cols(p, s);
-  return env && strcmp(env, "tiles16") == 0 ? launch_prefill(p, s) : launch_prefill_stream(p, s);
+  if (cols) return kPrefillColumns;
+  return env && strcmp(env, "tiles16") == 0 ? kPrefillTiles16 : kPrefillStream;
+}
+
+static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
+  switch (prefill_kernel_for(p)) {
+    case kPrefillColumns: return launch_prefill_cols(p, s);
+    case kPrefillTiles16: return launch_prefill(p, s);
+    default: return launch_prefill_stream(p, s);
+  }
 }
 
 // Checks a prefill call's arguments and fills *p; p->num_seqs == 0 means
@@ -546,6 +558,15 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     dp.x_seqs = chunks->num_seqs;
     dp.x_max_q = chunks->max_q_len;
     dp.new_dtype = PKV_BF16;
+    // PKV_MIXED=one: appends, decodes and prefill in one launch, when the
+    // prefill takes the key-stream kernel. Two launches (the decodes with the
+    // appends, then the prefill) are the default: the one-launch step was
+    // measured about 1% slower on the shared-prefix workload (a compute unit
+    // holds one workgroup of either kind, so one grid saves only the kernel
+    // boundary, and its prefill waits on the appends).
+    const char* menv = getenv("PKV_MIXED");
+    const bool one = menv && strcmp(menv, "one") == 0;
+    if (one && prefill_kernel_for(pp) == kPrefillStream) return hip_status(launch_mixed_one(dp, pp, s), fn);
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
   if (pp.num_seqs == 0) return PKV_OK;

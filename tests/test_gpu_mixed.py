@@ -15,6 +15,11 @@ from gpu_helpers import device, new_pools
 
 pytestmark = pytest.mark.gpu
 
+# PKV_MIXED: "one" runs the appends, the decodes and the prefill in one
+# launch (when the prefill takes the key-stream kernel); "two", the default,
+# the decode launch with the appends followed by the prefill launch
+LAUNCHES = ["one", "two"]
+
 
 def _bf16(shape, gen, dev):
     return torch.randn(*shape, generator=gen, device=dev).to(torch.bfloat16)
@@ -113,8 +118,10 @@ def _oracle_check(c, out_p, out_d):
 @pytest.mark.parametrize("hq,hkv,dh,pt", [(32, 8, 128, 0), (32, 8, 128, 64), (16, 2, 64, 0), (8, 8, 128, 32),
                                           (32, 1, 64, 48)])
 @pytest.mark.parametrize("prefill_kernel", ["tiles", "columns"])
-def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, monkeypatch):
+@pytest.mark.parametrize("launches", LAUNCHES)
+def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, launches, monkeypatch):
     monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
+    monkeypatch.setenv("PKV_MIXED", launches)
     dev = device()
     chunks = [(0, 1), (5, 17), (100, 64), (1000, 130), (31, 33)]
     dec_ctx = [0, 1, 15, 16, 200, 1023, 77]
@@ -133,10 +140,12 @@ def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, monk
 
 @pytest.mark.parametrize("bs", [32, 64])
 @pytest.mark.parametrize("prefill_kernel", ["tiles", "columns"])
-def test_mixed_step_at_block_sizes_32_and_64(bs, prefill_kernel, monkeypatch):
+@pytest.mark.parametrize("launches", LAUNCHES)
+def test_mixed_step_at_block_sizes_32_and_64(bs, prefill_kernel, launches, monkeypatch):
     """The mixed step on pools of 32- and 64-token blocks: chunk and decode
     tokens land inside larger blocks; bit-identical to the separate calls."""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
+    monkeypatch.setenv("PKV_MIXED", launches)
     dev = device()
     c = _case(dev, [(0, 1), (5, 17), (100, 64), (1000, 130), (31, 33)], [0, 1, 15, 16, 200, 1023, 77],
               32, 8, 128, seed=90 + bs, bs=bs)
@@ -151,7 +160,10 @@ def test_mixed_step_at_block_sizes_32_and_64(bs, prefill_kernel, monkeypatch):
     _oracle_check(c, mp, md)
 
 
-def test_mixed_step_chunks_only_and_decodes_only():
+@pytest.mark.parametrize("launches", LAUNCHES)
+def test_mixed_step_chunks_only_and_decodes_only(launches, monkeypatch):
+    monkeypatch.setenv("PKV_MIXED", launches)
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
     dev = device()
     # chunks only: the decode launch carries just the appending workgroups
     c = _case(dev, [(40, 100), (0, 16)], [], 32, 8, 128, seed=5)
