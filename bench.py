@@ -789,7 +789,7 @@ def run_prefill_chunk(args, dev):
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
     kernel = env if env in ("tiles", "tiles16", "columns") else (
-        "columns" if C * hq < 256 * 64 and nb * bsz <= 8192 else "tiles")
+        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles")
     names = {"tiles": "prefill_stream_kernel", "tiles16": "prefill_kernel",
              "columns": "decode_mfma_kernel (prefill columns)"}
     tf = flops / (avg * 1e-3) / 1e12

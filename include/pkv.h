@@ -282,17 +282,20 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   q_start:  device int32 [num_seqs + 1], nondecreasing, q_start[0] = 0
  *   seq_lens: device int32 [num_seqs], T_s >= C_s
  *   max_q_len: host bound on C_s (sizes the grid)
+ *   scale:    score scale, positive and finite (1/sqrt(head_dim) for standard
+ *             attention); anything else is PKV_EINVAL
  *   out:      device fp32, same shape as q
  * Cache dtype BF16, block_size 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2 or a
  * multiple of 4 up to 64. No workspace is needed.
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
- * workgroup, key tiles shared through LDS), and the matrix-core decode kernel
- * with (query head, query) pairs as its 16 columns and the keys split across
- * its waves (tables of at most 8192 tokens). The call takes the column form
- * when num_seqs · max_q_len · num_q_heads < 256 · 64 (too few rows to give
- * every compute unit a tile kernel workgroup), the tile kernel otherwise;
- * the environment variable PKV_PREFILL_KERNEL=tiles or =columns, read at
- * every call, forces one where it applies. */
+ * workgroup, four key streams sharing 32-key tiles through LDS), and the
+ * matrix-core decode kernel with (query head, query) pairs as its 16 columns
+ * and the keys split across its waves (tables of at most 8192 tokens). The
+ * call takes the column form when num_seqs · max_q_len · num_q_heads <
+ * 128 · 64 (too few rows to give half the compute units a tile kernel
+ * workgroup), the tile kernel otherwise; the environment variable
+ * PKV_PREFILL_KERNEL=tiles or =columns, read at every call, forces one where
+ * it applies (=tiles16: the earlier tile kernel, 16 query rows per wave). */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,
