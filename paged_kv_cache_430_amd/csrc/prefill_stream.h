@@ -386,7 +386,10 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // The full update of tile j: mask, row maximum, base moved when the maximum
   // passes it by more than kSlack (l rescaled here; *alpha is O's factor),
   // P as high and low bf16 parts. Returns whether any row of the wave moved.
-  auto softmax = [&](int j, f32x16_t st, int valid_units, Pbits& P, float* alpha) -> bool {
+  // keys the lane's row does not see (causal mask, inclusive) or that lie in
+  // units outside the pool: −inf; only tiles reaching past the workgroup's
+  // first query, or holding such a unit, need it
+  auto mask_scores = [&](int j, f32x16_t& st, int valid_units) {
     const int key0 = (stream + NS * j) * kSTile;
     if (key0 + kSTile - 1 > first_pos || valid_units != 3) {
 #pragma unroll
@@ -395,10 +398,17 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
         if (key > row_pos || !((valid_units >> (r >> 3)) & 1)) st[r] = -INFINITY;
       }
     }
+  };
+  // the row maximum of (masked) scores, in log2 units
+  auto row_max = [&](const f32x16_t& st) -> float {
     float mx = st[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = pair_halves32(mx, MaxOp()) * c2;
+    return pair_halves32(mx, MaxOp()) * c2;
+  };
+  auto softmax = [&](int j, f32x16_t st, int valid_units, Pbits& P, float* alpha) -> bool {
+    mask_scores(j, st, valid_units);
+    const float mx = row_max(st);
     const bool need = mx > m_run + kSlack;             // never while the row has seen nothing (−inf)
     const float moved_by = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mx);
     *alpha = need ? moved_by : 1.0f;
@@ -441,27 +451,47 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // zeros. vq: valid-unit bits of the tiles whose K is requested (bits 2i,
   // 2i+1: tile j+i); ea, eb: entries of the next two V requests, which trail
   // K by two tiles.
+  // The prologue requests K of tiles 0 and 1 and pairs 0 … RK−4, and
+  // prepares pair RK−3 for iteration 0 to issue (as iteration j−1 prepares
+  // pair j+RK−3 for iteration j).
   int vq = 0;
   Ent ea, eb;
   {
-    Ent e[RK];
+    Ent e[RK - 1];
 #pragma unroll
-    for (int t = 0; t < RK; ++t) {
-      vq |= vbits(t) << (2 * t);
+    for (int t = 0; t < RK - 1; ++t) {
+      vq |= vbits(t) << (2 * (t + 1));          // as at iteration −1: bits 2i, 2i+1 for tile i−1
       e[t] = take_entry(t);
       issue_req(false, make_req(e[t], false, t));
-      if (t >= 2) issue_req(true, make_req(e[t - 2], true, t - 2));   // pairs 0 … RK−3
+      if (t >= 2) issue_req(true, make_req(e[t - 2], true, t - 2));   // pairs 0 … RK−4
     }
-    ea = e[RK - 2];
-    eb = e[RK - 1];
+    ea = e[RK - 3];
+    eb = e[RK - 2];
   }
-  wait_loads_but<LPU + (RK - 2) * PAIR>();    // K of tile 0
+  // V of "tile −1" (the slot iteration 0's PV reads, with P = 0): zeros, so
+  // the first iteration's products add nothing
+  {
+    uint8_t* zslot = vst + ((RV - 1) % RV) * TB + half * (kBlockSize * RB);
+#pragma unroll
+    for (int i = 0; i < kBlockSize * RB / (16 * kWave); ++i)
+      *reinterpret_cast<uint4*>(zslot + (i * kWave + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  wait_loads_but<LPU + (RK - 3) * PAIR>();    // K of tile 0
   __syncthreads();
   f32x16_t s_cur = scores(0);
-  wait_loads_but<(RK - 2) * PAIR>();          // K of tile 1
+  {
+    // each row's exponent base: the maximum of its visible scores in tile 0
+    // (a row that sees none of them keeps −inf; its first visible tile takes
+    // the full update through the steady iteration's redo)
+    f32x16_t st = s_cur;
+    mask_scores(0, st, vq >> 2 & 3);
+    m_run = row_max(st);
+  }
+  wait_loads_but<(RK - 3) * PAIR>();          // K of tile 1
   wait_lds_reads();
   __syncthreads();
   Pbits p_prev;
+  p_prev.hi[0] = p_prev.hi[1] = p_prev.lo[0] = p_prev.lo[1] = bf16x8_t{};
 
   // the requests iteration j+1 issues (prepared during iteration j)
   Req pend_k, pend_v;
@@ -475,55 +505,28 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     ea = eb;
     eb = e;
   };
-  auto issue_pending = [&]() {
-    issue_req(true, pend_v);
-    issue_req(false, pend_k);
-  };
   auto end_of_iteration = [&]() {
     wait_loads_but<(RK - 3) * PAIR>();        // pair j: K of tile j+2, V of tile j
     wait_lds_reads();
     __syncthreads();
   };
-  // Iteration j with the full update. The first has no PV, the last no Sᵀ of
-  // a next tile.
-  auto body = [&](auto first_tag, auto last_tag, int j) {
-    constexpr bool FIRST = decltype(first_tag)::value;
-    constexpr bool LAST = decltype(last_tag)::value;
-    if constexpr (!FIRST) issue_pending();
-    // PV(j−1) first, so its P and this tile's scores die before new ones are
-    // made (these iterations are rare; the phases are fenced apart)
-    if constexpr (!FIRST) pv(j - 1, p_prev);
-    __builtin_amdgcn_sched_barrier(0);
-    float alpha;
-    const bool moved = softmax(j, s_cur, vq & 3, p_prev, &alpha);
-    if (moved) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;       // O holds PV(j−1), in the old base
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!LAST) s_cur = scores(j + 1);
-    if constexpr (!LAST) prepare_next(j);
-    end_of_iteration();
-  };
-  // The steady iteration (neither first nor last), scheduled by hand: the
-  // wave issues P(j)'s vector work between the products and requests LDS
-  // operands well before they are used; scheduling barriers fence each step
-  // so the compiler keeps this order.
+  prepare_next(-1);
+  // Iteration j, scheduled by hand: the wave issues P(j)'s vector work
+  // between the products and requests LDS operands well before they are
+  // used; scheduling barriers fence each step so the compiler keeps this
+  // order. Iteration 0's PV multiplies a zero P with zeros; the last
+  // iteration's Sᵀ scores a tile past NT (zeros) and is not used.
   auto body_steady = [&](int j) {
-    const uint8_t* vb = vst + ((j - 1) % RV) * TB;          // V of tile j−1
+    const uint8_t* vb = vst + ((j + RV - 1) % RV) * TB;     // V of tile j−1
     const uint8_t* kb = kst + ((j + 1) % RK) * TB;          // K of tile j+1
     f32x16_t st = s_cur;
     const int vu = vq & 3;
-    const int key0 = (stream + NS * j) * kSTile;
-    if (key0 + kSTile - 1 > first_pos || vu != 3) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hg + (r & 3);
-        if (key > row_pos || !((vu >> (r >> 3)) & 1)) st[r] = -INFINITY;
-      }
-    }
-    // every row of the wave has a finite base here (checked by the caller)
-    const float mb = m_run;
+    mask_scores(j, st, vu);
+    // A row without a base (−inf: it has seen no key yet) exponentiates
+    // against 2^100 below zero: a visible key overflows to +inf, which sends
+    // the tile to the redo below, and masked keys stay 0 (no NaN is ever
+    // made: the guard's comparison is not NaN-safe under -fno-honor-nans).
+    const float mb = m_run == -INFINITY ? -0x1p100f : m_run;
     bf16x8_t v0[NDT], v1[NDT], kk[NDC];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) v0[dt] = vread(vb, dt, 0);
@@ -601,18 +604,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     prepare_next(j);
     end_of_iteration();
   };
-  if (NT == 1) {
-    body(std::true_type{}, std::true_type{}, 0);
-  } else {
-    body(std::true_type{}, std::false_type{}, 0);
-    int j = 1;
-    // full updates until every row of the wave has a base (a row whose keys
-    // have all been masked so far has none)
-    for (; j < NT - 1 && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0; ++j)
-      body(std::false_type{}, std::false_type{}, j);
-    for (; j < NT - 1; ++j) body_steady(j);
-    body(std::false_type{}, std::true_type{}, NT - 1);
-  }
+  for (int j = 0; j < NT; ++j) body_steady(j);
   pv(NT - 1, p_prev);
 
   // ---- merge the streams: each wave writes its Oᵀ, m and l; the waves of a
