@@ -191,6 +191,18 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int half = w & 1, stream = w >> 1;
+  // The first batch of table entries (see the request table below), read
+  // before the sequence's lengths arrive: it needs only the table's size, so
+  // the entries' latency overlaps the lengths'. Units past the keys the
+  // workgroup sees are dropped when the table is built.
+  const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
+  auto batch_ids = [&](int b) -> int {
+    const int jj = b * kSBatch + (lane >> 1);
+    const int u = 2 * (stream + NS * jj) + (lane & 1);
+    const int e = (u >> a.unit_shift) < a.max_blocks ? bt[u >> a.unit_shift] : -1;
+    return (unsigned)e < (unsigned)a.num_blocks ? e : -1;
+  };
+  const int ids0 = batch_ids(0);
   const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
   const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;
   const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], (a.max_blocks << a.unit_shift) * kBlockSize));
@@ -231,25 +243,19 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   const int koff0 = (lane / CPR) * RB + (((lane % CPR) ^ swz_k<DH>(lane / CPR)) << 4);
   const int voff0 = (lane / CPR) * RB + (((lane % CPR) ^ swz_v<DH>(lane / CPR)) << 4);
   static_assert(DH == 64 || DH == 128, "the swizzle steps above");
-  const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
   const int unit_mask = (1 << a.unit_shift) - 1;
   const size_t head_stride = ((size_t)kBlockSize * RB) << a.unit_shift;   // bytes of one (pool block, head)
   const char* kbase = reinterpret_cast<const char*>(a.kc);
   const char* vbase = reinterpret_cast<const char*>(a.vc);
 
   // Request table of the stream's tiles, one entry per lane: batch b holds
-  // units 2t and 2t+1 of tiles t = stream + NS·(32b + lane/2). An entry is
-  // the K address of its unit (low word; the next 16 address bits and the
-  // unit's bytes before the workgroup's last visible key in the other word).
-  // An id outside the pool, or a unit past that key, has 0 bytes: its loads
-  // fill zeros. Requests read entries back with lane reads, so no iteration
-  // waits on a memory load or spends scalar work on addresses.
-  auto batch_ids = [&](int b) -> int {
-    const int jj = b * kSBatch + (lane >> 1);
-    const int u = 2 * (stream + NS * jj) + (lane & 1);
-    const int e = u * kBlockSize < kend ? bt[u >> a.unit_shift] : -1;
-    return (unsigned)e < (unsigned)a.num_blocks ? e : -1;
-  };
+  // units 2t and 2t+1 of tiles t = stream + NS·(32b + lane/2) (ids from
+  // batch_ids above). An entry is the K address of its unit (low word; the
+  // next 16 address bits and the unit's bytes before the workgroup's last
+  // visible key in the other word). An id outside the pool, or a unit past
+  // that key, has 0 bytes: its loads fill zeros. Requests read entries back
+  // with lane reads, so no iteration waits on a memory load or spends scalar
+  // work on addresses.
   uint32_t tl, th;        // entries of the batch holding the next K request
   uint64_t vmask;         // bit 2i+h: unit h of the batch's tile i holds keys
   auto make_table = [&](int b, int e) {
@@ -262,7 +268,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     th = ((uint32_t)(addr >> 32) & 0xffffu) | ((uint32_t)(rows * RB) << 16);
     vmask = __builtin_amdgcn_ballot_w64(rows > 0);
   };
-  make_table(0, batch_ids(0));
+  make_table(0, ids0);
   int ids_nxt = NT > kSBatch ? batch_ids(1) : -1;     // ids of the batch after it
   const uint64_t dv = (uint64_t)(vbase - kbase);      // V's unit lies this far from K's
   // valid-unit bits of tile t (in the current batch)
@@ -604,7 +610,19 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     prepare_next(j);
     end_of_iteration();
   };
-  for (int j = 0; j < NT; ++j) body_steady(j);
+  {
+    // The ring slots repeat every RK·RV iterations (RV = RK − 1, coprime):
+    // unrolled by that period the slots' LDS offsets are constants that the
+    // reads carry as immediates. Where the period is long, two iterations per
+    // trip still spare the copies of the operands one iteration hands on.
+    constexpr int U = RK * RV <= 6 ? RK * RV : 2;
+    int j = 0;
+    for (; j + U - 1 < NT; j += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) body_steady(j + u);
+    }
+    for (; j < NT; ++j) body_steady(j);
+  }
   pv(NT - 1, p_prev);
 
   // ---- merge the streams: each wave writes its Oᵀ, m and l; the waves of a
@@ -612,15 +630,19 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   wait_all_loads();            // requests past the last tile still write their zeros
   wait_lds_reads();
   __syncthreads();
-  float* mo = reinterpret_cast<float*>(lds);                   // [wave][dt][16][64] Oᵀ parts
-  float* ml = mo + (size_t)NW * NDT * 16 * kWave;              // [wave][64][2] m, l
+  // Oᵀ parts as [wave][dt][q4][lane] float4 (values 4q4 … 4q4+3 of a lane's
+  // accumulator), so each store and each read moves 16 bytes per lane
+  float4* mo = reinterpret_cast<float4*>(lds);
+  float* ml = reinterpret_cast<float*>(mo + (size_t)NW * NDT * 4 * kWave);   // [wave][64][2] m, l
   const float l_row = pair_halves32(l_run, AddOp());
   {
-    float* my = mo + (size_t)w * NDT * 16 * kWave;
+    float4* my = mo + (size_t)w * NDT * 4 * kWave;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) my[(dt * 16 + r) * kWave + lane] = o[dt][r];
+      for (int q4 = 0; q4 < 4; ++q4)
+        my[(dt * 4 + q4) * kWave + lane] =
+            make_float4(o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]);
     ml[(w * kWave + lane) * 2 + 0] = m_run;
     ml[(w * kWave + lane) * 2 + 1] = l_row;
   }
@@ -647,9 +669,11 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
       float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const float* src = mo + (size_t)(2 * k + half) * NDT * 16 * kWave + (dt * 16 + 4 * q4) * kWave + lane;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] += f[k] * src[t * kWave];
+        const float4 x = mo[((size_t)(2 * k + half) * NDT * 4 + dt * 4 + q4) * kWave + lane];
+        v[0] += f[k] * x.x;
+        v[1] += f[k] * x.y;
+        v[2] += f[k] * x.z;
+        v[3] += f[k] * x.w;
       }
       *reinterpret_cast<float4*>(op + 32 * dt + 8 * q4) = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     }
