@@ -1014,30 +1014,44 @@ def run_swap(args, dev):
 def run_mfma_ceiling(args, dev):
     """pkv_debug_mfma_rate: the prefill steady iteration's 24 bf16 products
     per wave, from one 8-wave workgroup per CU (two waves per SIMD, as the
-    prefill runs) on N(0,1) operands, timed with events over K launches."""
+    prefill runs) on N(0,1) operands, timed with events over K launches.
+    Beside it, pkv_debug_prefill_mix: the same products with the iteration's
+    vector work, then also its LDS operand reads (mode 1), then also its
+    LDS-direct tile loads and barrier (mode 2), per iteration as many as the
+    prefill moves."""
     import torch
 
     import paged_kv_cache_430_amd as pkv
 
     gen = torch.Generator(device=dev).manual_seed(4307)
     ops = torch.randn(1024, generator=gen, device=dev).to(torch.bfloat16)
+    tiles = torch.randn((1 << 20) // 2, generator=gen, device=dev).to(torch.bfloat16)
     nwg = torch.cuda.get_device_properties(dev).multi_processor_count
     iters = 4096
     sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        pkv.pkv_debug_mfma_rate(ops, iters, nwg, sink)
-    torch.cuda.synchronize()
-    timer = Timer(stream, args.steps)
-    for _ in range(args.steps):
-        timer.start()
-        pkv.pkv_debug_mfma_rate(ops, iters, nwg, sink)
-        timer.stop()
-    torch.cuda.synchronize()
-    ms = timer.ms()
-    avg = sum(ms) / len(ms)
     flops = nwg * 8 * iters * 24 * 2 * 32 * 32 * 16
+
+    def timed(call):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        timer = Timer(stream, args.steps)
+        for _ in range(args.steps):
+            timer.start()
+            call()
+            timer.stop()
+        torch.cuda.synchronize()
+        ms = timer.ms()
+        return ms, sum(ms) / len(ms)
+
+    ms, avg = timed(lambda: pkv.pkv_debug_mfma_rate(ops, iters, nwg, sink))
     tf = flops / (avg * 1e-3) / 1e12
+    mix = {}
+    for mode, name in ((0, "products+vector"), (1, "+lds_reads"), (2, "+lds_reads+tile_loads+barrier")):
+        _, a = timed(lambda: pkv.pkv_debug_prefill_mix(ops, tiles, mode, iters, nwg, sink))
+        mix[name] = {"call_us": round(a * 1e3, 2), "tflops": round(flops / (a * 1e-3) / 1e12, 1),
+                     "us_per_iteration": round(a * 1e3 / iters, 4)}
     return {
         "metric": "sustained bf16 MFMA TFLOP/s, prefill steady-iteration products, every CU busy",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -1049,6 +1063,7 @@ def run_mfma_ceiling(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "mfma_rate_kernel",
                      "flops_per_launch": flops},
+        "prefill_mix": mix,
     }
 
 

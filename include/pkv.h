@@ -423,6 +423,29 @@ PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int3
 PKV_API int pkv_debug_mfma_rate(const void* operands, int32_t iterations, int32_t num_workgroups, float* sink,
                                 pkv_stream stream);
 
+/* Measurement aid: the chunked prefill's steady iteration with its data
+ * movement and without its arithmetic dependences ("07｜KV Cache、
+ * FlashAttention与PagedAttention的内部过程", FlashAttention section: tiles
+ * staged on chip, products done tile by tile). Per wave and iteration: the
+ * same 24 v_mfma_f32_32x32x16_bf16 products as pkv_debug_mfma_rate, 96
+ * vector FMAs and 16 exponentials over the Sᵀ results; mode 1 adds the
+ * prefill's LDS operand reads (8 ds_read_b128 of a K tile, 16 transposing
+ * 8-byte reads of a V tile: 128 KiB per workgroup and iteration); mode 2 also
+ * its tile stream (8 LDS-direct loads of 1 KiB per wave, 64 KiB per
+ * workgroup), a wait for them and a workgroup barrier. One 8-wave workgroup
+ * per num_workgroups entry, 128 KiB of LDS each.
+ *   operands: device bf16, at least 664 values, 16-byte aligned;
+ *   tiles: device, tiles_bytes ≥ 1 MiB (only the first MiB is read), 16-byte
+ *          aligned: the first 64 KiB fill the LDS read region, the tile
+ *          loads read 1 KiB units of the first MiB;
+ *   sink: device fp32 [num_workgroups * 512], written.
+ * Flops per call: num_workgroups * 8 * iterations * 24 * 2 * 32*32*16.
+ * PKV_EINVAL for a negative iteration count, num_workgroups outside
+ * [1, 2^31 - 1], a mode outside 0-2, tiles below 1 MiB, NULL pointers or
+ * misaligned operands or tiles. Asynchronous. */
+PKV_API int pkv_debug_prefill_mix(const void* operands, const void* tiles, int64_t tiles_bytes, int32_t mode,
+                                  int32_t iterations, int32_t num_workgroups, float* sink, pkv_stream stream);
+
 /* Test aid: read one sequence back through its table into the semantic
  * layout [num_kv_heads, seq_len, head_dim] of the stored dtype ([P2] Q025:
  * K and V each [B, H_kv, T, Dh]; Q028: paging changes placement, not order).

@@ -20,7 +20,7 @@ __all__ = [
     "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_auto_partition", "pkv_attn_decode",
     "pkv_attn_decode_append", "pkv_attn_decode_noalloc",
     "pkv_attn_prefill_chunk", "pkv_attn_mixed_step", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_debug_gather",
-    "pkv_debug_stream_read", "pkv_debug_mfma_rate",
+    "pkv_debug_stream_read", "pkv_debug_mfma_rate", "pkv_debug_prefill_mix",
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]
 
@@ -90,6 +90,7 @@ _SIGS = {
     "pkv_debug_gather": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, _VP, _VP]),
     "pkv_debug_stream_read": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, _I32, _I32, _VP, _VP]),
     "pkv_debug_mfma_rate": (ctypes.c_int, [_VP, _I32, _I32, _VP, _VP]),
+    "pkv_debug_prefill_mix": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _I32, _I32, _I32, _VP, _VP]),
     "pkv_swap_out": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "pkv_swap_in": (ctypes.c_int, [ctypes.POINTER(_CacheStruct), _VP, ctypes.c_size_t, _VP, _I32, _VP]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _VP, ctypes.POINTER(_VP)]),
@@ -364,6 +365,24 @@ def pkv_debug_mfma_rate(operands, iterations, num_workgroups, sink=None, stream=
     if sink is None:
         sink = torch.empty(num_workgroups * 512, dtype=torch.float32, device=dev)
     _check(load().pkv_debug_mfma_rate(_ptr(operands), iterations, num_workgroups, _ptr(sink), _stream(stream, dev)))
+    return sink
+
+
+def pkv_debug_prefill_mix(operands, tiles, mode, iterations, num_workgroups, sink=None, stream=None):
+    """Run the prefill's steady-iteration mix (products and vector work; mode
+    1 adds its LDS operand reads, mode 2 also its LDS-direct tile loads and a
+    barrier) `iterations` times in `num_workgroups` 8-wave workgroups;
+    `operands` device bf16 (at least 664 values), `tiles` a device tensor of
+    at least 1 MiB. Returns the per-lane sums (device float32
+    [num_workgroups * 512])."""
+    dev = operands.device
+    if operands.dtype != torch.bfloat16 or operands.numel() < 664:
+        raise PKVError(PKV_EINVAL, "operands: bf16, at least 664 values")
+    if sink is None:
+        sink = torch.empty(num_workgroups * 512, dtype=torch.float32, device=dev)
+    nbytes = tiles.numel() * tiles.element_size()
+    _check(load().pkv_debug_prefill_mix(_ptr(operands), _ptr(tiles), nbytes, mode, iterations, num_workgroups,
+                                        _ptr(sink), _stream(stream, dev)))
     return sink
 
 

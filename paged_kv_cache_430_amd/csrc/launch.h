@@ -96,6 +96,11 @@ int decode_heads_per_wg(int group, int kernel);
 // bf16 values; sink num_wgs * 512 floats.
 constexpr int kMfmaProbeOperands = 8 * (64 + 19);
 hipError_t launch_mfma_rate(const void* operands, int iterations, int num_wgs, float* sink, hipStream_t s);
+// The prefill's steady-iteration mix (mfma_probe.hip): tiles holds at least
+// 1 MiB; mode 0, 1 or 2.
+constexpr int kPrefillMixTileBytes = 1 << 20;
+hipError_t launch_prefill_mix(const void* operands, const void* tiles, int mode, int iterations, int num_wgs,
+                              float* sink, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t buf_tiles, const int32_t* ids, int n_tiles, int num_wgs,
                               uint32_t* sink, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

@@ -654,6 +654,20 @@ PKV_API int pkv_debug_mfma_rate(const void* operands, int32_t iterations, int32_
                     fn);
 }
 
+PKV_API int pkv_debug_prefill_mix(const void* operands, const void* tiles, int64_t tiles_bytes, int32_t mode,
+                                  int32_t iterations, int32_t num_workgroups, float* sink, pkv_stream stream) {
+  clear_error();
+  const char* fn = "pkv_debug_prefill_mix";
+  if (iterations < 0 || num_workgroups <= 0 || num_workgroups > kMaxWorkgroups || mode < 0 || mode > 2)
+    return fail(PKV_EINVAL, std::string(fn) + ": bad size or mode");
+  if (tiles_bytes < kPrefillMixTileBytes) return fail(PKV_EINVAL, std::string(fn) + ": tiles must hold 1 MiB");
+  if (!operands || !tiles || !sink) return fail(PKV_EINVAL, std::string(fn) + ": NULL pointer");
+  if (!aligned16(operands) || !aligned16(tiles))
+    return fail(PKV_EINVAL, std::string(fn) + ": operands and tiles must be 16-byte aligned");
+  return hip_status(launch_prefill_mix(operands, tiles, mode, iterations, num_workgroups, sink,
+                                       static_cast<hipStream_t>(stream)), fn);
+}
+
 PKV_API int pkv_debug_stream_read(const void* buf, int64_t buf_tiles, const int32_t* tile_ids, int32_t n_tiles,
                                   int32_t num_workgroups, uint32_t* sink, pkv_stream stream) {
   clear_error();

@@ -28,7 +28,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert len(names) == 33
+    assert len(names) == 34
     for n in names:
         assert hasattr(lib, n), n
     # and the binding declares a signature for each of them
@@ -215,6 +215,13 @@ def test_mixed_step_validation(lib):
 
 def test_probe_argument_validation(lib):
     """The measurement probes check sizes and pointers before launching."""
+    mix = lib.pkv_debug_prefill_mix
+    assert mix(0x50000, 0x70000, 1 << 20, 2, -1, 4, 0x60000, None) == pkv.PKV_EINVAL   # negative iteration count
+    assert mix(0x50000, 0x70000, 1 << 20, 3, 8, 4, 0x60000, None) == pkv.PKV_EINVAL    # no such mode
+    assert mix(0x50000, 0x70000, (1 << 20) - 16, 1, 8, 4, 0x60000, None) == pkv.PKV_EINVAL   # tiles below 1 MiB
+    assert mix(0x50000, 0x70008, 1 << 20, 1, 8, 4, 0x60000, None) == pkv.PKV_EINVAL    # misaligned tiles
+    assert mix(0x50000, None, 1 << 20, 0, 8, 4, 0x60000, None) == pkv.PKV_EINVAL
+    assert mix(0x50000, 0x70000, 1 << 20, 0, 8, 0, 0x60000, None) == pkv.PKV_EINVAL   # no workgroups
     rate = lib.pkv_debug_mfma_rate
     assert rate(0x50000, -1, 4, 0x60000, None) == pkv.PKV_EINVAL          # negative iteration count
     assert rate(0x50000, 8, 0, 0x60000, None) == pkv.PKV_EINVAL           # no workgroups
