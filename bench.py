@@ -74,7 +74,8 @@ CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h",
                   "paged_kv_cache_430_amd/csrc/append_common.h"]
-PREFILL_SOURCES = ["paged_kv_cache_430_amd/csrc/prefill.hip", "paged_kv_cache_430_amd/csrc/device_common.h"]
+PREFILL_SOURCES = ["paged_kv_cache_430_amd/csrc/prefill.hip", "paged_kv_cache_430_amd/csrc/prefill_stream.h",
+                   "paged_kv_cache_430_amd/csrc/device_common.h"]
 # decode workloads: name → (generator, its arguments)
 DECODE_WORKLOADS = {
     "gqa-b32-t4096": ("gqa_b32", "all4096"),        # the headline: B=32 Hq=32 Hkv=8 Dh=128 T=4096 bf16
