@@ -229,16 +229,19 @@ def trace_key(workload, chunk):
     return f"{workload}-c{chunk}" if workload == "prefill-chunk" else workload
 
 
-def load_trace(kernel, key, sources, flops_or_bytes, peak, unit):
+def load_trace(kernel, key, sources, flops_or_bytes, peak, unit, name_has=None):
     """The kernel's mean duration from a committed rocprofv3 kernel-trace
     summary of this workload (profiles/<kernel>_<key>_trace.json), if it was
-    taken on the current sources, as a roofline entry; else None."""
+    taken on the current sources (and of a kernel whose name holds
+    `name_has`), as a roofline entry; else None."""
     path = os.path.join(PROFILES, f"{kernel}_{key}_trace.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
     if tr.get("source_hash") != source_hash(sources):
+        return None
+    if name_has and name_has not in tr.get("kernel", ""):
         return None
     ns = tr["mean_ns"]
     scale = 1e12 if unit == "TFLOP/s" else 1e9
@@ -789,9 +792,10 @@ def run_prefill_chunk(args, dev):
     avg = sum(call) / len(call)
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
-    kernel = env if env in ("tiles", "tiles16", "columns") else (
-        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles")
-    names = {"tiles": "prefill_stream_kernel", "tiles16": "prefill_kernel",
+    kernel = env if env in ("tiles", "tiles128", "tiles16", "columns") else (
+        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles128" if C * hq >= 128 * 256 else "tiles")
+    names = {"tiles": "prefill_stream_kernel", "tiles128": "prefill_stream_kernel (128 rows)",
+             "tiles16": "prefill_kernel",
              "columns": "decode_mfma_kernel (prefill columns)"}
     tf = flops / (avg * 1e-3) / 1e12
     pipelined = flops / (ms * 1e-3) / 1e12
@@ -810,7 +814,9 @@ def run_prefill_chunk(args, dev):
                      "pipelined": {"timing": "K back-to-back calls between two events", "achieved": round(pipelined, 2),
                                    "frac": round(pipelined / PEAK_BF16_TFLOPS, 4)},
                      "trace": (load_trace("prefill_stream", trace_key("prefill-chunk", C), PREFILL_SOURCES, flops,
-                                          PEAK_BF16_TFLOPS, "TFLOP/s") if kernel == "tiles" else None)},
+                                          PEAK_BF16_TFLOPS, "TFLOP/s",
+                                          name_has=f"prefill_stream_kernel<{dh}, {4 if kernel == 'tiles128' else 2}>")
+                               if kernel in ("tiles", "tiles128") else None)},
     }
     return line
 

@@ -288,14 +288,16 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  * Cache dtype BF16, block_size 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2 or a
  * multiple of 4 up to 64. No workspace is needed.
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
- * workgroup, four key streams sharing 32-key tiles through LDS), and the
- * matrix-core decode kernel with (query head, query) pairs as its 16 columns
- * and the keys split across its waves (tables of at most 8192 tokens). The
- * call takes the column form when num_seqs · max_q_len · num_q_heads <
- * 128 · 64 (too few rows to give half the compute units a tile kernel
- * workgroup), the tile kernel otherwise; the environment variable
- * PKV_PREFILL_KERNEL=tiles or =columns, read at every call, forces one where
- * it applies (=tiles16: the earlier tile kernel, 16 query rows per wave). */
+ * workgroup in four key streams sharing 32-key tiles through LDS, or 128
+ * rows in two streams), and the matrix-core decode kernel with (query head,
+ * query) pairs as its 16 columns and the keys split across its waves (tables
+ * of at most 8192 tokens). With rows = num_seqs · max_q_len · num_q_heads,
+ * the call takes the column form when rows < 128 · 64 (too few to give half
+ * the compute units a tile kernel workgroup), the tile kernel with 128 rows
+ * per workgroup when rows ≥ 128 · 256 (every compute unit gets one), and
+ * with 64 rows otherwise; the environment variable PKV_PREFILL_KERNEL=tiles
+ * (64 rows), =tiles128 or =columns, read at every call, forces one where it
+ * applies (=tiles16: the earlier tile kernel, 16 query rows per wave). */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,

@@ -128,9 +128,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // bf16 cache, matrix-core decode; the split-KV reduce follows when the decodes
 // are split (see decode.hip).
 hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s);
-// The key-stream tile kernel: 64 query rows per workgroup, four key streams,
-// each a wave per 32-row half (see prefill.hip).
-hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s);
+// The key-stream tile kernel: rows = 64 query rows per workgroup in four key
+// streams of two 32-row waves, or 128 rows in two streams of four (see
+// prefill_stream.h).
+hipError_t launch_prefill_stream(const PrefillParams& p, int rows, hipStream_t s);
 
 // The same chunked prefill on the matrix-core decode kernel: each workgroup
 // takes 16 (query head, query) columns of one KV group — prefill_cols_heads

@@ -391,28 +391,39 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
 // is faster once the chunks give half the compute units their 64 rows
 // (measured at Hq=32, Hkv=8 on 2048 cached tokens: C=256, 8192 rows, 37.9
 // against 43.9 µs; C=128, 22.9 against 34.8 µs for the columns); below that
-// the column form is used. PKV_PREFILL_KERNEL=tiles, tiles16 or columns, read
-// at every call, overrides the choice where it applies.
+// the column form is used. Once the rows give every compute unit 128 of them,
+// the tile kernel takes 128 rows per workgroup (two key streams of four
+// waves: half the tile stream per product; C=1024 77.7 against 84.7 µs back
+// to back, C=2048 160.8 against 178.3, C=4096 388.7 against 427.7 per call;
+// at C=512 it would leave half the units idle). PKV_PREFILL_KERNEL=tiles
+// (64 rows), tiles128, tiles16 or columns, read at every call, overrides the
+// choice where it applies.
 constexpr int64_t kPrefillTileRows = 128 * 64;
+constexpr int64_t kPrefillTile128Rows = (int64_t)128 * kComputeUnits;
 // The prefill kernel a call runs: the decode kernel's (head, query) columns
-// for small chunks, else the key-stream tile kernel; PKV_PREFILL_KERNEL
-// (tiles, tiles16, columns) overrides.
-enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream };
+// for small chunks, the key-stream tile kernel with 64 rows per workgroup,
+// or with 128 for large ones; PKV_PREFILL_KERNEL (tiles, tiles128, tiles16,
+// columns) overrides.
+enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream, kPrefillStream128 };
 static PrefillKernel prefill_kernel_for(const PrefillParams& p) {
   const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
-  if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0)) cols = false;
+  if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0 || strcmp(env, "tiles128") == 0)) cols = false;
   if (env && strcmp(env, "columns") == 0) cols = cols_ok;
   if (cols) return kPrefillColumns;
-  return env && strcmp(env, "tiles16") == 0 ? kPrefillTiles16 : kPrefillStream;
+  if (env && strcmp(env, "tiles16") == 0) return kPrefillTiles16;
+  if (env && strcmp(env, "tiles128") == 0) return kPrefillStream128;
+  if (env && strcmp(env, "tiles") == 0) return kPrefillStream;
+  return (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads >= kPrefillTile128Rows ? kPrefillStream128 : kPrefillStream;
 }
 
 static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
   switch (prefill_kernel_for(p)) {
     case kPrefillColumns: return launch_prefill_cols(p, s);
     case kPrefillTiles16: return launch_prefill(p, s);
-    default: return launch_prefill_stream(p, s);
+    case kPrefillStream128: return launch_prefill_stream(p, 128, s);
+    default: return launch_prefill_stream(p, 64, s);
   }
 }
 

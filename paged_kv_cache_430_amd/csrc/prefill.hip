@@ -412,25 +412,27 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
 // Key-stream form: the body is in prefill_stream.h.
 namespace {
 
-template <int DH, int NS>
-__global__ __launch_bounds__(2 * NS * kWave, 1) void prefill_stream_kernel(SArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[stream_lds_bytes<DH, NS>()];
-  prefill_stream_body<DH, NS>(a, lds, xcd_logical_index(flat_block_id(), flat_grid_size()));
+template <int DH, int RG>
+__global__ __launch_bounds__(8 * kWave, 1) void prefill_stream_kernel(SArgs a) {
+  constexpr int NS = StreamShape<RG>::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[stream_lds_bytes<DH, NS, RG>()];
+  prefill_stream_body<DH, NS, RG>(a, lds, xcd_logical_index(flat_block_id(), flat_grid_size()));
 }
 
-template <int DH>
+template <int DH, int RG>
 hipError_t launch_stream_dh(const PrefillParams& p, hipStream_t s) {
-  const SArgs a = make_sargs(p);
+  const SArgs a = make_sargs(p, StreamShape<RG>::ROWS);
   const size_t n = stream_workgroups(p, a);
-  hipLaunchKernelGGL((prefill_stream_kernel<DH, kStreams>), dim3((unsigned)n), dim3(2 * kStreams * kWave), 0, s, a);
+  hipLaunchKernelGGL((prefill_stream_kernel<DH, RG>), dim3((unsigned)n), dim3(8 * kWave), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_stream(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_prefill_stream(const PrefillParams& p, int rows, hipStream_t s) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
-  return p.cache.head_dim == 64 ? launch_stream_dh<64>(p, s) : launch_stream_dh<128>(p, s);
+  if (rows == 128) return p.cache.head_dim == 64 ? launch_stream_dh<64, 4>(p, s) : launch_stream_dh<128, 4>(p, s);
+  return p.cache.head_dim == 64 ? launch_stream_dh<64, 2>(p, s) : launch_stream_dh<128, 2>(p, s);
 }
 
 }  // namespace pkv

@@ -16,20 +16,23 @@
 namespace pkv {
 
 // Key-stream form (the tile kernel): a workgroup of eight waves, two per SIMD,
-// owns 64 query rows (GW ≤ 4 heads of one KV group × 64/GW queries). Wave w
-// takes row half w % 2 (32 rows) of key stream w / 2: stream s scores the
-// 32-key tiles s, s+4, s+8, …, and the two waves of a stream share each tile
-// through LDS. Two waves per SIMD let one wave's vector work, waits and loads
-// run while the other's products occupy the matrix core. Per tile:
+// owns 32·RG query rows (GW ≤ 4 heads of one KV group × 32·RG/GW queries),
+// RG = 2 or 4. Wave w takes row group w % RG (32 rows) of key stream w / RG:
+// stream s of the NS = 8/RG streams scores the 32-key tiles s, s+NS, …, and
+// the RG waves of a stream share each tile through LDS (with RG = 4 a tile
+// feeds twice the products per byte loaded). Two waves per SIMD let one
+// wave's vector work, waits and loads run while the other's products occupy
+// the matrix core. Per tile:
 //   * K and V reach LDS through LDS-direct buffer loads (no registers): one
 //     1 KiB load writes 16 bytes per lane in lane order, so a lane's global
-//     address decides which chunk of which row lands where. Each wave of a
-//     stream loads one 16-row unit of the tile. Rows past the last key the
-//     workgroup sees, and blocks outside the pool, read as zeros (and their
-//     scores are masked). Unit addresses come from a per-lane table built
+//     address decides which chunk of which row lands where. The waves of a
+//     stream load the tile's two 16-row units (RG/2 waves each). Rows past
+//     the last key the workgroup sees, and blocks outside the pool, read as
+//     zeros (and their scores are masked). Unit addresses come from a per-lane table built
 //     once per 32 tiles; the loads of a tile are spread between the products
 //     of the iteration before the one that needs them. K and V have rings of
-//     their own (three and two slots at Dh 128: all of the CU's 160 KiB).
+//     their own (three and two slots at Dh 128 with RG = 2: all of the CU's
+//     160 KiB).
 //   * Sᵀ = K·Qᵀ on v_mfma_f32_32x32x16_bf16 (32 keys × the wave's 32 rows),
 //     K operands read 16 bytes per lane, chunks XOR-swizzled by row so the 16
 //     lanes of a read meet 16 different bank groups.
@@ -46,9 +49,9 @@ namespace pkv {
 //     first tiles only.
 //   * Iteration j: the scores of tile j become P(j) while the matrix cores run
 //     PV of tile j−1 and Sᵀ of tile j+1; then one barrier makes the next
-//     tiles visible to both waves of each stream and frees the slots the
+//     tiles visible to every wave of each stream and frees the slots the
 //     next iteration's loads go to.
-// The four streams' states are merged through LDS at the end.
+// The streams' states are merged through LDS at the end.
 namespace {
 
 constexpr int kStreams = 4;            // key streams of a workgroup (a wave per row half each)
@@ -145,40 +148,58 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_
 // (a redo of that tile reads it again); V of tile t stays in V slot t % RV
 // until PV(t) is done. With RK = RV + 1 the K and V of one pair of requests
 // are both first needed RK − 2 iterations after they are issued. The deepest
-// rings that fit 160 KiB of LDS, at most five K slots.
-template <int DH, int NS>
+// rings that fit 160 KiB of LDS, at most KMAX K slots.
+template <int DH, int NS, int KMAX = 5>
 struct StreamRings {
   static constexpr int TB = kSTile * DH * 2;
   static constexpr int fit = (160 * 1024 / (NS * TB) + 1) / 2;   // NS·(2RK − 1)·TB ≤ 160 KiB
-  static constexpr int RK = fit > 5 ? 5 : fit;
+  static constexpr int RK = fit > KMAX ? KMAX : fit;
   static constexpr int RV = RK - 1;
   static_assert(RK >= 3, "one iteration of cover at least");
 };
 
+// Row groups of 32 query rows per key stream: 2 (64 rows per workgroup, four
+// streams) or 4 (128 rows, two streams). With four the workgroup's tile
+// stream per product is halved; rings of three K slots keep the loop's
+// unrolled period at six iterations.
+template <int RG>
+struct StreamShape {
+  static_assert(RG == 2 || RG == 4, "two or four row groups per stream");
+  static constexpr int NS = 8 / RG;           // key streams of the eight waves
+  static constexpr int ROWS = 32 * RG;        // query rows of a workgroup
+  static constexpr int KMAX = RG == 2 ? 5 : 3;
+};
+
 // LDS bytes the body uses (its argument `lds`, 1 KiB aligned)
-template <int DH, int NS>
+template <int DH, int NS, int RG = 2>
 constexpr int stream_lds_bytes() {
   constexpr int TB = kSTile * DH * 2;
-  constexpr int KV = NS * (StreamRings<DH, NS>::RK + StreamRings<DH, NS>::RV) * TB;
-  constexpr int MERGE = 2 * NS * ((DH / 32) * 16 + 2) * kWave * 4;
+  using Rg = StreamRings<DH, NS, StreamShape<RG>::KMAX>;
+  constexpr int KV = NS * (Rg::RK + Rg::RV) * TB;
+  constexpr int MERGE = RG * NS * ((DH / 32) * 16 + 2) * kWave * 4;
   return KV > MERGE ? KV : MERGE;
 }
 
-// The kernel's work for logical workgroup L (see xcd_logical_index), on 2·NS
-// waves and stream_lds_bytes<DH, NS>() bytes of LDS at `lds`.
-template <int DH, int NS>
+// The kernel's work for logical workgroup L (see xcd_logical_index), on RG·NS
+// = 8 waves and stream_lds_bytes<DH, NS, RG>() bytes of LDS at `lds`.
+template <int DH, int NS, int RG = 2>
 __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds, uint32_t L) {
-  constexpr int NW = 2 * NS;                  // waves: (stream, row half)
+  static_assert(NS == StreamShape<RG>::NS, "eight waves: NS streams of RG row groups");
+  constexpr int NW = RG * NS;                 // waves: (stream, row group)
   constexpr int RB = DH * 2;                  // bytes of one key row of one head
   constexpr int TB = kSTile * RB;             // bytes of one K or V tile
-  constexpr int RK = StreamRings<DH, NS>::RK, RV = StreamRings<DH, NS>::RV;
+  constexpr int RK = StreamRings<DH, NS, StreamShape<RG>::KMAX>::RK;
+  constexpr int RV = StreamRings<DH, NS, StreamShape<RG>::KMAX>::RV;
   constexpr int NDC = DH / 16;                // k-steps of Sᵀ
   constexpr int NDT = DH / 32;                // 32-row dh tiles of Oᵀ
   constexpr int CPR = RB / 16;                // 16-byte chunks per row
   constexpr int RPL = kWave / CPR;            // rows per 1 KiB load
   constexpr int LPU = kBlockSize / RPL;       // loads per 16-row unit
-  constexpr int PAIR = 2 * LPU;               // loads of one (K, V) request pair
-  static_assert(stream_lds_bytes<DH, NS>() <= 160 * 1024, "LDS of a CU");
+  constexpr int WPU = RG / 2;                 // waves loading one unit
+  constexpr int LPW = LPU / WPU;              // a wave's loads per unit request
+  constexpr int PAIR = 2 * LPW;               // a wave's loads of one (K, V) request pair
+  static_assert(LPW >= 1, "every wave loads part of a unit");
+  static_assert(stream_lds_bytes<DH, NS, RG>() <= 160 * 1024, "LDS of a CU");
   static_assert((4 * NDT) % NS == 0, "output groups per stream");
   // lds: [stream][K slot] tiles, then [stream][V slot]; the merge reuses it
 
@@ -190,7 +211,10 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   const int s = L / a.num_qtiles / a.num_chunks / a.hkv;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int half = w & 1, stream = w >> 1;
+  const int rg = w % RG, stream = w / RG;
+  // the wave's part of each tile's loads: unit `unit` (rows 16·unit …), its
+  // loads sub·LPW … sub·LPW + LPW − 1
+  const int unit = rg / WPU, sub = rg % WPU;
   // The first batch of table entries (see the request table below), read
   // before the sequence's lengths arrive: it needs only the table's size, so
   // the entries' latency overlaps the lengths'. Units past the keys the
@@ -206,13 +230,13 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
   const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;
   const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], (a.max_blocks << a.unit_shift) * kBlockSize));
-  const int QW = kSRows / a.gw;                // queries of the workgroup
+  const int QW = StreamShape<RG>::ROWS / a.gw;  // queries of the workgroup
   if (qtile * QW >= C || T <= 0) return;       // uniform over the workgroup
   const int base_pos = T - C;                  // position of query 0
   const int n = lane & 31, hg = lane >> 5;     // Sᵀ column (the lane's row) and lane half
 
-  // the lane's row: workgroup row half·32 + n
-  const int R = half * 32 + n;
+  // the lane's row: workgroup row rg·32 + n
+  const int R = rg * 32 + n;
   const int qi = qtile * QW + R % QW;
   const bool row_ok = qi < C;
   const int row_q = q_lo + (row_ok ? qi : 0);
@@ -279,7 +303,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // the wave's entry of tile t; after a batch's last tile the next batch
   // becomes current
   auto take_entry = [&](int t) -> Ent {
-    const int ln = 2 * (t & (kSBatch - 1)) + half;
+    const int ln = 2 * (t & (kSBatch - 1)) + unit;
     const Ent e{(uint32_t)__builtin_amdgcn_readlane((int)tl, ln), (uint32_t)__builtin_amdgcn_readlane((int)th, ln)};
     if (((t + 1) & (kSBatch - 1)) == 0 && t + 1 < NT) {
       const int b = (t + 1) / kSBatch;
@@ -299,7 +323,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     if (is_v) addr += dv;
     const uint8_t* slot = is_v ? vst + (t % RV) * TB : kst + (t % RK) * TB;
     return Req{(int)(uint32_t)addr, (int)(uint32_t)(addr >> 32), (int)(e.hi >> 16),
-               lds_addr(slot + half * (kBlockSize * RB))};
+               lds_addr(slot + unit * (kBlockSize * RB))};
   };
   // (the resource is assembled from scalar words here: a vector of them
   // carried across iterations may be given vector registers)
@@ -310,7 +334,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     r[2] = __builtin_amdgcn_readfirstlane(q.bytes);
     r[3] = kBufferRsrcWord3;
     const uint32_t d = __builtin_amdgcn_readfirstlane(q.d);
-    switch (i) {
+    switch (sub * LPW + i) {
       case 0: lds_load_one<0>(r, is_v ? voff0 : koff0, d); break;
       case 1: lds_load_one<1>(r, is_v ? voff0 : koff0 ^ 64, d); break;
       case 2: lds_load_one<2>(r, is_v ? voff0 : koff0 ^ 128, d); break;
@@ -319,7 +343,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   };
   auto issue_req = [&](bool is_v, const Req& q) {
 #pragma unroll
-    for (int i = 0; i < LPU; ++i) issue_one(is_v, q, i);
+    for (int i = 0; i < LPW; ++i) issue_one(is_v, q, i);
   };
 
   // Vᵀ operand reads: lane (group G = lane/16, m = lane%16) of dh tile dt,
@@ -477,12 +501,12 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // V of "tile −1" (the slot iteration 0's PV reads, with P = 0): zeros, so
   // the first iteration's products add nothing
   {
-    uint8_t* zslot = vst + ((RV - 1) % RV) * TB + half * (kBlockSize * RB);
+    uint8_t* zslot = vst + ((RV - 1) % RV) * TB + unit * (kBlockSize * RB) + sub * LPW * 16 * kWave;
 #pragma unroll
-    for (int i = 0; i < kBlockSize * RB / (16 * kWave); ++i)
+    for (int i = 0; i < LPW; ++i)
       *reinterpret_cast<uint4*>(zslot + (i * kWave + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
   }
-  wait_loads_but<LPU + (RK - 3) * PAIR>();    // K of tile 0
+  wait_loads_but<LPW + (RK - 3) * PAIR>();    // K of tile 0
   __syncthreads();
   f32x16_t s_cur = scores(0);
   {
@@ -584,8 +608,8 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[NDT + h], qop[NDT + h], acc, 0, 0, 0);
       }
       if (k % 3 == 0 && k / 3 < 8) piece(k / 3);
-      if (k >= 1 && k <= LPU) issue_one(true, pend_v, k - 1);
-      if (k > LPU && k <= 2 * LPU) issue_one(false, pend_k, k - 1 - LPU);
+      if (k >= 1 && k <= LPW) issue_one(true, pend_v, k - 1);
+      if (k > LPW && k <= 2 * LPW) issue_one(false, pend_k, k - 1 - LPW);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -650,12 +674,12 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   float f[NS], mx = -INFINITY, lsum = 0.0f;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    f[k] = ml[((2 * k + half) * kWave + lane) * 2];
+    f[k] = ml[((RG * k + rg) * kWave + lane) * 2];
     mx = fmaxf(mx, f[k]);
   }
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const float lk = ml[((2 * k + half) * kWave + lane) * 2 + 1];
+    const float lk = ml[((RG * k + rg) * kWave + lane) * 2 + 1];
     f[k] = f[k] == -INFINITY ? 0.0f : fast_exp2(f[k] - mx);
     lsum += f[k] * lk;
   }
@@ -669,7 +693,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
       float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const float4 x = mo[((size_t)(2 * k + half) * NDT * 4 + dt * 4 + q4) * kWave + lane];
+        const float4 x = mo[((size_t)(RG * k + rg) * NDT * 4 + dt * 4 + q4) * kWave + lane];
         v[0] += f[k] * x.x;
         v[1] += f[k] * x.y;
         v[2] += f[k] * x.z;
@@ -681,7 +705,8 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
 }
 
 // The kernel arguments of a prefill call.
-inline SArgs make_sargs(const PrefillParams& p) {
+// (rows: the workgroup's query rows, StreamShape<RG>::ROWS)
+inline SArgs make_sargs(const PrefillParams& p, int rows = kSRows) {
   const int group = p.num_q_heads / p.cache.num_kv_heads;
   const int gw = group >= 4 ? 4 : group;
   SArgs a;
@@ -698,7 +723,7 @@ inline SArgs make_sargs(const PrefillParams& p) {
   a.max_blocks = p.max_blocks;
   a.gw = gw;
   a.num_chunks = group / gw;
-  a.num_qtiles = (p.max_q_len + (kSRows / gw) - 1) / (kSRows / gw);
+  a.num_qtiles = (p.max_q_len + (rows / gw) - 1) / (rows / gw);
   a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   return a;

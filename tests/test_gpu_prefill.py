@@ -13,14 +13,14 @@ from gpu_helpers import device, new_pools, parity
 
 pytestmark = pytest.mark.gpu
 
-PREFILL_KERNELS = ["tiles", "tiles16", "columns"]
+PREFILL_KERNELS = ["tiles", "tiles128", "tiles16", "columns"]
 
 
 @pytest.fixture(params=PREFILL_KERNELS)
 def prefill_kernel(request, monkeypatch):
-    """Every prefill kernel (PKV_PREFILL_KERNEL): the key-stream tile kernel,
-    the 16-row tile kernel, and the matrix-core decode kernel with (head,
-    query) columns."""
+    """Every prefill kernel (PKV_PREFILL_KERNEL): the key-stream tile kernel
+    with 64 and with 128 query rows per workgroup, the 16-row tile kernel,
+    and the matrix-core decode kernel with (head, query) columns."""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", request.param)
     return request.param
 
@@ -88,10 +88,15 @@ def test_ragged_chunks_one_call(hq, hkv, dh, prefill_kernel):
 
 
 @pytest.mark.parametrize("seqs", [[(0, 2048)], [(100, 64), (0, 1), (3000, 700), (5, 1500)]])
-def test_tile_kernel_four_wave_workgroups(seqs, monkeypatch):
-    """Enough query tiles (512 or more) for the tile kernel's four-wave
-    workgroups, three per CU."""
-    monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
+@pytest.mark.parametrize("kernel", ["auto", "tiles"])
+def test_tile_kernel_many_query_tiles(seqs, kernel, monkeypatch):
+    """Chunks with rows enough for several rounds of tile kernel workgroups:
+    the library's own choice (128 rows per workgroup at these sizes) and the
+    64-row form."""
+    if kernel == "auto":
+        monkeypatch.delenv("PKV_PREFILL_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("PKV_PREFILL_KERNEL", kernel)
     dev = device()
     err, rel = _prefill_case(dev, seqs, 32, 8, 128, seed=11 + len(seqs))
     assert err <= 2e-3, f"max-abs {err:.3e}"
