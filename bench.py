@@ -792,13 +792,16 @@ def run_prefill_chunk(args, dev):
     avg = sum(call) / len(call)
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
-    kernel = env if env in ("tiles", "tiles128", "tiles16", "columns") else (
-        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles128" if C * hq >= 128 * 256 else "tiles")
+    kernel = env if env in ("tiles", "tiles128", "tiles256", "tiles16", "columns") else (
+        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles256" if C * hq >= 2 * 256 * 256
+        else "tiles128" if C * hq >= 128 * 256 else "tiles")
     names = {"tiles": "prefill_stream_kernel", "tiles128": "prefill_stream_kernel (128 rows)",
+             "tiles256": "prefill_stream_kernel (256 rows)",
              "tiles16": "prefill_kernel",
              "columns": "decode_mfma_kernel (prefill columns)"}
     tf = flops / (avg * 1e-3) / 1e12
     pipelined = flops / (ms * 1e-3) / 1e12
+    rg = {"tiles128": 4, "tiles256": 8 if dh == 128 else 4}.get(kernel, 2)   # row groups per key stream
     line = {
         "metric": f"prefill chunk TFLOP/s (bf16 MFMA), C={C} on P={P}",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -815,8 +818,8 @@ def run_prefill_chunk(args, dev):
                                    "frac": round(pipelined / PEAK_BF16_TFLOPS, 4)},
                      "trace": (load_trace("prefill_stream", trace_key("prefill-chunk", C), PREFILL_SOURCES, flops,
                                           PEAK_BF16_TFLOPS, "TFLOP/s",
-                                          name_has=f"prefill_stream_kernel<{dh}, {4 if kernel == 'tiles128' else 2}>")
-                               if kernel in ("tiles", "tiles128") else None)},
+                                          name_has=f"prefill_stream_kernel<{dh}, {rg}>")
+                               if kernel in ("tiles", "tiles128", "tiles256") else None)},
     }
     return line
 

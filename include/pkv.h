@@ -289,15 +289,17 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  * multiple of 4 up to 64. No workspace is needed.
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
  * workgroup in four key streams sharing 32-key tiles through LDS, or 128
- * rows in two streams), and the matrix-core decode kernel with (query head,
- * query) pairs as its 16 columns and the keys split across its waves (tables
- * of at most 8192 tokens). With rows = num_seqs · max_q_len · num_q_heads,
- * the call takes the column form when rows < 128 · 64 (too few to give half
- * the compute units a tile kernel workgroup), the tile kernel with 128 rows
- * per workgroup when rows ≥ 128 · 256 (every compute unit gets one), and
- * with 64 rows otherwise; the environment variable PKV_PREFILL_KERNEL=tiles
- * (64 rows), =tiles128 or =columns, read at every call, forces one where it
- * applies (=tiles16: the earlier tile kernel, 16 query rows per wave). */
+ * rows in two streams, or 256 in one), and the matrix-core decode kernel
+ * with (query head, query) pairs as its 16 columns and the keys split across
+ * its waves (tables of at most 8192 tokens). With rows = num_seqs ·
+ * max_q_len · num_q_heads, the call takes the column form when rows < 128 ·
+ * 64 (too few to give half the compute units a tile kernel workgroup), the
+ * tile kernel with 256 rows per workgroup when rows ≥ 2 · 256 · 256 and
+ * head_dim is 128 (two per compute unit), with 128 when rows ≥ 128 · 256
+ * (one per unit), and with 64 otherwise; the environment variable
+ * PKV_PREFILL_KERNEL=tiles (64 rows), =tiles128, =tiles256 (128 at head_dim
+ * 64) or =columns, read at every call, forces one where it applies
+ * (=tiles16: the earlier tile kernel, 16 query rows per wave). */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,

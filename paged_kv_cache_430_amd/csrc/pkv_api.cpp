@@ -395,27 +395,36 @@ static int decode_impl(const char* fn, const pkv_cache* cache, const NewTokens* 
 // the tile kernel takes 128 rows per workgroup (two key streams of four
 // waves: half the tile stream per product; C=1024 77.7 against 84.7 µs back
 // to back, C=2048 160.8 against 178.3, C=4096 388.7 against 427.7 per call;
-// at C=512 it would leave half the units idle). PKV_PREFILL_KERNEL=tiles
-// (64 rows), tiles128, tiles16 or columns, read at every call, overrides the
-// choice where it applies.
+// at C=512 it would leave half the units idle), and once they give every unit
+// two workgroups of 256 rows, 256 (one stream of eight waves, head dim 128;
+// C=4096 363.4 against 378.7 µs; at C=2048 one round of them is slower,
+// 180.8 against 161.3). PKV_PREFILL_KERNEL=tiles (64 rows), tiles128,
+// tiles256, tiles16 or columns, read at every call, overrides the choice
+// where it applies.
 constexpr int64_t kPrefillTileRows = 128 * 64;
 constexpr int64_t kPrefillTile128Rows = (int64_t)128 * kComputeUnits;
+constexpr int64_t kPrefillTile256Rows = (int64_t)2 * 256 * kComputeUnits;
 // The prefill kernel a call runs: the decode kernel's (head, query) columns
 // for small chunks, the key-stream tile kernel with 64 rows per workgroup,
 // or with 128 for large ones; PKV_PREFILL_KERNEL (tiles, tiles128, tiles16,
 // columns) overrides.
-enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream, kPrefillStream128 };
+enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream, kPrefillStream128, kPrefillStream256 };
 static PrefillKernel prefill_kernel_for(const PrefillParams& p) {
   const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
-  if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0 || strcmp(env, "tiles128") == 0)) cols = false;
+  if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0 || strcmp(env, "tiles128") == 0 ||
+              strcmp(env, "tiles256") == 0))
+    cols = false;
   if (env && strcmp(env, "columns") == 0) cols = cols_ok;
   if (cols) return kPrefillColumns;
   if (env && strcmp(env, "tiles16") == 0) return kPrefillTiles16;
   if (env && strcmp(env, "tiles128") == 0) return kPrefillStream128;
+  if (env && strcmp(env, "tiles256") == 0) return kPrefillStream256;
   if (env && strcmp(env, "tiles") == 0) return kPrefillStream;
-  return (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads >= kPrefillTile128Rows ? kPrefillStream128 : kPrefillStream;
+  const int64_t rows = (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads;
+  if (rows >= kPrefillTile256Rows && p.cache.head_dim == 128) return kPrefillStream256;
+  return rows >= kPrefillTile128Rows ? kPrefillStream128 : kPrefillStream;
 }
 
 static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
@@ -423,6 +432,7 @@ static hipError_t run_prefill(const PrefillParams& p, hipStream_t s) {
     case kPrefillColumns: return launch_prefill_cols(p, s);
     case kPrefillTiles16: return launch_prefill(p, s);
     case kPrefillStream128: return launch_prefill_stream(p, 128, s);
+    case kPrefillStream256: return launch_prefill_stream(p, 256, s);
     default: return launch_prefill_stream(p, 64, s);
   }
 }

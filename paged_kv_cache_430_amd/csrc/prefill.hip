@@ -431,7 +431,8 @@ hipError_t launch_stream_dh(const PrefillParams& p, hipStream_t s) {
 
 hipError_t launch_prefill_stream(const PrefillParams& p, int rows, hipStream_t s) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
-  if (rows == 128) return p.cache.head_dim == 64 ? launch_stream_dh<64, 4>(p, s) : launch_stream_dh<128, 4>(p, s);
+  if (rows == 256 && p.cache.head_dim == 128) return launch_stream_dh<128, 8>(p, s);
+  if (rows >= 128) return p.cache.head_dim == 64 ? launch_stream_dh<64, 4>(p, s) : launch_stream_dh<128, 4>(p, s);
   return p.cache.head_dim == 64 ? launch_stream_dh<64, 2>(p, s) : launch_stream_dh<128, 2>(p, s);
 }
 

@@ -159,12 +159,13 @@ struct StreamRings {
 };
 
 // Row groups of 32 query rows per key stream: 2 (64 rows per workgroup, four
-// streams) or 4 (128 rows, two streams). With four the workgroup's tile
-// stream per product is halved; rings of three K slots keep the loop's
-// unrolled period at six iterations.
+// streams), 4 (128 rows, two streams) or 8 (256 rows, one stream: no merge
+// across streams). Each doubling halves the workgroup's tile stream per
+// product; rings of three K slots keep the loop's unrolled period at six
+// iterations.
 template <int RG>
 struct StreamShape {
-  static_assert(RG == 2 || RG == 4, "two or four row groups per stream");
+  static_assert(RG == 2 || RG == 4 || RG == 8, "two, four or eight row groups per stream");
   static constexpr int NS = 8 / RG;           // key streams of the eight waves
   static constexpr int ROWS = 32 * RG;        // query rows of a workgroup
   static constexpr int KMAX = RG == 2 ? 5 : 3;
@@ -176,7 +177,7 @@ constexpr int stream_lds_bytes() {
   constexpr int TB = kSTile * DH * 2;
   using Rg = StreamRings<DH, NS, StreamShape<RG>::KMAX>;
   constexpr int KV = NS * (Rg::RK + Rg::RV) * TB;
-  constexpr int MERGE = RG * NS * ((DH / 32) * 16 + 2) * kWave * 4;
+  constexpr int MERGE = NS == 1 ? 0 : RG * NS * ((DH / 32) * 16 + 2) * kWave * 4;
   return KV > MERGE ? KV : MERGE;
 }
 
@@ -650,9 +651,25 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   pv(NT - 1, p_prev);
 
   // ---- merge the streams: each wave writes its Oᵀ, m and l; the waves of a
-  // row half then finish a quarter (NS = 4) or half (NS = 2) of its outputs ----
+  // row group then finish a quarter (NS = 4) or half (NS = 2) of its outputs;
+  // a single stream's waves write their rows' outputs directly ----
   wait_all_loads();            // requests past the last tile still write their zeros
   wait_lds_reads();
+  if constexpr (NS == 1) {
+    const float l_row = pair_halves32(l_run, AddOp());
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;    // no valid key at all: zeros
+    if (row_ok) {
+      float* op = a.out + ((size_t)row_q * a.hq + row_head) * DH + 4 * hg;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(op + 32 * dt + 8 * q4) =
+              make_float4(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv, o[dt][4 * q4 + 2] * inv,
+                          o[dt][4 * q4 + 3] * inv);
+    }
+    return;
+  }
   __syncthreads();
   // Oᵀ parts as [wave][dt][q4][lane] float4 (values 4q4 … 4q4+3 of a lane's
   // accumulator), so each store and each read moves 16 bytes per lane

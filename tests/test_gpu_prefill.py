@@ -13,14 +13,15 @@ from gpu_helpers import device, new_pools, parity
 
 pytestmark = pytest.mark.gpu
 
-PREFILL_KERNELS = ["tiles", "tiles128", "tiles16", "columns"]
+PREFILL_KERNELS = ["tiles", "tiles128", "tiles256", "tiles16", "columns"]
 
 
 @pytest.fixture(params=PREFILL_KERNELS)
 def prefill_kernel(request, monkeypatch):
     """Every prefill kernel (PKV_PREFILL_KERNEL): the key-stream tile kernel
-    with 64 and with 128 query rows per workgroup, the 16-row tile kernel,
-    and the matrix-core decode kernel with (head, query) columns."""
+    with 64, 128 and 256 query rows per workgroup (256: head dim 128; at 64
+    the call runs 128), the 16-row tile kernel, and the matrix-core decode
+    kernel with (head, query) columns."""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", request.param)
     return request.param
 
@@ -91,8 +92,8 @@ def test_ragged_chunks_one_call(hq, hkv, dh, prefill_kernel):
 @pytest.mark.parametrize("kernel", ["auto", "tiles"])
 def test_tile_kernel_many_query_tiles(seqs, kernel, monkeypatch):
     """Chunks with rows enough for several rounds of tile kernel workgroups:
-    the library's own choice (128 rows per workgroup at these sizes) and the
-    64-row form."""
+    the library's own choice (128 rows per workgroup for the first, 256 for
+    the second) and the 64-row form."""
     if kernel == "auto":
         monkeypatch.delenv("PKV_PREFILL_KERNEL", raising=False)
     else:

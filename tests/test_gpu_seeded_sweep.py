@@ -67,7 +67,7 @@ def test_decode_seeded_shapes(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
-@pytest.mark.parametrize("prefill_kernel", ["tiles", "tiles128", "columns"])
+@pytest.mark.parametrize("prefill_kernel", ["tiles", "tiles128", "tiles256", "columns"])
 def test_prefill_seeded_shapes(seed, prefill_kernel, monkeypatch):
     monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
     rng = np.random.default_rng(7000 + seed)
