@@ -790,6 +790,8 @@ def run_prefill_chunk(args, dev):
     torch.cuda.synchronize()
     call = timer.ms()
     avg = sum(call) / len(call)
+    if getattr(args, "calib_copy", False):
+        calib_copy(dev)
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
     kernel = env if env in ("tiles", "tiles128", "tiles256", "tiles16", "columns") else (
@@ -812,7 +814,10 @@ def run_prefill_chunk(args, dev):
                    "kernel": names[kernel]},
         "call_us": stats_us(call),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_launch": flops,
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (load_prefill_traffic(C, f"prefill_stream_kernel<{dh}, {rg}>")
+                                 if kernel in ("tiles", "tiles128", "tiles256") else None),
+                     "flops_per_launch": flops,
                      "timing": "HIP events around each call on its stream (launch included)",
                      "pipelined": {"timing": "K back-to-back calls between two events", "achieved": round(pipelined, 2),
                                    "frac": round(pipelined / PEAK_BF16_TFLOPS, 4)},
@@ -828,10 +833,11 @@ def run_prefill_chunk(args, dev):
 # counter summaries
 # ---------------------------------------------------------------------------
 
-def summarize_counters(fetch_csv, write_csv, workload):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernels, each
-    scaled by the factor that maps the calibration copy's reading onto the
-    bytes it is known to move."""
+def summarize_counters(fetch_csv, write_csv, workload, chunk=None):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernels (or,
+    for prefill-chunk, of the key-stream prefill kernel), each scaled by the
+    factor that maps the calibration copy's reading onto the bytes it is
+    known to move."""
     def load(path, counter):
         per = {}
         with open(path) as f:
@@ -854,14 +860,20 @@ def summarize_counters(fetch_csv, write_csv, workload):
     _, cw = pick(write, "copy_blocks_kernel")
     f_scale = CALIB_BYTES / cf[-1]
     w_scale = CALIB_BYTES / cw[-1]
-    out = {"workload": workload, "source_hash": source_hash(DECODE_SOURCES),
+    prefill = workload == "prefill-chunk"
+    out = {"workload": trace_key(workload, chunk) if prefill else workload,
+           "source_hash": source_hash(PREFILL_SOURCES if prefill else DECODE_SOURCES),
            "calibration": {"kernel": "copy_blocks_kernel", "bytes": CALIB_BYTES,
                            "fetch_bytes_read": cf[-1], "write_bytes_read": cw[-1],
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": {}}
     total = 0.0
-    base = "decode_mfma" if any("decode_mfma_kernel" in n for n in fetch) else "decode_split"
-    for key in (base + "_kernel", "decode_merge_kernel"):
+    if prefill:
+        base, keys = "prefill_stream", ("prefill_stream_kernel",)
+    else:
+        base = "decode_mfma" if any("decode_mfma_kernel" in n for n in fetch) else "decode_split"
+        keys = (base + "_kernel", "decode_merge_kernel")
+    for key in keys:
         names = [n for n in fetch if key in n]
         if not names:
             continue
@@ -873,11 +885,28 @@ def summarize_counters(fetch_csv, write_csv, workload):
         total += fb + wb
     out["bytes_per_launch"] = round(total)
     os.makedirs(PROFILES, exist_ok=True)
-    path = os.path.join(PROFILES, f"{base}_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"{base}_{out['workload']}_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return out
+
+
+def load_prefill_traffic(chunk, kernel_name_has):
+    """HBM bytes per launch of the key-stream prefill from a committed counter
+    summary of this chunk size, if taken on the current sources and of the
+    same kernel form; else None."""
+    path = os.path.join(PROFILES, f"prefill_stream_{trace_key('prefill-chunk', chunk)}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("source_hash") != source_hash(PREFILL_SOURCES):
+        return None
+    k = tr.get("kernels", {}).get("prefill_stream_kernel", {})
+    if kernel_name_has not in k.get("name", ""):
+        return None
+    return tr["bytes_per_launch"]
 
 
 # ---------------------------------------------------------------------------
@@ -1315,7 +1344,7 @@ def run_allocator(args):
 def main():
     args = parse()
     if args.counters:
-        summarize_counters(args.counters[0], args.counters[1], args.workload)
+        summarize_counters(args.counters[0], args.counters[1], args.workload, args.chunk)
         return
     if args.trace_summary:
         summarize_trace(args.trace_summary, args.workload, args.chunk)
