@@ -28,7 +28,9 @@ bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
 and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
 streaming-read rate for the decode's 4 KiB tiles, in order and scattered;
 `mfma-ceiling`: the bf16 matrix-core rate sustained with every CU running the
-prefill's steady-iteration products (the chip's clock drops under that load).
+prefill's steady-iteration products (the chip's clock drops under that load),
+and beside it the rate of the same products with the iteration's vector work,
+LDS operand reads and tile loads added in turn.
 `append`: slot mapping and KV append in one launch, at the mixed step's size and in bulk.
 `allocator`: the host block allocator on the shared-prefix workload's bookkeeping.
 
@@ -36,10 +38,11 @@ Counter summaries: `--calib-copy` adds, after the timed steps, one
 pkv_copy_blocks launch over a 256 MiB scratch cache (a plain copy of known
 size). Run the bench under `rocprofv3 --pmc FETCH_SIZE` and again under
 `--pmc WRITE_SIZE` with that flag, then `python bench.py --counters
-FETCH_CSV WRITE_CSV --workload W` (no GPU needed) scales each counter by what
-it read for the copy and writes profiles/<kernel>_<workload>_traffic.json
-(picked up by later runs as roofline.traffic while the decode sources are
-unchanged) plus a text summary.
+FETCH_CSV WRITE_CSV --workload W [--chunk C]` (no GPU needed) scales each
+counter by what it read for the copy and writes
+profiles/<kernel>_<workload>_traffic.json (picked up by later runs as
+roofline.traffic while the decode, or prefill, sources are unchanged) plus a
+text summary.
 
 Trace summaries: `python bench.py --trace-summary KERNEL_STATS_CSV --workload W
 [--chunk C]` (no GPU needed) records the mean duration of the workload's main
