@@ -77,6 +77,7 @@ CALIB_BYTES = 256 * 2 ** 20       # K+V bytes moved by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_430_amd/csrc/decode.hip", "paged_kv_cache_430_amd/csrc/device_common.h",
                   "paged_kv_cache_430_amd/csrc/append_common.h"]
+APPEND_SOURCES = ["paged_kv_cache_430_amd/csrc/kv_append.hip", "paged_kv_cache_430_amd/csrc/append_common.h"]
 PREFILL_SOURCES = ["paged_kv_cache_430_amd/csrc/prefill.hip", "paged_kv_cache_430_amd/csrc/prefill_stream.h",
                    "paged_kv_cache_430_amd/csrc/device_common.h"]
 # decode workloads: name → (generator, its arguments)
@@ -217,13 +218,13 @@ def decode_kernel_base(cache_dtype):
     return "decode_mfma"
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, sources=DECODE_SOURCES):
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
-    if tr.get("source_hash") != source_hash(DECODE_SOURCES):
+    if tr.get("source_hash") != source_hash(sources):
         return None
     return tr.get("bytes_per_launch")
 
@@ -838,9 +839,10 @@ def run_prefill_chunk(args, dev):
 
 def summarize_counters(fetch_csv, write_csv, workload, chunk=None):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernels (or,
-    for prefill-chunk, of the key-stream prefill kernel), each scaled by the
-    factor that maps the calibration copy's reading onto the bytes it is
-    known to move."""
+    for prefill-chunk, of the key-stream prefill kernel; for append, of the
+    bulk append's dispatches, the second half of the run's append dispatches),
+    each scaled by the factor that maps the calibration copy's reading onto
+    the bytes it is known to move."""
     def load(path, counter):
         per = {}
         with open(path) as f:
@@ -864,8 +866,10 @@ def summarize_counters(fetch_csv, write_csv, workload, chunk=None):
     f_scale = CALIB_BYTES / cf[-1]
     w_scale = CALIB_BYTES / cw[-1]
     prefill = workload == "prefill-chunk"
+    append = workload == "append"
+    sources = PREFILL_SOURCES if prefill else APPEND_SOURCES if append else DECODE_SOURCES
     out = {"workload": trace_key(workload, chunk) if prefill else workload,
-           "source_hash": source_hash(PREFILL_SOURCES if prefill else DECODE_SOURCES),
+           "source_hash": source_hash(sources),
            "calibration": {"kernel": "copy_blocks_kernel", "bytes": CALIB_BYTES,
                            "fetch_bytes_read": cf[-1], "write_bytes_read": cw[-1],
                            "fetch_scale": f_scale, "write_scale": w_scale},
@@ -873,6 +877,13 @@ def summarize_counters(fetch_csv, write_csv, workload, chunk=None):
     total = 0.0
     if prefill:
         base, keys = "prefill_stream", ("prefill_stream_kernel",)
+    elif append:
+        base, keys = "kv_append_paged", ("kv_append_paged_kernel",)
+        # the step shape is timed first, then the bulk shape, with the same
+        # number of dispatches each: keep the bulk half
+        for per in (fetch, write):
+            for n in [n for n in per if keys[0] in n]:
+                per[n] = per[n][len(per[n]) // 2:]
     else:
         base = "decode_mfma" if any("decode_mfma_kernel" in n for n in fetch) else "decode_split"
         keys = (base + "_kernel", "decode_merge_kernel")
@@ -1172,7 +1183,9 @@ def run_append(args, dev):
     of 16 sequences x 2048 tokens (32768 tokens), whose rate is `value`.
     Algorithmic bytes per token: K and V read from the input and written to
     the pool (2 x Hkv x Dh x 2 bytes each way) plus one table entry and one
-    slot computation's inputs (8 bytes)."""
+    slot computation's inputs (8 bytes). Each shape rotates through copies of
+    its pool and inputs (at least 2 GiB together), so that no call finds the
+    previous call's lines in the caches."""
     import numpy as np
     import torch
 
@@ -1194,21 +1207,26 @@ def run_append(args, dev):
             nb = -(-(f + c) // bs)
             bt[i, :nb] = perm[pos:pos + nb]
             pos += nb
-        kp = torch.zeros(total_blocks, hkv, bs, dh, dtype=torch.bfloat16, device=dev)
-        cache = pkv.Cache(kp, torch.zeros_like(kp))
         n = sum(counts)
-        k = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+        copy_bytes = (total_blocks * bs + n) * hkv * dh * 2 * 2
+        sets = []
+        for _ in range(max(1, min(16, math.ceil(MALL_BYTES / copy_bytes)))):
+            kp = torch.zeros(total_blocks, hkv, bs, dh, dtype=torch.bfloat16, device=dev)
+            k = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn(n, hkv, dh, generator=gen, device=dev).to(torch.bfloat16)
+            sets.append((pkv.Cache(kp, torch.zeros_like(kp)), k, v))
         cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=dev)
         fp = torch.tensor(np.array(first, dtype=np.int32), device=dev)
-        return cache, k, v, torch.from_numpy(bt).to(dev), cu, fp, max(counts), bt, n
+        return sets, torch.from_numpy(bt).to(dev), cu, fp, max(counts), bt, n
 
     def timed(c):
-        cache, k, v, btd, cu, fp, mx, _, n = c
-        for _ in range(args.warmup):
+        sets, btd, cu, fp, mx, _, n = c
+        for i in range(args.warmup):
+            cache, k, v = sets[i % len(sets)]
             pkv.pkv_kv_append_paged(cache, k, v, btd, cu, fp, mx)
         timer = Timer(stream, args.steps)
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            cache, k, v = sets[(args.warmup + i) % len(sets)]
             timer.start()
             pkv.pkv_kv_append_paged(cache, k, v, btd, cu, fp, mx)
             timer.stop()
@@ -1218,24 +1236,29 @@ def run_append(args, dev):
     step = setup([2048] + [int(t) for t in rng.integers(256, 2049, 64)], [512] + [1] * 64)
     bulk = setup([0] * 16, [2048] * 16)
     ms_step, ms_bulk = timed(step), timed(bulk)
+    if getattr(args, "calib_copy", False):
+        calib_copy(dev)
     avg_bulk = sum(ms_bulk) / len(ms_bulk)
     gbs = bulk[-1] * per_token / (avg_bulk * 1e-3) / 1e9
+    traffic = load_traffic("kv_append_paged", "append", APPEND_SOURCES)
     line = {
         "metric": "paged KV append (slot mapping + append, one launch), bulk 32768 tokens, GB/s",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(avg_bulk, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "append", "kv_heads": hkv, "head_dim": dh, "block_size": bs,
-                   "bulk_tokens": bulk[-1], "step_tokens": step[-1], "bytes_per_token": per_token},
+                   "bulk_tokens": bulk[-1], "step_tokens": step[-1], "bytes_per_token": per_token,
+                   "pool_copies": {"bulk": len(bulk[0]), "step": len(step[0])}},
         "bulk_us": stats_us(ms_bulk),
         "step_576_tokens_us": stats_us(ms_step),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "kv_append_paged_kernel",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": "kv_append_paged_kernel",
                      "bytes_per_launch": bulk[-1] * per_token},
     }
     if not args.no_cpu_baseline:
         import oracle
-        _, k, v, _, _, _, _, bt, _ = bulk
+        sets, _, _, _, _, bt, _ = bulk
+        _, k, v = sets[0]
         kh = k.float().cpu().numpy()
         vh = v.float().cpu().numpy()
         pool_k = np.zeros((int(bt.max()) + 1, hkv, bs, dh), dtype=np.float32)
