@@ -106,7 +106,7 @@ def parse():
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
-                   help="tokens per pool block for the B=32 and T=8192 decode workloads")
+                   help="tokens per pool block for the B=32 and T=8192 decode workloads and prefill-chunk")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sharers-decode", action="store_true",
                    help="shared-prefix-mixed: the 15 idle sharers (2048 tokens each) decode one token too")
@@ -741,8 +741,8 @@ def cpu_baseline_prefill(m, p0, flops):
 
 def run_prefill_chunk(args, dev):
     """One sequence: a causal chunk of --chunk queries over --prefix cached
-    tokens plus the chunk's own (Hq=32, Hkv=8, Dh=128, bf16 N(0,1), 16-token
-    blocks at a seeded random permutation). A step is one
+    tokens plus the chunk's own (Hq=32, Hkv=8, Dh=128, bf16 N(0,1), blocks of
+    --block-size tokens at a seeded random permutation). A step is one
     pkv_attn_prefill_chunk call; the kernel is the library's choice unless
     PKV_PREFILL_KERNEL names one."""
     import numpy as np
@@ -754,8 +754,6 @@ def run_prefill_chunk(args, dev):
     P, C = args.prefix, args.chunk
     T = P + C
     bsz = args.block_size
-    if bsz < 16:
-        raise SystemExit("prefill-chunk: the prefill takes 16-, 32- or 64-token blocks")
     nb = -(-T // bsz)
     rng = np.random.default_rng(4306)
     gen = torch.Generator(device=dev).manual_seed(4306)
@@ -799,7 +797,7 @@ def run_prefill_chunk(args, dev):
     flops = prefill_flops(P, C, hq, dh)
     env = os.environ.get("PKV_PREFILL_KERNEL")
     kernel = env if env in ("tiles", "tiles128", "tiles256", "tiles16", "columns") else (
-        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 else "tiles256" if C * hq >= 2 * 256 * 256
+        "columns" if C * hq < 128 * 64 and nb * bsz <= 8192 and bsz >= 16 else "tiles256" if C * hq >= 2 * 256 * 256
         else "tiles128" if C * hq >= 128 * 256 else "tiles")
     names = {"tiles": "prefill_stream_kernel", "tiles128": "prefill_stream_kernel (128 rows)",
              "tiles256": "prefill_stream_kernel (256 rows)",
@@ -807,7 +805,11 @@ def run_prefill_chunk(args, dev):
              "columns": "decode_mfma_kernel (prefill columns)"}
     tf = flops / (avg * 1e-3) / 1e12
     pipelined = flops / (ms * 1e-3) / 1e12
+    if kernel in ("tiles16", "columns") and bsz < 16:
+        kernel = "tiles"                   # 8-token blocks: the key-stream kernel whatever is asked
     rg = {"tiles128": 4, "tiles256": 8 if dh == 128 else 4}.get(kernel, 2)   # row groups per key stream
+    # the key-stream kernel's name: prefill_stream_kernel<Dh, row groups, 8-token blocks>
+    stream_name = f"prefill_stream_kernel<{dh}, {rg}, {'true' if bsz == 8 else 'false'}>"
     line = {
         "metric": f"prefill chunk TFLOP/s (bf16 MFMA), C={C} on P={P}",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -819,7 +821,7 @@ def run_prefill_chunk(args, dev):
         "call_us": stats_us(call),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (load_prefill_traffic(C, f"prefill_stream_kernel<{dh}, {rg}>")
+                     "traffic": (load_prefill_traffic(C, stream_name)
                                  if kernel in ("tiles", "tiles128", "tiles256") else None),
                      "flops_per_launch": flops,
                      "timing": "HIP events around each call on its stream (launch included)",
@@ -827,7 +829,7 @@ def run_prefill_chunk(args, dev):
                                    "frac": round(pipelined / PEAK_BF16_TFLOPS, 4)},
                      "trace": (load_trace("prefill_stream", trace_key("prefill-chunk", C), PREFILL_SOURCES, flops,
                                           PEAK_BF16_TFLOPS, "TFLOP/s",
-                                          name_has=f"prefill_stream_kernel<{dh}, {rg}>")
+                                          name_has=stream_name)
                                if kernel in ("tiles", "tiles128", "tiles256") else None)},
     }
     return line

@@ -69,8 +69,7 @@ typedef void* pkv_stream;   /* a hipStream_t */
 /* One layer's paged cache. Borrowed: the library keeps no pointer past a call.
  * Supported: block_size 8, 16, 32 or 64; head_dim 64 or 128; dtype F32, BF16 or
  * FP8_E4M3. Every call takes 8-, 16-, 32- and 64-token blocks except the F32
- * decode (its vector-ALU kernel, 16 only), pkv_attn_prefill_chunk and
- * pkv_attn_mixed_step (16, 32 or 64). [P2]
+ * decode (its vector-ALU kernel, 16 only). [P2]
  * Q028 leaves the block size to the implementation and, in its follow-up on
  * smaller blocks, names the trade: a larger block wastes more tail slots
  * (blocks·bs − T) but needs fewer table entries and lookups.
@@ -285,8 +284,8 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  *   scale:    score scale, positive and finite (1/sqrt(head_dim) for standard
  *             attention); anything else is PKV_EINVAL
  *   out:      device fp32, same shape as q
- * Cache dtype BF16, block_size 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2 or a
- * multiple of 4 up to 64. No workspace is needed.
+ * Cache dtype BF16, block_size 8, 16, 32 or 64; head_dim 64 or 128; Hq/Hkv 1, 2
+ * or a multiple of 4 up to 64. No workspace is needed.
  * Two kernels compute it: a tile kernel (64 query rows of one KV group per
  * workgroup in four key streams sharing 32-key tiles through LDS, or 128
  * rows in two streams, or 256 in one), and the matrix-core decode kernel
@@ -299,7 +298,9 @@ PKV_API int32_t pkv_attn_decode_auto_partition(int32_t cache_dtype, int32_t batc
  * (one per unit), and with 64 otherwise; the environment variable
  * PKV_PREFILL_KERNEL=tiles (64 rows), =tiles128, =tiles256 (128 at head_dim
  * 64) or =columns, read at every call, forces one where it applies
- * (=tiles16: the earlier tile kernel, 16 query rows per wave). */
+ * (=tiles16: the earlier tile kernel, 16 query rows per wave). Pools of
+ * 8-token blocks always take the tile kernel (64, 128 or 256 rows), whose
+ * 16-row units then span table entries 2u and 2u+1. */
 PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_t q_dtype,
                                    int32_t num_seqs, int32_t num_q_heads, const int32_t* q_start,
                                    const int32_t* block_tables, int32_t max_blocks,
@@ -319,7 +320,8 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * last workgroups write the chunks' tokens, then the prefill kernel (a third,
  * the split-KV reduce, when the decodes use more than one partition). With
  * the environment variable PKV_MIXED=one, and when the prefill takes the
- * key-stream kernel, the appends, decodes and prefill run as one launch:
+ * key-stream kernel's 64-row form on blocks of 16 tokens or more, the
+ * appends, decodes and prefill run as one launch:
  * the prefill workgroups, last in the grid, wait on a per-call counter until
  * the appending workgroups, first in the grid, have published the chunks'
  * tokens (a library-owned table of 1024 such counters per GPU, so at most
@@ -327,7 +329,7 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * bytes and both outputs are bit-identical to the separate calls'.
  *   chunks:  see pkv_chunk_batch; num_seqs may be 0
  *   decodes: see pkv_decode_batch; batch may be 0
- * BF16 cache and inputs, block_size 16, 32 or 64, the matrix-core decode whatever
+ * BF16 cache and inputs, block_size 8, 16, 32 or 64, the matrix-core decode whatever
  * PKV_DECODE_KERNEL says. A chunk's new positions must not lie in blocks the
  * decodes read (shared prefix blocks are full, so copy-on-write of a shared
  * tail keeps this). */

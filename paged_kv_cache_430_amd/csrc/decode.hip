@@ -1286,8 +1286,12 @@ hipError_t launch_mfma(const DecodeParams& p, const KernelArgs& a, hipStream_t s
   const dim3 block(kDecodeWaves * kWave);
   if (a.x_wgs > 0) {
     if constexpr (KV == kBF16) {
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, true>), dim3((unsigned)(n + a.x_wgs)),
-                         block, 0, s, a);
+      if (a.block_size == 8)
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, true, false, true>),
+                           dim3((unsigned)(n + a.x_wgs)), block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, DH, kDecodeWaves, true, true>), dim3((unsigned)(n + a.x_wgs)),
+                           block, 0, s, a);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;   // the mixed step takes bf16 caches only

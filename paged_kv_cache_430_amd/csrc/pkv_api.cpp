@@ -410,7 +410,10 @@ constexpr int64_t kPrefillTile256Rows = (int64_t)2 * 256 * kComputeUnits;
 // columns) overrides.
 enum PrefillKernel { kPrefillColumns, kPrefillTiles16, kPrefillStream, kPrefillStream128, kPrefillStream256 };
 static PrefillKernel prefill_kernel_for(const PrefillParams& p) {
-  const bool cols_ok = (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
+  // the column form and the 16-row tile kernel address 16-row units inside
+  // blocks of 16 tokens or more; 8-token blocks take the key-stream kernel
+  const bool cols_ok =
+      p.cache.block_size >= 16 && (int64_t)p.max_blocks * p.cache.block_size <= kPrefillColsMaxKeys;
   const char* env = getenv("PKV_PREFILL_KERNEL");
   bool cols = cols_ok && (int64_t)p.num_seqs * p.max_q_len * p.num_q_heads < kPrefillTileRows;
   if (env && (strcmp(env, "tiles") == 0 || strcmp(env, "tiles16") == 0 || strcmp(env, "tiles128") == 0 ||
@@ -418,7 +421,7 @@ static PrefillKernel prefill_kernel_for(const PrefillParams& p) {
     cols = false;
   if (env && strcmp(env, "columns") == 0) cols = cols_ok;
   if (cols) return kPrefillColumns;
-  if (env && strcmp(env, "tiles16") == 0) return kPrefillTiles16;
+  if (env && strcmp(env, "tiles16") == 0 && p.cache.block_size >= 16) return kPrefillTiles16;
   if (env && strcmp(env, "tiles128") == 0) return kPrefillStream128;
   if (env && strcmp(env, "tiles256") == 0) return kPrefillStream256;
   if (env && strcmp(env, "tiles") == 0) return kPrefillStream;
@@ -445,7 +448,6 @@ static int prefill_prepare(const char* fn, const CacheView& c, const void* q, in
                            hipStream_t s, PrefillParams* p) {
   p->num_seqs = 0;
   if (c.dtype != PKV_BF16 || q_dtype != PKV_BF16) return fail(PKV_EDTYPE, std::string(fn) + ": cache and q must be BF16");
-  if (c.block_size < 16) return fail(PKV_EINVAL, std::string(fn) + ": block_size must be 16, 32 or 64");
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0 || max_q_len < 0)
     return fail(PKV_EINVAL, std::string(fn) + ": bad size");
   if (num_q_heads % c.num_kv_heads != 0)
@@ -588,7 +590,8 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     // boundary, and its prefill waits on the appends).
     const char* menv = getenv("PKV_MIXED");
     const bool one = menv && strcmp(menv, "one") == 0;
-    if (one && prefill_kernel_for(pp) == kPrefillStream) return hip_status(launch_mixed_one(dp, pp, s), fn);
+    if (one && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
+      return hip_status(launch_mixed_one(dp, pp, s), fn);
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
   if (pp.num_seqs == 0) return PKV_OK;

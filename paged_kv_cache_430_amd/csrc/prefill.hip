@@ -412,18 +412,22 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
 // Key-stream form: the body is in prefill_stream.h.
 namespace {
 
-template <int DH, int RG>
+template <int DH, int RG, bool B8>
 __global__ __launch_bounds__(8 * kWave, 1) void prefill_stream_kernel(SArgs a) {
   constexpr int NS = StreamShape<RG>::NS;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[stream_lds_bytes<DH, NS, RG>()];
-  prefill_stream_body<DH, NS, RG>(a, lds, xcd_logical_index(flat_block_id(), flat_grid_size()));
+  prefill_stream_body<DH, NS, RG, B8>(a, lds, xcd_logical_index(flat_block_id(), flat_grid_size()));
 }
 
+// (B8: pools of 8-token blocks)
 template <int DH, int RG>
 hipError_t launch_stream_dh(const PrefillParams& p, hipStream_t s) {
   const SArgs a = make_sargs(p, StreamShape<RG>::ROWS);
   const size_t n = stream_workgroups(p, a);
-  hipLaunchKernelGGL((prefill_stream_kernel<DH, RG>), dim3((unsigned)n), dim3(8 * kWave), 0, s, a);
+  if (p.cache.block_size == kBlockSize / 2)
+    hipLaunchKernelGGL((prefill_stream_kernel<DH, RG, true>), dim3((unsigned)n), dim3(8 * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_stream_kernel<DH, RG, false>), dim3((unsigned)n), dim3(8 * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ struct SArgs {
   const int32_t* seq_lens;
   float* out;
   int num_blocks, hkv, hq, max_blocks, num_qtiles, num_chunks, gw;
-  int unit_shift;   // log2(block_size / 16): a pool block holds 1, 2 or 4 16-row units
+  int unit_shift;   // log2(block_size / 16): a pool block holds 1, 2 or 4 16-row units (0 for 8-token blocks)
   float scale_log2;
 };
 
@@ -183,7 +183,9 @@ constexpr int stream_lds_bytes() {
 
 // The kernel's work for logical workgroup L (see xcd_logical_index), on RG·NS
 // = 8 waves and stream_lds_bytes<DH, NS, RG>() bytes of LDS at `lds`.
-template <int DH, int NS, int RG = 2>
+// B8: pools of 8-token blocks; a 16-row unit is then the rows of table
+// entries 2u and 2u+1, and each of its loads reads from one of the two.
+template <int DH, int NS, int RG = 2, bool B8 = false>
 __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds, uint32_t L) {
   static_assert(NS == StreamShape<RG>::NS, "eight waves: NS streams of RG row groups");
   constexpr int NW = RG * NS;                 // waves: (stream, row group)
@@ -202,6 +204,9 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   static_assert(LPW >= 1, "every wave loads part of a unit");
   static_assert(stream_lds_bytes<DH, NS, RG>() <= 160 * 1024, "LDS of a CU");
   static_assert((4 * NDT) % NS == 0, "output groups per stream");
+  static_assert(!B8 || RPL <= kBlockSize / 2, "with 8-token blocks a load lies in one block");
+  constexpr int VB = B8 ? 4 : 2;              // validity bits per tile: 8- or 16-key pieces
+  constexpr int VFULL = (1 << VB) - 1;
   // lds: [stream][K slot] tiles, then [stream][V slot]; the merge reuses it
 
   // workgroup → (sequence, KV head, head chunk, query tile); query tiles run
@@ -221,16 +226,21 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // the entries' latency overlaps the lengths'. Units past the keys the
   // workgroup sees are dropped when the table is built.
   const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
-  auto batch_ids = [&](int b) -> int {
-    const int jj = b * kSBatch + (lane >> 1);
-    const int u = 2 * (stream + NS * jj) + (lane & 1);
-    const int e = (u >> a.unit_shift) < a.max_blocks ? bt[u >> a.unit_shift] : -1;
+  // table entry of unit u (B8: its first half; h = 1: its second half)
+  auto unit_id = [&](int u, int h) -> int {
+    const int x = B8 ? 2 * u + h : u >> a.unit_shift;
+    const int e = x < a.max_blocks ? bt[x] : -1;
     return (unsigned)e < (unsigned)a.num_blocks ? e : -1;
   };
+  auto batch_unit = [&](int b) { return 2 * (stream + NS * (b * kSBatch + (lane >> 1))) + (lane & 1); };
+  auto batch_ids = [&](int b) -> int { return unit_id(batch_unit(b), 0); };
+  auto batch_ids2 = [&](int b) -> int { return B8 ? unit_id(batch_unit(b), 1) : -1; };
   const int ids0 = batch_ids(0);
+  const int ids0b = batch_ids2(0);
   const int q_lo = __builtin_amdgcn_readfirstlane(a.q_start[s]);
   const int C = __builtin_amdgcn_readfirstlane(a.q_start[s + 1]) - q_lo;
-  const int T = __builtin_amdgcn_readfirstlane(min(a.seq_lens[s], (a.max_blocks << a.unit_shift) * kBlockSize));
+  const int T = __builtin_amdgcn_readfirstlane(
+      min(a.seq_lens[s], B8 ? a.max_blocks * (kBlockSize / 2) : (a.max_blocks << a.unit_shift) * kBlockSize));
   const int QW = StreamShape<RG>::ROWS / a.gw;  // queries of the workgroup
   if (qtile * QW >= C || T <= 0) return;       // uniform over the workgroup
   const int base_pos = T - C;                  // position of query 0
@@ -269,7 +279,8 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   const int voff0 = (lane / CPR) * RB + (((lane % CPR) ^ swz_v<DH>(lane / CPR)) << 4);
   static_assert(DH == 64 || DH == 128, "the swizzle steps above");
   const int unit_mask = (1 << a.unit_shift) - 1;
-  const size_t head_stride = ((size_t)kBlockSize * RB) << a.unit_shift;   // bytes of one (pool block, head)
+  // bytes of one (pool block, head)
+  const size_t head_stride = B8 ? (size_t)(kBlockSize / 2) * RB : ((size_t)kBlockSize * RB) << a.unit_shift;
   const char* kbase = reinterpret_cast<const char*>(a.kc);
   const char* vbase = reinterpret_cast<const char*>(a.vc);
 
@@ -280,36 +291,65 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // visible key in the other word). An id outside the pool, or a unit past
   // that key, has 0 bytes: its loads fill zeros. Requests read entries back
   // with lane reads, so no iteration waits on a memory load or spends scalar
-  // work on addresses.
+  // work on addresses. With 8-token blocks a second table holds each unit's
+  // second block, its address taken 8 rows back so that the loads' offsets
+  // (rows 8-15 of the unit) and the byte count mean the same in both.
   uint32_t tl, th;        // entries of the batch holding the next K request
-  uint64_t vmask;         // bit 2i+h: unit h of the batch's tile i holds keys
-  auto make_table = [&](int b, int e) {
-    const int jj = b * kSBatch + (lane >> 1);
-    const int u = 2 * (stream + NS * jj) + (lane & 1);
-    const int rows = e < 0 ? 0 : max(0, min(kBlockSize, kend - u * kBlockSize));
+  uint32_t tl2 = 0, th2 = 0;
+  uint64_t vmask;         // bit 2i+h: unit h of the batch's tile i holds keys (B8: its first 8 rows)
+  uint64_t vmask2 = 0;    // B8: bit 2i+h: the second 8 rows of unit h of tile i hold keys
+  auto make_table = [&](int b, int e, int e2) {
+    const int u = batch_unit(b);
+    const int in_range = max(0, min(kBlockSize, kend - u * kBlockSize));   // the unit's rows before kend
+    const int rows = e < 0 ? 0 : in_range;
     const uint64_t addr = (uint64_t)(kbase + ((size_t)(e < 0 ? 0 : e) * a.hkv + g) * head_stride +
-                                     (size_t)((u & unit_mask) * kBlockSize) * RB);
+                                     (size_t)((B8 ? 0 : u & unit_mask) * kBlockSize) * RB);
     tl = (uint32_t)addr;
     th = ((uint32_t)(addr >> 32) & 0xffffu) | ((uint32_t)(rows * RB) << 16);
     vmask = __builtin_amdgcn_ballot_w64(rows > 0);
+    if constexpr (B8) {
+      const int rows2 = e2 < 0 ? 0 : in_range;
+      const uint64_t addr2 = e2 < 0 ? (uint64_t)kbase
+                                    : (uint64_t)(kbase + ((size_t)e2 * a.hkv + g) * head_stride) -
+                                          (uint64_t)((kBlockSize / 2) * RB);
+      tl2 = (uint32_t)addr2;
+      th2 = ((uint32_t)(addr2 >> 32) & 0xffffu) | ((uint32_t)(rows2 * RB) << 16);
+      vmask2 = __builtin_amdgcn_ballot_w64(rows2 > kBlockSize / 2);
+    }
   };
-  make_table(0, ids0);
+  make_table(0, ids0, ids0b);
   int ids_nxt = NT > kSBatch ? batch_ids(1) : -1;     // ids of the batch after it
+  int ids_nxt2 = NT > kSBatch ? batch_ids2(1) : -1;
   const uint64_t dv = (uint64_t)(vbase - kbase);      // V's unit lies this far from K's
-  // valid-unit bits of tile t (in the current batch)
-  auto vbits = [&](int t) -> int { return (int)(uint32_t)(vmask >> (2 * (t & (kSBatch - 1)))) & 3; };
+  // validity bits of tile t (in the current batch), one per 16-key unit, or
+  // with 8-token blocks one per 8 keys
+  auto vbits = [&](int t) -> int {
+    const int sh = 2 * (t & (kSBatch - 1));
+    const int v0 = (int)(uint32_t)(vmask >> sh) & 3;
+    if constexpr (!B8) {
+      return v0;
+    } else {
+      const int v1 = (int)(uint32_t)(vmask2 >> sh) & 3;
+      return (v0 & 1) | ((v1 & 1) << 1) | ((v0 & 2) << 1) | ((v1 & 2) << 2);
+    }
+  };
   struct Ent {
-    uint32_t lo, hi;
+    uint32_t lo, hi, lo2, hi2;
   };
   // the wave's entry of tile t; after a batch's last tile the next batch
   // becomes current
   auto take_entry = [&](int t) -> Ent {
     const int ln = 2 * (t & (kSBatch - 1)) + unit;
-    const Ent e{(uint32_t)__builtin_amdgcn_readlane((int)tl, ln), (uint32_t)__builtin_amdgcn_readlane((int)th, ln)};
+    Ent e{(uint32_t)__builtin_amdgcn_readlane((int)tl, ln), (uint32_t)__builtin_amdgcn_readlane((int)th, ln), 0u, 0u};
+    if constexpr (B8) {
+      e.lo2 = (uint32_t)__builtin_amdgcn_readlane((int)tl2, ln);
+      e.hi2 = (uint32_t)__builtin_amdgcn_readlane((int)th2, ln);
+    }
     if (((t + 1) & (kSBatch - 1)) == 0 && t + 1 < NT) {
       const int b = (t + 1) / kSBatch;
-      make_table(b, ids_nxt);
+      make_table(b, ids_nxt, ids_nxt2);
       ids_nxt = NT > (b + 1) * kSBatch ? batch_ids(b + 1) : -1;
+      ids_nxt2 = NT > (b + 1) * kSBatch ? batch_ids2(b + 1) : -1;
     }
     return e;
   };
@@ -318,21 +358,32 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   struct Req {
     int lo, hi, bytes;    // buffer resource words 0-2
     uint32_t d;
+    int lo2, hi2, bytes2; // B8: the resource of the unit's second block
   };
   auto make_req = [&](Ent e, bool is_v, int t) -> Req {
     uint64_t addr = ((uint64_t)(e.hi & 0xffffu) << 32) | e.lo;
     if (is_v) addr += dv;
     const uint8_t* slot = is_v ? vst + (t % RV) * TB : kst + (t % RK) * TB;
-    return Req{(int)(uint32_t)addr, (int)(uint32_t)(addr >> 32), (int)(e.hi >> 16),
-               lds_addr(slot + unit * (kBlockSize * RB))};
+    Req q{(int)(uint32_t)addr, (int)(uint32_t)(addr >> 32), (int)(e.hi >> 16),
+          lds_addr(slot + unit * (kBlockSize * RB)), 0, 0, 0};
+    if constexpr (B8) {
+      uint64_t addr2 = ((uint64_t)(e.hi2 & 0xffffu) << 32) | e.lo2;
+      if (is_v) addr2 += dv;
+      q.lo2 = (int)(uint32_t)addr2;
+      q.hi2 = (int)(uint32_t)(addr2 >> 32);
+      q.bytes2 = (int)(e.hi2 >> 16);
+    }
+    return q;
   };
   // (the resource is assembled from scalar words here: a vector of them
   // carried across iterations may be given vector registers)
   auto issue_one = [&](bool is_v, const Req& q, int i) {
+    // B8: loads of rows 8-15 of the unit read its second block
+    const bool second = B8 && (sub * LPW + i) * RPL >= kBlockSize / 2;
     i32x4_t r;
-    r[0] = __builtin_amdgcn_readfirstlane(q.lo);
-    r[1] = __builtin_amdgcn_readfirstlane(q.hi);
-    r[2] = __builtin_amdgcn_readfirstlane(q.bytes);
+    r[0] = __builtin_amdgcn_readfirstlane(second ? q.lo2 : q.lo);
+    r[1] = __builtin_amdgcn_readfirstlane(second ? q.hi2 : q.hi);
+    r[2] = __builtin_amdgcn_readfirstlane(second ? q.bytes2 : q.bytes);
     r[3] = kBufferRsrcWord3;
     const uint32_t d = __builtin_amdgcn_readfirstlane(q.d);
     switch (sub * LPW + i) {
@@ -422,11 +473,13 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // first query, or holding such a unit, need it
   auto mask_scores = [&](int j, f32x16_t& st, int valid_units) {
     const int key0 = (stream + NS * j) * kSTile;
-    if (key0 + kSTile - 1 > first_pos || valid_units != 3) {
+    if (key0 + kSTile - 1 > first_pos || valid_units != VFULL) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        // (register r holds key 8(r/4) + 4hg + r%4 of the tile: 16-key unit
+        // r/8, 8-key piece r/4)
         const int key = key0 + 8 * (r >> 2) + 4 * hg + (r & 3);
-        if (key > row_pos || !((valid_units >> (r >> 3)) & 1)) st[r] = -INFINITY;
+        if (key > row_pos || !((valid_units >> (B8 ? r >> 2 : r >> 3)) & 1)) st[r] = -INFINITY;
       }
     }
   };
@@ -479,8 +532,8 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // and iteration j+1 issues pair j+RK−2 (K of tile j+RK, V of tile j+RK−2)
   // into those slots, its loads spread between its products so the vector
   // memory path moves them while the matrix cores work. Requests past NT fill
-  // zeros. vq: valid-unit bits of the tiles whose K is requested (bits 2i,
-  // 2i+1: tile j+i); ea, eb: entries of the next two V requests, which trail
+  // zeros. vq: validity bits of the tiles whose K is requested (bits VB·i …
+  // VB·i + VB − 1: tile j+i); ea, eb: entries of the next two V requests, which trail
   // K by two tiles.
   // The prologue requests K of tiles 0 and 1 and pairs 0 … RK−4, and
   // prepares pair RK−3 for iteration 0 to issue (as iteration j−1 prepares
@@ -491,7 +544,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     Ent e[RK - 1];
 #pragma unroll
     for (int t = 0; t < RK - 1; ++t) {
-      vq |= vbits(t) << (2 * (t + 1));          // as at iteration −1: bits 2i, 2i+1 for tile i−1
+      vq |= vbits(t) << (VB * (t + 1));         // as at iteration −1: bits VB·i … for tile i−1
       e[t] = take_entry(t);
       issue_req(false, make_req(e[t], false, t));
       if (t >= 2) issue_req(true, make_req(e[t - 2], true, t - 2));   // pairs 0 … RK−4
@@ -515,7 +568,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     // (a row that sees none of them keeps −inf; its first visible tile takes
     // the full update through the steady iteration's redo)
     f32x16_t st = s_cur;
-    mask_scores(0, st, vq >> 2 & 3);
+    mask_scores(0, st, vq >> VB & VFULL);
     m_run = row_max(st);
   }
   wait_loads_but<(RK - 3) * PAIR>();          // K of tile 1
@@ -532,7 +585,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     const int nb = vbits(t);
     const Ent e = take_entry(t);
     pend_k = make_req(e, false, t);
-    vq = (vq >> 2) | (nb << (2 * (RK - 1)));
+    vq = (vq >> VB) | (nb << (VB * (RK - 1)));
     ea = eb;
     eb = e;
   };
@@ -551,7 +604,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
     const uint8_t* vb = vst + ((j + RV - 1) % RV) * TB;     // V of tile j−1
     const uint8_t* kb = kst + ((j + 1) % RK) * TB;          // K of tile j+1
     f32x16_t st = s_cur;
-    const int vu = vq & 3;
+    const int vu = vq & VFULL;
     mask_scores(j, st, vu);
     // A row without a base (−inf: it has seen no key yet) exponentiates
     // against 2^100 below zero: a visible key overflows to +inf, which sends
@@ -741,7 +794,7 @@ inline SArgs make_sargs(const PrefillParams& p, int rows = kSRows) {
   a.gw = gw;
   a.num_chunks = group / gw;
   a.num_qtiles = (p.max_q_len + (rows / gw) - 1) / (rows / gw);
-  a.unit_shift = __builtin_ctz((unsigned)p.cache.block_size / kBlockSize);
+  a.unit_shift = p.cache.block_size > kBlockSize ? __builtin_ctz((unsigned)p.cache.block_size / kBlockSize) : 0;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   return a;
 }

@@ -165,7 +165,7 @@ def test_auto_partition_rule(lib, monkeypatch):
 
 
 def test_block_size_rules(lib, monkeypatch):
-    """8-, 16-, 32- and 64-token blocks; the F32 (vector) decode takes 16 only, the prefill 16, 32 or 64."""
+    """8-, 16-, 32- and 64-token blocks; the F32 (vector) decode takes 16 only."""
     def decode(ref, b=1, msl=64, dtype=pkv.PKV_BF16):
         return lib.pkv_attn_decode(ref, 0x50000, dtype, b, 8, 0x60000, 4, 0x70000, msl, 0.1, 0, 0x80000,
                                    None, 0, None)
@@ -180,13 +180,10 @@ def test_block_size_rules(lib, monkeypatch):
         monkeypatch.setenv("PKV_DECODE_KERNEL", "vector")
         assert decode(ref) == pkv.PKV_EINVAL
         monkeypatch.delenv("PKV_DECODE_KERNEL")
-        if bs == 8:   # the prefill and the mixed step take 16, 32 or 64
-            assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 1, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                              None) == pkv.PKV_EINVAL
-            assert "block_size" in lib.pkv_last_error().decode()
-        else:         # accepted: nothing to launch with no sequences
-            assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 0, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
-                                              None) == pkv.PKV_OK
+        # the prefill takes every block size (8: the key-stream kernel);
+        # accepted: nothing to launch with no sequences
+        assert lib.pkv_attn_prefill_chunk(ref, 0x50000, pkv.PKV_BF16, 0, 32, 0x1, 0x2, 4, 0x3, 16, 0.1, 0x80000,
+                                          None) == pkv.PKV_OK
 
 
 def test_mixed_step_validation(lib):
@@ -197,8 +194,8 @@ def test_mixed_step_validation(lib):
     assert call(ref, ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK        # nothing to do, nothing launched
     assert call(ref, None, ctypes.byref(de)) == pkv.PKV_EINVAL
     assert call(_fake_cache(dtype=pkv.PKV_FP8_E4M3)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EDTYPE
-    assert call(_fake_cache(bs=8)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_EINVAL    # prefill: 16, 32, 64
-    assert call(_fake_cache(bs=32)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK       # nothing to launch
+    for bs in (8, 32):
+        assert call(_fake_cache(bs=bs)[0], ctypes.byref(ch), ctypes.byref(de)) == pkv.PKV_OK  # nothing to launch
     assert call(ref, ctypes.byref(ch), ctypes.byref(de), hq=24) == pkv.PKV_EINVAL             # group 3
     # a chunk without its new K/V is refused before any launch
     ch2 = pkv._ChunkBatch(1, 0x50000, 0x1, None, None, 0x2, 4, 0x3, 16, 0x80000)

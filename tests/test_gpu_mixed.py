@@ -138,12 +138,15 @@ def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, laun
     _oracle_check(c, mp, md)
 
 
-@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("bs", [8, 32, 64])
 @pytest.mark.parametrize("prefill_kernel", ["tiles", "columns"])
 @pytest.mark.parametrize("launches", LAUNCHES)
-def test_mixed_step_at_block_sizes_32_and_64(bs, prefill_kernel, launches, monkeypatch):
-    """The mixed step on pools of 32- and 64-token blocks: chunk and decode
-    tokens land inside larger blocks; bit-identical to the separate calls."""
+def test_mixed_step_at_block_sizes_8_32_and_64(bs, prefill_kernel, launches, monkeypatch):
+    """The mixed step on pools of 8-, 32- and 64-token blocks: chunk and
+    decode tokens land inside larger blocks, or a 16-row unit spans two
+    blocks; bit-identical to the separate calls. (With 8-token blocks the
+    prefill takes the key-stream kernel whatever PKV_PREFILL_KERNEL says, and
+    the step takes two launches.)"""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", prefill_kernel)
     monkeypatch.setenv("PKV_MIXED", launches)
     dev = device()

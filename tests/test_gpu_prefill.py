@@ -103,6 +103,21 @@ def test_tile_kernel_many_query_tiles(seqs, kernel, monkeypatch):
     assert err <= 2e-3, f"max-abs {err:.3e}"
 
 
+@pytest.mark.parametrize("kernel", ["tiles", "tiles128", "tiles256"])
+@pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (16, 8, 64)])
+def test_eight_token_blocks_every_stream_form(kernel, hq, hkv, dh, monkeypatch):
+    """Pools of 8-token blocks under the key-stream kernel's 64-, 128- and
+    256-row forms (256: head dim 128; at 64 the call runs 128): chunks long
+    enough for several table batches (32 tiles each per stream), ragged
+    prefixes and chunk ends inside blocks."""
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", kernel)
+    dev = device()
+    seqs = [(100, 64), (0, 1), (3000, 700), (5, 1500), (13, 29)]
+    err, rel = _prefill_case(dev, seqs, hq, hkv, dh, seed=808 + dh, bs=8)
+    assert err <= 2e-3, f"max-abs {err:.3e}"
+    assert rel < 5e-2
+
+
 def test_long_table_and_small_chunk(prefill_kernel):
     """A small chunk on a table longer than the column form takes (8192
     tokens): the library runs the tile kernel whatever PKV_PREFILL_KERNEL says."""
@@ -117,12 +132,14 @@ def test_512_chunk_on_2048_tokens_full_size(prefill_kernel):
                   norm_tol=1e-4)
 
 
-@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("bs", [8, 32, 64])
 @pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (16, 8, 64), (4, 1, 64)])
-def test_ragged_chunks_at_block_sizes_32_and_64(bs, hq, hkv, dh, prefill_kernel):
-    """Both prefill kernels on pools of 32- and 64-token blocks: a 16-row unit
-    is part of a pool block (rows (u mod bs/16)·16 of entry u / (bs/16)); chunks
-    and prefixes that start and end inside blocks."""
+def test_ragged_chunks_at_block_sizes_8_32_and_64(bs, hq, hkv, dh, prefill_kernel):
+    """The prefill kernels on pools of 8-, 32- and 64-token blocks: a 16-row
+    unit is part of a pool block (rows (u mod bs/16)·16 of entry u / (bs/16)),
+    or with 8-token blocks the rows of entries 2u and 2u+1 (only the
+    key-stream kernel takes those: the other settings of PKV_PREFILL_KERNEL
+    fall back to it); chunks and prefixes that start and end inside blocks."""
     dev = device()
     seqs = [(0, 1), (0, 17), (5, 16), (100, 64), (33, 100), (2048, 3), (0, 130), (40, 9)]
     err, rel = _prefill_case(dev, seqs, hq, hkv, dh, seed=70 + bs + dh, bs=bs)
@@ -233,17 +250,19 @@ def test_copy_on_write_of_shared_partial_tail():
     del kb_new
 
 
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32])
 def test_blocks_missing_from_the_table_contribute_nothing(bs, prefill_kernel):
     """A table entry of −1, or an id outside the pool, inside a sequence: the
     tokens of that block are not attended to (the library's reading of an id
     that names no pool block), by either prefill kernel. The oracle attends
-    over the remaining keys only, in their logical order."""
+    over the remaining keys only, in their logical order. With 8-token blocks
+    the missing entries are the second half of a 16-row unit (block 1, 5) and
+    the first half of one (block 2)."""
     dev = device()
     gen = torch.Generator(device=dev).manual_seed(21 + bs)
     hq, hkv, dh = 32, 8, 128
     seqs = [(100, 40), (300, 64), (0, 90)]
-    nb_pool = 64
+    nb_pool = 64 if bs >= 16 else 96
     kp, vp = new_pools(nb_pool, hkv, dh, "bf16", dev, block_size=bs)
     cache = pkv.Cache(kp, vp)
     max_blocks = max(-(-(p + c) // bs) for p, c in seqs)
