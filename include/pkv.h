@@ -326,7 +326,13 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * the appending workgroups, first in the grid, have published the chunks'
  * tokens (a library-owned table of 1024 such counters per GPU, so at most
  * 1024 of these calls may be in flight on one GPU). Either way the pool
- * bytes and both outputs are bit-identical to the separate calls'.
+ * bytes and both outputs are bit-identical to the separate calls'. With
+ * PKV_MIXED=pair (same conditions, and decode partitions of at most 4096
+ * tokens) the one launch uses four-wave workgroups, two per compute unit,
+ * so that each unit runs a prefill tile beside a decode workgroup: the pool
+ * bytes are bit-identical, the outputs equal the separate calls' up to the
+ * summation order (two key streams instead of four; four decode waves
+ * instead of eight).
  *   chunks:  see pkv_chunk_batch; num_seqs may be 0
  *   decodes: see pkv_decode_batch; batch may be 0
  * BF16 cache and inputs, block_size 8, 16, 32 or 64, the matrix-core decode whatever

@@ -714,17 +714,17 @@ __device__ __forceinline__ void new_token_bytes(const uint8_t* base, size_t elem
   }
 }
 
-// A mixed step's further appends: extra workgroup idx takes kExtraTokens
-// tokens of one sequence, NTH / kExtraTokens threads per token, each token
-// stored exactly as the append kernels store it.
+// A mixed step's further appends: extra workgroup idx takes TOK tokens of
+// one sequence (a.x_wgs_per_seq workgroups per sequence), NTH / TOK threads
+// per token, each token stored exactly as the append kernels store it.
 constexpr int kExtraTokens = 16;
-template <int KV, int DH, int NTH>
+template <int KV, int DH, int NTH, int TOK = kExtraTokens>
 __device__ __forceinline__ void extra_append(const KernelArgs& a, int idx) {
-  constexpr int per = NTH / kExtraTokens;
+  constexpr int per = NTH / TOK;
   const int s = idx / a.x_wgs_per_seq, j = idx % a.x_wgs_per_seq;
   if (s >= a.x_seqs) return;
   const int lo = a.x_cu[s], C = a.x_cu[s + 1] - lo;
-  const int i = j * kExtraTokens + (int)threadIdx.x / per;
+  const int i = j * TOK + (int)threadIdx.x / per;
   if (i >= C) return;
   const int slot = slot_of(a.x_tables + (size_t)s * a.x_max_blocks, a.x_max_blocks, a.x_lens[s] - C + i,
                            a.block_size);
@@ -1221,7 +1221,39 @@ __device__ unsigned mixed_sync[kMixedSlots][2];   // [slot]: appends done, prefi
 
 struct MixedLayout {
   uint32_t n_app, n_dec, n_dec_pad, n_pf, slot;
+  uint32_t n_app_pad, n_pf_pad;   // the paired form: appends and prefill rounded up to the XCD rotation
 };
+
+// An append workgroup's stores are done: every wave's stores reach the XCD's
+// L2; then one release at agent scope writes the L2 back (a fence per wave
+// would write it back once per wave) and counts the workgroup.
+__device__ __forceinline__ void mixed_append_done(unsigned* sync) {
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A prefill workgroup waits for the n_app append workgroups (bounded).
+__device__ __forceinline__ void mixed_wait_appends(unsigned* sync, uint32_t n_app) {
+  if (threadIdx.x == 0) {
+    for (int spins = 0; spins < kMixedMaxSpins; ++spins) {
+      if (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_app) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // one invalidate, not one per poll
+  }
+  __syncthreads();
+}
+
+// A prefill workgroup is done; the last of n_pf returns the slot to zero.
+__device__ __forceinline__ void mixed_prefill_done(unsigned* sync, uint32_t n_app, uint32_t n_pf) {
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n_pf - 1) {
+    __hip_atomic_fetch_sub(&sync[0], n_app, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_sub(&sync[1], n_pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 template <int DH>
 constexpr int mixed_lds_bytes() {
@@ -1237,11 +1269,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void mixed_step_kernel(Ker
   const uint32_t flat = flat_block_id();
   if (flat < m.n_app) {
     extra_append<kBF16, DH, kDecodeWaves * kWave>(a, (int)flat);
-    // every wave's stores reach the XCD's L2; then one release at agent
-    // scope writes the L2 back (a fence per wave would write it back 8 times)
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    mixed_append_done(sync);
     return;
   }
   if (flat < m.n_app + m.n_dec_pad) {
@@ -1249,21 +1277,53 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void mixed_step_kernel(Ker
     if (id < m.n_dec) decode_mfma_body<kBF16, DH, kDecodeWaves, true, false>(a, lds, id, m.n_dec);
     return;
   }
-  if (threadIdx.x == 0) {
-    for (int spins = 0; spins < kMixedMaxSpins; ++spins) {
-      if (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= m.n_app) break;
-      __builtin_amdgcn_s_sleep(8);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // one invalidate, not one per poll
-  }
-  __syncthreads();
+  mixed_wait_appends(sync, m.n_app);
   prefill_stream_body<DH, kStreams>(pa, lds, xcd_logical_index(flat - m.n_app - m.n_dec_pad, m.n_pf));
-  __syncthreads();
-  if (threadIdx.x == 0 &&
-      __hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == m.n_pf - 1) {
-    __hip_atomic_fetch_sub(&sync[0], m.n_app, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_sub(&sync[1], m.n_pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  mixed_prefill_done(sync, m.n_app, m.n_pf);
+}
+
+// The paired form: four-wave workgroups small enough (registers, at most
+// 80 KiB of LDS) for two to share a CU, ordered appends, then the prefill
+// query tiles (two key streams of two row groups, rings of three K and two
+// V slots), then the decodes. The first round of dispatch gives each CU a
+// prefill tile, the second a decode unit beside it, so the matrix-core
+// prefill and the memory-bound decode overlap on every CU. The decodes'
+// workgroups take at most 64·16·4 tokens each (their table covers 64 units
+// per wave).
+constexpr int kPairWaves = 4;
+constexpr int kPairPrefillKmax = 3;
+constexpr int kPairExtraTokens = 16;
+constexpr int kPairMaxPartition = 64 * kBlockSize * kPairWaves;
+
+template <int DH>
+constexpr int mixed_pair_lds_bytes() {
+  constexpr int d = mfma_lds_bytes<kBF16, DH, kPairWaves>(), p = stream_lds_bytes<DH, 2, 2, kPairPrefillKmax>();
+  return d > p ? d : p;
+}
+
+template <int DH>
+__global__ __launch_bounds__(kPairWaves * kWave, 2) void mixed_pair_kernel(KernelArgs a, SArgs pa, MixedLayout m) {
+  static_assert(2 * mixed_pair_lds_bytes<DH>() <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[mixed_pair_lds_bytes<DH>()];
+  unsigned* sync = mixed_sync[m.slot];
+  const uint32_t flat = flat_block_id();
+  if (flat < m.n_app_pad) {
+    if (flat < m.n_app) {
+      extra_append<kBF16, DH, kPairWaves * kWave, kPairExtraTokens>(a, (int)flat);
+      mixed_append_done(sync);
+    }
+    return;
   }
+  if (flat >= m.n_app_pad + m.n_pf_pad) {
+    const uint32_t id = flat - m.n_app_pad - m.n_pf_pad;
+    if (id < m.n_dec) decode_mfma_body<kBF16, DH, kPairWaves, true, false>(a, lds, id, m.n_dec);
+    return;
+  }
+  const uint32_t pid = flat - m.n_app_pad;
+  if (pid >= m.n_pf) return;
+  mixed_wait_appends(sync, m.n_app);
+  prefill_stream_body<DH, 2, 2, false, kPairPrefillKmax>(pa, lds, xcd_logical_index(pid, m.n_pf));
+  mixed_prefill_done(sync, m.n_app, m.n_pf);
 }
 
 // Lanes per K row: 4 keeps the score reduction to two DPP steps and one
@@ -1390,8 +1450,12 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
 std::atomic<uint32_t> g_mixed_slot{0};
 
 template <int DH>
-hipError_t launch_mixed_dh(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s) {
-  const KernelArgs a = make_kernel_args(dp);
+hipError_t launch_mixed_dh(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s) {
+  KernelArgs a = make_kernel_args(dp);
+  if (pair) {   // kPairExtraTokens tokens per append workgroup
+    a.x_wgs_per_seq = (dp.x_max_q + kPairExtraTokens - 1) / kPairExtraTokens;
+    a.x_wgs = dp.x_seqs > 0 && a.x_wgs_per_seq > 0 ? (dp.x_seqs * a.x_wgs_per_seq + 7) / 8 * 8 : 0;
+  }
   const SArgs pa = make_sargs(pp);
   MixedLayout m;
   m.n_app = (uint32_t)a.x_wgs;
@@ -1399,19 +1463,29 @@ hipError_t launch_mixed_dh(const DecodeParams& dp, const PrefillParams& pp, hipS
   m.n_dec_pad = (m.n_dec + 7) / 8 * 8;      // keeps the prefill's ids aligned to the XCD rotation
   m.n_pf = (uint32_t)stream_workgroups(pp, pa);
   m.slot = g_mixed_slot.fetch_add(1, std::memory_order_relaxed) % kMixedSlots;
-  const size_t n = (size_t)m.n_app + m.n_dec_pad + m.n_pf;
-  hipLaunchKernelGGL(mixed_step_kernel<DH>, dim3((unsigned)n), dim3(kDecodeWaves * kWave), 0, s, a, pa, m);
-  hipError_t e = hipGetLastError();
+  m.n_app_pad = (m.n_app + 7) / 8 * 8;
+  m.n_pf_pad = (m.n_pf + 7) / 8 * 8;
+  hipError_t e;
+  if (pair) {
+    const size_t n = (size_t)m.n_app_pad + m.n_pf_pad + m.n_dec;
+    if (n > (size_t)INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mixed_pair_kernel<DH>, dim3((unsigned)n), dim3(kPairWaves * kWave), 0, s, a, pa, m);
+  } else {
+    const size_t n = (size_t)m.n_app + m.n_dec_pad + m.n_pf;
+    hipLaunchKernelGGL(mixed_step_kernel<DH>, dim3((unsigned)n), dim3(kDecodeWaves * kWave), 0, s, a, pa, m);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || dp.batch == 0 || dp.num_parts <= 1) return e;
   return launch_merge(dp, s);
 }
 
 }  // namespace
 
-hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s) {
+hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s) {
   if (dp.kernel != kDecodeMatrix || dp.cache.dtype != kBF16 || pp.num_seqs == 0 || pp.max_q_len == 0)
     return hipErrorInvalidValue;
-  return dp.cache.head_dim == 64 ? launch_mixed_dh<64>(dp, pp, s) : launch_mixed_dh<128>(dp, pp, s);
+  if (pair && dp.batch > 0 && dp.part_tokens > kPairMaxPartition) return hipErrorInvalidValue;
+  return dp.cache.head_dim == 64 ? launch_mixed_dh<64>(dp, pp, pair, s) : launch_mixed_dh<128>(dp, pp, pair, s);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {

@@ -126,8 +126,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // The mixed step in one launch: the chunks' appends, the decodes (each
 // appending its token) and the chunks' prefill (key-stream form) in one grid;
 // bf16 cache, matrix-core decode; the split-KV reduce follows when the decodes
-// are split (see decode.hip).
-hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s);
+// are split (see decode.hip). pair: four-wave workgroups, two per CU, the
+// prefill tiles dispatched before the decodes so that each CU runs one of
+// each (decode partitions of at most 4096 tokens).
+hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s);
 // The key-stream tile kernel: rows = 64 query rows per workgroup in four key
 // streams of two 32-row waves, or 128 rows in two streams of four (see
 // prefill_stream.h).

@@ -590,8 +590,9 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     // boundary, and its prefill waits on the appends).
     const char* menv = getenv("PKV_MIXED");
     const bool one = menv && strcmp(menv, "one") == 0;
-    if (one && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
-      return hip_status(launch_mixed_one(dp, pp, s), fn);
+    const bool pair = menv && strcmp(menv, "pair") == 0 && dp.part_tokens <= 64 * 16 * 4;
+    if ((one || pair) && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
+      return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
   if (pp.num_seqs == 0) return PKV_OK;

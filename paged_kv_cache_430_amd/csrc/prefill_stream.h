@@ -172,27 +172,28 @@ struct StreamShape {
 };
 
 // LDS bytes the body uses (its argument `lds`, 1 KiB aligned)
-template <int DH, int NS, int RG = 2>
+template <int DH, int NS, int RG = 2, int KMAX = StreamShape<RG>::KMAX>
 constexpr int stream_lds_bytes() {
   constexpr int TB = kSTile * DH * 2;
-  using Rg = StreamRings<DH, NS, StreamShape<RG>::KMAX>;
+  using Rg = StreamRings<DH, NS, KMAX>;
   constexpr int KV = NS * (Rg::RK + Rg::RV) * TB;
   constexpr int MERGE = NS == 1 ? 0 : RG * NS * ((DH / 32) * 16 + 2) * kWave * 4;
   return KV > MERGE ? KV : MERGE;
 }
 
 // The kernel's work for logical workgroup L (see xcd_logical_index), on RG·NS
-// = 8 waves and stream_lds_bytes<DH, NS, RG>() bytes of LDS at `lds`.
-// B8: pools of 8-token blocks; a 16-row unit is then the rows of table
-// entries 2u and 2u+1, and each of its loads reads from one of the two.
-template <int DH, int NS, int RG = 2, bool B8 = false>
+// waves (8; or 4, two streams of two row groups, for a workgroup that shares
+// its CU with another) and stream_lds_bytes<DH, NS, RG, KMAX>() bytes of LDS
+// at `lds`. B8: pools of 8-token blocks; a 16-row unit is then the rows of
+// table entries 2u and 2u+1, and each of its loads reads from one of the two.
+template <int DH, int NS, int RG = 2, bool B8 = false, int KMAX = StreamShape<RG>::KMAX>
 __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds, uint32_t L) {
-  static_assert(NS == StreamShape<RG>::NS, "eight waves: NS streams of RG row groups");
+  static_assert(NS == StreamShape<RG>::NS || (NS == 2 && RG == 2), "NS streams of RG row groups: 8 or 4 waves");
   constexpr int NW = RG * NS;                 // waves: (stream, row group)
   constexpr int RB = DH * 2;                  // bytes of one key row of one head
   constexpr int TB = kSTile * RB;             // bytes of one K or V tile
-  constexpr int RK = StreamRings<DH, NS, StreamShape<RG>::KMAX>::RK;
-  constexpr int RV = StreamRings<DH, NS, StreamShape<RG>::KMAX>::RV;
+  constexpr int RK = StreamRings<DH, NS, KMAX>::RK;
+  constexpr int RV = StreamRings<DH, NS, KMAX>::RV;
   constexpr int NDC = DH / 16;                // k-steps of Sᵀ
   constexpr int NDT = DH / 32;                // 32-row dh tiles of Oᵀ
   constexpr int CPR = RB / 16;                // 16-byte chunks per row
@@ -202,7 +203,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   constexpr int LPW = LPU / WPU;              // a wave's loads per unit request
   constexpr int PAIR = 2 * LPW;               // a wave's loads of one (K, V) request pair
   static_assert(LPW >= 1, "every wave loads part of a unit");
-  static_assert(stream_lds_bytes<DH, NS, RG>() <= 160 * 1024, "LDS of a CU");
+  static_assert(stream_lds_bytes<DH, NS, RG, KMAX>() <= 160 * 1024, "LDS of a CU");
   static_assert((4 * NDT) % NS == 0, "output groups per stream");
   static_assert(!B8 || RPL <= kBlockSize / 2, "with 8-token blocks a load lies in one block");
   constexpr int VB = B8 ? 4 : 2;              // validity bits per tile: 8- or 16-key pieces

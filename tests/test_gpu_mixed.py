@@ -16,9 +16,23 @@ from gpu_helpers import device, new_pools
 pytestmark = pytest.mark.gpu
 
 # PKV_MIXED: "one" runs the appends, the decodes and the prefill in one
-# launch (when the prefill takes the key-stream kernel); "two", the default,
-# the decode launch with the appends followed by the prefill launch
-LAUNCHES = ["one", "two"]
+# launch (when the prefill takes the key-stream kernel); "pair" the same with
+# four-wave workgroups, a prefill tile and a decode unit sharing each CU;
+# "two", the default, the decode launch with the appends followed by the
+# prefill launch
+LAUNCHES = ["one", "pair", "two"]
+
+
+def _same(launches, got, ref):
+    """Outputs of the mixed step against the separate calls': bit-identical,
+    except in the paired form, whose prefill runs two key streams instead of
+    four and whose decodes run four waves instead of eight (other summation
+    orders of the same sums)."""
+    if launches == "pair":
+        assert got.shape == ref.shape
+        assert got.numel() == 0 or (got - ref).abs().max().item() <= 1e-4
+    else:
+        assert torch.equal(got, ref)
 
 
 def _bf16(shape, gen, dev):
@@ -133,8 +147,8 @@ def test_mixed_step_matches_separate_calls(hq, hkv, dh, pt, prefill_kernel, laun
     torch.cuda.synchronize()
     assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
-    assert torch.equal(mp, rp)
-    assert torch.equal(md, rd)
+    _same(launches, mp, rp)
+    _same(launches, md, rd)
     _oracle_check(c, mp, md)
 
 
@@ -158,8 +172,8 @@ def test_mixed_step_at_block_sizes_8_32_and_64(bs, prefill_kernel, launches, mon
     torch.cuda.synchronize()
     assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
-    assert torch.equal(mp, rp)
-    assert torch.equal(md, rd)
+    _same(launches, mp, rp)
+    _same(launches, md, rd)
     _oracle_check(c, mp, md)
 
 
@@ -177,7 +191,7 @@ def test_mixed_step_chunks_only_and_decodes_only(launches, monkeypatch):
     assert md.numel() == 0
     assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
-    assert torch.equal(mp, rp)
+    _same(launches, mp, rp)
     _oracle_check(c, mp, None)
     # decodes only
     c = _case(dev, [], [3, 300, 4095], 32, 8, 128, seed=6)
@@ -188,8 +202,26 @@ def test_mixed_step_chunks_only_and_decodes_only(launches, monkeypatch):
     assert mp.numel() == 0
     assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
     assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
-    assert torch.equal(md, rd)
+    _same(launches, md, rd)
     _oracle_check(c, None, md)
+
+
+def test_paired_step_with_long_decode_partitions_falls_back(monkeypatch):
+    """PKV_MIXED=pair with decodes whose partitions exceed the four-wave
+    workgroup's 4096 tokens: the step takes two launches, bit-identical to
+    the separate calls."""
+    monkeypatch.setenv("PKV_MIXED", "pair")
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
+    dev = device()
+    c = _case(dev, [(40, 100)], [8000, 20], 32, 8, 128, seed=8)
+    ref, mix = _clone(c["cache"]), _clone(c["cache"])
+    rp, rd = _separate(c, ref, 8192)
+    mp, md = _mixed(c, mix, 8192)
+    torch.cuda.synchronize()
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mp, rp)
+    assert torch.equal(md, rd)
+    _oracle_check(c, mp, md)
 
 
 def test_shared_prefix_step_with_sharers_decoding():
