@@ -316,23 +316,24 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * The chunk sequences' new K/V are appended and their chunks attend causally
  * (as pkv_kv_append_paged followed by pkv_attn_prefill_chunk), and every
  * decode sequence appends its token and attends (as pkv_attn_decode_append).
- * Two launches on the stream instead of three: the decode kernel, whose
- * last workgroups write the chunks' tokens, then the prefill kernel (a third,
- * the split-KV reduce, when the decodes use more than one partition). With
- * the environment variable PKV_MIXED=one, and when the prefill takes the
- * key-stream kernel's 64-row form on blocks of 16 tokens or more, the
- * appends, decodes and prefill run as one launch:
- * the prefill workgroups, last in the grid, wait on a per-call counter until
- * the appending workgroups, first in the grid, have published the chunks'
- * tokens (a library-owned table of 1024 such counters per GPU, so at most
- * 1024 of these calls may be in flight on one GPU). Either way the pool
- * bytes and both outputs are bit-identical to the separate calls'. With
- * PKV_MIXED=pair (same conditions, and decode partitions of at most 4096
- * tokens) the one launch uses four-wave workgroups, two per compute unit,
- * so that each unit runs a prefill tile beside a decode workgroup: the pool
- * bytes are bit-identical, the outputs equal the separate calls' up to the
+ * By default, when the prefill takes the key-stream kernel's 64-row form on
+ * blocks of 16 tokens or more and the decode partitions hold at most 4096
+ * tokens, all of it is one launch of four-wave workgroups, two per compute
+ * unit: first the workgroups appending the chunks' tokens, then the chunks'
+ * prefill query tiles (one per unit in the first round of dispatch), then
+ * the decodes, which run beside them; a prefill wave waits on a per-call
+ * counter for the appends only before it requests its first tile holding
+ * chunk keys (a library-owned table of 1024 such counters per GPU, so at
+ * most 1024 of these calls may be in flight on one GPU). The pool bytes are
+ * bit-identical to the separate calls', the outputs equal theirs up to the
  * summation order (two key streams instead of four; four decode waves
- * instead of eight).
+ * instead of eight). Otherwise, or with the environment variable
+ * PKV_MIXED=two, two launches: the decode kernel, whose last workgroups
+ * write the chunks' tokens, then the prefill kernel; PKV_MIXED=one: one
+ * launch of eight-wave workgroups (appends, decodes, then the prefill
+ * waiting for the appends). Both are bit-identical to the separate calls in
+ * pool bytes and outputs. In every form the split-KV reduce follows as a
+ * launch of its own when the decodes use more than one partition.
  *   chunks:  see pkv_chunk_batch; num_seqs may be 0
  *   decodes: see pkv_decode_batch; batch may be 0
  * BF16 cache and inputs, block_size 8, 16, 32 or 64, the matrix-core decode whatever

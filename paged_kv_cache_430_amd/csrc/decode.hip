@@ -1245,6 +1245,22 @@ __device__ __forceinline__ void mixed_wait_appends(unsigned* sync, uint32_t n_ap
   __syncthreads();
 }
 
+// The paired form's prefill waves wait for the appends only before their
+// first request of a tile that holds chunk keys (the prefix before it is in
+// the pool already): each wave polls, then acquires at agent scope.
+struct AppendGate {
+  static constexpr bool kActive = true;
+  unsigned* sync;
+  uint32_t n_app;
+  __device__ void wait() const {
+    for (int spins = 0; spins < kMixedMaxSpins; ++spins) {
+      if (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_app) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+};
+
 // A prefill workgroup is done; the last of n_pf returns the slot to zero.
 __device__ __forceinline__ void mixed_prefill_done(unsigned* sync, uint32_t n_app, uint32_t n_pf) {
   __syncthreads();
@@ -1321,8 +1337,8 @@ __global__ __launch_bounds__(kPairWaves * kWave, 2) void mixed_pair_kernel(Kerne
   }
   const uint32_t pid = flat - m.n_app_pad;
   if (pid >= m.n_pf) return;
-  mixed_wait_appends(sync, m.n_app);
-  prefill_stream_body<DH, 2, 2, false, kPairPrefillKmax>(pa, lds, xcd_logical_index(pid, m.n_pf));
+  prefill_stream_body<DH, 2, 2, false, kPairPrefillKmax>(pa, lds, xcd_logical_index(pid, m.n_pf),
+                                                         AppendGate{sync, m.n_app});
   mixed_prefill_done(sync, m.n_app, m.n_pf);
 }
 

@@ -582,15 +582,20 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     dp.x_seqs = chunks->num_seqs;
     dp.x_max_q = chunks->max_q_len;
     dp.new_dtype = PKV_BF16;
-    // PKV_MIXED=one: appends, decodes and prefill in one launch, when the
-    // prefill takes the key-stream kernel. Two launches (the decodes with the
-    // appends, then the prefill) are the default: the one-launch step was
-    // measured about 1% slower on the shared-prefix workload (a compute unit
-    // holds one workgroup of either kind, so one grid saves only the kernel
-    // boundary, and its prefill waits on the appends).
+    // One launch, paired (the default where it applies): four-wave
+    // workgroups, a prefill tile and a decode workgroup on every CU, the
+    // prefill waiting for the appends only where it reaches the chunk's own
+    // keys (the shared-prefix step, a 512-token chunk on 2048 cached tokens
+    // and 64 decodes: 80.0-80.8 us against 88.3-88.4 for two launches).
+    // It needs the key-stream prefill's 64-row form on blocks of 16 tokens or
+    // more and decode partitions of at most 4096 tokens. PKV_MIXED=two: two
+    // launches (the decode launch with the appends, then the prefill),
+    // bit-identical to the separate calls; PKV_MIXED=one: one launch of
+    // eight-wave workgroups (the prefill after the decodes).
     const char* menv = getenv("PKV_MIXED");
+    const bool two = menv && strcmp(menv, "two") == 0;
     const bool one = menv && strcmp(menv, "one") == 0;
-    const bool pair = menv && strcmp(menv, "pair") == 0 && dp.part_tokens <= 64 * 16 * 4;
+    const bool pair = !two && !one && dp.part_tokens <= 64 * 16 * 4;
     if ((one || pair) && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
       return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
   }

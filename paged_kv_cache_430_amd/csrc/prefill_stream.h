@@ -181,13 +181,22 @@ constexpr int stream_lds_bytes() {
   return KV > MERGE ? KV : MERGE;
 }
 
+// A condition a key stream waits for before it requests its first tile that
+// holds one of the chunk's own keys (their K/V written by the same launch):
+// none here; a mixed step's one-launch form passes its own.
+struct NoGate {
+  static constexpr bool kActive = false;
+  __device__ void wait() const {}
+};
+
 // The kernel's work for logical workgroup L (see xcd_logical_index), on RG·NS
 // waves (8; or 4, two streams of two row groups, for a workgroup that shares
 // its CU with another) and stream_lds_bytes<DH, NS, RG, KMAX>() bytes of LDS
 // at `lds`. B8: pools of 8-token blocks; a 16-row unit is then the rows of
 // table entries 2u and 2u+1, and each of its loads reads from one of the two.
-template <int DH, int NS, int RG = 2, bool B8 = false, int KMAX = StreamShape<RG>::KMAX>
-__device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds, uint32_t L) {
+template <int DH, int NS, int RG = 2, bool B8 = false, int KMAX = StreamShape<RG>::KMAX, class Gate = NoGate>
+__device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds, uint32_t L,
+                                                    const Gate& gate = Gate{}) {
   static_assert(NS == StreamShape<RG>::NS || (NS == 2 && RG == 2), "NS streams of RG row groups: 8 or 4 waves");
   constexpr int NW = RG * NS;                 // waves: (stream, row group)
   constexpr int RB = DH * 2;                  // bytes of one key row of one head
@@ -541,10 +550,20 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   // pair j+RK−3 for iteration j).
   int vq = 0;
   Ent ea, eb;
+  bool gated = !Gate::kActive;   // the gate's wait is behind this wave (or there is none)
+  auto gate_tile = [&](int t) {  // before the wave's first request of a tile holding chunk keys
+    if constexpr (Gate::kActive) {
+      if (!gated && (stream + NS * t) * kSTile + kSTile - 1 >= base_pos) {
+        gate.wait();
+        gated = true;
+      }
+    }
+  };
   {
     Ent e[RK - 1];
 #pragma unroll
     for (int t = 0; t < RK - 1; ++t) {
+      gate_tile(t);
       vq |= vbits(t) << (VB * (t + 1));         // as at iteration −1: bits VB·i … for tile i−1
       e[t] = take_entry(t);
       issue_req(false, make_req(e[t], false, t));
@@ -583,6 +602,7 @@ __device__ __forceinline__ void prefill_stream_body(const SArgs& a, uint8_t* lds
   auto prepare_next = [&](int j) {
     pend_v = make_req(ea, true, j + RK - 2);
     const int t = j + RK;
+    gate_tile(t);
     const int nb = vbits(t);
     const Ent e = take_entry(t);
     pend_k = make_req(e, false, t);
