@@ -22,8 +22,9 @@ sample of the same batch on this host.
 --workload selects other decode workloads (same kind of line);
 `shared-prefix-mixed`: one mixed step of the shared-prefix workload — a causal
 512-token prefill chunk on a 2048-token cache plus 64 single-token decodes,
-run as pkv_attn_mixed_step — whose line reports the prefill chunk against the
-bf16 MFMA peak and the decodes against HBM; `prefill-chunk`: one chunk alone
+run as pkv_attn_mixed_step (ms_per_step; PKV_MIXED picks its form) — whose
+line also reports the chunk and the decodes, each timed as its own call,
+against the bf16 MFMA peak and HBM; `prefill-chunk`: one chunk alone
 (--chunk queries on --prefix tokens); `swap`: blocks to pinned host memory
 and back; `prefix-index`: the host prefix-cache index; `read-ceiling`: the GPU's
 streaming-read rate for the decode's 4 KiB tiles, in order and scattered;
@@ -697,8 +698,11 @@ def run_mixed(args, dev):
                    "sharers": m.n_share, "decodes": n_dec,
                    "sharers_decoding": m.n_share - 1 if args.sharers_decode else 0,
                    "decode_ctx_mean": float(np.mean(S["dec_ctx"])) + 1.0,
-                   "step": ("append launch + prefill + decode" if args.unfused else
-                            "pkv_attn_mixed_step: decode launch that also appends the chunk, then the prefill")},
+                   "step": ("append launch + prefill + decode" if args.unfused else {
+                       "two": "pkv_attn_mixed_step: decode launch that also appends the chunk, then the prefill",
+                       "one": "pkv_attn_mixed_step: one launch of eight-wave workgroups (appends, decodes, prefill)",
+                   }.get(os.environ.get("PKV_MIXED"), "pkv_attn_mixed_step: one launch, a prefill tile beside a "
+                                                       "decode workgroup on every CU (four-wave workgroups)"))},
         "prefill_us": stats_us(p_ms),
         "prefill_flops": flops,
         "decode_us": stats_us(d_ms),
@@ -706,7 +710,7 @@ def run_mixed(args, dev):
         "decode_bytes": d_bytes,
         "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel", "flops_per_launch": flops},
+                     "kernel": "prefill_stream_kernel (the chunk as its own call)", "flops_per_launch": flops},
         "decode_roofline": {"bound": "hbm", "achieved": round(d_bytes / (d_avg * 1e-3) / 1e9, 2),
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(d_bytes / (d_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
