@@ -17,16 +17,21 @@ namespace pkv {
 
 // Key-stream form (the tile kernel): a workgroup of eight waves, two per SIMD,
 // owns 32·RG query rows (GW ≤ 4 heads of one KV group × 32·RG/GW queries),
-// RG = 2 or 4. Wave w takes row group w % RG (32 rows) of key stream w / RG:
-// stream s of the NS = 8/RG streams scores the 32-key tiles s, s+NS, …, and
-// the RG waves of a stream share each tile through LDS (with RG = 4 a tile
-// feeds twice the products per byte loaded). Two waves per SIMD let one
-// wave's vector work, waits and loads run while the other's products occupy
-// the matrix core. Per tile:
+// RG = 2, 4 or 8. Wave w takes row group w % RG (32 rows) of key stream
+// w / RG: stream s of the NS = 8/RG streams scores the 32-key tiles s, s+NS,
+// …, and the RG waves of a stream share each tile through LDS (with RG = 4 a
+// tile feeds twice the products per byte loaded, with RG = 8 four times).
+// Two waves per SIMD let one wave's vector work, waits and loads run while
+// the other's products occupy the matrix core. (The mixed step's paired
+// launch runs a four-wave form, NS = 2 and RG = 2 with rings capped at 80
+// KiB, so that a decode workgroup fits on the same CU; it also passes a gate
+// that each wave waits on before its first tile holding the chunk's own
+// keys.) Per tile:
 //   * K and V reach LDS through LDS-direct buffer loads (no registers): one
 //     1 KiB load writes 16 bytes per lane in lane order, so a lane's global
 //     address decides which chunk of which row lands where. The waves of a
-//     stream load the tile's two 16-row units (RG/2 waves each). Rows past
+//     stream load the tile's two 16-row units (RG/2 waves each; with 8-token
+//     blocks a unit's two halves come from two table entries). Rows past
 //     the last key the workgroup sees, and blocks outside the pool, read as
 //     zeros (and their scores are masked). Unit addresses come from a per-lane table built
 //     once per 32 tiles; the loads of a tile are spread between the products
