@@ -206,6 +206,44 @@ def test_mixed_step_chunks_only_and_decodes_only(launches, monkeypatch):
     _oracle_check(c, None, md)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_mixed_step_seeded_shapes(seed, monkeypatch):
+    """Random mixed steps (head layout, head dim, block size, 1-3 chunks on
+    prefixes of 0-1500 tokens, 0-12 decodes of 0-2000 cached tokens, the
+    partition size) with the key-stream prefill, so that the default takes
+    the paired one launch wherever it applies: pool bytes bit-identical to the
+    separate calls', outputs within 1e-4 of theirs and within 2e-3 of the
+    oracle; the two-launch form bit-identical."""
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
+    rng = np.random.default_rng(9100 + seed)
+    hq, hkv = [(32, 8), (16, 2), (8, 8), (32, 1), (64, 8), (48, 4)][int(rng.integers(6))]
+    dh = [64, 128][int(rng.integers(2))]
+    bs = [16, 32, 64, 8][seed % 4]
+    chunks = [(int(rng.integers(0, 1501)), int(rng.integers(1, 301))) for _ in range(int(rng.integers(1, 4)))]
+    dec_ctx = [int(t) for t in rng.integers(0, 2001, int(rng.integers(0, 13)))]
+    pt = [0, 48, 256][int(rng.integers(3))]
+    print(f"seed {seed}: {hq}/{hkv} dh{dh} bs{bs} chunks {chunks} decodes {dec_ctx} pt {pt}", flush=True)
+    dev = device()
+    c = _case(dev, chunks, dec_ctx, hq, hkv, dh, seed=9100 + seed, bs=bs)
+    ref = _clone(c["cache"])
+    rp, rd = _separate(c, ref, pt)
+    for launches in ("default", "two"):
+        if launches == "default":
+            monkeypatch.delenv("PKV_MIXED", raising=False)
+        else:
+            monkeypatch.setenv("PKV_MIXED", launches)
+        mix = _clone(c["cache"])
+        mp, md = _mixed(c, mix, pt)
+        torch.cuda.synchronize()
+        assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16)), launches
+        assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16)), launches
+        form = "pair" if launches == "default" else launches
+        _same(form, mp, rp)
+        if rd is not None:
+            _same(form, md, rd)
+        _oracle_check(c, mp, md if rd is not None else None)
+
+
 def test_paired_step_with_long_decode_partitions_falls_back(monkeypatch):
     """PKV_MIXED=pair with decodes whose partitions exceed the four-wave
     workgroup's 4096 tokens: the step takes two launches, bit-identical to
