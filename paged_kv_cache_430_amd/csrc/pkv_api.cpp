@@ -595,7 +595,7 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     const char* menv = getenv("PKV_MIXED");
     const bool two = menv && strcmp(menv, "two") == 0;
     const bool one = menv && strcmp(menv, "one") == 0;
-    const bool pair = !two && !one && dp.part_tokens <= 64 * 16 * 4;
+    const bool pair = !two && !one && dp.part_tokens <= kMixedPairMaxPartition;
     if ((one || pair) && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
       return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
   }
