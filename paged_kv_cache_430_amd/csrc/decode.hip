@@ -1309,7 +1309,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void mixed_step_kernel(Ker
 constexpr int kPairWaves = 4;
 constexpr int kPairPrefillKmax = 3;
 constexpr int kPairExtraTokens = 16;
-static_assert(kMixedPairMaxPartition == 64 * kBlockSize * kPairWaves, "a wave's table covers 64 units");
+constexpr int kPairMaxPartition = 64 * kBlockSize * kPairWaves;
 
 template <int DH>
 constexpr int mixed_pair_lds_bytes() {
@@ -1500,7 +1500,7 @@ hipError_t launch_mixed_dh(const DecodeParams& dp, const PrefillParams& pp, bool
 hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s) {
   if (dp.kernel != kDecodeMatrix || dp.cache.dtype != kBF16 || pp.num_seqs == 0 || pp.max_q_len == 0)
     return hipErrorInvalidValue;
-  if (pair && dp.batch > 0 && dp.part_tokens > kMixedPairMaxPartition) return hipErrorInvalidValue;
+  if (pair && dp.batch > 0 && dp.part_tokens > kPairMaxPartition) return hipErrorInvalidValue;
   return dp.cache.head_dim == 64 ? launch_mixed_dh<64>(dp, pp, pair, s) : launch_mixed_dh<128>(dp, pp, pair, s);
 }
 

@@ -131,7 +131,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // each (decode partitions of at most 4096 tokens).
 hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s);
 // the paired form's four-wave decode workgroups cover partitions of at most
-// this many tokens (64 16-row units per wave)
+// this many tokens (64 16-row units per wave; launch_mixed_one refuses more)
 constexpr int kMixedPairMaxPartition = 64 * 16 * 4;
 // The key-stream tile kernel: rows = 64 query rows per workgroup in four key
 // streams of two 32-row waves, or 128 rows in two streams of four (see
