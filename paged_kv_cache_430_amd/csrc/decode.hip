@@ -1308,7 +1308,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 1) void mixed_step_kernel(Ker
 // per wave).
 constexpr int kPairWaves = 4;
 constexpr int kPairPrefillKmax = 3;
-constexpr int kPairExtraTokens = 16;
+constexpr int kPairExtraTokens = 16;   // tokens per append workgroup (4 measured slower: more L2 write-backs)
 constexpr int kPairMaxPartition = 64 * kBlockSize * kPairWaves;
 
 template <int DH>
