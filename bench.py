@@ -105,6 +105,9 @@ def parse():
                             "read-ceiling", "mfma-ceiling", "append", "allocator"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
+    p.add_argument("--mixed-chunk", type=int, default=512,
+                   help="shared-prefix-mixed: tokens of S0's chunk (512 is the workload; smaller chunks take "
+                        "the prefill's column form)")
     p.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
                    help="tokens per pool block for the B=32 and T=8192 decode workloads and prefill-chunk")
@@ -525,10 +528,10 @@ def _host_libs():
 # mixed chunked prefill + decode with a shared prefix
 # ---------------------------------------------------------------------------
 
-def make_mixed_setup(dev, sharers_decode=False):
+def make_mixed_setup(dev, sharers_decode=False, chunk=512):
     """Blocks come from the library's allocator with the workload's seeded free
     order: 16 sequences share the prefix blocks (refcount 16) and own their
-    private blocks; S0 reserves its 512-token chunk; 64 decode sequences hold
+    private blocks; S0 reserves its chunk (512 tokens unless asked otherwise); 64 decode sequences hold
     their context plus the step's token. With sharers_decode the other 15
     sharers also decode: each reserves a private block for its token at
     position 2048 and joins the decode batch after the 64."""
@@ -538,7 +541,7 @@ def make_mixed_setup(dev, sharers_decode=False):
     import paged_kv_cache_430_amd as pkv
     import workloads
 
-    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=sharers_decode)
+    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=sharers_decode, chunk=chunk)
     bs, hkv, dh = 16, m.hkv, m.head_dim
     alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
     kp = torch.full((m.num_blocks, hkv, bs, dh), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -605,7 +608,7 @@ def run_mixed(args, dev):
 
     import paged_kv_cache_430_amd as pkv
 
-    S = make_mixed_setup(dev, args.sharers_decode)
+    S = make_mixed_setup(dev, args.sharers_decode, getattr(args, "mixed_chunk", 512))
     m = S["m"]
     hq, hkv, dh = m.hq, m.hkv, m.head_dim
     n_dec = len(S["dec_ctx"])
@@ -681,7 +684,7 @@ def run_mixed(args, dev):
     d_bytes = decode_bytes(S["dec_ctx"] + 1, hq, hkv, dh, 2, 2, False)
     p_tflops = flops / (p_avg * 1e-3) / 1e12
     line = {
-        "metric": f"mixed step: causal 512-token prefill chunk TFLOP/s (bf16 MFMA) + {n_dec} decodes, shared prefix",
+        "metric": f"mixed step: causal {m.chunk}-token prefill chunk TFLOP/s (bf16 MFMA) + {n_dec} decodes, shared prefix",
         "value": round(p_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

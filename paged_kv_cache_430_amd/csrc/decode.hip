@@ -1342,6 +1342,33 @@ __global__ __launch_bounds__(kPairWaves * kWave, 2) void mixed_pair_kernel(Kerne
   mixed_prefill_done(sync, m.n_app, m.n_pf);
 }
 
+// The one launch for small chunks, whose prefill takes the column form (the
+// decode body with (query head, query) columns): appends, decodes, then the
+// chunks' query blocks, all eight-wave workgroups of the same body, so the
+// query blocks fill the decodes' ragged tail. The query blocks wait for the
+// appends as the eight-wave form's prefill does (they are last in the grid:
+// the appends are done by then). Bit-identical to the separate calls.
+template <int DH>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void mixed_cols_kernel(KernelArgs a, KernelArgs ca,
+                                                                          MixedLayout m) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<kBF16, DH, kDecodeWaves>()];
+  unsigned* sync = mixed_sync[m.slot];
+  const uint32_t flat = flat_block_id();
+  if (flat < m.n_app) {
+    extra_append<kBF16, DH, kDecodeWaves * kWave>(a, (int)flat);
+    mixed_append_done(sync);
+    return;
+  }
+  if (flat < m.n_app + m.n_dec_pad) {
+    const uint32_t id = flat - m.n_app;
+    if (id < m.n_dec) decode_mfma_body<kBF16, DH, kDecodeWaves, true, false>(a, lds, id, m.n_dec);
+    return;
+  }
+  mixed_wait_appends(sync, m.n_app);
+  decode_mfma_body<kBF16, DH, kDecodeWaves, false, false, true>(ca, lds, flat - m.n_app - m.n_dec_pad, m.n_pf);
+  mixed_prefill_done(sync, m.n_app, m.n_pf);
+}
+
 // Lanes per K row: 4 keeps the score reduction to two DPP steps and one
 // exponential per lane and head; eight heads per workgroup take 8 so that
 // their q slices fit in fewer registers.
@@ -1409,6 +1436,38 @@ int decode_heads_per_wg(int group, int kernel) {
 }
 
 namespace {
+
+// The column form's arguments (the prefill on the decode body); *n: its
+// workgroups. False when the call does not fit the form.
+bool make_cols_args(const PrefillParams& p, KernelArgs* out, size_t* n) {
+  const int hkv = p.cache.num_kv_heads, group = p.num_q_heads / hkv;
+  const int hg = prefill_cols_heads(group);
+  const int64_t keys = (int64_t)p.max_blocks * p.cache.block_size;
+  if (keys > kPrefillColsMaxKeys || p.cache.block_size < kBlockSize || p.cache.dtype != kBF16) return false;
+  KernelArgs a = {};
+  a.kc = static_cast<uint8_t*>(p.cache.k);
+  a.vc = static_cast<uint8_t*>(p.cache.v);
+  a.q = p.q;
+  a.block_tables = p.block_tables;
+  a.seq_lens = p.seq_lens;
+  a.out = p.out;
+  a.num_blocks = p.cache.num_blocks;
+  a.hkv = hkv;
+  a.hq = p.num_q_heads;
+  a.max_blocks = p.max_blocks;
+  a.max_seq_len = (int)keys;
+  a.part_tokens = (int)keys;
+  a.num_parts = 1;
+  a.num_chunks = group / hg;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.block_size = p.cache.block_size;
+  a.q_start = p.q_start;
+  a.p_hg_shift = __builtin_ctz((unsigned)hg);
+  a.p_nqb = (p.max_q_len + kMfmaHeads / hg - 1) / (kMfmaHeads / hg);
+  *out = a;
+  *n = (size_t)p.num_seqs * hkv * a.num_chunks * a.p_nqb;
+  return true;
+}
 
 KernelArgs make_kernel_args(const DecodeParams& p) {
   const int group = p.num_q_heads / p.cache.num_kv_heads;
@@ -1504,6 +1563,37 @@ hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, boo
   return dp.cache.head_dim == 64 ? launch_mixed_dh<64>(dp, pp, pair, s) : launch_mixed_dh<128>(dp, pp, pair, s);
 }
 
+size_t prefill_cols_workgroups(const PrefillParams& p) {
+  KernelArgs a;
+  size_t n = 0;
+  return make_cols_args(p, &a, &n) ? n : 0;
+}
+
+hipError_t launch_mixed_cols(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s) {
+  if (dp.kernel != kDecodeMatrix || dp.cache.dtype != kBF16 || pp.num_seqs == 0 || pp.max_q_len == 0)
+    return hipErrorInvalidValue;
+  KernelArgs ca;
+  size_t n_pf = 0;
+  if (!make_cols_args(pp, &ca, &n_pf)) return hipErrorInvalidValue;
+  const KernelArgs a = make_kernel_args(dp);
+  MixedLayout m{};
+  m.n_app = (uint32_t)a.x_wgs;
+  m.n_dec = dp.batch > 0 ? (uint32_t)((size_t)dp.batch * dp.cache.num_kv_heads * a.num_chunks * dp.num_parts) : 0u;
+  m.n_dec_pad = (m.n_dec + 7) / 8 * 8;      // keeps the query blocks' ids aligned to the XCD rotation
+  m.n_pf = (uint32_t)n_pf;
+  m.slot = g_mixed_slot.fetch_add(1, std::memory_order_relaxed) % kMixedSlots;
+  const size_t n = (size_t)m.n_app + m.n_dec_pad + m.n_pf;
+  if (n > (size_t)INT32_MAX) return hipErrorInvalidValue;
+  const dim3 block(kDecodeWaves * kWave);
+  if (dp.cache.head_dim == 64)
+    hipLaunchKernelGGL(mixed_cols_kernel<64>, dim3((unsigned)n), block, 0, s, a, ca, m);
+  else
+    hipLaunchKernelGGL(mixed_cols_kernel<128>, dim3((unsigned)n), block, 0, s, a, ca, m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || dp.batch == 0 || dp.num_parts <= 1) return e;
+  return launch_merge(dp, s);
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (p.batch == 0 && p.x_seqs == 0) return hipSuccess;
   const int group = p.num_q_heads / p.cache.num_kv_heads;
@@ -1555,32 +1645,9 @@ hipError_t decode_static_scratch(void** ptr) {
 
 hipError_t launch_prefill_cols(const PrefillParams& p, hipStream_t s) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
-  const int hkv = p.cache.num_kv_heads, group = p.num_q_heads / hkv;
-  const int hg = prefill_cols_heads(group);
-  const int64_t keys = (int64_t)p.max_blocks * p.cache.block_size;
-  if (keys > kPrefillColsMaxKeys || p.cache.block_size < kBlockSize || p.cache.dtype != kBF16)
-    return hipErrorInvalidValue;
-  KernelArgs a = {};
-  a.kc = static_cast<uint8_t*>(p.cache.k);
-  a.vc = static_cast<uint8_t*>(p.cache.v);
-  a.q = p.q;
-  a.block_tables = p.block_tables;
-  a.seq_lens = p.seq_lens;
-  a.out = p.out;
-  a.num_blocks = p.cache.num_blocks;
-  a.hkv = hkv;
-  a.hq = p.num_q_heads;
-  a.max_blocks = p.max_blocks;
-  a.max_seq_len = (int)keys;
-  a.part_tokens = (int)keys;
-  a.num_parts = 1;
-  a.num_chunks = group / hg;
-  a.scale_log2 = p.scale * 1.4426950408889634f;
-  a.block_size = p.cache.block_size;
-  a.q_start = p.q_start;
-  a.p_hg_shift = __builtin_ctz((unsigned)hg);
-  a.p_nqb = (p.max_q_len + kMfmaHeads / hg - 1) / (kMfmaHeads / hg);
-  const size_t n = (size_t)p.num_seqs * hkv * a.num_chunks * a.p_nqb;
+  KernelArgs a;
+  size_t n = 0;
+  if (!make_cols_args(p, &a, &n)) return hipErrorInvalidValue;
   const dim3 block(kDecodeWaves * kWave);
   if (p.cache.head_dim == 64)
     hipLaunchKernelGGL((decode_mfma_kernel<kBF16, 64, kDecodeWaves, false, false, true>), dim3((unsigned)n), block, 0,

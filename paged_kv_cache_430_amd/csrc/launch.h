@@ -130,6 +130,13 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // prefill tiles dispatched before the decodes so that each CU runs one of
 // each (decode partitions of at most 4096 tokens).
 hipError_t launch_mixed_one(const DecodeParams& dp, const PrefillParams& pp, bool pair, hipStream_t s);
+// The mixed step in one launch when the prefill takes the column form (small
+// chunks): appends, decodes, then the chunks' query blocks on the decode
+// body; bit-identical to the separate calls.
+hipError_t launch_mixed_cols(const DecodeParams& dp, const PrefillParams& pp, hipStream_t s);
+// the column form's workgroups (query blocks) for a prefill call; 0 when the
+// call does not fit the form
+size_t prefill_cols_workgroups(const PrefillParams& p);
 // the paired form's four-wave decode workgroups cover partitions of at most
 // this many tokens (64 16-row units per wave; launch_mixed_one refuses more)
 constexpr int kMixedPairMaxPartition = 64 * 16 * 4;

@@ -596,8 +596,19 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     const bool two = menv && strcmp(menv, "two") == 0;
     const bool one = menv && strcmp(menv, "one") == 0;
     const bool pair = !two && !one && dp.part_tokens <= kMixedPairMaxPartition;
-    if ((one || pair) && prefill_kernel_for(pp) == kPrefillStream && c.block_size >= 16)
+    const PrefillKernel pk = prefill_kernel_for(pp);
+    if ((one || pair) && pk == kPrefillStream && c.block_size >= 16)
       return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
+    // Small chunks (the column form): appends, decodes and the chunks' query
+    // blocks in one launch of the decode body, unless PKV_MIXED=two, while
+    // the query blocks are fewer than the compute units, so that they fit in
+    // the decodes' ragged tail (the shared-prefix step with a C-token chunk:
+    // C=32 53.4-53.8 us against 64.5-65.2 for two launches, C=64 -8%, C=96
+    // -4.5%; at C=128, 256 query blocks, 1-3% slower).
+    if (!two && pk == kPrefillColumns) {
+      const size_t qblocks = prefill_cols_workgroups(pp);
+      if (qblocks > 0 && qblocks < (size_t)kComputeUnits) return hip_status(launch_mixed_cols(dp, pp, s), fn);
+    }
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);
   if (pp.num_seqs == 0) return PKV_OK;

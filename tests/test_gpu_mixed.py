@@ -244,6 +244,32 @@ def test_mixed_step_seeded_shapes(seed, monkeypatch):
         _oracle_check(c, mp, md if rd is not None else None)
 
 
+@pytest.mark.parametrize("hq,hkv,dh,pt", [(32, 8, 128, 0), (16, 2, 64, 48), (8, 8, 128, 0), (32, 1, 64, 256)])
+def test_small_chunk_step_in_one_launch(hq, hkv, dh, pt, monkeypatch):
+    """Chunks small enough for the prefill's column form, with fewer query
+    blocks than compute units: by default appends, decodes and the query
+    blocks run as one launch of the decode body, bit-identical to the
+    separate calls and to the two-launch form."""
+    monkeypatch.delenv("PKV_PREFILL_KERNEL", raising=False)
+    dev = device()
+    c = _case(dev, [(100, 20), (0, 9), (37, 3)], [0, 5, 300, 1023, 16], hq, hkv, dh, seed=hq + dh + pt)
+    ref = _clone(c["cache"])
+    rp, rd = _separate(c, ref, pt)
+    for launches in ("default", "two"):
+        if launches == "default":
+            monkeypatch.delenv("PKV_MIXED", raising=False)
+        else:
+            monkeypatch.setenv("PKV_MIXED", launches)
+        mix = _clone(c["cache"])
+        mp, md = _mixed(c, mix, pt)
+        torch.cuda.synchronize()
+        assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16)), launches
+        assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16)), launches
+        assert torch.equal(mp, rp), launches
+        assert torch.equal(md, rd), launches
+    _oracle_check(c, mp, md)
+
+
 def test_paired_step_with_long_decode_partitions_falls_back(monkeypatch):
     """PKV_MIXED=pair with decodes whose partitions exceed the four-wave
     workgroup's 4096 tokens: the step takes two launches, bit-identical to
