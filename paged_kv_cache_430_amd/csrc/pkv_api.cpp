@@ -599,15 +599,19 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     const PrefillKernel pk = prefill_kernel_for(pp);
     if ((one || pair) && pk == kPrefillStream && c.block_size >= 16)
       return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
-    // Small chunks (the column form): appends, decodes and the chunks' query
-    // blocks in one launch of the decode body, unless PKV_MIXED=two, while
-    // the query blocks are fewer than the compute units, so that they fit in
-    // the decodes' ragged tail (the shared-prefix step with a C-token chunk:
-    // C=32 53.4-53.8 us against 64.5-65.2 for two launches, C=64 -8%, C=96
-    // -4.5%; at C=128, 256 query blocks, 1-3% slower).
+    // Small chunks, where the prefill alone takes the column form. Fewer than
+    // 128 query blocks: appends, decodes and the query blocks in one launch of
+    // the decode body (they fit in the decodes' ragged tail). More: the
+    // paired launch with the key-stream tiles, whose idle CUs run the decodes
+    // (unless PKV_PREFILL_KERNEL names a kernel). Measured on the
+    // shared-prefix step with a C-token chunk (Hq=32, Hkv=8): C=32 53 us in
+    // the first form against 56.5 paired and 64.4 in two launches; C=64 60 /
+    // 59 / 66; C=128 63 paired against 68.7; C=192 65.4 against 86.8.
     if (!two && pk == kPrefillColumns) {
       const size_t qblocks = prefill_cols_workgroups(pp);
-      if (qblocks > 0 && qblocks < (size_t)kComputeUnits) return hip_status(launch_mixed_cols(dp, pp, s), fn);
+      if (qblocks > 0 && qblocks < 128) return hip_status(launch_mixed_cols(dp, pp, s), fn);
+      if (!one && dp.part_tokens <= kMixedPairMaxPartition && !getenv("PKV_PREFILL_KERNEL"))
+        return hip_status(launch_mixed_one(dp, pp, true, s), fn);
     }
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);

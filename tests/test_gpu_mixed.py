@@ -270,6 +270,36 @@ def test_small_chunk_step_in_one_launch(hq, hkv, dh, pt, monkeypatch):
     _oracle_check(c, mp, md)
 
 
+@pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (16, 2, 64)])
+def test_small_chunks_with_many_query_blocks_take_the_paired_launch(hq, hkv, dh, monkeypatch):
+    """Chunks whose prefill alone takes the column form, with 128 query blocks
+    or more: by default the step is the paired launch with the key-stream
+    tiles (pool bytes bit-identical to the separate calls, outputs within
+    1e-4 of theirs and 2e-3 of the oracle); PKV_PREFILL_KERNEL=columns keeps
+    the column form (two launches, bit-identical)."""
+    monkeypatch.delenv("PKV_PREFILL_KERNEL", raising=False)
+    monkeypatch.delenv("PKV_MIXED", raising=False)
+    dev = device()
+    c = _case(dev, [(200, 70), (0, 60), (513, 21)], [0, 7, 900, 2000], hq, hkv, dh, seed=hq * 5 + dh)
+    ref = _clone(c["cache"])
+    rp, rd = _separate(c, ref, 0)
+    mix = _clone(c["cache"])
+    mp, md = _mixed(c, mix, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mix.v.view(torch.int16), ref.v.view(torch.int16))
+    _same("pair", mp, rp)
+    _same("pair", md, rd)
+    _oracle_check(c, mp, md)
+    monkeypatch.setenv("PKV_PREFILL_KERNEL", "columns")
+    mix = _clone(c["cache"])
+    mp, md = _mixed(c, mix, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(mix.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(mp, rp)
+    assert torch.equal(md, rd)
+
+
 def test_paired_step_with_long_decode_partitions_falls_back(monkeypatch):
     """PKV_MIXED=pair with decodes whose partitions exceed the four-wave
     workgroup's 4096 tokens: the step takes two launches, bit-identical to
