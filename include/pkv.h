@@ -327,11 +327,13 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * most 1024 of these calls may be in flight on one GPU). The pool bytes are
  * bit-identical to the separate calls', the outputs equal theirs up to the
  * summation order (two key streams instead of four; four decode waves
- * instead of eight). When the prefill takes the column form (small chunks)
- * and its query blocks are fewer than the compute units, all of it is one
- * launch of the decode body (appends, decodes, then the query blocks, which
- * wait for the appends), bit-identical to the separate calls. Otherwise, or
- * with the environment variable PKV_MIXED=two, two launches: the decode kernel, whose last workgroups
+ * instead of eight). When the prefill alone would take the column form
+ * (small chunks): with fewer than 128 query blocks all of it is one launch of
+ * the decode body (appends, decodes, then the query blocks, which wait for
+ * the appends), bit-identical to the separate calls; with more, the paired
+ * launch above, its prefill on the key-stream tiles (unless
+ * PKV_PREFILL_KERNEL names a kernel). Otherwise, or with the environment
+ * variable PKV_MIXED=two, two launches: the decode kernel, whose last workgroups
  * write the chunks' tokens, then the prefill kernel; PKV_MIXED=one: one
  * launch of eight-wave workgroups (appends, decodes, then the prefill
  * waiting for the appends). Both are bit-identical to the separate calls in
