@@ -105,6 +105,8 @@ def parse():
                             "read-ceiling", "mfma-ceiling", "append", "allocator"])
     p.add_argument("--prefix", type=int, default=2048, help="prefill-chunk: cached tokens before the chunk")
     p.add_argument("--chunk", type=int, default=128, help="prefill-chunk: queries in the chunk")
+    p.add_argument("--mixed-decodes", type=int, default=64,
+                   help="shared-prefix-mixed: decode sequences beside the chunk (64 is the workload)")
     p.add_argument("--mixed-chunk", type=int, default=512,
                    help="shared-prefix-mixed: tokens of S0's chunk (512 is the workload; smaller chunks take "
                         "the prefill's column form)")
@@ -528,7 +530,7 @@ def _host_libs():
 # mixed chunked prefill + decode with a shared prefix
 # ---------------------------------------------------------------------------
 
-def make_mixed_setup(dev, sharers_decode=False, chunk=512):
+def make_mixed_setup(dev, sharers_decode=False, chunk=512, n_decode=64):
     """Blocks come from the library's allocator with the workload's seeded free
     order: 16 sequences share the prefix blocks (refcount 16) and own their
     private blocks; S0 reserves its chunk (512 tokens unless asked otherwise); 64 decode sequences hold
@@ -541,7 +543,7 @@ def make_mixed_setup(dev, sharers_decode=False, chunk=512):
     import paged_kv_cache_430_amd as pkv
     import workloads
 
-    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=sharers_decode, chunk=chunk)
+    m = workloads.shared_prefix_mixed(device=dev, sharers_decode=sharers_decode, chunk=chunk, n_decode=n_decode)
     bs, hkv, dh = 16, m.hkv, m.head_dim
     alloc = pkv.BlockAllocator(m.num_blocks, bs, free_order=m.free_order)
     kp = torch.full((m.num_blocks, hkv, bs, dh), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -608,7 +610,7 @@ def run_mixed(args, dev):
 
     import paged_kv_cache_430_amd as pkv
 
-    S = make_mixed_setup(dev, args.sharers_decode, getattr(args, "mixed_chunk", 512))
+    S = make_mixed_setup(dev, args.sharers_decode, getattr(args, "mixed_chunk", 512), getattr(args, "mixed_decodes", 64))
     m = S["m"]
     hq, hkv, dh = m.hq, m.hkv, m.head_dim
     n_dec = len(S["dec_ctx"])

@@ -592,10 +592,19 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     // launches (the decode launch with the appends, then the prefill),
     // bit-identical to the separate calls; PKV_MIXED=one: one launch of
     // eight-wave workgroups (the prefill after the decodes).
+    // The paired launch pays only beside enough decode work (its prefill
+    // tiles run at one wave per SIMD): by default it needs at least 2^20
+    // (sequence, KV head, position) rows in the decodes' tables, as 64
+    // decodes of up to 2048 tokens at Hkv=8 give. Measured on the shared-
+    // prefix step (decode contexts up to 2048) against two launches: 32
+    // decodes +3% (C=512) and +8% (C=128), one decode +20%; 64 decodes -9.5%
+    // and -11%. PKV_MIXED=pair forces it.
     const char* menv = getenv("PKV_MIXED");
     const bool two = menv && strcmp(menv, "two") == 0;
     const bool one = menv && strcmp(menv, "one") == 0;
-    const bool pair = !two && !one && dp.part_tokens <= kMixedPairMaxPartition;
+    const bool force_pair = menv && strcmp(menv, "pair") == 0;
+    const bool enough_decodes = (int64_t)dp.batch * dp.max_seq_len * c.num_kv_heads >= ((int64_t)1 << 20);
+    const bool pair = !two && !one && dp.part_tokens <= kMixedPairMaxPartition && (force_pair || enough_decodes);
     const PrefillKernel pk = prefill_kernel_for(pp);
     if ((one || pair) && pk == kPrefillStream && c.block_size >= 16)
       return hip_status(launch_mixed_one(dp, pp, pair, s), fn);
@@ -610,8 +619,7 @@ PKV_API int pkv_attn_mixed_step(const pkv_cache* cache, int32_t num_q_heads, flo
     if (!two && pk == kPrefillColumns) {
       const size_t qblocks = prefill_cols_workgroups(pp);
       if (qblocks > 0 && qblocks < 128) return hip_status(launch_mixed_cols(dp, pp, s), fn);
-      if (!one && dp.part_tokens <= kMixedPairMaxPartition && !getenv("PKV_PREFILL_KERNEL"))
-        return hip_status(launch_mixed_one(dp, pp, true, s), fn);
+      if (pair && !getenv("PKV_PREFILL_KERNEL")) return hip_status(launch_mixed_one(dp, pp, true, s), fn);
     }
   }
   if (hipError_t e = launch_decode(dp, s)) return hip_status(e, fn);

@@ -210,10 +210,10 @@ def test_mixed_step_chunks_only_and_decodes_only(launches, monkeypatch):
 def test_mixed_step_seeded_shapes(seed, monkeypatch):
     """Random mixed steps (head layout, head dim, block size, 1-3 chunks on
     prefixes of 0-1500 tokens, 0-12 decodes of 0-2000 cached tokens, the
-    partition size) with the key-stream prefill, so that the default takes
-    the paired one launch wherever it applies: pool bytes bit-identical to the
-    separate calls', outputs within 1e-4 of theirs and within 2e-3 of the
-    oracle; the two-launch form bit-identical."""
+    partition size) with the key-stream prefill, in the paired one launch
+    (PKV_MIXED=pair, wherever it applies), the default and two launches:
+    pool bytes bit-identical to the separate calls', outputs within 1e-4 of
+    theirs and within 2e-3 of the oracle; two launches bit-identical."""
     monkeypatch.setenv("PKV_PREFILL_KERNEL", "tiles")
     rng = np.random.default_rng(9100 + seed)
     hq, hkv = [(32, 8), (16, 2), (8, 8), (32, 1), (64, 8), (48, 4)][int(rng.integers(6))]
@@ -227,7 +227,7 @@ def test_mixed_step_seeded_shapes(seed, monkeypatch):
     c = _case(dev, chunks, dec_ctx, hq, hkv, dh, seed=9100 + seed, bs=bs)
     ref = _clone(c["cache"])
     rp, rd = _separate(c, ref, pt)
-    for launches in ("default", "two"):
+    for launches in ("pair", "default", "two"):
         if launches == "default":
             monkeypatch.delenv("PKV_MIXED", raising=False)
         else:
@@ -273,12 +273,13 @@ def test_small_chunk_step_in_one_launch(hq, hkv, dh, pt, monkeypatch):
 @pytest.mark.parametrize("hq,hkv,dh", [(32, 8, 128), (16, 2, 64)])
 def test_small_chunks_with_many_query_blocks_take_the_paired_launch(hq, hkv, dh, monkeypatch):
     """Chunks whose prefill alone takes the column form, with 128 query blocks
-    or more: by default the step is the paired launch with the key-stream
-    tiles (pool bytes bit-identical to the separate calls, outputs within
-    1e-4 of theirs and 2e-3 of the oracle); PKV_PREFILL_KERNEL=columns keeps
-    the column form (two launches, bit-identical)."""
+    or more: the paired launch (PKV_MIXED=pair; the default beside enough
+    decode work) runs their prefill on the key-stream tiles (pool bytes
+    bit-identical to the separate calls, outputs within 1e-4 of theirs and
+    2e-3 of the oracle); PKV_PREFILL_KERNEL=columns keeps the column form
+    (two launches, bit-identical)."""
     monkeypatch.delenv("PKV_PREFILL_KERNEL", raising=False)
-    monkeypatch.delenv("PKV_MIXED", raising=False)
+    monkeypatch.setenv("PKV_MIXED", "pair")
     dev = device()
     c = _case(dev, [(200, 70), (0, 60), (513, 21)], [0, 7, 900, 2000], hq, hkv, dh, seed=hq * 5 + dh)
     ref = _clone(c["cache"])
