@@ -317,8 +317,10 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * (as pkv_kv_append_paged followed by pkv_attn_prefill_chunk), and every
  * decode sequence appends its token and attends (as pkv_attn_decode_append).
  * By default, when the prefill takes the key-stream kernel's 64-row form on
- * blocks of 16 tokens or more and the decode partitions hold at most 4096
- * tokens, all of it is one launch of four-wave workgroups, two per compute
+ * blocks of 16 tokens or more, the decode partitions hold at most 4096
+ * tokens and the decodes are large enough to run beside it (batch ·
+ * max_seq_len · Hkv ≥ 2^20; PKV_MIXED=pair forces it), all of it is one
+ * launch of four-wave workgroups, two per compute
  * unit: first the workgroups appending the chunks' tokens, then the chunks'
  * prefill query tiles (one per unit in the first round of dispatch), then
  * the decodes, which run beside them; a prefill wave waits on a per-call
