@@ -333,8 +333,8 @@ PKV_API int pkv_attn_prefill_chunk(const pkv_cache* cache, const void* q, int32_
  * (small chunks): with fewer than 128 query blocks all of it is one launch of
  * the decode body (appends, decodes, then the query blocks, which wait for
  * the appends), bit-identical to the separate calls; with more, the paired
- * launch above, its prefill on the key-stream tiles (unless
- * PKV_PREFILL_KERNEL names a kernel). Otherwise, or with the environment
+ * launch above where its conditions hold, its prefill on the key-stream
+ * tiles (unless PKV_PREFILL_KERNEL names a kernel). Otherwise, or with the environment
  * variable PKV_MIXED=two, two launches: the decode kernel, whose last workgroups
  * write the chunks' tokens, then the prefill kernel; PKV_MIXED=one: one
  * launch of eight-wave workgroups (appends, decodes, then the prefill
